@@ -1,0 +1,513 @@
+"""CPU oracle for the KVarN 2-bit KV-cache quantizer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module. The library path never calls it; it shares no code, header,
+table or constant generator with the HIP kernels.
+
+It is a plain, slow, fp64 NumPy implementation of what the KVarN pages define,
+written step by step in the pages' order. Citations name the page and its
+section:
+
+  [RP]  researchpapers.dev, "KVarN: calibration-free 2-bit KV cache quantization"
+  [FB]  friday-blog, "Memory breakout: KVarN ..." (sections 1-5)
+  [AP]  ai-paper-analysis, "KVarN: variance normalization lets 2-bit KV cache ..."
+        (sections 1-8, subsections 3.1 and 3.2, the error equation in section 2)
+  [CP]  chatpaper.ai abstract (Spanish and English)
+
+Method ([AP] section 3; [RP] "how KVarN does it"; [CP] abstract):
+  1. rotate each K/V token along head_dim by a randomized Hadamard matrix H with
+     H H^T = I ([AP] 3.1);
+  2. VarN: alternately bring every token's variance and every channel's variance
+     to 1, repeated 2-3 times, Sinkhorn-Knopp style ([AP] 3.2 steps 1-3);
+  3. keep the scales (grouped, restorable at dequantization) and quantize
+     uniformly to 2 bits, 4 levels ([AP] 3.2 and the closing remark of 3.2);
+  4. decode attention reads the cache with Q rotated by the same H, so that
+     Q K^T is unchanged ([AP] 3.1).
+
+Where the pages leave a step open, the reading taken is stated at the function
+that implements it (fp16 canonical input, second-moment "variance", Sylvester
+ordering of H, fp16 stored scales, per-channel min/max grid over a group of G
+tokens, round-half-to-even, fp16 tail of unrotated tokens, tile record layout).
+
+Pinned by tests/test_oracle_*.py against closed forms, invariants, brute force
+and library routines (see each test's docstring).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------- format constants
+# Written out here on purpose: the oracle includes nothing from the library.
+MAGIC = 0x4E52564B          # bytes 'K','V','R','N' little-endian
+VERSION = 1
+FLAG_CAPACITY = 1           # an append found the cache full (token dropped)
+FLAG_SATURATED = 2          # an input value was outside the fp16 range and was saturated
+FLAG_SCALE_CLAMPED = 4      # a stored scale hit the fp16 clamp range
+Q_PREROTATED = 1            # attention flag: the query is already rotated (q H)
+FP16_MAX = 65504.0
+SCALE_MIN = 2.0 ** -14      # smallest normal fp16; lower clamp of r and c
+HEADER_FIXED = 512          # len[] starts here
+SIGMA_OFFSET = 64
+FLAGS_OFFSET = 36
+
+
+def align256(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
+# ----------------------------------------------------------------------------- number formats
+def fp16_round(x) -> np.ndarray:
+    """Round to IEEE binary16, round-half-to-even, subnormals kept, overflow to inf."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def fp16_saturate(x) -> tuple[np.ndarray, np.ndarray]:
+    """Clamp to [-65504, 65504], then round to fp16. Returns (values, was_clamped)."""
+    x = np.asarray(x, dtype=np.float64)
+    clamped = np.abs(x) > FP16_MAX
+    return fp16_round(np.clip(x, -FP16_MAX, FP16_MAX)), clamped
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def canonicalize(bits) -> tuple[np.ndarray, bool]:
+    """Reading: every K/V input token is first brought to fp16, the dtype of the
+    decode-time tail, so a token quantizes identically whether it arrives in a
+    prefill or through the tail. bf16 -> fp16 is exact for 2^-14 <= |x| <= 65504;
+    smaller values round (RNE) to the fp16 subnormal grid, larger ones saturate."""
+    v, clamped = fp16_saturate(bf16_to_f64(bits))
+    return v, bool(clamped.any())
+
+
+def fp16_bits(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def fp16_from_bits(b) -> np.ndarray:
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- rotation ([AP] 3.1)
+def hadamard_sylvester(d: int) -> np.ndarray:
+    """Reading of "Hadamard matrix": Sylvester ordering, H[i, j] = (-1)^popcount(i & j)."""
+    i = np.arange(d)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    pc = np.zeros_like(bits)
+    while bits.any():
+        pc += bits & 1
+        bits >>= 1
+    return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
+
+
+def rotation_matrix(sigma) -> np.ndarray:
+    """H_D = diag(sigma) H_syl / sqrt(D): the randomized Hadamard matrix, H_D H_D^T = I."""
+    s = np.asarray(sigma, dtype=np.float64)
+    d = s.shape[0]
+    return s[:, None] * hadamard_sylvester(d) / np.sqrt(d)
+
+
+def rotate(x, sigma) -> np.ndarray:
+    """Row vectors x (last axis = head_dim) times H_D."""
+    return np.asarray(x, dtype=np.float64) @ rotation_matrix(sigma)
+
+
+def unrotate(w, sigma) -> np.ndarray:
+    """Inverse rotation: w H_D^T."""
+    return np.asarray(w, dtype=np.float64) @ rotation_matrix(sigma).T
+
+
+# ----------------------------------------------------------------------------- VarN ([AP] 3.2)
+def varn(w, n_it: int) -> tuple[np.ndarray, np.ndarray]:
+    """Dual-axis variance normalization of tile(s) w[..., G, D]; returns (r[..., G], c[..., D]).
+
+    [AP] 3.2: (1) normalize along the token axis so each token's variance is 1,
+    (2) normalize along the channel axis so each channel's variance is 1,
+    (3) repeat 2-3 times so both axes approach 1 together (Sinkhorn-Knopp like).
+    Readings: "variance" is the mean square (second moment about zero, divide by N);
+    the scales are cumulative and multiplicative, Y = W / (r_t c_j), starting at 1;
+    one iteration is a token pass followed by a channel pass; a pass leaves the
+    scale unchanged where the mean square is 0 (all-zero row or column).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    r = np.ones(w.shape[:-1])
+    c = np.ones(w.shape[:-2] + w.shape[-1:])
+    for _ in range(n_it):
+        y = w / (r[..., :, None] * c[..., None, :])
+        ms_t = np.mean(y * y, axis=-1)                       # token axis: one value per token
+        r = np.where(ms_t > 0, r * np.sqrt(ms_t), r)
+        y = w / (r[..., :, None] * c[..., None, :])
+        ms_j = np.mean(y * y, axis=-2)                       # channel axis: one value per channel
+        c = np.where(ms_j > 0, c * np.sqrt(ms_j), c)
+    return r, c
+
+
+def stored_scales(r, c) -> tuple[np.ndarray, np.ndarray, bool]:
+    """The scales are kept so dequantization can undo them ([AP] 3.2, grouped scales).
+    Reading: stored as fp16 (RNE), clamped to [2^-14, 65504]."""
+    r = np.asarray(r, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    rc = np.clip(r, SCALE_MIN, FP16_MAX)
+    cc = np.clip(c, SCALE_MIN, FP16_MAX)
+    clamped = bool((rc != r).any() or (cc != c).any())
+    return fp16_round(rc), fp16_round(cc), clamped
+
+
+def normalize(w, r16, c16) -> np.ndarray:
+    """Y = W / (r16 (x) c16), with the stored scales so r16 c16 Y recovers W exactly."""
+    return np.asarray(w, dtype=np.float64) / (np.asarray(r16)[..., :, None] * np.asarray(c16)[..., None, :])
+
+
+# ----------------------------------------------------------------------------- 2-bit grid
+def grid(y) -> tuple[np.ndarray, np.ndarray, bool]:
+    """Uniform 2-bit grid, one per channel over the tile's G tokens ([AP] 3.2: one scale
+    per group of 32 or 64 entries; [RP]: a scale shared across tokens is what outlier
+    tokens stretch). Reading: asymmetric min/max, levels z + s*{0,1,2,3},
+    s = (max - min)/3, both stored as fp16 (RNE, saturating)."""
+    y = np.asarray(y, dtype=np.float64)
+    mn = y.min(axis=-2)
+    mx = y.max(axis=-2)
+    s16, sat_s = fp16_saturate((mx - mn) / 3.0)
+    z16, sat_z = fp16_saturate(mn)
+    return s16, z16, bool(sat_s.any() or sat_z.any())
+
+
+def codes(y, s16, z16) -> np.ndarray:
+    """q = clamp(round_half_even((Y - z) / s), 0, 3); q = 0 in a channel whose s is 0."""
+    y = np.asarray(y, dtype=np.float64)
+    s = np.asarray(s16)[..., None, :]
+    z = np.asarray(z16)[..., None, :]
+    safe = np.where(s == 0, 1.0, s)
+    u = (y - z) / safe
+    q = np.clip(np.rint(u), 0, 3)               # np.rint rounds half to even
+    return np.where(s == 0, 0, q).astype(np.uint8)
+
+
+def pre_rounding(y, s16, z16) -> np.ndarray:
+    """u = (Y - z)/s, the value whose rounding gives the code (for edge-band checks)."""
+    s = np.asarray(s16)[..., None, :]
+    z = np.asarray(z16)[..., None, :]
+    return (np.asarray(y) - z) / np.where(s == 0, 1.0, s)
+
+
+def quantize_tile(w, n_it: int) -> dict:
+    """Rotated tile(s) w[..., G, D] -> stored scales, grid, codes (steps of [AP] 3.2)."""
+    r, c = varn(w, n_it)
+    r16, c16, clamped = stored_scales(r, c)
+    y = normalize(w, r16, c16)
+    s16, z16, sat = grid(y)
+    q = codes(y, s16, z16)
+    return dict(r=r, c=c, r16=r16, c16=c16, y=y, s16=s16, z16=z16, q=q,
+                flags=(FLAG_SCALE_CLAMPED if (clamped or sat) else 0))
+
+
+def dequantize_tile(q, r16, c16, s16, z16) -> np.ndarray:
+    """W_hat = r16_t c16_j (z16_j + s16_j q_tj): undo the grid and both scales."""
+    q = np.asarray(q, dtype=np.float64)
+    return (np.asarray(r16)[..., :, None] * np.asarray(c16)[..., None, :]
+            * (np.asarray(z16)[..., None, :] + np.asarray(s16)[..., None, :] * q))
+
+
+# ----------------------------------------------------------------------------- tile record (format v1)
+def record_bytes(g: int, d: int) -> int:
+    """codes G*D/4 | r fp16[G] | c fp16[D] | s fp16[D] | z fp16[D]."""
+    return g * d // 4 + 2 * g + 6 * d
+
+
+def pack_codes(q, stream: int) -> np.ndarray:
+    """Four 2-bit codes per byte, low bits first.
+    K (stream 0): code (t, j) in byte t*D/4 + j//4 at bit 2*(j%4)   (channels fastest);
+    V (stream 1): code (t, j) in byte j*G/4 + t//4 at bit 2*(t%4)   (tokens fastest)."""
+    q = np.asarray(q, dtype=np.uint8)
+    g, d = q.shape
+    if stream == 0:
+        qq = q.reshape(g, d // 4, 4)                       # [t][j//4][j%4]
+    else:
+        qq = q.T.reshape(d, g // 4, 4)                     # [j][t//4][t%4]
+    b = (qq[..., 0] | (qq[..., 1] << 2) | (qq[..., 2] << 4) | (qq[..., 3] << 6)).astype(np.uint8)
+    return b.reshape(-1)
+
+
+def unpack_codes(b, g: int, d: int, stream: int) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    parts = np.stack([(b >> (2 * m)) & 3 for m in range(4)], axis=-1)
+    if stream == 0:
+        return parts.reshape(g, d).astype(np.uint8)
+    return parts.reshape(d, g).T.astype(np.uint8)
+
+
+def pack_record(q, r16, c16, s16, z16, stream: int) -> np.ndarray:
+    return np.concatenate([pack_codes(q, stream),
+                           fp16_bits(r16).view(np.uint8), fp16_bits(c16).view(np.uint8),
+                           fp16_bits(s16).view(np.uint8), fp16_bits(z16).view(np.uint8)])
+
+
+def unpack_record(rec, g: int, d: int, stream: int) -> dict:
+    rec = np.asarray(rec, dtype=np.uint8)
+    n = g * d // 4
+    f = lambda off, k: fp16_from_bits(rec[off:off + 2 * k].view(np.uint16))  # noqa: E731
+    return dict(q=unpack_codes(rec[:n], g, d, stream), r16=f(n, g), c16=f(n + 2 * g, d),
+                s16=f(n + 2 * g + 2 * d, d), z16=f(n + 2 * g + 4 * d, d))
+
+
+# ----------------------------------------------------------------------------- cache buffer (format v1)
+class Geom:
+    """batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits."""
+
+    def __init__(self, batch, num_kv_heads, head_dim=128, capacity=0, group=32, varn_iters=3, bits=2):
+        self.batch, self.num_kv_heads, self.head_dim = batch, num_kv_heads, head_dim
+        self.capacity, self.group, self.varn_iters, self.bits = capacity, group, varn_iters, bits
+
+    def as_tuple(self):
+        return (self.batch, self.num_kv_heads, self.head_dim, self.capacity, self.group,
+                self.varn_iters, self.bits)
+
+    # layout
+    @property
+    def tr(self):
+        return record_bytes(self.group, self.head_dim)
+
+    @property
+    def header(self):
+        return align256(HEADER_FIXED + 8 * self.batch * self.num_kv_heads)
+
+    @property
+    def tiles_per_seq(self):
+        return self.capacity // self.group
+
+    @property
+    def tail_offset(self):
+        return self.header + align256(self.batch * self.num_kv_heads * self.tiles_per_seq * 2 * self.tr)
+
+    @property
+    def total(self):
+        return self.tail_offset + align256(self.batch * self.num_kv_heads * 2 * self.group * self.head_dim * 2)
+
+    def record_offset(self, b, h, tile, s):
+        return self.header + ((((b * self.num_kv_heads + h) * self.tiles_per_seq + tile) * 2 + s) * self.tr)
+
+    def tail_slot_offset(self, b, h, s, slot):
+        return self.tail_offset + ((((b * self.num_kv_heads + h) * 2 + s) * self.group + slot)
+                                   * self.head_dim * 2)
+
+
+class Cache:
+    """A layer's cache as the byte buffer the library keeps in device memory."""
+
+    def __init__(self, geom: Geom, sigma):
+        self.g = geom
+        self.buf = np.zeros(geom.total, dtype=np.uint8)
+        hdr = self.buf[:geom.header]
+        hdr[0:4].view(np.uint32)[0] = MAGIC
+        hdr[4:8].view(np.uint32)[0] = VERSION
+        hdr[8:36].view(np.int32)[:] = geom.as_tuple()
+        hdr[SIGMA_OFFSET:SIGMA_OFFSET + geom.head_dim].view(np.int8)[:] = np.asarray(sigma, np.int8)
+
+    # header fields
+    @property
+    def sigma(self):
+        d = self.g.head_dim
+        return self.buf[SIGMA_OFFSET:SIGMA_OFFSET + d].view(np.int8).astype(np.float64)
+
+    @property
+    def flags(self) -> int:
+        return int(self.buf[FLAGS_OFFSET:FLAGS_OFFSET + 4].view(np.uint32)[0])
+
+    def or_flags(self, f: int):
+        self.buf[FLAGS_OFFSET:FLAGS_OFFSET + 4].view(np.uint32)[0] |= np.uint32(f)
+
+    @property
+    def lens(self) -> np.ndarray:
+        n = self.g.batch * self.g.num_kv_heads * 2
+        return self.buf[HEADER_FIXED:HEADER_FIXED + 4 * n].view(np.int32).reshape(
+            self.g.batch, self.g.num_kv_heads, 2)
+
+    # records and tail
+    def record(self, b, h, tile, s) -> np.ndarray:
+        o = self.g.record_offset(b, h, tile, s)
+        return self.buf[o:o + self.g.tr]
+
+    def tail(self, b, h, s) -> np.ndarray:
+        """fp16 view [G][D] of one tail."""
+        o = self.g.tail_slot_offset(b, h, s, 0)
+        n = self.g.group * self.g.head_dim * 2
+        return self.buf[o:o + n].view(np.float16).reshape(self.g.group, self.g.head_dim)
+
+    def defined_mask(self) -> np.ndarray:
+        """Bytes whose content the format defines given the current lengths."""
+        g = self.g
+        m = np.zeros(g.total, dtype=bool)
+        m[:g.header] = True
+        for b in range(g.batch):
+            for h in range(g.num_kv_heads):
+                for s in range(2):
+                    n = int(self.lens[b, h, s])
+                    for tile in range(n // g.group):
+                        o = g.record_offset(b, h, tile, s)
+                        m[o:o + g.tr] = True
+                    o = g.tail_slot_offset(b, h, s, 0)
+                    m[o:o + (n % g.group) * g.head_dim * 2] = True
+        return m
+
+
+def _quantize_stream(x, sigma, g: Geom, stream: int):
+    """x[..., n_tiles*G, D] canonical fp64 tokens -> (records [..., n_tiles, TR], flags)."""
+    lead = x.shape[:-2]
+    nt = x.shape[-2] // g.group
+    w = rotate(x, sigma).reshape(lead + (nt, g.group, g.head_dim))
+    t = quantize_tile(w, g.varn_iters)
+    recs = np.zeros(lead + (nt, g.tr), dtype=np.uint8)
+    for idx in np.ndindex(*(lead + (nt,))):
+        recs[idx] = pack_record(t["q"][idx], t["r16"][idx], t["c16"][idx], t["s16"][idx],
+                                t["z16"][idx], stream)
+    return recs, t["flags"]
+
+
+def quantize_prefill(cache: Cache, k_bits, v_bits, num_tokens: int) -> None:
+    """Reset the cache to hold tokens [0, T) of k, v (bf16 bits [B][T][Hkv][D]).
+    Full groups of G tokens become tile records; the last T mod G tokens stay in
+    the fp16 tail, unrotated ([AP] 3.2: the current group is still being filled)."""
+    g = cache.g
+    T = int(num_tokens)
+    assert 0 <= T <= g.capacity
+    nfull = T // g.group
+    for s, bits in enumerate((k_bits, v_bits)):
+        x, sat = canonicalize(np.asarray(bits)[:, :T])          # [B][T][Hkv][D]
+        if sat:
+            cache.or_flags(FLAG_SATURATED)
+        xt = np.transpose(x, (0, 2, 1, 3))                       # [B][Hkv][T][D]
+        if nfull:
+            recs, f = _quantize_stream(xt[:, :, :nfull * g.group], cache.sigma, g, s)
+            cache.or_flags(f)
+            for b in range(g.batch):
+                for h in range(g.num_kv_heads):
+                    for tile in range(nfull):
+                        cache.record(b, h, tile, s)[:] = recs[b, h, tile]
+        for b in range(g.batch):
+            for h in range(g.num_kv_heads):
+                tail = cache.tail(b, h, s)
+                for t in range(nfull * g.group, T):
+                    tail[t % g.group] = xt[b, h, t].astype(np.float16)
+    cache.lens[:] = T
+
+
+def append_decode(cache: Cache, k_bits, v_bits) -> None:
+    """Append one token per (batch, kv head) (bf16 bits [B][Hkv][D]) through the fp16 tail.
+    When a group of G fills, it is rotated, normalized and quantized into the next
+    tile record ([AP] 3.2: statistics of the current group are updated as tokens arrive)."""
+    g = cache.g
+    for s, bits in enumerate((k_bits, v_bits)):
+        x, sat = canonicalize(bits)                              # [B][Hkv][D]
+        if sat:
+            cache.or_flags(FLAG_SATURATED)
+        for b in range(g.batch):
+            for h in range(g.num_kv_heads):
+                pos = int(cache.lens[b, h, s])
+                if pos >= g.capacity:
+                    cache.or_flags(FLAG_CAPACITY)
+                    continue
+                tail = cache.tail(b, h, s)
+                tail[pos % g.group] = x[b, h].astype(np.float16)
+                if (pos + 1) % g.group == 0:
+                    tile_x = tail.astype(np.float64)[None]         # [1][G][D]
+                    recs, f = _quantize_stream(tile_x, cache.sigma, g, s)
+                    cache.or_flags(f)
+                    cache.record(b, h, (pos + 1) // g.group - 1, s)[:] = recs[0]
+                cache.lens[b, h, s] = pos + 1
+
+
+def stream_values(cache: Cache, b: int, h: int, s: int, rotated: bool = False) -> np.ndarray:
+    """All stored tokens of one stream, dequantized, in original space (fp64 [len][D]).
+    With rotated=True the tile tokens are returned in rotated space and tail tokens
+    are rotated too (used for checks that work in the rotated basis)."""
+    g = cache.g
+    n = int(cache.lens[b, h, s])
+    out = np.zeros((n, g.head_dim))
+    nfull = n // g.group
+    for tile in range(nfull):
+        u = unpack_record(cache.record(b, h, tile, s), g.group, g.head_dim, s)
+        w = dequantize_tile(u["q"], u["r16"], u["c16"], u["s16"], u["z16"])
+        out[tile * g.group:(tile + 1) * g.group] = w if rotated else unrotate(w, cache.sigma)
+    tail = cache.tail(b, h, s).astype(np.float64)
+    for t in range(nfull * g.group, n):
+        out[t] = rotate(tail[t % g.group], cache.sigma) if rotated else tail[t % g.group]
+    return out
+
+
+def dequantize(cache: Cache, max_tokens: int) -> tuple[np.ndarray, np.ndarray]:
+    """K_hat, V_hat as fp64 [B][max_tokens][Hkv][D]; rows at or past a sequence's length are 0.
+    Tile tokens: undo grid and scales, then rotate back by H_D^T ([AP] 3.2: the scaling
+    is restored at dequantization). Tail tokens are returned as stored."""
+    g = cache.g
+    outs = []
+    for s in range(2):
+        o = np.zeros((g.batch, max_tokens, g.num_kv_heads, g.head_dim))
+        for b in range(g.batch):
+            for h in range(g.num_kv_heads):
+                vals = stream_values(cache, b, h, s)[:max_tokens]
+                o[b, :vals.shape[0], h] = vals
+        outs.append(o)
+    return outs[0], outs[1]
+
+
+def attn_decode(cache: Cache, q_bits, num_q_heads: int, softmax_scale: float = 0.0,
+                flags: int = 0) -> np.ndarray:
+    """Single-query decode attention over the dequantized cache, by its definition:
+    l_t = scale * (q . k_hat_t), p = softmax(l), out = sum_t p_t v_hat_t  (fp64 [B][Hq][D]).
+    Query head g reads KV head g // (Hq / Hkv). Readings: scale defaults to 1/sqrt(D);
+    with Q_PREROTATED the given query is q H_D and is mapped back by H_D^T ([AP] 3.1:
+    (qH)(kH)^T = q k^T). An empty sequence gives 0."""
+    g = cache.g
+    d = g.head_dim
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
+    q = bf16_to_f64(q_bits)                                     # [B][Hq][D]
+    if flags & Q_PREROTATED:
+        q = unrotate(q, cache.sigma)
+    grp = num_q_heads // g.num_kv_heads
+    out = np.zeros((g.batch, num_q_heads, d))
+    for b in range(g.batch):
+        for h in range(g.num_kv_heads):
+            k = stream_values(cache, b, h, 0)
+            v = stream_values(cache, b, h, 1)
+            if k.shape[0] == 0:
+                continue
+            for gi in range(h * grp, (h + 1) * grp):
+                logits = scale * (k @ q[b, gi])
+                p = np.exp(logits - logits.max())
+                p /= p.sum()
+                out[b, gi] = p @ v
+    return out
+
+
+# ----------------------------------------------------------------------------- diagnostics ([AP] section 2)
+def error_split(x, xhat) -> tuple[np.ndarray, np.ndarray]:
+    """Magnitude and direction parts of eps = xhat - x ([AP] section 2, error equation):
+    E_M = (|xhat| - |x|) x/|x|,  E_D = |xhat| (xhat/|xhat| - x/|x|).
+    Conventions: |x| = 0 gives E_M = 0, E_D = xhat; |xhat| = 0 gives E_D = 0."""
+    x = np.asarray(x, dtype=np.float64)
+    xh = np.asarray(xhat, dtype=np.float64)
+    nx = np.linalg.norm(x, axis=-1, keepdims=True)
+    nxh = np.linalg.norm(xh, axis=-1, keepdims=True)
+    ux = np.where(nx > 0, x / np.where(nx > 0, nx, 1), 0.0)
+    uxh = np.where(nxh > 0, xh / np.where(nxh > 0, nxh, 1), 0.0)
+    e_m = np.where(nx > 0, (nxh - nx) * ux, 0.0)
+    e_d = np.where(nx > 0, np.where(nxh > 0, nxh * (uxh - ux), 0.0), xh)
+    return e_m, e_d
+
+
+def axis_mean_squares(y) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token and per-channel mean squares of a normalized tile y[..., G, D]."""
+    y = np.asarray(y, dtype=np.float64)
+    return np.mean(y * y, axis=-1), np.mean(y * y, axis=-2)
+
+
+def relative_token_error(x, xhat) -> np.ndarray:
+    """|xhat - x|^2 / |x|^2 per token (tokens with |x| = 0 give 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    num = np.sum((np.asarray(xhat) - x) ** 2, axis=-1)
+    den = np.sum(x * x, axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), 0.0)

@@ -1,0 +1,129 @@
+"""Pins of the oracle's 2-bit grid, rounding, exact scale recovery and record layout.
+
+Brute force: each code must be the nearest of the 4 levels z + s k (ties to even k).
+Recovery: the stored scales restore the pre-rounding tensor (ai-paper-analysis page,
+section 3.2: the grouped scales are undone at dequantization, nothing is lost).
+Layout: hand-computed bytes in tests/golden/layout_v1.txt.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import kvarn_ref as R
+from kv_cache_bit_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "layout_v1.txt")
+
+
+def brute_codes(y, s, z):
+    """argmin_k |z + s k - y| over k in {0,1,2,3}; exact ties go to the even k."""
+    g, d = y.shape
+    q = np.zeros((g, d), dtype=np.uint8)
+    for t in range(g):
+        for j in range(d):
+            if s[j] == 0:
+                continue
+            dist = [abs(z[j] + s[j] * k - y[t, j]) for k in range(4)]
+            best = min(dist)
+            ks = [k for k in range(4) if dist[k] == best]
+            q[t, j] = ks[0] if len(ks) == 1 else [k for k in ks if k % 2 == 0][0]
+    return q
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_codes_brute_force_random(seed):
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((8, 16)) * rng.uniform(0.1, 3, 16)
+    s, z, _ = R.grid(y)
+    assert np.array_equal(R.codes(y, s, z), brute_codes(y, s, z))
+
+
+def test_codes_exact_ties_and_clamp():
+    s = R.fp16_round(np.array([0.375, 1.25, 0.5, 2.0]))
+    z = R.fp16_round(np.array([-0.5, -2.0, 0.25, -3.0]))
+    # rows: u = 0.5, 1.5, 2.5 exactly (ties -> 0, 2, 2), then far below and far above the grid
+    u = np.array([0.5, 1.5, 2.5, -7.0, 11.0])
+    y = z[None, :] + s[None, :] * u[:, None]          # exact in fp64 (fp16 operands)
+    q = R.codes(y, s, z)
+    assert np.array_equal(q, brute_codes(y, s, z))
+    assert q[:, 0].tolist() == [0, 2, 2, 0, 3]
+
+
+def test_grid_min_and_max_hit_end_codes():
+    rng = np.random.default_rng(7)
+    y = rng.standard_normal((32, 128))
+    s, z, _ = R.grid(y)
+    q = R.codes(y, s, z)
+    assert np.all(q[y.argmin(axis=0), np.arange(128)] == 0)
+    assert np.all(q[y.argmax(axis=0), np.arange(128)] == 3)
+
+
+def test_exact_recovery_of_pre_rounding_tensor():
+    k, _ = synth.kv_host(0, 1, 256, 1)
+    s = synth.sign_vector(0)
+    w = R.rotate(R.canonicalize(k[0, :, 0])[0], s).reshape(8, 32, 128)
+    t = R.quantize_tile(w, 3)
+    u = R.pre_rounding(t["y"], t["s16"], t["z16"])
+    back = t["r16"][..., :, None] * t["c16"][..., None, :] * (t["z16"][..., None, :] + t["s16"][..., None, :] * u)
+    rms = np.sqrt(np.mean(w * w, axis=-1, keepdims=True))
+    assert np.abs(back - w).max() / rms.min() < 1e-12
+    # and the dequantized codes are within half a grid step of Y
+    deq = R.dequantize_tile(t["q"], t["r16"], t["c16"], t["s16"], t["z16"])
+    step = t["r16"][..., :, None] * t["c16"][..., None, :] * t["s16"][..., None, :]
+    assert np.all(np.abs(deq - w) <= 0.5 * step * (1 + 1e-9) + 1e-300)
+
+
+def _golden():
+    rows = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            head, vals = line.split(":")
+            rows[head.split()[0] + (head.split()[1] if head.startswith("OFFSETS") else "")] = vals.split()
+    return rows
+
+
+def test_golden_layout_bytes():
+    gold = _golden()
+    g, d = 32, 128
+    t = np.arange(g)[:, None]
+    j = np.arange(d)[None, :]
+    q = ((t + 3 * j) % 4).astype(np.uint8)
+    kb = R.pack_codes(q, 0)
+    vb = R.pack_codes(q, 1)
+    kvals = [int(x, 16) for x in gold["K"]]
+    vvals = [int(x, 16) for x in gold["V"]]
+    assert kb.shape == (1024,) and vb.shape == (1024,)
+    for tt in range(g):
+        assert np.all(kb[tt * 32:(tt + 1) * 32] == kvals[tt % 4])
+    for jj in range(d):
+        assert np.all(vb[jj * 8:(jj + 1) * 8] == vvals[jj % 4])
+    for stream in (0, 1):
+        assert np.array_equal(R.unpack_codes(R.pack_codes(q, stream), g, d, stream), q)
+
+
+@pytest.mark.parametrize("g", [32, 64])
+def test_golden_record_offsets(g):
+    gold = _golden()["OFFSETS" + str(g)]
+    offs = [int(x) for x in gold]
+    assert R.record_bytes(g, 128) == offs[-1]
+    rng = np.random.default_rng(g)
+    q = rng.integers(0, 4, (g, 128)).astype(np.uint8)
+    r = R.fp16_round(rng.uniform(0.5, 2, g))
+    c, s, z = (R.fp16_round(rng.uniform(-2, 2, 128)) for _ in range(3))
+    rec = R.pack_record(q, r, c, s, z, 1)
+    assert rec.shape == (offs[-1],)
+    assert np.array_equal(R.fp16_from_bits(rec[offs[1]:offs[2]].view(np.uint16)), r)
+    assert np.array_equal(R.fp16_from_bits(rec[offs[2]:offs[3]].view(np.uint16)), c)
+    assert np.array_equal(R.fp16_from_bits(rec[offs[3]:offs[4]].view(np.uint16)), s)
+    assert np.array_equal(R.fp16_from_bits(rec[offs[4]:offs[5]].view(np.uint16)), z)
+    u = R.unpack_record(rec, g, 128, 1)
+    assert np.array_equal(u["q"], q)
+
+
+def test_density_vs_bf16():
+    # bits per element including scales: 3.625 at G=32 and 2.875 at G=64
+    assert R.record_bytes(32, 128) * 8 / (32 * 128) == 3.625
+    assert R.record_bytes(64, 128) * 8 / (64 * 128) == 2.875
