@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the KVarN hot path on one MI355X.
+
+Headline (`value`): prefill quantization throughput in GB/s of bf16 input on the
+Llama-3.1-8B-shaped KV workload -- 32 layers x 8 KV heads x head_dim 128, 32768
+tokens, batch 1, group 32, 3 VarN iterations, 2 bits -- one step = the 32 layer
+caches quantized from 32 distinct input buffers resident in HBM. Beside it:
+  * roofline of the quantize kernel: algorithmic bytes per launch (bf16 in + tile
+    records out) over its average launch time measured with HIP events on the
+    launch stream, against the 8 TB/s HBM peak;
+  * decode: Phi-4-14B-shaped decode (40 layers x 10 KV heads, 40 query heads,
+    batch 32, 16384 prior tokens), tokens/s of the append + fused attention loop;
+  * cpu_baseline: the CPU oracle on a bounded sample of the same prefill workload.
+
+Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV quantize GB/s (bf16 in) & % of HBM peak; decode-append tokens/s at 1 GPU"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def record_bytes(g: int) -> int:
+    return g * 128 // 4 + 2 * g + 6 * 128
+
+
+def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32, n_it=3):
+    g = K.geom(1, H, T, G, n_it)
+    sig = synth.sign_vector(0)
+    log(f"prefill workload: {layers} layers x B=1 x T={T} x Hkv={H}, G={G}, iters={n_it}")
+    ks, vs, caches = [], [], []
+    for l in range(layers):
+        k, v = synth.kv_device(synth.sub_seed(2, l, 0), 1, T, H)
+        ks.append(k)
+        vs.append(v)
+        caches.append(K.alloc_cache(g, sig))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for l in range(layers):
+            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps * layers)]
+    t0 = time.perf_counter()
+    i = 0
+    for _ in range(steps):
+        for l in range(layers):
+            ev[i][0].record(stream)
+            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T, stream)
+            ev[i][1].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    bytes_in = 2 * 2 * T * H * 128                       # K and V, bf16
+    bytes_out = 2 * H * (T // G) * record_bytes(G)       # tile records
+    flags = K.kvarn_cache_flags(caches[0])
+    del ks, vs, caches
+    torch.cuda.empty_cache()
+    return dict(wall=wall, launch_ms=launch_ms, bytes_in=bytes_in, bytes_out=bytes_out, layers=layers,
+                T=T, H=H, G=G, n_it=n_it, flags=flags)
+
+
+def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40, T0=16384, cap=17408, G=32,
+                 n_it=3, pool=128):
+    g = K.geom(B, H, cap, G, n_it)
+    sig = synth.sign_vector(0)
+    log(f"decode workload: {layers} layers x B={B} x Hkv={H} x Hq={Hq}, {T0} prior tokens, {steps} timed steps")
+    k0, v0 = synth.kv_device(synth.sub_seed(4, 0, 0), B, T0, H)
+    caches = []
+    for l in range(layers):
+        c = K.alloc_cache(g, sig)
+        K.kvarn_quantize_prefill(g, c, k0, v0, T0)
+        caches.append(c)
+    del k0, v0
+    kp, vp = synth.kv_device(synth.sub_seed(4, 0, 1), B, pool, H)     # [B][pool][H][D]
+    kp = kp.transpose(0, 1).contiguous()                              # [pool][B][H][D]
+    vp = vp.transpose(0, 1).contiguous()
+    qp = torch.stack([synth.q_device(synth.sub_seed(4, 0, 2, s), B, Hq) for s in range(pool)])
+    ws, nws = K.alloc_workspace(g, Hq)
+    out = torch.empty(B, Hq, 128, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(s, ev=None):
+        for l in range(layers):
+            K.kvarn_append_decode(g, caches[l], kp[s % pool], vp[s % pool], stream)
+            if ev is not None:
+                ev[0].record(stream)
+            K.kvarn_attn_decode(g, caches[l], qp[s % pool], Hq, 0.0, 0, ws, nws, out, stream)
+            if ev is not None:
+                ev[1].record(stream)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(warmup + s, evs[s])   # one attention launch per step is timed with events
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    flags = K.kvarn_cache_flags(caches[0])
+    ctx_mid = T0 + warmup + steps // 2
+    # attention bytes per layer-step: K and V records of the full tiles + tail rows + q + out
+    nfull = ctx_mid // G
+    attn_bytes = B * H * (2 * nfull * record_bytes(G) + 2 * (ctx_mid % G) * 256) + B * Hq * (256 + 512)
+    del caches
+    torch.cuda.empty_cache()
+    return dict(wall=wall, steps=steps, B=B, layers=layers, attn_ms=attn_ms, attn_bytes=attn_bytes, flags=flags,
+                ctx_start=T0 + warmup, H=H, Hq=Hq)
+
+
+def cpu_baseline(synth, tokens):
+    """The oracle's prefill on layer 0 of the prefill workload, first `tokens` tokens (host cores)."""
+    import numpy as np
+    from oracle import kvarn_ref as R
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    H, G = 8, 32
+    k, v = synth.kv_host(synth.sub_seed(2, 0, 0), 1, tokens, H)
+    c = R.Cache(R.Geom(1, H, 128, tokens, G, 3, 2), synth.sign_vector(0))
+    t0 = time.perf_counter()
+    R.quantize_prefill(c, k, v, tokens)
+    dt = time.perf_counter() - t0
+    gbs = 2 * 2 * tokens * H * 128 / dt / 1e9
+    return dict(value=round(gbs, 5), unit="GB/s", cores=int(blas), kind="oracle",
+                sample=f"layer 0 of the prefill workload, {tokens} tokens x 8 KV heads x K and V "
+                       f"({2 * H * tokens // G} tiles), {dt:.1f} s; NumPy fp64, BLAS threads = cores")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=32)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the quantizer shards by KV head and sequence with no exchange, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cache_bit_amd import kvarn as K
+    from kv_cache_bit_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log("device", torch.cuda.get_device_name(0))
+    pf = bench_prefill(K, synth, torch, args.steps, args.warmup)
+    ms_step = pf["wall"] * 1e3 / args.steps
+    value = pf["layers"] * pf["bytes_in"] / (ms_step * 1e-3) / 1e9
+    total_gbs = pf["layers"] * (pf["bytes_in"] + pf["bytes_out"]) / (ms_step * 1e-3) / 1e9
+    lm = sorted(pf["launch_ms"])
+    avg_launch = sum(lm) / len(lm)
+    achieved = (pf["bytes_in"] + pf["bytes_out"]) / (avg_launch * 1e-3) / 1e9
+    log(f"prefill: {ms_step:.3f} ms/step, {value:.1f} GB/s bf16-in, {total_gbs:.1f} GB/s total; "
+        f"kernel avg {avg_launch * 1e3:.1f} us -> {achieved:.1f} GB/s")
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "llama3.1-8b-shaped KV prefill quantize", "layers": pf["layers"], "batch": 1,
+                   "tokens": pf["T"], "kv_heads": pf["H"], "head_dim": 128, "group": pf["G"],
+                   "varn_iters": pf["n_it"], "bits": 2, "input": "bf16, outlier channels x20, 5% lognormal tokens"},
+        "hbm_frac_step": round(total_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<1,false>", "bytes_per_launch": pf["bytes_in"] + pf["bytes_out"],
+                     "avg_launch_us": round(avg_launch * 1e3, 2), "median_launch_us": round(lm[len(lm) // 2] * 1e3, 2)},
+        "flags": pf["flags"],
+    }
+    if not args.no_decode:
+        dc = bench_decode(K, synth, torch, args.decode_steps)
+        tok_s = dc["B"] * dc["steps"] / dc["wall"]
+        am = sorted(dc["attn_ms"])
+        a_avg = sum(am) / len(am)
+        res["decode"] = {
+            "workload": "phi-4-14b-shaped decode: append + attn_decode", "tokens_per_s": round(tok_s, 1),
+            "ms_per_step": round(dc["wall"] * 1e3 / dc["steps"], 3), "steps_timed": dc["steps"],
+            "layers": dc["layers"], "batch": dc["B"], "kv_heads": dc["H"], "q_heads": dc["Hq"],
+            "context_at_start": dc["ctx_start"], "attn_avg_us": round(a_avg * 1e3, 2),
+            "attn_GBps": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9, 1),
+            "attn_frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "flags": dc["flags"]}
+        log(f"decode: {tok_s:.1f} tok/s, attn {a_avg * 1e3:.1f} us/layer-step")
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(synth, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * libkvarn -- KVarN 2-bit KV-cache quantizer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only. Device pointers are HIP device memory
+ * owned by the caller; `stream` is a hipStream_t passed as void*. The library
+ * never allocates, frees or synchronizes (except kvarn_cache_flags), keeps no
+ * global mutable state, and enqueues all work on the caller's stream.
+ *
+ * Method (KVarN pages): each K/V token is rotated along head_dim by a randomized
+ * Hadamard matrix H with H H^T = I (ai-paper-analysis page, section 3.1); VarN then
+ * alternates a token-axis and a channel-axis variance normalization 2-3 times,
+ * Sinkhorn-Knopp style, with grouped scales that dequantization undoes (section
+ * 3.2); the result is quantized uniformly to 2 bits (4 levels). Decode attention
+ * reads the cache with Q rotated by the same H so that Q K^T is unchanged
+ * (section 3.1).
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   H_D = diag(sigma) H_syl / sqrt(D), H_syl[i][j] = (-1)^popcount(i & j), sigma in {+1,-1}^D;
+ *   inputs are canonicalized bf16 -> fp16 (round-half-to-even, saturating at +-65504);
+ *   "variance" is the mean square; a tile is G consecutive tokens x D channels of
+ *   one (batch, kv head, stream); r (per token) and c (per channel) are stored as
+ *   fp16 clamped to [2^-14, 65504]; the 2-bit grid is per channel over the tile's
+ *   G tokens, asymmetric min/max, levels z + s*{0,1,2,3}, s and z fp16;
+ *   codes round half to even and clamp to [0, 3].
+ *
+ * Cache buffer, format v1 (one caller-owned buffer per layer, 256-B aligned regions):
+ *   header  align256(512 + 8*B*Hkv) bytes:
+ *           u32 magic 0x4E52564B, u32 version 1, i32 geom[7] (batch, num_kv_heads,
+ *           head_dim, capacity, group, varn_iters, bits), u32 flags (sticky),
+ *           i8 sigma[D] at byte 64, i32 len[B][Hkv][2] at byte 512;
+ *   tiles   [B][Hkv][capacity/G][2 (K,V)][TR] tile records, region padded to 256 B;
+ *   tail    [B][Hkv][2][G][D] fp16, unrotated tokens of the group being filled,
+ *           slot = token index mod G.
+ *   Tile record TR = G*D/4 + 2G + 6D bytes (1856 at G=32, 2944 at G=64):
+ *     codes  G*D/4 B: K: code(t,j) in byte t*D/4 + j/4, bits 2*(j%4) (channels fastest)
+ *                     V: code(t,j) in byte j*G/4 + t/4, bits 2*(t%4) (tokens fastest)
+ *     r fp16[G], c fp16[D], s fp16[D], z fp16[D].
+ *   A tile token dequantizes as x_hat = (r_t c_j (z_j + s_j q_tj))_j H_D^T.
+ *
+ * Errors: every argument check runs on the host before any HIP call; on error
+ * nothing is enqueued and the cache is untouched. A failed launch returns
+ * KVARN_ERR_DEVICE. Device-side conditions set sticky header flags.
+ * One cache must not be written from two streams at once; reads may overlap.
+ */
+#ifndef KVARN_H
+#define KVARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KVARN_API __attribute__((visibility("default")))
+#else
+#define KVARN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVARN_OK = 0,
+    KVARN_ERR_NULL = 1,         /* a required pointer is NULL                              */
+    KVARN_ERR_ALIGN = 2,        /* a device pointer is not 16-byte aligned                 */
+    KVARN_ERR_GEOM = 3,         /* inconsistent geometry or sizes                          */
+    KVARN_ERR_UNSUPPORTED = 4,  /* valid request outside what this build implements        */
+    KVARN_ERR_RANGE = 5,        /* token count, head count or buffer size out of range     */
+    KVARN_ERR_DEVICE = 6        /* the HIP runtime reported an error                       */
+} kvarn_status;
+
+/* Geometry of one layer cache. v1 supports head_dim = 128, group in {32, 64},
+ * bits = 2, 0 <= varn_iters <= 8, capacity a positive multiple of group. */
+typedef struct {
+    int32_t batch;          /* B   sequences                                   */
+    int32_t num_kv_heads;   /* Hkv                                             */
+    int32_t head_dim;       /* D                                               */
+    int32_t capacity;       /* max tokens per sequence                         */
+    int32_t group;          /* G   tokens per tile (the pages' 32 or 64)       */
+    int32_t varn_iters;     /* VarN iterations (token pass + channel pass)     */
+    int32_t bits;           /* code width (2)                                  */
+} kvarn_geom;
+
+enum { KVARN_OUT_F32 = 0, KVARN_OUT_BF16 = 1 };            /* dequantize output dtype     */
+enum { KVARN_Q_PREROTATED = 1u };                          /* attention: q is already q H_D */
+enum { KVARN_FLAG_CAPACITY = 1u,      /* an append found a full sequence; token dropped      */
+       KVARN_FLAG_SATURATED = 2u,     /* an input had |x| > 65504 and was saturated          */
+       KVARN_FLAG_SCALE_CLAMPED = 4u  /* r or c hit [2^-14, 65504], or s/z saturated        */ };
+
+/* Format version of the cache buffer (1). */
+KVARN_API int kvarn_format_version(void);
+
+/* Size in bytes of a cache buffer for geometry *g. Host only. */
+KVARN_API kvarn_status kvarn_cache_bytes(const kvarn_geom* g, size_t* bytes);
+
+/* Write the header (magic, version, geometry, sigma) and zero len[] and flags.
+ * signs_host: host int8[head_dim], each +1 or -1: the random signs of H_D
+ * (ai-paper-analysis page, section 3.1: randomized Hadamard matrix).
+ * Asynchronous on `stream`; signs_host may be reused once the call returns. */
+KVARN_API kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* signs_host, void* stream);
+
+/* Reset the cache to hold tokens [0, num_tokens) of k and v.
+ * k_bf16, v_bf16: device bf16 [B][num_tokens][Hkv][D], contiguous.
+ * Full groups of G tokens are rotated, VarN-normalized and quantized into tile
+ * records (ai-paper-analysis page, sections 3.1-3.2); the last num_tokens mod G
+ * tokens go to the fp16 tail. Sets len = num_tokens. 0 <= num_tokens <= capacity. */
+KVARN_API kvarn_status kvarn_quantize_prefill(const kvarn_geom* g, void* cache, const void* k_bf16,
+                                    const void* v_bf16, int32_t num_tokens, void* stream);
+
+/* Append one token to every (batch, kv head): k_bf16, v_bf16 device bf16 [B][Hkv][D].
+ * The token enters the fp16 tail; when the group of G fills it is quantized into
+ * the next tile record (ai-paper-analysis page, section 3.2: the current group's
+ * statistics are computed as tokens are written). A full sequence drops the token
+ * and sets KVARN_FLAG_CAPACITY. */
+KVARN_API kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, const void* k_bf16,
+                                 const void* v_bf16, void* stream);
+
+/* Dequantize into k_out, v_out: device [B][max_tokens][Hkv][D], f32 or bf16 per
+ * out_dtype. Tile tokens undo grid and scales and rotate back by H_D^T
+ * (ai-paper-analysis page, section 3.2: the scaling is restored at
+ * dequantization); tail tokens are copied; rows at or past len are zero. */
+KVARN_API kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_out, void* v_out,
+                              int32_t max_tokens, int32_t out_dtype, void* stream);
+
+/* Workspace bytes kvarn_attn_decode needs for num_q_heads query heads. Host only. */
+KVARN_API kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes);
+
+/* Single-query decode attention over every cached token:
+ *   out[b][g] = sum_t softmax_t(scale * q[b][g] . k_hat_t) v_hat_t,
+ * KV head of query head g = g / (num_q_heads / num_kv_heads).
+ * q_bf16: device bf16 [B][Hq][D] in original space, rotated in-kernel by H_D
+ * (ai-paper-analysis page, section 3.1: Q takes the same rotation so Q K^T is
+ * unchanged), or already rotated when flags has KVARN_Q_PREROTATED.
+ * softmax_scale <= 0 selects 1/sqrt(D). Tiles are read in rotated space with the
+ * dequantization folded into the dot products; tail tokens in original space.
+ * workspace: device, >= kvarn_attn_workspace_bytes; out: device f32 [B][Hq][D],
+ * original space. An empty sequence gives 0. num_q_heads / num_kv_heads <= 8. */
+KVARN_API kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const void* q_bf16,
+                               int32_t num_q_heads, float softmax_scale, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/* Read the sticky flags into *flags_host. Synchronizes `stream`. */
+KVARN_API kvarn_status kvarn_cache_flags(const void* cache, void* stream, uint32_t* flags_host);
+
+/* Static string for a status code. */
+KVARN_API const char* kvarn_status_str(kvarn_status s);
+
+/* Test hook: kvarn_quantize_prefill plus the fp32 intermediates of the full tiles:
+ * w = rotated tokens, y = normalized tokens W / (r16 c16), each device f32
+ * [B][T_full][Hkv][D], T_full = G * floor(num_tokens / G). Any of w_*, y_* may be NULL. */
+KVARN_API kvarn_status kvarn_debug_prefill(const kvarn_geom* g, void* cache, const void* k_bf16,
+                                 const void* v_bf16, int32_t num_tokens, float* w_k, float* w_v,
+                                 float* y_k, float* y_v, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVARN_H */

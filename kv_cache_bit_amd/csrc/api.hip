@@ -1,0 +1,217 @@
+// libkvarn C ABI: argument validation (host only, before any HIP call) and launches.
+#include <math.h>
+#include <string.h>
+
+#include "kvarn_common.h"
+#include "kvarn_launch.h"
+
+using namespace kvarn;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+kvarn_status check_geom(const kvarn_geom* g) {
+  if (!g) return KVARN_ERR_NULL;
+  if (g->batch <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0 || g->capacity <= 0 || g->group <= 0 ||
+      g->varn_iters < 0 || g->bits <= 0)
+    return KVARN_ERR_GEOM;
+  if (g->head_dim != kD || (g->group != 32 && g->group != 64) || g->bits != 2 || g->varn_iters > 8)
+    return KVARN_ERR_UNSUPPORTED;
+  if (g->capacity % g->group != 0) return KVARN_ERR_GEOM;
+  // keep every element index of a [B][capacity][Hkv][D] tensor and every tile count in range
+  if ((long long)g->batch * g->capacity * g->num_kv_heads * kD >= (1LL << 40)) return KVARN_ERR_RANGE;
+  if ((long long)g->batch * g->num_kv_heads * (g->capacity / g->group) * 2 >= (1LL << 31)) return KVARN_ERR_RANGE;
+  return KVARN_OK;
+}
+
+kvarn_status dev(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_DEVICE; }
+
+kvarn_status check_prefill(const kvarn_geom* g, void* cache, const void* k, const void* v, int32_t T) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (!cache || ((!k || !v) && T > 0)) return KVARN_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(k) || !aligned16(v)) return KVARN_ERR_ALIGN;
+  if (T < 0 || T > g->capacity) return KVARN_ERR_RANGE;
+  return KVARN_OK;
+}
+
+kvarn_status prefill_impl(const kvarn_geom* g, void* cache, const void* k, const void* v, int32_t T,
+                          float* wk, float* wv, float* yk, float* yv, void* stream) {
+  kvarn_status st = check_prefill(g, cache, k, v, T);
+  if (st != KVARN_OK) return st;
+  for (const float* p : {wk, wv, yk, yv})
+    if (p && !aligned16(p)) return KVARN_ERR_ALIGN;
+  PrefillArgs a{};
+  a.L = make_layout(*g);
+  a.cache = static_cast<uint8_t*>(cache);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.T = T;
+  a.nfull = T / g->group;
+  a.jobs = (long long)g->batch * g->num_kv_heads * a.nfull * 2;
+  a.wk = wk;
+  a.wv = wv;
+  a.yk = yk;
+  a.yv = yv;
+  return dev(launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvarn_format_version(void) { return kVersion; }
+
+const char* kvarn_status_str(kvarn_status s) {
+  switch (s) {
+    case KVARN_OK: return "ok";
+    case KVARN_ERR_NULL: return "null pointer";
+    case KVARN_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case KVARN_ERR_GEOM: return "inconsistent geometry";
+    case KVARN_ERR_UNSUPPORTED: return "unsupported geometry (v1: head_dim 128, group 32/64, 2 bits, <= 8 VarN iterations)";
+    case KVARN_ERR_RANGE: return "size out of range";
+    case KVARN_ERR_DEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kvarn_status kvarn_cache_bytes(const kvarn_geom* g, size_t* bytes) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (!bytes) return KVARN_ERR_NULL;
+  *bytes = (size_t)make_layout(*g).total;
+  return KVARN_OK;
+}
+
+kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* signs_host, void* stream) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (!cache || !signs_host) return KVARN_ERR_NULL;
+  if (!aligned16(cache)) return KVARN_ERR_ALIGN;
+  for (int j = 0; j < kD; ++j)
+    if (signs_host[j] != 1 && signs_host[j] != -1) return KVARN_ERR_RANGE;
+  InitArgs a{};
+  a.cache = static_cast<uint8_t*>(cache);
+  a.geom[0] = g->batch;
+  a.geom[1] = g->num_kv_heads;
+  a.geom[2] = g->head_dim;
+  a.geom[3] = g->capacity;
+  a.geom[4] = g->group;
+  a.geom[5] = g->varn_iters;
+  a.geom[6] = g->bits;
+  memcpy(a.sigma, signs_host, kD);
+  a.n_len = 2LL * g->batch * g->num_kv_heads;
+  return dev(launch_init(a, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_quantize_prefill(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
+                                    int32_t num_tokens, void* stream) {
+  return prefill_impl(g, cache, k_bf16, v_bf16, num_tokens, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+kvarn_status kvarn_debug_prefill(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
+                                 int32_t num_tokens, float* w_k, float* w_v, float* y_k, float* y_v,
+                                 void* stream) {
+  return prefill_impl(g, cache, k_bf16, v_bf16, num_tokens, w_k, w_v, y_k, y_v, stream);
+}
+
+kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
+                                 void* stream) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (!cache || !k_bf16 || !v_bf16) return KVARN_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(k_bf16) || !aligned16(v_bf16)) return KVARN_ERR_ALIGN;
+  AppendArgs a{};
+  a.L = make_layout(*g);
+  a.cache = static_cast<uint8_t*>(cache);
+  a.k = static_cast<const uint16_t*>(k_bf16);
+  a.v = static_cast<const uint16_t*>(v_bf16);
+  return dev(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_out, void* v_out, int32_t max_tokens,
+                              int32_t out_dtype, void* stream) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (!cache || ((!k_out || !v_out) && max_tokens > 0)) return KVARN_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(k_out) || !aligned16(v_out)) return KVARN_ERR_ALIGN;
+  if (max_tokens < 0 || max_tokens > g->capacity) return KVARN_ERR_RANGE;
+  if (out_dtype != KVARN_OUT_F32 && out_dtype != KVARN_OUT_BF16) return KVARN_ERR_UNSUPPORTED;
+  if (max_tokens == 0) return KVARN_OK;
+  DequantArgs a{};
+  a.L = make_layout(*g);
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.ko = k_out;
+  a.vo = v_out;
+  a.maxT = max_tokens;
+  a.bf16out = out_dtype == KVARN_OUT_BF16;
+  a.nblk = (max_tokens + 31) / 32;
+  a.jobs = (long long)g->batch * g->num_kv_heads * 2 * a.nblk;
+  return dev(launch_dequant(a, static_cast<hipStream_t>(stream)));
+}
+
+// Split-K over tiles: enough work-groups to cover the chip about twice, at least 8
+// tiles per split. Depends only on the geometry, so the workspace size is static.
+static int attn_splits(const kvarn_geom* g, int* tiles_per_split) {
+  const int tiles = g->capacity / g->group;
+  const long long seqs = (long long)g->batch * g->num_kv_heads;
+  long long want = (2048 + seqs - 1) / seqs;
+  long long maxs = (tiles + 7) / 8;
+  if (want > maxs) want = maxs;
+  if (want < 1) want = 1;
+  const int tps = (int)((tiles + want - 1) / want);
+  *tiles_per_split = tps;
+  return (tiles + tps - 1) / tps;  // the tail sits at tile index len/G < tiles when present
+}
+
+kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (!bytes) return KVARN_ERR_NULL;
+  if (num_q_heads <= 0 || num_q_heads % g->num_kv_heads != 0) return KVARN_ERR_GEOM;
+  if (num_q_heads / g->num_kv_heads > 8) return KVARN_ERR_UNSUPPORTED;
+  int tps;
+  const int ns = attn_splits(g, &tps);
+  *bytes = (size_t)g->batch * num_q_heads * ns * (2 + 2 * kD) * sizeof(float);
+  return KVARN_OK;
+}
+
+kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const void* q_bf16, int32_t num_q_heads,
+                               float softmax_scale, uint32_t flags, void* workspace, size_t workspace_bytes,
+                               float* out, void* stream) {
+  size_t need = 0;
+  kvarn_status st = kvarn_attn_workspace_bytes(g, num_q_heads, &need);
+  if (st != KVARN_OK) return st;
+  if (!cache || !q_bf16 || !workspace || !out) return KVARN_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(q_bf16) || !aligned16(workspace) || !aligned16(out)) return KVARN_ERR_ALIGN;
+  if (workspace_bytes < need) return KVARN_ERR_RANGE;
+  if ((flags & ~(uint32_t)KVARN_Q_PREROTATED) != 0) return KVARN_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVARN_ERR_RANGE;
+  AttnArgs a{};
+  a.L = make_layout(*g);
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.Hq = num_q_heads;
+  a.grp = num_q_heads / g->num_kv_heads;
+  a.n_split = attn_splits(g, &a.tiles_per_split);
+  a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)kD);
+  a.flags = flags;
+  return dev(launch_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_cache_flags(const void* cache, void* stream, uint32_t* flags_host) {
+  if (!cache || !flags_host) return KVARN_ERR_NULL;
+  if (!aligned16(cache)) return KVARN_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t f = 0;
+  if (hipMemcpyAsync(&f, static_cast<const uint8_t*>(cache) + kFlagsOff, 4, hipMemcpyDeviceToHost, st) != hipSuccess)
+    return KVARN_ERR_DEVICE;
+  if (hipStreamSynchronize(st) != hipSuccess) return KVARN_ERR_DEVICE;
+  *flags_host = f;
+  return KVARN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+// Shared device/host definitions of libkvarn: cache layout, wave shuffles, number formats.
+// gfx950 only: wave64, DPP quad permutes, ds_swizzle for in-row exchanges.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvarn.h"
+
+namespace kvarn {
+
+constexpr int kD = 128;                     // head_dim supported by this build
+constexpr uint32_t kMagic = 0x4E52564Bu;    // 'K' 'V' 'R' 'N'
+constexpr int kVersion = 1;
+constexpr int kHdrFixed = 512;              // len[] offset
+constexpr int kSigmaOff = 64;
+constexpr int kFlagsOff = 36;
+constexpr float kFp16Max = 65504.0f;
+constexpr float kScaleMin = 6.103515625e-05f;          // 2^-14
+constexpr float kInvSqrtD = 0.08838834764831845f;      // 1/sqrt(128), fp32-rounded
+
+inline __host__ __device__ long long align256(long long n) { return (n + 255) / 256 * 256; }
+
+// Byte layout of one layer cache (format v1), computed on the host and passed by value.
+struct Layout {
+  int B, Hkv, cap, G, n_it, tiles;  // tiles = cap / G
+  int tr;                           // tile record bytes
+  long long header, tail_off, total;
+
+  __host__ __device__ long long record(int b, int h, int tile, int s) const {
+    return header + ((((long long)b * Hkv + h) * tiles + tile) * 2 + s) * tr;
+  }
+  __host__ __device__ long long tail_row(int b, int h, int s, int slot) const {
+    return tail_off + ((((long long)b * Hkv + h) * 2 + s) * G + slot) * (kD * 2);
+  }
+  __host__ __device__ long long len_off(int b, int h, int s) const {
+    return kHdrFixed + (((long long)b * Hkv + h) * 2 + s) * 4;
+  }
+};
+
+inline __host__ Layout make_layout(const kvarn_geom& g) {
+  Layout L;
+  L.B = g.batch;
+  L.Hkv = g.num_kv_heads;
+  L.cap = g.capacity;
+  L.G = g.group;
+  L.n_it = g.varn_iters;
+  L.tiles = g.capacity / g.group;
+  L.tr = g.group * kD / 4 + 2 * g.group + 6 * kD;
+  L.header = align256(kHdrFixed + 8LL * g.batch * g.num_kv_heads);
+  L.tail_off = L.header + align256((long long)g.batch * g.num_kv_heads * L.tiles * 2 * L.tr);
+  L.total = L.tail_off + align256((long long)g.batch * g.num_kv_heads * 2 * g.group * kD * 2);
+  return L;
+}
+
+#if defined(__HIPCC__)
+// ----------------------------------------------------------------------------- lane exchange
+// xor-partner exchange inside a wave. Masks 1 and 2 use DPP quad permutes (no LDS
+// traffic); 4, 8 and 16 use ds_swizzle's bit-mask mode (within 32 lanes); 32 uses
+// ds_bpermute.
+template <int M>
+__device__ __forceinline__ float xshfl(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4 || M == 8 || M == 16) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1F));
+  } else {
+    static_assert(M == 32, "xor mask");
+    return __shfl_xor(v, 32);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t xshfl_u(uint32_t v) {
+  return (uint32_t)__float_as_int(xshfl<M>(__int_as_float((int)v)));
+}
+
+// Sum over the 16 lanes of a row (lanes sharing lane>>4). Each stage adds a lane's
+// value to its partner's; addition is commutative, so every lane ends bit-identical.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += xshfl<1>(v);
+  v += xshfl<2>(v);
+  v += xshfl<4>(v);
+  v += xshfl<8>(v);
+  return v;
+}
+// Sum over the 4 rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float col4_sum(float v) {
+  v += xshfl<16>(v);
+  v += xshfl<32>(v);
+  return v;
+}
+__device__ __forceinline__ float col4_min(float v) {
+  v = fminf(v, xshfl<16>(v));
+  return fminf(v, xshfl<32>(v));
+}
+__device__ __forceinline__ float col4_max(float v) {
+  v = fmaxf(v, xshfl<16>(v));
+  return fmaxf(v, xshfl<32>(v));
+}
+
+// ----------------------------------------------------------------------------- number formats
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __int_as_float((int)(w << 16)); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __int_as_float((int)(w & 0xFFFF0000u)); }
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t f16bits(float x) {  // RNE, x assumed within fp16 range
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x; }
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {  // f32 -> bf16 bits, half to even
+  const uint32_t u = (uint32_t)__float_as_int(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+// ----------------------------------------------------------------------------- Hadamard
+__device__ __forceinline__ void fwht8(float (&a)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((e & h) == 0) {
+        const float x = a[e], y = a[e + h];
+        a[e] = x + y;
+        a[e + h] = x - y;
+      }
+    }
+  }
+}
+
+// Butterfly across lanes differing in bit M: the lane with the bit clear keeps
+// own + partner, the lane with it set keeps partner - own.
+template <int M>
+__device__ __forceinline__ void xstage(float (&a)[8], int cg) {
+  const float sgn = (cg & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = fmaf(a[e], sgn, xshfl<M>(a[e]));
+}
+
+// Unnormalized Sylvester-ordered Walsh-Hadamard transform of the 128-vector held by
+// the 16 lanes of a row (channel 8*cg + e): out[n] = sum_k in[k] (-1)^popcount(k & n).
+__device__ __forceinline__ void fwht128(float (&a)[8], int cg) {
+  fwht8(a);
+  xstage<1>(a, cg);
+  xstage<2>(a, cg);
+  xstage<4>(a, cg);
+  xstage<8>(a, cg);
+}
+
+__device__ __forceinline__ void load_sigma(const uint8_t* hdr, int cg, float (&sg)[8]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(hdr + kSigmaOff + 8 * cg);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sg[e] = (float)(int8_t)((w.x >> (8 * e)) & 0xFF);
+    sg[e + 4] = (float)(int8_t)((w.y >> (8 * e)) & 0xFF);
+  }
+}
+
+__device__ __forceinline__ void store8f(float* p, const float (&a)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(a[0], a[1], a[2], a[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(a[4], a[5], a[6], a[7]);
+}
+
+#endif  // __HIPCC__
+
+}  // namespace kvarn

@@ -1,0 +1,61 @@
+// Kernel argument blocks and launchers (internal to libkvarn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvarn_common.h"
+
+namespace kvarn {
+
+struct InitArgs {
+  uint8_t* cache;
+  int32_t geom[7];
+  int8_t sigma[kD];
+  long long n_len;  // entries of len[]
+};
+
+struct PrefillArgs {
+  Layout L;
+  uint8_t* cache;
+  const uint16_t* k;  // bf16 [B][T][Hkv][D]
+  const uint16_t* v;
+  int T, nfull;       // tokens; full tiles per sequence
+  long long jobs;     // B * Hkv * nfull * 2 tile-streams
+  float *wk, *wv, *yk, *yv;  // optional fp32 intermediates [B][nfull*G][Hkv][D]
+};
+
+struct AppendArgs {
+  Layout L;
+  uint8_t* cache;
+  const uint16_t* k;  // bf16 [B][Hkv][D]
+  const uint16_t* v;
+};
+
+struct DequantArgs {
+  Layout L;
+  const uint8_t* cache;
+  void* ko;
+  void* vo;
+  int maxT, bf16out, nblk;  // nblk = ceil(maxT / 32)
+  long long jobs;           // B * Hkv * 2 * nblk
+};
+
+struct AttnArgs {
+  Layout L;
+  const uint8_t* cache;
+  const uint16_t* q;  // bf16 [B][Hq][D]
+  float* ws;          // [B][Hq][n_split][2 + 2D]
+  float* out;         // [B][Hq][D]
+  int Hq, grp, n_split, tiles_per_split;
+  float scale;
+  uint32_t flags;
+};
+
+hipError_t launch_init(const InitArgs& a, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+}  // namespace kvarn

@@ -455,12 +455,13 @@ def dequantize(cache: Cache, max_tokens: int) -> tuple[np.ndarray, np.ndarray]:
 
 
 def attn_decode(cache: Cache, q_bits, num_q_heads: int, softmax_scale: float = 0.0,
-                flags: int = 0) -> np.ndarray:
+                flags: int = 0, pairs=None) -> np.ndarray:
     """Single-query decode attention over the dequantized cache, by its definition:
     l_t = scale * (q . k_hat_t), p = softmax(l), out = sum_t p_t v_hat_t  (fp64 [B][Hq][D]).
     Query head g reads KV head g // (Hq / Hkv). Readings: scale defaults to 1/sqrt(D);
     with Q_PREROTATED the given query is q H_D and is mapped back by H_D^T ([AP] 3.1:
-    (qH)(kH)^T = q k^T). An empty sequence gives 0."""
+    (qH)(kH)^T = q k^T). An empty sequence gives 0. `pairs` optionally restricts the
+    work to a list of (batch, kv head); other outputs stay 0."""
     g = cache.g
     d = g.head_dim
     scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
@@ -469,17 +470,17 @@ def attn_decode(cache: Cache, q_bits, num_q_heads: int, softmax_scale: float = 0
         q = unrotate(q, cache.sigma)
     grp = num_q_heads // g.num_kv_heads
     out = np.zeros((g.batch, num_q_heads, d))
-    for b in range(g.batch):
-        for h in range(g.num_kv_heads):
-            k = stream_values(cache, b, h, 0)
-            v = stream_values(cache, b, h, 1)
-            if k.shape[0] == 0:
-                continue
-            for gi in range(h * grp, (h + 1) * grp):
-                logits = scale * (k @ q[b, gi])
-                p = np.exp(logits - logits.max())
-                p /= p.sum()
-                out[b, gi] = p @ v
+    todo = pairs if pairs is not None else [(b, h) for b in range(g.batch) for h in range(g.num_kv_heads)]
+    for b, h in todo:
+        k = stream_values(cache, b, h, 0)
+        v = stream_values(cache, b, h, 1)
+        if k.shape[0] == 0:
+            continue
+        for gi in range(h * grp, (h + 1) * grp):
+            logits = scale * (k @ q[b, gi])
+            p = np.exp(logits - logits.max())
+            p /= p.sum()
+            out[b, gi] = p @ v
     return out
 
 

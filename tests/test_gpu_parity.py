@@ -1,0 +1,304 @@
+"""GPU parity of libkvarn against the CPU oracle (run on an MI355X: pytest -m gpu).
+
+Every case prints its name before touching the GPU so a failing run names it.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_bit_amd import kvarn as K
+from kv_cache_bit_amd import synth
+from oracle import kvarn_ref as R
+
+from parity import GpuCache, check_attention, check_prefill, close_rowwise, from_u16, gpu_prefill, to_u16
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def outlier_kv(seed, B, T, H, law="lognormal", **kw):
+    return synth.kv_host(seed, B, T, H, law=law, **kw)
+
+
+# ----------------------------------------------------------------------------- prefill
+@pytest.mark.parametrize("T", [256, 250, 31, 0])
+def test_prefill_single_head_parity(T):
+    say("prefill c1", T)
+    k, v = outlier_kv(0, 1, max(T, 1), 1)
+    gc = GpuCache(1, 1, 288)
+    w, y = gpu_prefill(gc, k, v, T, debug=True)
+    st = check_prefill(gc, k, v, T, w, y)
+    say("stats", st)
+
+
+@pytest.mark.parametrize("n_it", [0, 1, 2, 8])
+def test_prefill_iterations(n_it):
+    say("prefill n_it", n_it)
+    k, v = outlier_kv(1, 1, 256, 2)
+    gc = GpuCache(1, 2, 256, 32, n_it)
+    w, y = gpu_prefill(gc, k, v, 256, debug=True)
+    check_prefill(gc, k, v, 256, w, y)
+
+
+def test_prefill_batch_heads_ragged():
+    say("prefill B=2 H=3 T=100")
+    k, v = outlier_kv(2, 2, 100, 3)
+    gc = GpuCache(2, 3, 128)
+    w, y = gpu_prefill(gc, k, v, 100, debug=True)
+    check_prefill(gc, k, v, 100, w, y)
+
+
+@pytest.mark.parametrize("T", [512, 532])
+def test_prefill_group64_spike_law(T):
+    say("prefill G=64 spike", T)
+    k, v = outlier_kv(3, 2, T, 2, law="spike", p=0.02, factor=50.0)
+    gc = GpuCache(2, 2, 576, 64, 2)
+    w, y = gpu_prefill(gc, k, v, T, debug=True)
+    check_prefill(gc, k, v, T, w, y)
+
+
+def test_prefill_student_t_heavy_tail():
+    say("prefill student-t")
+    k, v = synth.kv_host(4, 1, 320, 2, n_outlier_ch=8, ch_mult=30.0, law="student_t", nu=3.0)
+    gc = GpuCache(1, 2, 320)
+    w, y = gpu_prefill(gc, k, v, 320, debug=True)
+    check_prefill(gc, k, v, 320, w, y)
+
+
+def test_prefill_deterministic_and_debug_free_path_identical():
+    say("determinism")
+    k, v = outlier_kv(5, 2, 200, 4)
+    a = GpuCache(2, 4, 256)
+    b = GpuCache(2, 4, 256)
+    gpu_prefill(a, k, v, 200, debug=False)
+    gpu_prefill(b, k, v, 200, debug=True)
+    ma = a.host_cache()
+    mb = b.host_cache()
+    m = ma.defined_mask()
+    assert np.array_equal(ma.buf[m], mb.buf[m])
+    gpu_prefill(a, k, v, 200)
+    assert np.array_equal(a.host_cache().buf[m], ma.buf[m])
+
+
+def test_saturation_and_scale_flags():
+    say("flags")
+    k, v = outlier_kv(6, 1, 64, 1)
+    k[0, 3, 0, 5] = 0x4780   # 65536
+    v[0, 40, 0, 7] = 0xC780  # -65536
+    gc = GpuCache(1, 1, 64)
+    gpu_prefill(gc, k, v, 64, debug=True)
+    assert K.kvarn_cache_flags(gc.buf) & K.KVARN_FLAG_SATURATED
+    check_prefill(gc, k, v, 64)
+    z = np.zeros((1, 32, 1, 128), dtype=np.uint16)
+    z[0, :, 0, :] = synth.f32_to_bf16_bits(np.full((32, 128), 1e-30, dtype=np.float32))
+    gc2 = GpuCache(1, 1, 32)
+    gpu_prefill(gc2, z, z, 32)
+    assert K.kvarn_cache_flags(gc2.buf) & K.KVARN_FLAG_SCALE_CLAMPED
+    check_prefill(gc2, z, z, 32)
+
+
+# ----------------------------------------------------------------------------- append
+@pytest.mark.parametrize("G,n_it,T", [(32, 3, 70), (64, 2, 140)])
+def test_append_equals_prefill(G, n_it, T):
+    say("append==prefill", G, n_it, T)
+    B, H = 2, 3
+    k, v = outlier_kv(7, B, T, H)
+    cap = ((T + G - 1) // G + 1) * G
+    a = GpuCache(B, H, cap, G, n_it)
+    gpu_prefill(a, k, v, T)
+    b = GpuCache(B, H, cap, G, n_it)
+    gpu_prefill(b, k, v, 0)
+    kd = from_u16(k)
+    vd = from_u16(v)
+    for t in range(T):
+        K.kvarn_append_decode(b.g, b.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+    ha, hb = a.host_cache(), b.host_cache()
+    m = ha.defined_mask()
+    assert np.array_equal(m, hb.defined_mask())
+    assert np.array_equal(ha.buf[m], hb.buf[m])
+    check_prefill(b, k, v, T)
+
+
+def test_append_capacity_flag():
+    say("capacity")
+    k, v = outlier_kv(8, 1, 33, 1)
+    gc = GpuCache(1, 1, 32)
+    gpu_prefill(gc, k, v, 32)
+    kd, vd = from_u16(k), from_u16(v)
+    K.kvarn_append_decode(gc.g, gc.buf, kd[:, 32].contiguous(), vd[:, 32].contiguous())
+    torch.cuda.synchronize()
+    assert K.kvarn_cache_flags(gc.buf) & K.KVARN_FLAG_CAPACITY
+    assert np.all(gc.host_cache().lens == 32)
+
+
+def test_checkpoint_restore_mid_decode():
+    say("checkpoint")
+    B, H, T0, steps = 2, 2, 50, 30
+    k, v = outlier_kv(9, B, T0 + steps, H)
+    kd, vd = from_u16(k), from_u16(v)
+    a = GpuCache(B, H, 128)
+    gpu_prefill(a, k, v, T0)
+    for t in range(T0, T0 + 10):
+        K.kvarn_append_decode(a.g, a.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+    snap = a.buf.clone()
+    b = GpuCache(B, H, 128)
+    b.buf.copy_(snap)
+    for gc in (a, b):
+        for t in range(T0 + 10, T0 + steps):
+            K.kvarn_append_decode(gc.g, gc.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(a.buf, b.buf)
+
+
+# ----------------------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("G,n_it,T,maxT", [(32, 3, 250, 256), (64, 2, 150, 200), (32, 3, 20, 40)])
+def test_dequantize_parity(G, n_it, T, maxT):
+    say("dequantize", G, n_it, T, maxT)
+    B, H = 2, 2
+    k, v = outlier_kv(10, B, T, H)
+    gc = GpuCache(B, H, 256, G, n_it)
+    gpu_prefill(gc, k, v, T)
+    hc = gc.host_cache()
+    kr, vr = R.dequantize(hc, maxT)
+    for dt in (K.KVARN_OUT_F32, K.KVARN_OUT_BF16):
+        tdt = torch.float32 if dt == K.KVARN_OUT_F32 else torch.bfloat16
+        ko = torch.full((B, maxT, H, 128), 7.0, dtype=tdt, device="cuda")
+        vo = torch.full((B, maxT, H, 128), 7.0, dtype=tdt, device="cuda")
+        K.kvarn_dequantize(gc.g, gc.buf, ko, vo, maxT, dt)
+        torch.cuda.synchronize()
+        for got, ref in ((ko, kr), (vo, vr)):
+            g = got.float().cpu().numpy().astype(np.float64)
+            rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+            if dt == K.KVARN_OUT_F32:
+                assert np.all(np.abs(g - ref) <= 1e-6 * np.maximum(rms, 1e-30) + 1e-30)
+            else:
+                ref_b = R.bf16_to_f64(synth.f32_to_bf16_bits(ref.astype(np.float32)))
+                ulp = np.abs(ref_b) * 2.0 ** -7 + 1e-38
+                assert np.all(np.abs(g - ref_b) <= ulp * 1.01)
+            assert np.all(g[:, T:] == 0)
+
+
+def test_dequantize_roundtrip_quality_guard():
+    say("roundtrip quality")
+    k, v = outlier_kv(0, 1, 256, 1)
+    errs = {}
+    for n_it in (0, 3):
+        gc = GpuCache(1, 1, 256, 32, n_it)
+        gpu_prefill(gc, k, v, 256)
+        ko = torch.empty(1, 256, 1, 128, device="cuda")
+        vo = torch.empty(1, 256, 1, 128, device="cuda")
+        K.kvarn_dequantize(gc.g, gc.buf, ko, vo, 256, K.KVARN_OUT_F32)
+        torch.cuda.synchronize()
+        e = []
+        for bits, o in ((k, ko), (v, vo)):
+            x = R.canonicalize(bits[0, :, 0])[0]
+            e.append(R.relative_token_error(x, o[0, :, 0].cpu().numpy()).mean())
+        errs[n_it] = float(np.mean(e))
+    say("errors", errs)
+    assert errs[3] < 0.2 and errs[3] < 0.1 * errs[0]
+
+
+# ----------------------------------------------------------------------------- attention
+def run_attn(gc, q_bits, Hq, scale=0.0, flags=0):
+    q = from_u16(q_bits)
+    ws, n = K.alloc_workspace(gc.g, Hq)
+    out = torch.full((gc.og.batch, Hq, 128), float("nan"), device="cuda")
+    K.kvarn_attn_decode(gc.g, gc.buf, q, Hq, scale, flags, ws, n, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("T,Hq,H", [(256, 4, 1), (250, 8, 2), (1, 1, 1), (20, 4, 2), (1000, 4, 2), (33, 2, 2)])
+def test_attention_parity(T, Hq, H):
+    say("attn", T, Hq, H)
+    B = 2
+    k, v = outlier_kv(11, B, T, H)
+    gc = GpuCache(B, H, 1024 + 32)
+    gpu_prefill(gc, k, v, T)
+    q = synth.q_host(12, B, Hq)
+    out = run_attn(gc, q, Hq)
+    worst = check_attention(out, gc.host_cache(), q, Hq)
+    say("worst rel", worst)
+
+
+def test_attention_prerotated_scale_zero_query_and_empty():
+    say("attn flags")
+    B, H, Hq, T = 1, 2, 8, 300
+    k, v = outlier_kv(13, B, T, H)
+    gc = GpuCache(B, H, 512)
+    gpu_prefill(gc, k, v, T)
+    hc = gc.host_cache()
+    q = synth.q_host(14, B, Hq)
+    check_attention(run_attn(gc, q, Hq, flags=K.KVARN_Q_PREROTATED), hc, q, Hq, flags=R.Q_PREROTATED)
+    check_attention(run_attn(gc, q, Hq, scale=0.3), hc, q, Hq, scale=0.3)
+    zq = np.zeros_like(q)
+    check_attention(run_attn(gc, zq, Hq), hc, zq, Hq)
+    empty = GpuCache(B, H, 512)
+    gpu_prefill(empty, k, v, 0)
+    assert np.all(run_attn(empty, q, Hq) == 0)
+
+
+@pytest.mark.parametrize("G,n_it", [(32, 3), (64, 2)])
+def test_attention_after_appends_many_splits(G, n_it):
+    say("attn after appends", G)
+    B, H, Hq, T0, steps = 2, 2, 4, 2000, 45
+    k, v = outlier_kv(15, B, T0 + steps, H)
+    gc = GpuCache(B, H, 4096, G, n_it)
+    gpu_prefill(gc, k, v, T0)
+    kd, vd = from_u16(k), from_u16(v)
+    q = synth.q_host(16, B, Hq)
+    for t in range(T0, T0 + steps):
+        K.kvarn_append_decode(gc.g, gc.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+    check_attention(run_attn(gc, q, Hq), gc.host_cache(), q, Hq)
+
+
+# ----------------------------------------------------------------------------- full-size spot checks
+def test_full_size_llama_layer_prefill_sampled():
+    """Llama-3.1-8B-shaped layer (8 KV heads, 32768 tokens, G=32, 3 iterations), the
+    benchmark's launch configuration; 64 sampled tiles through the full chain."""
+    say("full-size prefill layer")
+    torch.manual_seed(0)
+    kd, vd = synth.kv_device(synth.sub_seed(2, 0, 0), 1, 32768, 8)
+    gc = GpuCache(1, 8, 32768)
+    K.kvarn_quantize_prefill(gc.g, gc.buf, kd, vd, 32768)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    picks = sorted({(0, int(rng.integers(8)), int(rng.integers(1024))) for _ in range(64)} | {(0, 7, 1023), (0, 0, 0)})
+    # host copies of just the sampled rows
+    k = np.zeros((1, 32768, 8, 128), dtype=np.uint16)
+    v = np.zeros_like(k)
+    for _, h, t in picks:
+        k[0, t * 32:(t + 1) * 32, h] = to_u16(kd[0, t * 32:(t + 1) * 32, h])
+        v[0, t * 32:(t + 1) * 32, h] = to_u16(vd[0, t * 32:(t + 1) * 32, h])
+    st = check_prefill(gc, k, v, 32768, tiles=picks)
+    say("stats", st)
+
+
+def test_full_size_phi4_decode_sampled():
+    """Phi-4-14B-shaped decode layer: 32 sequences x 10 KV heads x 16384 prior tokens,
+    40 query heads, then appends across a group boundary; attention checked on
+    sampled (batch, kv head) pairs against the oracle on the GPU-written bytes."""
+    say("full-size decode layer")
+    B, H, Hq, T0, cap = 32, 10, 40, 16384, 17408
+    kd, vd = synth.kv_device(synth.sub_seed(4, 0, 0), B, T0, H)
+    gc = GpuCache(B, H, cap)
+    K.kvarn_quantize_prefill(gc.g, gc.buf, kd, vd, T0)
+    del kd, vd
+    kn, vn = synth.kv_device(synth.sub_seed(4, 0, 1), B, 40, H)
+    for t in range(40):
+        K.kvarn_append_decode(gc.g, gc.buf, kn[:, t].contiguous(), vn[:, t].contiguous())
+    q = synth.q_host(17, B, Hq)
+    out = run_attn(gc, q, Hq)
+    hc = gc.host_cache()
+    assert np.all(hc.lens == T0 + 40)
+    pairs = [(0, 0), (5, 3), (31, 9), (17, 6)]
+    ref = R.attn_decode(hc, q, Hq, pairs=pairs)
+    grp = Hq // H
+    for b, h in pairs:
+        for g in range(h * grp, (h + 1) * grp):
+            m = np.abs(ref[b, g]).max()
+            assert np.abs(out[b, g] - ref[b, g]).max() <= 2e-3 * m, (b, g)
+    assert np.all(np.isfinite(out))

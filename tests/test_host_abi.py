@@ -1,0 +1,118 @@
+"""Host-side checks of libkvarn that need no GPU: the library loads, exports every
+entry point include/kvarn.h declares, sizes agree with the oracle's layout, and
+every invalid argument is rejected with its status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_bit_amd import kvarn as K
+from oracle import kvarn_ref as R
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvarn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"KVARN_API\s+[\w\s\*]+?\b(kvarn_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(K.lib, n), n
+    assert sorted(K.EXPORTS) == names
+
+
+def test_format_version_and_status_strings():
+    assert K.kvarn_format_version() == 1
+    for s in range(7):
+        assert K.status_str(s)
+    assert K.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("B,H,cap,G", [(1, 1, 32, 32), (2, 3, 96, 32), (1, 8, 32768, 32), (8, 8, 16384, 64),
+                                       (32, 10, 17408, 32), (3, 5, 640, 64)])
+def test_cache_bytes_match_oracle_layout(B, H, cap, G):
+    assert K.kvarn_cache_bytes(K.geom(B, H, cap, G, 3)) == R.Geom(B, H, 128, cap, G, 3, 2).total
+
+
+def test_workspace_bytes():
+    g = K.geom(32, 10, 17408, 32, 3)
+    n = K.kvarn_attn_workspace_bytes(g, 40)
+    assert n > 0 and n % (4 * (2 + 2 * 128)) == 0
+    with pytest.raises(K.KvarnError) as e:
+        K.kvarn_attn_workspace_bytes(g, 41)
+    assert e.value.status == K.KVARN_ERR_GEOM
+    with pytest.raises(K.KvarnError) as e:
+        K.kvarn_attn_workspace_bytes(K.geom(1, 1, 64, 32, 3), 9)
+    assert e.value.status == K.KVARN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), K.KVARN_ERR_UNSUPPORTED),
+    (dict(group=48), K.KVARN_ERR_UNSUPPORTED),
+    (dict(bits=4), K.KVARN_ERR_UNSUPPORTED),
+    (dict(varn_iters=9), K.KVARN_ERR_UNSUPPORTED),
+    (dict(varn_iters=-1), K.KVARN_ERR_GEOM),
+    (dict(capacity=100), K.KVARN_ERR_GEOM),
+    (dict(capacity=0), K.KVARN_ERR_GEOM),
+    (dict(batch=0), K.KVARN_ERR_GEOM),
+])
+def test_geometry_rejected(kw, status):
+    base = dict(batch=1, num_kv_heads=2, head_dim=128, capacity=128, group=32, varn_iters=3, bits=2)
+    base.update(kw)
+    g = K.kvarn_geom(*[base[n] for n, _ in K.kvarn_geom._fields_])
+    with pytest.raises(K.KvarnError) as e:
+        K.kvarn_cache_bytes(g)
+    assert e.value.status == status
+
+
+# Fake device addresses: the calls below must fail validation before touching them.
+A, A2, MIS = 0x10000, 0x20000, 0x10008
+
+
+def _code(fn, *args):
+    try:
+        fn(*args)
+    except K.KvarnError as e:
+        return e.status
+    return K.KVARN_OK
+
+
+def test_argument_errors_return_before_any_launch():
+    g = K.geom(1, 2, 128, 32, 3)
+    signs = [1] * 128
+    assert _code(K.kvarn_cache_init, g, 0, signs, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_cache_init, g, MIS, signs, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_cache_init, g, A, [1] * 127 + [0], 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_quantize_prefill, g, 0, A, A2, 10, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_quantize_prefill, g, A, 0, A2, 10, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_quantize_prefill, g, A, MIS, A2, 10, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_quantize_prefill, g, A, A, A2, 129, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_quantize_prefill, g, A, A, A2, -1, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_debug_prefill, g, A, A, A2, 64, MIS, None, None, None, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_append_decode, g, A, 0, A2, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_append_decode, g, A, A, MIS, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_dequantize, g, A, A, A2, 129, 0, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_dequantize, g, A, A, A2, 64, 7, 0) == K.KVARN_ERR_UNSUPPORTED
+    assert _code(K.kvarn_dequantize, g, A, MIS, A2, 64, 0, 0) == K.KVARN_ERR_ALIGN
+    ws = K.kvarn_attn_workspace_bytes(g, 4)
+    assert _code(K.kvarn_attn_decode, g, A, A2, 4, 0.0, 0, A, ws - 1, A2, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_attn_decode, g, A, A2, 3, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_GEOM
+    assert _code(K.kvarn_attn_decode, g, A, A2, 4, 0.0, 8, A, ws, A2, 0) == K.KVARN_ERR_UNSUPPORTED
+    assert _code(K.kvarn_attn_decode, g, A, A2, 4, float("nan"), 0, A, ws, A2, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_attn_decode, g, A, 0, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_cache_flags, 0, 0) == K.KVARN_ERR_NULL
+    bad = K.geom(1, 2, 100, 32, 3)
+    assert _code(K.kvarn_quantize_prefill, bad, A, A, A2, 10, 0) == K.KVARN_ERR_GEOM
+    assert _code(K.kvarn_cache_init, None if False else K.geom(1, 2, 128, 32, 3, head_dim=96), A, signs, 0) \
+        == K.KVARN_ERR_UNSUPPORTED
+
+
+def test_null_geometry():
+    f = K.lib.kvarn_cache_bytes
+    n = ctypes.c_size_t()
+    assert f(None, ctypes.byref(n)) == K.KVARN_ERR_NULL
