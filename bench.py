@@ -123,6 +123,28 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
                 ctx_start=T0 + warmup, H=H, Hq=Hq)
 
 
+def copy_ceiling(torch, gib=4):
+    """Device-to-device copy of `gib` GiB: the practical HBM ceiling (read + write bytes / time)."""
+    n = gib * (1 << 30)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return dict(bytes=2 * n, ms=round(ms, 3), GBps=round(2 * n / (ms * 1e-3) / 1e9, 1))
+
+
 def cpu_baseline(synth, tokens):
     """The oracle's prefill on layer 0 of the prefill workload, first `tokens` tokens (host cores)."""
     import numpy as np
@@ -153,6 +175,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--no-copy", action="store_true", help="skip the 4 GiB device copy ceiling")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -192,6 +215,9 @@ def main():
                      "avg_launch_us": round(avg_launch * 1e3, 2), "median_launch_us": round(lm[len(lm) // 2] * 1e3, 2)},
         "flags": pf["flags"],
     }
+    if not args.no_copy:
+        res["copy_ceiling"] = copy_ceiling(torch)
+        log(f"copy ceiling: {res['copy_ceiling']}")
     if not args.no_decode:
         dc = bench_decode(K, synth, torch, args.decode_steps)
         tok_s = dc["B"] * dc["steps"] / dc["wall"]

@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "quantize.hip", "attn.hip"]
+SOURCES = ["api.hip", "quantize.hip", "dequant.hip", "attn.hip"]
 LIB = os.path.join(HERE, "libkvarn.so")
 ARCH = "gfx950"
 

@@ -102,6 +102,7 @@ kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* si
   a.geom[6] = g->bits;
   memcpy(a.sigma, signs_host, kD);
   a.n_len = 2LL * g->batch * g->num_kv_heads;
+  a.hdr_bytes = make_layout(*g).header;
   return dev(launch_init(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // B: scores; thread = (token, 16-channel part)
+    // B: scores; thread = (token, code word `part`: channels 16m + 2 part + d in slot 8d + m)
     {
       const int part = tid & 7;
       for (int tok = tid >> 3; tok < G; tok += 32) {
@@ -111,7 +111,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int gi = 0; gi < GM; ++gi) d[gi] = 0.0f;
         for (int k = 0; k < 16; ++k) {
           const float qq = (float)((cw >> (2 * k)) & 3u);
-          for (int gi = 0; gi < grp; ++gi) d[gi] = fmaf(sh.av[gi][16 * part + k], qq, d[gi]);
+          const int j = 16 * (k & 7) + 2 * part + (k >> 3);
+          for (int gi = 0; gi < grp; ++gi) d[gi] = fmaf(sh.av[gi][j], qq, d[gi]);
         }
         const float rt = (float)*reinterpret_cast<const _Float16*>(rk + ro + 2 * tok);
         for (int gi = 0; gi < grp; ++gi) {

@@ -1,0 +1,144 @@
+// KVarN inverse path on gfx950: dequantization of the 2-bit cache, and the header
+// writer used by kvarn_cache_init.
+//
+// Dequantization undoes the grid and both VarN scales (ai-paper-analysis page,
+// section 3.2: the grouped scales are restored at dequantization) and rotates back
+// by H_D^T = H_syl diag(sigma) / sqrt(D) (section 3.1). One wave per 32-token block;
+// lane = 16 rg + cg holds tokens 8 rg + i and channels 8 cg + e, so the inverse
+// Walsh-Hadamard transform is 3 in-lane butterfly stages plus 4 across the row.
+#include "kvarn_common.h"
+#include "kvarn_launch.h"
+
+namespace kvarn {
+
+__device__ __forceinline__ void widen8_f16(const uint4 w, float (&x)[8]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = f16lo(ws[k]);
+    x[2 * k + 1] = f16hi(ws[k]);
+  }
+}
+
+// ----------------------------------------------------------------------------- dequantize
+// One wave per 32-token block of one (b, h, s): undo grid and scales, rotate back.
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rg = lane >> 4, cg = lane & 15;
+  const Layout& L = a.L;
+  const long long job = (long long)blockIdx.x * 4 + wave;
+  if (job >= a.jobs) return;
+  // job = ((b * nblk + blk) * 2 + s) * Hkv + h
+  const int h = (int)(job % L.Hkv);
+  const int s = (int)((job / L.Hkv) % 2);
+  const int blk = (int)((job / L.Hkv / 2) % a.nblk);
+  const int b = (int)(job / L.Hkv / 2 / a.nblk);
+  const int n = *reinterpret_cast<const int32_t*>(a.cache + L.len_off(b, h, s));
+  const int nfull = n / L.G;
+  const int t0 = blk * 32 + rg * 8;
+  void* outp = s ? a.vo : a.ko;
+  auto store_row = [&](int t, const float (&y)[8]) {
+    if (t >= a.maxT) return;
+    const long long off = (((long long)b * a.maxT + t) * L.Hkv + h) * kD + 8 * cg;
+    if (a.bf16out) {
+      uint4 o;
+      o.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
+      o.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
+      o.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
+      o.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(outp) + off) = o;
+    } else {
+      store8f(reinterpret_cast<float*>(outp) + off, y);
+    }
+  };
+  const int tile = (blk * 32) / L.G;
+  if (tile < nfull) {
+    const uint8_t* rec = a.cache + L.record(b, h, tile, s);
+    const int G = L.G;
+    const int ro = G * kD / 4, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
+    const int tw0 = (blk * 32) % G + rg * 8;
+    float cj[8], sj[8], zj[8], ri[8], sg[8];
+    widen8_f16(*reinterpret_cast<const uint4*>(rec + co + 16 * cg), cj);
+    widen8_f16(*reinterpret_cast<const uint4*>(rec + so + 16 * cg), sj);
+    widen8_f16(*reinterpret_cast<const uint4*>(rec + zo + 16 * cg), zj);
+    widen8_f16(*reinterpret_cast<const uint4*>(rec + ro + 2 * tw0), ri);
+    load_sigma(a.cache, cg, sg);
+    float w[8][8];
+    if (s == 0) {
+      // channel j = 8cg + e sits in word (j%16)/2 = 4(cg%2) + e/2, slot 8(e%2) + cg/2
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 q4 = *reinterpret_cast<const uint4*>(rec + (tw0 + i) * 32 + 16 * (cg & 1));
+        const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[i][e] = (float)((qw[e >> 1] >> (2 * (8 * (e & 1) + (cg >> 1)))) & 3u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t hq = *reinterpret_cast<const uint16_t*>(rec + (8 * cg + e) * (G / 4) + tw0 / 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i][e] = (float)((hq >> (2 * i)) & 3u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[i][e] = (ri[i] * cj[e]) * fmaf(sj[e], w[i][e], zj[e]);
+      fwht128(w[i], cg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[i][e] *= kInvSqrtD * sg[e];
+      store_row(blk * 32 + rg * 8 + i, w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + i;
+      float y[8];
+      if (t < n) {
+        widen8_f16(*reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * cg), y);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+      }
+      store_row(t, y);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- header
+__global__ void init_kernel(InitArgs a) {
+  const int t = threadIdx.x;
+  uint32_t* h32 = reinterpret_cast<uint32_t*>(a.cache);
+  if (t == 0) {
+    h32[0] = kMagic;
+    h32[1] = kVersion;
+    for (int k = 0; k < 7; ++k) h32[2 + k] = (uint32_t)a.geom[k];
+    h32[9] = 0;  // flags
+  }
+  for (int k = t; k < 128; k += blockDim.x) {  // bytes 40..511: pad, sigma, pad
+    const int off = 40 + 4 * k;
+    if (off >= kHdrFixed) break;
+    uint32_t w = 0;
+    for (int q = 0; q < 4; ++q) {
+      const int byte = off + q;
+      if (byte >= kSigmaOff && byte < kSigmaOff + kD) w |= (uint32_t)(uint8_t)a.sigma[byte - kSigmaOff] << (8 * q);
+    }
+    h32[off / 4] = w;
+  }
+  for (long long k = kHdrFixed / 4 + t; k < a.hdr_bytes / 4; k += blockDim.x) h32[k] = 0;  // len[] and padding
+}
+
+// ----------------------------------------------------------------------------- launchers
+hipError_t launch_init(const InitArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(init_kernel, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.jobs + 3) / 4));
+  hipLaunchKernelGGL(dequant_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvarn

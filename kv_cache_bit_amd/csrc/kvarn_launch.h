@@ -13,6 +13,7 @@ struct InitArgs {
   int32_t geom[7];
   int8_t sigma[kD];
   long long n_len;  // entries of len[]
+  long long hdr_bytes;  // header size; everything past len[] is zeroed
 };
 
 struct PrefillArgs {

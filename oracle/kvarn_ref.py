@@ -218,25 +218,41 @@ def record_bytes(g: int, d: int) -> int:
     return g * d // 4 + 2 * g + 6 * d
 
 
+def k_code_position(j: int) -> tuple[int, int]:
+    """K stream: (32-bit word w, 2-bit slot p) holding channel j of a token.
+    Word w holds the 16 channels {16 m + 2 w + d : m < 8, d < 2} at slot p = 8 d + m."""
+    return (j % 16) // 2, 8 * (j % 2) + j // 16
+
+
 def pack_codes(q, stream: int) -> np.ndarray:
-    """Four 2-bit codes per byte, low bits first.
-    K (stream 0): code (t, j) in byte t*D/4 + j//4 at bit 2*(j%4)   (channels fastest);
-    V (stream 1): code (t, j) in byte j*G/4 + t//4 at bit 2*(t%4)   (tokens fastest)."""
+    """Four 2-bit codes per byte, slot k of a byte at bits 2k..2k+1 (little-endian words).
+    K (stream 0): token t owns bytes t*D/4 .. t*D/4 + D/4 - 1, read as D/16 words;
+                  channel j sits in word w, slot p (k_code_position): byte t*D/4 + 4w + p//4,
+                  bits 2*(p%4);
+    V (stream 1): code (t, j) in byte j*G/4 + t//4 at bits 2*(t%4) (tokens fastest)."""
     q = np.asarray(q, dtype=np.uint8)
     g, d = q.shape
     if stream == 0:
-        qq = q.reshape(g, d // 4, 4)                       # [t][j//4][j%4]
-    else:
-        qq = q.T.reshape(d, g // 4, 4)                     # [j][t//4][t%4]
+        out = np.zeros((g, d // 4), dtype=np.uint8)
+        for j in range(d):
+            w, p = k_code_position(j)
+            out[:, 4 * w + p // 4] |= (q[:, j] << (2 * (p % 4))).astype(np.uint8)
+        return out.reshape(-1)
+    qq = q.T.reshape(d, g // 4, 4)                         # [j][t//4][t%4]
     b = (qq[..., 0] | (qq[..., 1] << 2) | (qq[..., 2] << 4) | (qq[..., 3] << 6)).astype(np.uint8)
     return b.reshape(-1)
 
 
 def unpack_codes(b, g: int, d: int, stream: int) -> np.ndarray:
     b = np.asarray(b, dtype=np.uint8)
-    parts = np.stack([(b >> (2 * m)) & 3 for m in range(4)], axis=-1)
     if stream == 0:
-        return parts.reshape(g, d).astype(np.uint8)
+        rows = b.reshape(g, d // 4)
+        q = np.zeros((g, d), dtype=np.uint8)
+        for j in range(d):
+            w, p = k_code_position(j)
+            q[:, j] = (rows[:, 4 * w + p // 4] >> (2 * (p % 4))) & 3
+        return q
+    parts = np.stack([(b >> (2 * m)) & 3 for m in range(4)], axis=-1)
     return parts.reshape(d, g).T.astype(np.uint8)
 
 

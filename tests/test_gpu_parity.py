@@ -93,7 +93,8 @@ def test_saturation_and_scale_flags():
     assert K.kvarn_cache_flags(gc.buf) & K.KVARN_FLAG_SATURATED
     check_prefill(gc, k, v, 64)
     z = np.zeros((1, 32, 1, 128), dtype=np.uint16)
-    z[0, :, 0, :] = synth.f32_to_bf16_bits(np.full((32, 128), 1e-30, dtype=np.float32))
+    # 1e-6 survives fp16 canonicalization (subnormal) but gives r < 2^-14: clamped
+    z[0, :, 0, :] = synth.f32_to_bf16_bits(np.full((32, 128), 1e-6, dtype=np.float32))
     gc2 = GpuCache(1, 1, 32)
     gpu_prefill(gc2, z, z, 32)
     assert K.kvarn_cache_flags(gc2.buf) & K.KVARN_FLAG_SCALE_CLAMPED
@@ -173,11 +174,12 @@ def test_dequantize_parity(G, n_it, T, maxT):
             g = got.float().cpu().numpy().astype(np.float64)
             rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
             if dt == K.KVARN_OUT_F32:
-                assert np.all(np.abs(g - ref) <= 1e-6 * np.maximum(rms, 1e-30) + 1e-30)
+                # fp32 bound: 3 roundings to form W_hat plus a 7-stage butterfly sum,
+                # gamma_7 * sqrt(D) ~ 4.7e-6 of the row RMS, plus the final scalings
+                assert np.all(np.abs(g - ref) <= 1e-5 * np.maximum(rms, 1e-30) + 1e-30)
             else:
-                ref_b = R.bf16_to_f64(synth.f32_to_bf16_bits(ref.astype(np.float32)))
-                ulp = np.abs(ref_b) * 2.0 ** -7 + 1e-38
-                assert np.all(np.abs(g - ref_b) <= ulp * 1.01)
+                # one bf16 rounding of a value that already carries the fp32 error above
+                assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) * 1.01 + 1e-5 * rms + 1e-30)
             assert np.all(g[:, T:] == 0)
 
 

@@ -81,7 +81,7 @@ def _golden():
             if line.startswith("#") or not line.strip():
                 continue
             head, vals = line.split(":")
-            rows[head.split()[0] + (head.split()[1] if head.startswith("OFFSETS") else "")] = vals.split()
+            rows[" ".join(head.split())] = vals.split()
     return rows
 
 
@@ -90,23 +90,33 @@ def test_golden_layout_bytes():
     g, d = 32, 128
     t = np.arange(g)[:, None]
     j = np.arange(d)[None, :]
-    q = ((t + 3 * j) % 4).astype(np.uint8)
+    q = ((t + j // 16 + 2 * (j % 2)) % 4).astype(np.uint8)
     kb = R.pack_codes(q, 0)
     vb = R.pack_codes(q, 1)
-    kvals = [int(x, 16) for x in gold["K"]]
-    vvals = [int(x, 16) for x in gold["V"]]
     assert kb.shape == (1024,) and vb.shape == (1024,)
     for tt in range(g):
-        assert np.all(kb[tt * 32:(tt + 1) * 32] == kvals[tt % 4])
-    for jj in range(d):
-        assert np.all(vb[jj * 8:(jj + 1) * 8] == vvals[jj % 4])
+        word = [int(x, 16) for x in gold[f"K t%4={tt % 4}"]]
+        assert kb[tt * 32:(tt + 1) * 32].tolist() == word * 8, tt
+    for key, val in gold.items():
+        if key.startswith("V j="):
+            jj = int(key[4:])
+            assert np.all(vb[jj * 8:(jj + 1) * 8] == int(val[0], 16)), jj
     for stream in (0, 1):
         assert np.array_equal(R.unpack_codes(R.pack_codes(q, stream), g, d, stream), q)
+    # and a random tile round-trips through both layouts
+    rq = np.random.default_rng(3).integers(0, 4, (64, 128)).astype(np.uint8)
+    for stream in (0, 1):
+        assert np.array_equal(R.unpack_codes(R.pack_codes(rq, stream), 64, 128, stream), rq)
+
+
+def test_k_word_slots_are_a_bijection():
+    seen = {R.k_code_position(jj) for jj in range(128)}
+    assert seen == {(w, p) for w in range(8) for p in range(16)}
 
 
 @pytest.mark.parametrize("g", [32, 64])
 def test_golden_record_offsets(g):
-    gold = _golden()["OFFSETS" + str(g)]
+    gold = _golden()[f"OFFSETS {g}"]
     offs = [int(x) for x in gold]
     assert R.record_bytes(g, 128) == offs[-1]
     rng = np.random.default_rng(g)
