@@ -18,6 +18,8 @@ FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared", "-fvisibility=hidden",
     # packed FP32 arithmetic off: plain v_fma_f32 / v_mul_f32 only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs: the VALU reads them without v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

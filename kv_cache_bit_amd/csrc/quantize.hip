@@ -35,31 +35,95 @@ template <int CTRL>
 __device__ __forceinline__ float dppf(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
-constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+// DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane ^ 7 within the row), row_mirror (lane ^ 15), row_newbcast:n
+constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140, kNewBcast = 0x150;
 
-// All 16 lanes of a row get the row total; the pairing order is the same in every
-// lane (commutative adds), so all lanes hold bit-identical values.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dppf<kQx1>(x);
-  x += dppf<kQx2>(x);
-  x += dppf<kHalfMirror>(x);
-  x += dppf<kMirror>(x);
-  return x;
+// Cross-lane min/max on values the compiler cannot prove canonical (they come
+// through DPP / permlane as integers): plain v_min/v_max, no NaN quieting needed
+// for the finite values that reach them.
+__device__ __forceinline__ float vmin(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
-
-// Combine the 4 rows (lanes c, c+16, c+32, c+48) with permlane swaps: rows 0+1 and
-// 2+3, then the two halves.
-template <typename Op>
-__device__ __forceinline__ float col_reduce4(float x, Op op) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-  x = op(__int_as_float(p[0]), __int_as_float(p[1]));
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return op(__int_as_float(q[0]), __int_as_float(q[1]));
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
-struct OpMin { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
-struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpMin { __device__ float operator()(float a, float b) const { return vmin(a, b); } };
+struct OpMax { __device__ float operator()(float a, float b) const { return vmax(a, b); } };
+
+// Reduce-scatter of 8 per-token partials over the 16 lanes of a row. Stages pair
+// lane c with c^15, c^7, c^2, c^1 (row_mirror, row_half_mirror, quad perms); at each
+// stage a lane keeps half of its tokens (chosen by bits 3, 2, 1 of c) and adds the
+// partner's partial of the same tokens. Lane c ends with the row total of token
+// c/2 (identical in lanes c and c^1).
+__device__ __forceinline__ float row_rs8(const float (&v)[8], int c) {
+  const bool b3 = c & 8, b2 = c & 4, b1 = c & 2;
+  float a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float send = b3 ? v[k] : v[k + 4], keep = b3 ? v[k + 4] : v[k];
+    a[k] = keep + dppf<kMirror>(send);
+  }
+  float bb[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float send = b2 ? a[k] : a[k + 2], keep = b2 ? a[k + 2] : a[k];
+    bb[k] = keep + dppf<kHalfMirror>(send);
+  }
+  const float send = b1 ? bb[0] : bb[1], keep = b1 ? bb[1] : bb[0];
+  const float d = keep + dppf<kQx2>(send);
+  return d + dppf<kQx1>(d);
+}
+// Token tau's value from its owner lanes (2 tau, 2 tau + 1) to the whole row.
+__device__ __forceinline__ void row_gather8(float own, float (&v)[8]) {
+  v[0] = dppf<kNewBcast + 0>(own);
+  v[1] = dppf<kNewBcast + 2>(own);
+  v[2] = dppf<kNewBcast + 4>(own);
+  v[3] = dppf<kNewBcast + 6>(own);
+  v[4] = dppf<kNewBcast + 8>(own);
+  v[5] = dppf<kNewBcast + 10>(own);
+  v[6] = dppf<kNewBcast + 12>(own);
+  v[7] = dppf<kNewBcast + 14>(own);
+}
+
+// Reduce-scatter of 8 per-channel partials (channel blocks nb) over the 4 rows:
+// permlane16_swap of two channel registers leaves rows 0+1 / 2+3 partials of one
+// channel in rows 0, 2 and of the other in rows 1, 3; permlane32_swap then combines
+// the halves. Row g ends with channel block g in out[0] and 4 + g in out[1].
+template <typename Op>
+__device__ __forceinline__ void col_rs8(const float (&v)[8], float (&out)[2], Op op) {
+  float y[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_int(v[2 * p]), __float_as_int(v[2 * p + 1]),
+                                                    false, false);
+    y[p] = op(__int_as_float(s[0]), __int_as_float(s[1]));
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(y[2 * q]), __float_as_int(y[2 * q + 1]),
+                                                    false, false);
+    out[q] = op(__int_as_float(s[0]), __int_as_float(s[1]));
+  }
+}
+// Inverse: row g holds channel blocks g and 4 + g; every row gets all 8.
+__device__ __forceinline__ void col_gather8(const float (&own)[2], float (&v)[8]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_int(own[q]), __float_as_int(own[q]), false, false);
+    const auto p0 = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto p1 = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    v[4 * q + 0] = __int_as_float(p0[0]);
+    v[4 * q + 1] = __int_as_float(p0[1]);
+    v[4 * q + 2] = __int_as_float(p1[0]);
+    v[4 * q + 3] = __int_as_float(p1[1]);
+  }
+}
 
 // ----------------------------------------------------------------------------- Hadamard fragments
 // B operand of the 16x16x32 MFMA for K-step ks (channels 32ks..32ks+31) and channel
@@ -89,39 +153,56 @@ __device__ __forceinline__ int frag_index(int ks, int nb) {
 }
 
 // ----------------------------------------------------------------------------- inputs
-// Sign masks for the 8 channels of chunk `chunk` (channels 8*chunk .. +7): bit 15 / 31
-// of dword d flips fp16 halves 2d / 2d+1 where sigma is -1.
-__device__ __forceinline__ void sigma_masks(const uint8_t* hdr, int chunk, uint32_t (&m)[4]) {
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// Sign masks for the 8 channels of chunk `chunk` (channels 8 chunk .. +7): bit 31 of
+// lo[d] / hi[d] is set where sigma of channel 2d / 2d+1 is -1.
+struct SigMask {
+  uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ SigMask sigma_masks(const uint8_t* hdr, int chunk) {
   const uint2 s = *reinterpret_cast<const uint2*>(hdr + kSigmaOff + 8 * chunk);
-  m[0] = ((s.x << 8) & 0x8000u) | ((s.x << 16) & 0x80000000u);
-  m[1] = ((s.x >> 8) & 0x8000u) | (s.x & 0x80000000u);
-  m[2] = ((s.y << 8) & 0x8000u) | ((s.y << 16) & 0x80000000u);
-  m[3] = ((s.y >> 8) & 0x8000u) | (s.y & 0x80000000u);
+  SigMask m;
+  m.lo[0] = (s.x & 0x80u) << 24;
+  m.hi[0] = (s.x & 0x8000u) << 16;
+  m.lo[1] = (s.x & 0x800000u) << 8;
+  m.hi[1] = s.x & 0x80000000u;
+  m.lo[2] = (s.y & 0x80u) << 24;
+  m.hi[2] = (s.y & 0x8000u) << 16;
+  m.lo[3] = (s.y & 0x800000u) << 8;
+  m.hi[3] = s.y & 0x80000000u;
+  return m;
 }
 
+// two fp32 -> packed fp16 pair, round half to even (v_cvt_pk_f16_f32)
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return f16bits(lo) | (f16bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, h2v));
 }
 
-// 8 bf16 -> 8 canonical fp16 (round half to even), times sigma. Without clamping a
-// value beyond fp16 becomes inf, which the caller detects and then redoes with CLAMP.
+// 8 bf16 -> 8 canonical fp16 (round half to even), times sigma: the sign flip rides on
+// the bf16 -> fp32 unpack ((w << 16) + bit31 flips bit 31; (w & hi16) ^ bit31 too).
+// Without clamping a value beyond fp16 becomes inf, which the caller detects and then
+// redoes with CLAMP.
 template <bool CLAMP>
-__device__ __forceinline__ h8v canon_a(const uint4 w, const uint32_t (&m)[4]) {
+__device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    float lo = bf16lo(ws[d]), hi = bf16hi(ws[d]);
+    float lo = __int_as_float((int)((ws[d] << 16) + m.lo[d]));
+    float hi = __int_as_float((int)((ws[d] & 0xFFFF0000u) ^ m.hi[d]));
     if constexpr (CLAMP) {
-      lo = fminf(fmaxf(lo, -kFp16Max), kFp16Max);
-      hi = fminf(fmaxf(hi, -kFp16Max), kFp16Max);
+      lo = __builtin_amdgcn_fmed3f(lo, -kFp16Max, kFp16Max);
+      hi = __builtin_amdgcn_fmed3f(hi, -kFp16Max, kFp16Max);
     }
-    o[d] = pack_f16x2(lo, hi) ^ m[d];
+    o[d] = pack_f16x2(lo, hi);
   }
   return __builtin_bit_cast(h8v, make_uint4(o[0], o[1], o[2], o[3]));
 }
-__device__ __forceinline__ h8v sign_a(const uint4 w, const uint32_t (&m)[4]) {  // fp16 input
-  return __builtin_bit_cast(h8v, make_uint4(w.x ^ m[0], w.y ^ m[1], w.z ^ m[2], w.w ^ m[3]));
+__device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp16 input
+  return __builtin_bit_cast(h8v, make_uint4(w.x ^ ((m.lo[0] >> 16) | m.hi[0]), w.y ^ ((m.lo[1] >> 16) | m.hi[1]),
+                                            w.z ^ ((m.lo[2] >> 16) | m.hi[2]), w.w ^ ((m.lo[3] >> 16) | m.hi[3])));
 }
 
 // W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]
@@ -155,148 +236,105 @@ struct TileLds {
   float red_b[NW][kD];
 };
 
-// channel partials of the NW waves of a tile, combined in wave order
+// Per-channel reduction of a tile: 4-row reduce-scatter inside the wave, then (G=64)
+// the partials of the NW waves through LDS in wave order. own[q] is channel
+// 16 (4q + g) + c. The trailing barrier lets the next call reuse the LDS slots.
 template <int NW, typename Op>
-__device__ __forceinline__ void chan_reduce(float (&s)[8], TileLds<NW>& sh, int g, int c, int sub, Op op) {
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) s[nb] = col_reduce4(s[nb], op);
+__device__ __forceinline__ void chan_reduce(const float (&v)[8], float (&own)[2], TileLds<NW>& sh, int g,
+                                            int c, int sub, float (*red)[kD], Op op) {
+  col_rs8(v, own, op);
   if constexpr (NW > 1) {
-    if (g == 0) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) sh.red_a[sub][16 * nb + c] = s[nb];
-    }
+    for (int q = 0; q < 2; ++q) red[sub][16 * (4 * q + g) + c] = own[q];
     __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      float t = sh.red_a[0][16 * nb + c];
+    for (int q = 0; q < 2; ++q) {
+      float t = red[0][16 * (4 * q + g) + c];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) t = op(t, sh.red_a[w][16 * nb + c]);
-      s[nb] = t;
-    }
-    __syncthreads();
-  }
-}
-
-template <int NW>
-__device__ __forceinline__ void chan_minmax(float (&mn)[8], float (&mx)[8], TileLds<NW>& sh, int g, int c,
-                                            int sub) {
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    mn[nb] = col_reduce4(mn[nb], OpMin());
-    mx[nb] = col_reduce4(mx[nb], OpMax());
-  }
-  if constexpr (NW > 1) {
-    if (g == 0) {
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        sh.red_a[sub][16 * nb + c] = mn[nb];
-        sh.red_b[sub][16 * nb + c] = mx[nb];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      float a = sh.red_a[0][16 * nb + c], b = sh.red_b[0][16 * nb + c];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        a = fminf(a, sh.red_a[w][16 * nb + c]);
-        b = fmaxf(b, sh.red_b[w][16 * nb + c]);
-      }
-      mn[nb] = a;
-      mx[nb] = b;
+      for (int w = 1; w < NW; ++w) t = op(t, red[w][16 * (4 * q + g) + c]);
+      own[q] = t;
     }
     __syncthreads();
   }
 }
 
 // ----------------------------------------------------------------------------- the tile core
-// From the rotated block W' = sqrt(D) W (acc) and its squares p, with st holding the
-// first token-axis sums (u = 1): VarN, stored scales, grid, codes; the record is
-// assembled in sh.rec. Steps follow the ai-paper-analysis page, section 3.2.
+// From the rotated block W' = sqrt(D) W (acc), its squares p and the first token-axis
+// sum of the lane's own token (u = 1): VarN, stored scales, grid, codes; the record
+// is assembled in sh.rec. Steps follow the ai-paper-analysis page, section 3.2.
 //
 // VarN with cumulative scales (the mean square of W/(r c) along the axis becomes 1):
 //   token pass   S'_t = sum_j W'_tj^2 / c_j^2,   r_t = sqrt(S'_t) / D,  v_t = D / S'_t
 //   channel pass S'_j = sum_t W'_tj^2 v_t,       c_j = sqrt(S'_j / G),  u_j = G / S'_j
 // (with W' = sqrt(D) W these are the oracle's r_t <- r_t sqrt(ms_t), c_j <- c_j sqrt(ms_j));
-// an all-zero line keeps its scale.
+// an all-zero line keeps its scale. Each lane owns one token (c/2 of its row's 8) and
+// two channels (16g + c, 64 + 16g + c): their scalars are computed once, by the owner,
+// and broadcast back.
 template <int NW, bool DBG>
-__device__ void tile_finish(f4v (&acc)[2][8], float (&p)[2][8][4], float (&st)[2][4], int lane, int sub,
-                            int stream, int n_it, TileLds<NW>& sh, uint32_t& flags, float* dbg_w,
-                            float* dbg_y, long long dstride) {
+__device__ void tile_finish(f4v (&acc)[2][8], float (&p)[2][8][4], float st_own, int lane, int sub, int stream,
+                            int n_it, TileLds<NW>& sh, uint32_t& flags, float* dbg_w, float* dbg_y,
+                            long long dstride) {
   constexpr int G = 32 * NW;
   const int g = lane >> 4, c = lane & 15;
+  const int tau_own = c >> 1;  // own token: mb = tau/4, i = tau%4
 
-  float u[8], v[2][4], rr[2][4], cc[8];
+  float u[8], v[8];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    u[nb] = 1.0f;
-    cc[nb] = 1.0f;
-  }
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[mb][i] = 1.0f / kD;
-      rr[mb][i] = 1.0f;
-    }
+  for (int k = 0; k < 8; ++k) u[k] = 1.0f;
+  float v_own = 1.0f / kD, s_tok = st_own;
+  float u_own[2] = {1.0f, 1.0f}, s_ch[2] = {0.0f, 0.0f};
   for (int it = 0; it < n_it; ++it) {
-    if (it > 0) {  // token pass (the first one arrives precomputed in st)
+    if (it > 0) {  // token pass (the first one arrives precomputed)
+      float tp[8];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float s = 0.0f;
+          float t = 0.0f;
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) s = fmaf(p[mb][nb][i], u[nb], s);
-          st[mb][i] = row_sum16(s);
+          for (int nb = 0; nb < 8; ++nb) t = fmaf(p[mb][nb][i], u[nb], t);
+          tp[4 * mb + i] = t;
         }
+      s_tok = row_rs8(tp, c);
     }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (st[mb][i] > 0.0f) {
-          v[mb][i] = (float)kD * __builtin_amdgcn_rcpf(st[mb][i]);
-          rr[mb][i] = __builtin_amdgcn_sqrtf(st[mb][i]) * (1.0f / kD);
-        }
-    float sj[8];  // channel pass
+    if (s_tok > 0.0f) v_own = (float)kD * __builtin_amdgcn_rcpf(s_tok);
+    row_gather8(v_own, v);
+    float cp[8];  // channel pass
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      float s = 0.0f;
+      float t = 0.0f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(p[mb][nb][i], v[mb][i], s);
-      sj[nb] = s;
+        for (int i = 0; i < 4; ++i) t = fmaf(p[mb][nb][i], v[4 * mb + i], t);
+      cp[nb] = t;
     }
-    chan_reduce<NW>(sj, sh, g, c, sub, OpAdd());
+    chan_reduce<NW>(cp, s_ch, sh, g, c, sub, sh.red_a, OpAdd());
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      if (sj[nb] > 0.0f) {
-        u[nb] = (float)G * __builtin_amdgcn_rcpf(sj[nb]);
-        cc[nb] = __builtin_amdgcn_sqrtf(sj[nb] * (1.0f / G));
-      }
+    for (int q = 0; q < 2; ++q)
+      if (s_ch[q] > 0.0f) u_own[q] = (float)G * __builtin_amdgcn_rcpf(s_ch[q]);
+    col_gather8(u_own, u);
   }
 
   // stored scales: fp16, clamped to [2^-14, 65504]
-  float r16[2][4], at[2][4], c16[8], ic[8];
+  const float r_own = (n_it > 0 && s_tok > 0.0f) ? __builtin_amdgcn_sqrtf(s_tok) * (1.0f / kD) : 1.0f;
+  const float rc = fminf(fmaxf(r_own, kScaleMin), kFp16Max);
+  if (rc != r_own) flags |= KVARN_FLAG_SCALE_CLAMPED;
+  const float r16_own = round_f16(rc);
+  float at[8];  // Y = W' / (sqrt(D) r16 c16): per-token factor 1 / (sqrt(D) r16)
+  row_gather8(kInvSqrtD * __builtin_amdgcn_rcpf(r16_own), at);
+  float c16_own[2], ic_own[2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = fminf(fmaxf(rr[mb][i], kScaleMin), kFp16Max);
-      if (x != rr[mb][i]) flags |= KVARN_FLAG_SCALE_CLAMPED;
-      r16[mb][i] = round_f16(x);
-      at[mb][i] = kInvSqrtD * __builtin_amdgcn_rcpf(r16[mb][i]);  // Y = W' / (sqrt(D) r16 c16)
-    }
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const float x = fminf(fmaxf(cc[nb], kScaleMin), kFp16Max);
-    if (x != cc[nb]) flags |= KVARN_FLAG_SCALE_CLAMPED;
-    c16[nb] = round_f16(x);
-    ic[nb] = __builtin_amdgcn_rcpf(c16[nb]);
+  for (int q = 0; q < 2; ++q) {
+    const float cv = (n_it > 0 && s_ch[q] > 0.0f) ? __builtin_amdgcn_sqrtf(s_ch[q] * (1.0f / G)) : 1.0f;
+    const float x = fminf(fmaxf(cv, kScaleMin), kFp16Max);
+    if (x != cv) flags |= KVARN_FLAG_SCALE_CLAMPED;
+    c16_own[q] = round_f16(x);
+    ic_own[q] = __builtin_amdgcn_rcpf(c16_own[q]);
   }
   if constexpr (DBG) {
+    float ic[8];
+    col_gather8(ic_own, ic);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -305,47 +343,52 @@ __device__ void tile_finish(f4v (&acc)[2][8], float (&p)[2][8][4], float (&st)[2
         for (int nb = 0; nb < 8; ++nb) {
           const long long off = (16 * mb + 4 * g + i) * dstride + 16 * nb + c;
           if (dbg_w) dbg_w[off] = acc[mb][nb][i] * kInvSqrtD;
-          if (dbg_y) dbg_y[off] = (acc[mb][nb][i] * at[mb][i]) * ic[nb];
+          if (dbg_y) dbg_y[off] = (acc[mb][nb][i] * at[4 * mb + i]) * ic[nb];
         }
   }
-  // Y' = W' a_t = Y c16 (the positive per-channel c16 is applied to the channel's min/max)
+  // Y' = W' / (sqrt(D) r16) = Y c16 (the positive c16 is applied to the channel's min/max)
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mb][nb][i] *= at[mb][i];
+      for (int i = 0; i < 4; ++i) acc[mb][nb][i] *= at[4 * mb + i];
 
   // per-channel asymmetric min/max 2-bit grid over the tile's G tokens
-  float mn[8], mx[8];
+  float mnl[8], mxl[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
-    float a = acc[0][nb][0], b = acc[0][nb][0];
+    float lo = acc[0][nb][0], hi = acc[0][nb][0];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a = fminf(a, acc[mb][nb][i]);
-        b = fmaxf(b, acc[mb][nb][i]);
+        lo = fminf(lo, acc[mb][nb][i]);
+        hi = fmaxf(hi, acc[mb][nb][i]);
       }
-    mn[nb] = a;
-    mx[nb] = b;
+    mnl[nb] = lo;
+    mxl[nb] = hi;
   }
-  chan_minmax<NW>(mn, mx, sh, g, c, sub);
-  float s16[8], z16[8], al[8], ga[8];
+  float mn_own[2], mx_own[2];
+  chan_reduce<NW>(mnl, mn_own, sh, g, c, sub, sh.red_a, OpMin());
+  chan_reduce<NW>(mxl, mx_own, sh, g, c, sub, sh.red_b, OpMax());
+  float s16_own[2], z16_own[2], al_own[2], ga_own[2];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const float lo = mn[nb] * ic[nb], hi = mx[nb] * ic[nb];
+  for (int q = 0; q < 2; ++q) {
+    const float lo = mn_own[q] * ic_own[q], hi = mx_own[q] * ic_own[q];
     const float sr = (hi - lo) * (1.0f / 3.0f);
     const float sc = fminf(sr, kFp16Max);
     const float zc = fminf(fmaxf(lo, -kFp16Max), kFp16Max);
     if (sc != sr || zc != lo) flags |= KVARN_FLAG_SCALE_CLAMPED;
-    s16[nb] = round_f16(sc);
-    z16[nb] = round_f16(zc);
-    const float is = s16[nb] > 0.0f ? __builtin_amdgcn_rcpf(s16[nb]) : 0.0f;
-    al[nb] = ic[nb] * is;  // u = (Y - z)/s = Y' (ic/s) - z/s
-    ga[nb] = -z16[nb] * is;
+    s16_own[q] = round_f16(sc);
+    z16_own[q] = round_f16(zc);
+    const float is = s16_own[q] > 0.0f ? __builtin_amdgcn_rcpf(s16_own[q]) : 0.0f;
+    al_own[q] = ic_own[q] * is;  // u = (Y - z)/s = Y' (ic/s) - z/s
+    ga_own[q] = -z16_own[q] * is;
   }
+  float al[8], ga[8];
+  col_gather8(al_own, al);
+  col_gather8(ga_own, ga);
 
   // codes, q = clamp(rne(u), 0, 3): clamp, then 1.5 * 2^23 + u rounds half to even
   // with q left in bits 0..1 and zeros in bits 2..21; shifted into its 2-bit slot,
@@ -384,42 +427,39 @@ __device__ void tile_finish(f4v (&acc)[2][8], float (&p)[2][8][4], float (&st)[2
       }
   }
   constexpr int RO = G * kD / 4, CO = RO + 2 * G, SO = CO + 2 * kD, ZO = SO + 2 * kD;
-  if (c == 0) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      uint2 w;
-      w.x = pack_f16x2(r16[mb][0], r16[mb][1]);
-      w.y = pack_f16x2(r16[mb][2], r16[mb][3]);
-      *reinterpret_cast<uint2*>(sh.rec + RO + 2 * (ttile0 + 16 * mb)) = w;
-    }
+  if ((c & 1) == 0) {
+    const int t = ttile0 + 16 * (tau_own >> 2) + (tau_own & 3);
+    *reinterpret_cast<uint16_t*>(sh.rec + RO + 2 * t) = (uint16_t)f16bits(r16_own);
   }
-  if (g == 0 && sub == 0) {
+  if (sub == 0) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const int j = 16 * nb + c;
-      *reinterpret_cast<uint16_t*>(sh.rec + CO + 2 * j) = (uint16_t)f16bits(c16[nb]);
-      *reinterpret_cast<uint16_t*>(sh.rec + SO + 2 * j) = (uint16_t)f16bits(s16[nb]);
-      *reinterpret_cast<uint16_t*>(sh.rec + ZO + 2 * j) = (uint16_t)f16bits(z16[nb]);
+    for (int q = 0; q < 2; ++q) {
+      const int j = 16 * (4 * q + g) + c;
+      *reinterpret_cast<uint16_t*>(sh.rec + CO + 2 * j) = (uint16_t)f16bits(c16_own[q]);
+      *reinterpret_cast<uint16_t*>(sh.rec + SO + 2 * j) = (uint16_t)f16bits(s16_own[q]);
+      *reinterpret_cast<uint16_t*>(sh.rec + ZO + 2 * j) = (uint16_t)f16bits(z16_own[q]);
     }
   }
   __syncthreads();
 }
 
-// squares of the rotated block and their per-token sums (the first token pass, u = 1)
-__device__ __forceinline__ void squares_and_token_sums(const f4v (&acc)[2][8], float (&p)[2][8][4],
-                                                       float (&st)[2][4]) {
+// squares of the rotated block and the row total of the lane's own token (the first
+// token pass, u = 1)
+__device__ __forceinline__ float squares_and_token_sum(const f4v (&acc)[2][8], float (&p)[2][8][4], int c) {
+  float tp[8];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float s = 0.0f;
+      float t = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         p[mb][nb][i] = acc[mb][nb][i] * acc[mb][nb][i];
-        s += p[mb][nb][i];
+        t += p[mb][nb][i];
       }
-      st[mb][i] = row_sum16(s);
+      tp[4 * mb + i] = t;
     }
+  return row_rs8(tp, c);
 }
 
 template <int NW>
@@ -510,12 +550,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 4; ++ks)
       raw[mb][ks] = *reinterpret_cast<const uint4*>(
           src + (((long long)b * a.T + t0 + 16 * mb + c) * L.Hkv + h) * kD + 8 * (4 * ks + g));
-  uint32_t msk[4][4];
+  SigMask msk[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) sigma_masks(hdr, 4 * ks + g, msk[ks]);
+  for (int ks = 0; ks < 4; ++ks) msk[ks] = sigma_masks(hdr, 4 * ks + g);
 
   f4v acc[2][8];
-  float p[2][8][4], st[2][4];
+  float p[2][8][4];
+  float st;
   {
     h8v av[2][4];
 #pragma unroll
@@ -524,20 +565,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int ks = 0; ks < 4; ++ks) av[mb][ks] = canon_a<false>(raw[mb][ks], msk[ks]);
     rotate_block(av, hf, acc);
   }
-  squares_and_token_sums(acc, p, st);
-  bool bad = false;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bad |= !(st[mb][i] <= 3.0e38f);
-  if (__any(bad)) {  // an input beyond fp16 (inf after conversion): redo saturating
+  st = squares_and_token_sum(acc, p, c);
+  if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion): redo saturating
     h8v av[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) av[mb][ks] = canon_a<true>(raw[mb][ks], msk[ks]);
     rotate_block(av, hf, acc);
-    squares_and_token_sums(acc, p, st);
+    st = squares_and_token_sum(acc, p, c);
     flags |= KVARN_FLAG_SATURATED;
   }
 
@@ -591,8 +627,7 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
     h8v av[2][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint32_t m[4];
-      sigma_masks(hdr, 4 * ks + g, m);
+      const SigMask m = sigma_masks(hdr, 4 * ks + g);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int t = sub * 32 + 16 * mb + c;  // token of this A row inside the tile
@@ -608,9 +643,9 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
       }
     }
     f4v acc[2][8];
-    float p[2][8][4], st[2][4];
+    float p[2][8][4];
     rotate_block(av, hf, acc);
-    squares_and_token_sums(acc, p, st);
+    const float st = squares_and_token_sum(acc, p, c);
     tile_finish<NW, false>(acc, p, st, lane, sub, s, L.n_it, sh, flags, nullptr, nullptr, 0);
     copy_record<NW>(sh, a.cache + L.record(b, h, (pos + 1) / G - 1, s), lane, sub);
   }
