@@ -68,6 +68,22 @@ def test_prefill_student_t_heavy_tail():
     check_prefill(gc, k, v, 320, w, y)
 
 
+def test_prefill_near_constant_tokens_clamp_path():
+    """All tokens equal up to tiny noise: after rotation every channel is nearly constant,
+    so the grid step is tiny next to |Y| and fp16 rounding of z can push u outside
+    [0, 3]; the kernel must take its clamping path and still match the oracle."""
+    say("near-constant tokens")
+    rng = np.random.default_rng(21)
+    base = rng.standard_normal(128) * 3.0
+    x = base[None, None, None, :] + 1e-3 * rng.standard_normal((1, 64, 2, 128))
+    k = synth.f32_to_bf16_bits(x.astype(np.float32))
+    v = synth.f32_to_bf16_bits((x[:, ::-1] * 0.5).astype(np.float32))
+    gc = GpuCache(1, 2, 64)
+    w, y = gpu_prefill(gc, k, v, 64, debug=True)
+    st = check_prefill(gc, k, v, 64, w, y)
+    say("stats", st)
+
+
 def test_prefill_deterministic_and_debug_free_path_identical():
     say("determinism")
     k, v = outlier_kv(5, 2, 200, 4)
