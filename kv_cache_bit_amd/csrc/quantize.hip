@@ -206,6 +206,12 @@ __device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp1
 }
 
 // W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]
+//
+// An MFMA whose destination shares registers with its A or B source reads clobbered
+// rows on this hardware. After each accumulation chain an empty asm takes the chain's
+// result as read-write and all its A and B fragments as inputs: the data dependency
+// pins it after the chain's MFMAs, so every source is still live when each of them
+// issues and the register allocator cannot hand a source's registers to the result.
 __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& hf, f4v (&acc)[2][8]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -215,15 +221,39 @@ __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& 
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+      asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
+                   "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
       acc[mb][nb] = s;
     }
   }
-  // Keep the A fragments allocated until every MFMA has issued: an MFMA whose
-  // destination reuses its own A registers reads clobbered rows on this hardware.
+}
+
+// Rotation fused with the squares and the first token-axis sums (u = 1): each chain's
+// W' block is squared as soon as it is complete, so the fp32 block is never held whole.
+// Returns the row total of the lane's own token (see row_rs8).
+__device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, float (&p)[2][8][4],
+                                                int c) {
+  float tp[8];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int k = 0; k < 8; ++k) tp[k] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(a[mb][ks]));
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+      asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
+                   "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[mb][nb][i] = s[i] * s[i];
+        tp[4 * mb + i] += p[mb][nb][i];
+      }
+    }
+  }
+  return row_rs8(tp, c);
 }
 
 // ----------------------------------------------------------------------------- LDS
@@ -323,9 +353,9 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
 // two channels (16g + c, 64 + 16g + c): their scalars are computed once, by the owner,
 // and broadcast back.
 template <int NW, bool DBG>
-__device__ void tile_finish(f4v (&acc)[2][8], float (&p)[2][8][4], float st_own, int lane, int sub, int stream,
-                            int n_it, TileLds<NW>& sh, uint32_t& flags, float* dbg_w, float* dbg_y,
-                            long long dstride) {
+__device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2][8][4], float st_own, int lane,
+                            int sub, int stream, int n_it, TileLds<NW>& sh, uint32_t& flags, float* dbg_w,
+                            float* dbg_y, long long dstride) {
   constexpr int G = 32 * NW;
   const int g = lane >> 4, c = lane & 15;
   const int tau_own = c >> 1;  // own token: mb = tau/4, i = tau%4
@@ -384,6 +414,19 @@ __device__ void tile_finish(f4v (&acc)[2][8], float (&p)[2][8][4], float st_own,
     c16_own[q] = round_f16(x);
     ic_own[q] = __builtin_amdgcn_rcpf(c16_own[q]);
   }
+  // W' again, from the kept fp16 inputs: the matrix cores redo the exact rotation so the
+  // 64 fp32 values need not stay in registers through VarN (the asm ties the inputs to
+  // the last VarN sums, so the recomputation is not hoisted back into VarN)
+  h8v av2[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      av2[mb][ks] = av[mb][ks];
+      asm volatile("" : "+v"(av2[mb][ks]) : "v"(s_tok), "v"(s_ch[0]), "v"(s_ch[1]));
+    }
+  f4v acc[2][8];
+  rotate_block(av2, hf, acc);
   if constexpr (DBG) {
     float ic[8];
     col_gather8(ic_own, ic);
@@ -476,25 +519,6 @@ __device__ void tile_finish(f4v (&acc)[2][8], float (&p)[2][8][4], float st_own,
   tile_sync<NW>();
 }
 
-// squares of the rotated block and the row total of the lane's own token (the first
-// token pass, u = 1)
-__device__ __forceinline__ float squares_and_token_sum(const f4v (&acc)[2][8], float (&p)[2][8][4], int c) {
-  float tp[8];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float t = 0.0f;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        p[mb][nb][i] = acc[mb][nb][i] * acc[mb][nb][i];
-        t += p[mb][nb][i];
-      }
-      tp[4 * mb + i] = t;
-    }
-  return row_rs8(tp, c);
-}
-
 template <int NW>
 __device__ __forceinline__ void copy_record(const TileLds<NW>& sh, uint8_t* dst, int lane, int sub) {
   constexpr int N16 = TileLds<NW>::TR / 16;
@@ -577,37 +601,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const Frags hf = hadamard_frags(g, c);
 
   // A rows are tokens t0 + 16mb + c; K chunk 4ks + g holds channels 8(4ks + g) .. +7
-  uint4 raw[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      raw[mb][ks] = *reinterpret_cast<const uint4*>(
-          src + (((long long)b * a.T + t0 + 16 * mb + c) * L.Hkv + h) * kD + 8 * (4 * ks + g));
-  SigMask msk[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) msk[ks] = sigma_masks(hdr, 4 * ks + g);
-
-  f4v acc[2][8];
+  const uint16_t* rows = src + (((long long)b * a.T + t0 + c) * L.Hkv + h) * kD + 8 * g;
+  const long long row16 = 16LL * L.Hkv * kD;  // 16 tokens further
   float p[2][8][4];
   float st;
+  h8v av[2][4];
   {
-    h8v av[2][4];
+    uint4 raw[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) av[mb][ks] = canon_a<false>(raw[mb][ks], msk[ks]);
-    rotate_block(av, hf, acc);
+      for (int ks = 0; ks < 4; ++ks) raw[mb][ks] = *reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const SigMask m = sigma_masks(hdr, 4 * ks + g);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) av[mb][ks] = canon_a<false>(raw[mb][ks], m);
+    }
   }
-  st = squares_and_token_sum(acc, p, c);
+  st = rotate_squares(av, hf, p, c);
   if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion): redo saturating
-    h8v av[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ks = 0; ks < 4; ++ks) {
+      const SigMask m = sigma_masks(hdr, 4 * ks + g);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) av[mb][ks] = canon_a<true>(raw[mb][ks], msk[ks]);
-    rotate_block(av, hf, acc);
-    st = squares_and_token_sum(acc, p, c);
+      for (int mb = 0; mb < 2; ++mb)
+        av[mb][ks] = canon_a<true>(*reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks), m);
+    }
+    st = rotate_squares(av, hf, p, c);
     flags |= KVARN_FLAG_SATURATED;
   }
 
@@ -623,7 +644,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     dw = (valid && pw) ? pw + doff : nullptr;
     dy = (valid && py) ? py + doff : nullptr;
   }
-  tile_finish<NW, DBG>(acc, p, st, lane, sub, s, L.n_it, sh, flags, dw, dy, dstride);
+  tile_finish<NW, DBG>(av, hf, p, st, lane, sub, s, L.n_it, sh, flags, dw, dy, dstride);
   if (valid) {
     copy_record<NW>(sh, a.cache + L.record(b, h, tile, s), lane, sub);
     raise_flags(hdr, flags);
@@ -676,11 +697,9 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
         av[mb][ks] = sign_a(w, m);
       }
     }
-    f4v acc[2][8];
     float p[2][8][4];
-    rotate_block(av, hf, acc);
-    const float st = squares_and_token_sum(acc, p, c);
-    tile_finish<NW, false>(acc, p, st, lane, sub, s, L.n_it, sh, flags, nullptr, nullptr, 0);
+    const float st = rotate_squares(av, hf, p, c);
+    tile_finish<NW, false>(av, hf, p, st, lane, sub, s, L.n_it, sh, flags, nullptr, nullptr, 0);
     copy_record<NW>(sh, a.cache + L.record(b, h, (pos + 1) / G - 1, s), lane, sub);
   }
   raise_flags(hdr, flags);
