@@ -32,8 +32,13 @@
  *   tail    [B][Hkv][2][G][D] fp16, unrotated tokens of the group being filled,
  *           slot = token index mod G.
  *   Tile record TR = G*D/4 + 2G + 6D bytes (1856 at G=32, 2944 at G=64):
- *     codes  G*D/4 B: K: code(t,j) in byte t*D/4 + j/4, bits 2*(j%4) (channels fastest)
- *                     V: code(t,j) in byte j*G/4 + t/4, bits 2*(t%4) (tokens fastest)
+ *     codes  G*D/4 B, four 2-bit codes per byte, slot k of a byte at bits 2k..2k+1:
+ *            K: token t owns the D/4 bytes from t*D/4 on, read as D/16 little-endian
+ *               32-bit words; channel j = 16m + 2w + d (m < 8, d < 2) sits in word w
+ *               at slot 4(m/2) + m%2 + 2d, i.e. byte t*D/4 + 4w + m/2, bits
+ *               2(m%2 + 2d): each byte holds the channel pairs (2i, 2i+1) of two
+ *               channel blocks of 16;
+ *            V: code(t,j) in byte j*G/4 + t/4, bits 2*(t%4) (tokens fastest);
  *     r fp16[G], c fp16[D], s fp16[D], z fp16[D].
  *   A tile token dequantizes as x_hat = (r_t c_j (z_j + s_j q_tj))_j H_D^T.
  *
@@ -121,7 +126,9 @@ KVARN_API kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, con
 KVARN_API kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_out, void* v_out,
                               int32_t max_tokens, int32_t out_dtype, void* stream);
 
-/* Workspace bytes kvarn_attn_decode needs for num_q_heads query heads. Host only. */
+/* Workspace bytes kvarn_attn_decode needs for num_q_heads query heads. Host only.
+ * The workspace holds one f32 partial (m, l, 2 pad, o[D]) per (batch, query head,
+ * span); a span is 4 x tpw tiles, tpw in [2, 16] chosen from the geometry alone. */
 KVARN_API kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes);
 
 /* Single-query decode attention over every cached token:
@@ -131,7 +138,9 @@ KVARN_API kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t n
  * (ai-paper-analysis page, section 3.1: Q takes the same rotation so Q K^T is
  * unchanged), or already rotated when flags has KVARN_Q_PREROTATED.
  * softmax_scale <= 0 selects 1/sqrt(D). Tiles are read in rotated space with the
- * dequantization folded into the dot products; tail tokens in original space.
+ * dequantization folded into the dot products (on the f16 MFMA, codes exact, the
+ * per-tile factors split into f16 hi + lo parts); tail tokens in original space.
+ * Two launches on `stream`: the tile pass, then the merge over spans and the tail.
  * workspace: device, >= kvarn_attn_workspace_bytes; out: device f32 [B][Hq][D],
  * original space. An empty sequence gives 0. num_q_heads / num_kv_heads <= 8. */
 KVARN_API kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const void* q_bf16,

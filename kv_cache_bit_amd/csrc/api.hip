@@ -152,18 +152,19 @@ kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_ou
   return dev(launch_dequant(a, static_cast<hipStream_t>(stream)));
 }
 
-// Split-K over tiles: enough work-groups to cover the chip about twice, at least 8
-// tiles per split. Depends only on the geometry, so the workspace size is static.
-static int attn_splits(const kvarn_geom* g, int* tiles_per_split) {
+// Work split of attn_decode: a work-group of 4 waves per (batch, kv head, group of up to
+// 4 query heads, span of 4 * tpw tiles). tpw is chosen for about 2048 work-groups over
+// the cache capacity, between 2 and 16 tiles per wave. Depends only on the geometry, so
+// the workspace size is static.
+static void attn_split(const kvarn_geom* g, int grp, int* tpw, int* nspan) {
   const int tiles = g->capacity / g->group;
-  const long long seqs = (long long)g->batch * g->num_kv_heads;
-  long long want = (2048 + seqs - 1) / seqs;
-  long long maxs = (tiles + 7) / 8;
-  if (want > maxs) want = maxs;
-  if (want < 1) want = 1;
-  const int tps = (int)((tiles + want - 1) / want);
-  *tiles_per_split = tps;
-  return (tiles + tps - 1) / tps;  // the tail sits at tile index len/G < tiles when present
+  const long long units = (long long)g->batch * g->num_kv_heads * ((grp + 3) / 4);
+  const long long want = (2048 + units - 1) / units;  // spans wanted per sequence
+  long long t = (tiles + 4 * want - 1) / (4 * want);
+  if (t < 2) t = 2;
+  if (t > 16) t = 16;
+  *tpw = (int)t;
+  *nspan = (int)((tiles + 4 * t - 1) / (4 * t));
 }
 
 kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes) {
@@ -172,9 +173,9 @@ kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads
   if (!bytes) return KVARN_ERR_NULL;
   if (num_q_heads <= 0 || num_q_heads % g->num_kv_heads != 0) return KVARN_ERR_GEOM;
   if (num_q_heads / g->num_kv_heads > 8) return KVARN_ERR_UNSUPPORTED;
-  int tps;
-  const int ns = attn_splits(g, &tps);
-  *bytes = (size_t)g->batch * num_q_heads * ns * (2 + 2 * kD) * sizeof(float);
+  int tpw, nspan;
+  attn_split(g, num_q_heads / g->num_kv_heads, &tpw, &nspan);
+  *bytes = (size_t)g->batch * num_q_heads * nspan * (4 + kD) * sizeof(float);
   return KVARN_OK;
 }
 
@@ -197,7 +198,8 @@ kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const voi
   a.out = out;
   a.Hq = num_q_heads;
   a.grp = num_q_heads / g->num_kv_heads;
-  a.n_split = attn_splits(g, &a.tiles_per_split);
+  a.nqg = (a.grp + 3) / 4;
+  attn_split(g, a.grp, &a.tpw, &a.nspan);
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)kD);
   a.flags = flags;
   return dev(launch_attn(a, static_cast<hipStream_t>(stream)));

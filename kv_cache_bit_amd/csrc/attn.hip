@@ -3,303 +3,508 @@
 // The query takes the same randomized Hadamard rotation as the keys, so scores are
 // computed in rotated space without rotating the cache back (ai-paper-analysis page,
 // section 3.1: H H^T = I leaves Q K^T unchanged). Dequantization is folded into the
-// dot products: for a K tile with scales r (token), c, s, z (channel),
-//   score_t = scale * r_t * (sum_j a_j q_tj + b),  a_j = q_rot,j c_j s_j,  b = sum_j q_rot,j c_j z_j,
-// and for a V tile with weights w_t = p_t r_t,
-//   o_rot,j += c_j (s_j sum_t w_t q_tj + z_j sum_t w_t).
-// Tail tokens (fp16, unrotated) are scored and accumulated in original space. Each
-// work-group handles one (batch, kv head, split) with an online softmax; a merge
-// kernel combines the splits in a fixed order (log-sum-exp), rotates the V
-// accumulator back by H_D^T, adds the tail part and normalizes.
+// products: for a K tile with scales r (token), c, s, z (channel) and codes q,
+//   score_t = scale * r_t * (sum_j q_tj a_j + b),  a_j = q_rot,j c_j s_j,  b = sum_j q_rot,j c_j z_j,
+// and for a V tile with weights w_t = p_t r_t (p the softmax numerators),
+//   o_rot,j += c_j s_j sum_t w_t q_tj + c_j z_j sum_t w_t.
+// Both sums over codes run on the 16x16x32 f16 MFMA:
+//   * codes become exact f16 values 0..3: a 2-bit code zero-extended to a nibble is
+//     the fp4 (e2m1) value q/2, and the packed fp4 -> f16 conversion with scale 2
+//     turns one byte (two nibbles) into two f16 codes;
+//   * the per-tile factors (a_j, w_t) are split into f16 hi + lo parts, held in two
+//     MFMA columns / rows and added after the product, so the result keeps about 22
+//     bits of each factor; a per-tile power-of-two scale puts the largest factor near
+//     2^14 first;
+//   * K: A = codes (16 tokens x 32 channels), B = a-values (32 channels x {hi, lo} x
+//     4 query heads); V: A = weights ({hi, lo} x 4 query heads x 32 tokens, twice:
+//     rows 8..15 hold the same weights against a second channel block), B = codes.
+// The K code word layout puts each channel pair (2i, 2i+1) in one byte, so a converted
+// byte is one dword of the MFMA operand; the V layout (tokens fastest) gives 8
+// consecutive tokens of a channel per 16-bit load.
+//
+// Work split: a work-group of 4 waves per (batch, kv head, group of up to 4 query heads,
+// span of 4 x tpw tiles); wave w takes tiles w, w + 4, ... of the span with its own
+// online softmax, the 4 wave states are merged in LDS and one partial (m, l, o_rot) per
+// query head and span goes to the workspace. The merge kernel combines the spans in
+// index order (log-sum-exp), adds the fp16 tail tokens (unrotated, scored in original
+// space), rotates the V part back by H_D^T and normalizes. Scores live in log2 units.
 #include "kvarn_common.h"
 #include "kvarn_launch.h"
 
 namespace kvarn {
 
-constexpr int kWs = 2 + 2 * kD;  // floats per (b, q head, split): m, l, o_rot[D], o_orig[D]
+constexpr int kPart = 4 + kD;  // floats per (b, q head, span): m (log2 units), l, 2 pad, o_rot[D]
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kNib = 0x33333333u;
 
-template <int GM>
+struct WaveLds {
+  uint4 bop[128];   // K-side B operand, unit (s, g, n8 ^ swz(s, g)) = 4 dwords
+  float2 vf[16][8]; // V fold factors (c s, c z) of channel 16 blk + n at [n][blk]
+};
 struct AttnLds {
-  float qrot[GM][kD];
-  float qorig[GM][kD];
-  float av[GM][kD];   // a_j of the current K tile
-  float bpart[2][GM];
-  float sc[GM][64];   // scores of the current tile
-  float wts[GM][64];  // softmax weights times the V token scale
-  float alpha[GM], sumw[GM];
+  float qrot[4][kD];
+  union {
+    WaveLds w[4];
+    float oo[4][4][kD];  // wave, query head, channel (after the tile loop)
+  } u;
+  float mm[4][4], ll[4][4];
 };
 
-template <int GM>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  __shared__ AttnLds<GM> sh;
-  const Layout& L = a.L;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = L.G, grp = a.grp;
-  const int split = blockIdx.x % a.n_split;
-  const int bh = blockIdx.x / a.n_split;
-  const int h = bh % L.Hkv, b = bh / L.Hkv;
-  const int n = *reinterpret_cast<const int32_t*>(a.cache + L.len_off(b, h, 0));
-  const int nfull = n / G, ntail = n % G;
-  const int lo = split * a.tiles_per_split;
-  const int hi = min(lo + a.tiles_per_split, nfull);
-  const bool do_tail = ntail > 0 && nfull >= lo && nfull < lo + a.tiles_per_split;
+// ----------------------------------------------------------------------------- helpers
+// Two f16 codes from byte BY of a nibble plane (each nibble a 2-bit code, e2m1 = q/2).
+template <int BY>
+__device__ __forceinline__ uint32_t cvt2(uint32_t plane) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(plane, 2.0f, BY));
+}
+__device__ __forceinline__ h8v as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint4 v = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(h8v, v);
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const f2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
+}
 
-  // --- query: rotate into the cache basis (or back, when it arrives rotated)
-  if (wave < 2) {
-    const int rg = lane >> 4, cg = lane & 15;
-    const int gi = wave * 4 + rg;
-    float sg[8];
-    load_sigma(a.cache, cg, sg);
+// max over the 64 lanes of non-negative floats (compared as integers), wave-uniform
+__device__ __forceinline__ uint32_t wave_max_pos(float x) {
+  uint32_t u = (uint32_t)__float_as_int(x);
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kQx1, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kQx2, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kHalfMirror, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kMirror, 0xF, 0xF, false));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)u, 0), (uint32_t)__builtin_amdgcn_readlane((int)u, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)u, 32), (uint32_t)__builtin_amdgcn_readlane((int)u, 48));
+  return max(a, b);
+}
+// Power-of-two scale 2^(14 - e) for a bound with biased exponent e, and its inverse;
+// e is clamped to [15, 254] so both are normal floats.
+__device__ __forceinline__ void pow2_scale(uint32_t bound_bits, float& s, float& inv) {
+  int e = (int)(bound_bits >> 23);
+  e = e < 15 ? 15 : (e > 254 ? 254 : e);
+  s = __int_as_float((268 - e) << 23);
+  inv = __int_as_float((e - 14) << 23);
+}
+// across the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float rows_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = vmax(__int_as_float(p[0]), __int_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return vmax(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(p[0]) + __int_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(q[0]) + __int_as_float(q[1]);
+}
+// Sum over the wave of 4 per-lane partials; lane c of every row returns the total of
+// partial (c >> 1) & 3. Reduce-scatter: row_half_mirror pairs lanes differing in bit 2
+// (each keeps the pair of partials its bit 2 selects), quad xor 2 pairs bit 1, then the
+// sets {c, c ^ 1} and the row halves (row_ror:8) and the 4 rows are summed.
+__device__ __forceinline__ float reduce4(const float (&v)[4], int c) {
+  const bool b2 = (c >> 2) & 1, b1 = (c >> 1) & 1;
+  const float k0 = b2 ? v[2] : v[0], k1 = b2 ? v[3] : v[1];
+  const float s0 = b2 ? v[0] : v[2], s1 = b2 ? v[1] : v[3];
+  const float u0 = k0 + dppf<kHalfMirror>(s0), u1 = k1 + dppf<kHalfMirror>(s1);
+  float x = (b1 ? u1 : u0) + dppf<kQx2>(b1 ? u0 : u1);
+  x += dppf<kQx1>(x);
+  x += dppf<kRor8>(x);
+  return rows_sum(x);
+}
+
+// ----------------------------------------------------------------------------- main kernel
+// Lane roles (g = lane / 16, c = lane % 16, m = lane):
+//  * K MFMA, token block mb: lane (c, g) supplies token 32 kb + 8 (c/4) + (c%2) +
+//    4 ((c/2)%2) + 2 (mb%2) (kb = mb/2), words 2g, 2g+1; the score output leaves lane
+//    (c, g) with tokens 32 kb + 8 g + tau(2 i + mb%2), tau = [0,2,1,3,4,6,5,7], in
+//    column c = 2 qh + part (c >= 8 repeats columns 0..7);
+//  * MFMA s takes word 2g + s/2, channel blocks nb = 4 (s%2) .. +3, one converted byte
+//    per block: element pair (2 (nb%4), +1) = channels (16 nb + 2w, +1);
+//  * lane m computes the a-values of channels (16 (m/8) + 2 (m%8), +1) for the 4 query
+//    heads and writes them to the B-operand slot (s, g, kk) = (2 (m%2) + m/32, (m%8)/2,
+//    (m/8)%4) in LDS; it also owns those channels' V fold factors;
+//  * V MFMA i (i < 4): columns = channels 16 i + c (rows 0..7 of A) and 16 (i+4) + c
+//    (rows 8..15), lane (c, g) folds rows 4 (g%2) .. +3 of block i + 4 (g/2), i.e. query
+//    heads 2 (g%2) + {0, 1} of channel 16 (i + 4 (g/2)) + c.
+template <int G>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  constexpr int NKB = G / 32;  // 32-token blocks per tile
+  constexpr int NMB = 2 * NKB; // 16-token K blocks per tile
+  constexpr int RO = G * kD / 4, CO = RO + 2 * G, SO = CO + 2 * kD, ZO = SO + 2 * kD;
+  __shared__ AttnLds sh;
+  const Layout& L = a.L;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  int bid = blockIdx.x;
+  const int span = bid % a.nspan;
+  bid /= a.nspan;
+  const int qg = bid % a.nqg;
+  bid /= a.nqg;
+  const int h = bid % L.Hkv, b = bid / L.Hkv;
+  const int n = *reinterpret_cast<const int32_t*>(a.cache + L.len_off(b, h, 0));
+  const int nfull = n / G;
+  const int t0 = span * 4 * a.tpw;
+  if (t0 >= nfull) return;  // uniform over the work-group
+  const int t1 = min(t0 + 4 * a.tpw, nfull);
+  const int q0 = qg * 4;
+  const float qscale = kLog2e * a.scale;
+
+  // --- query heads q0 .. q0+3 of this kv head, rotated into the cache basis
+  if (wave == 0) {
     float qv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (gi < grp) {
-      const uint4 w = *reinterpret_cast<const uint4*>(a.q + ((long long)b * a.Hq + h * grp + gi) * kD + 8 * cg);
+    if (q0 + g < a.grp) {
+      const uint4 w = *reinterpret_cast<const uint4*>(a.q + ((long long)b * a.Hq + h * a.grp + q0 + g) * kD + 8 * c);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
       for (int k = 0; k < 4; ++k) {
         qv[2 * k] = bf16lo(ws[k]);
         qv[2 * k + 1] = bf16hi(ws[k]);
       }
     }
-    float t[8];
-    const bool pre = a.flags & KVARN_Q_PREROTATED;
-    for (int e = 0; e < 8; ++e) t[e] = pre ? qv[e] : qv[e] * sg[e];
-    fwht128(t, cg);
-    for (int e = 0; e < 8; ++e) t[e] *= kInvSqrtD;
-    if (pre)
-      for (int e = 0; e < 8; ++e) t[e] *= sg[e];  // q = q_rot H_D^T
-    if (gi < GM) {
-      for (int e = 0; e < 8; ++e) {
-        sh.qrot[gi][8 * cg + e] = pre ? qv[e] : t[e];
-        sh.qorig[gi][8 * cg + e] = pre ? t[e] : qv[e];
-      }
+    if (!(a.flags & KVARN_Q_PREROTATED)) {
+      float sg[8];
+      load_sigma(a.cache, c, sg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] *= sg[e];
+      fwht128(qv, c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] *= kInvSqrtD;
     }
+    store8f(&sh.qrot[g][8 * c], qv);
   }
   __syncthreads();
 
-  float m[GM], l[GM], orot[GM], oorig[GM];  // o*: channel j = tid >> 1 (lanes with tid even)
-  for (int gi = 0; gi < GM; ++gi) {
-    m[gi] = -INFINITY;
-    l[gi] = 0.0f;
-    orot[gi] = oorig[gi] = 0.0f;
+  // --- per-lane constants
+  const int nbm = lane >> 3, wm = lane & 7;
+  const int j0 = 16 * nbm + 2 * wm;
+  float qr[4][2];
+  float mql = 0.0f;
+#pragma unroll
+  for (int qh = 0; qh < 4; ++qh) {
+    const float2 v = *reinterpret_cast<const float2*>(&sh.qrot[qh][j0]);
+    qr[qh][0] = v.x;
+    qr[qh][1] = v.y;
+    mql = fmaxf(mql, fmaxf(fabsf(v.x), fabsf(v.y)));
   }
-  const float scale = a.scale;
-  const int ro = G * kD / 4, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
+  const float mq = __int_as_float((int)wave_max_pos(mql));
+  WaveLds& wl = sh.u.w[wave];
+  uint32_t* bop = reinterpret_cast<uint32_t*>(wl.bop);
+  const int s_m = 2 * (wm & 1) + (nbm >> 2), g_m = wm >> 1, kk_m = nbm & 3;
+  const int wbase = (s_m * 4 + g_m) * 8, wswz = (2 * s_m + (g_m >> 1)) & 7;
+  int krow[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+    krow[mb] = 32 * (mb >> 1) + 8 * (c >> 2) + (c & 1) + 4 * ((c >> 1) & 1) + 2 * (mb & 1);
+  const float partf = (float)(c & 1);
+  const bool rows_lo = c < 8;
+  const uint32_t sh_g1 = (uint32_t)(g & 1);
 
-  for (int tile = lo; tile < hi; ++tile) {
+  float m_run = -INFINITY, l_run = 0.0f;
+  float o[2][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[0][k] = o[1][k] = 0.0f;
+
+  for (int tile = t0 + wave; tile < t1; tile += 4) {
     const uint8_t* rk = a.cache + L.record(b, h, tile, 0);
-    const uint8_t* rvp = rk + L.tr;
-    // A: per-channel query factors of this K tile
-    if (tid < kD) {
-      const int j = tid;
-      const float c = (float)*reinterpret_cast<const _Float16*>(rk + co + 2 * j);
-      const float s = (float)*reinterpret_cast<const _Float16*>(rk + so + 2 * j);
-      const float z = (float)*reinterpret_cast<const _Float16*>(rk + zo + 2 * j);
-      for (int gi = 0; gi < grp; ++gi) {
-        const float qc = sh.qrot[gi][j] * c;
-        sh.av[gi][j] = qc * s;
-        float bz = qc * z;
-        for (int o = 32; o >= 1; o >>= 1) bz += __shfl_xor(bz, o);
-        if (lane == 0) sh.bpart[wave][gi] = bz;
+    const uint8_t* rv = rk + L.tr;
+    // ---- loads
+    uint2 kc[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) kc[mb] = *reinterpret_cast<const uint2*>(rk + krow[mb] * 32 + 8 * g);
+    const uint32_t kcs = *reinterpret_cast<const uint32_t*>(rk + CO + 4 * lane);
+    const uint32_t kss = *reinterpret_cast<const uint32_t*>(rk + SO + 4 * lane);
+    const uint32_t kzs = *reinterpret_cast<const uint32_t*>(rk + ZO + 4 * lane);
+    const uint32_t vcs = *reinterpret_cast<const uint32_t*>(rv + CO + 4 * lane);
+    const uint32_t vss = *reinterpret_cast<const uint32_t*>(rv + SO + 4 * lane);
+    const uint32_t vzs = *reinterpret_cast<const uint32_t*>(rv + ZO + 4 * lane);
+    uint4 kr[NKB], vr[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      kr[kb] = *reinterpret_cast<const uint4*>(rk + RO + 2 * (32 * kb + 8 * g));
+      vr[kb] = *reinterpret_cast<const uint4*>(rv + RO + 2 * (32 * kb + 8 * g));
+    }
+    uint32_t vq[4][NKB];  // channel 16 i + c (low half) and 16 (i + 4) + c (high half)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(rv + (16 * i + c) * (G / 4) + 2 * (4 * kb + g));
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(rv + (16 * (i + 4) + c) * (G / 4) + 2 * (4 * kb + g));
+        vq[i][kb] = lo | (hi << 16);
+      }
+
+    // ---- K-side factors of this lane's channel pair; per-tile scale of the a-values
+    const float cs0 = f16lo(kcs) * f16lo(kss), cs1 = f16hi(kcs) * f16hi(kss);
+    const float cz0 = f16lo(kcs) * f16lo(kzs), cz1 = f16hi(kcs) * f16hi(kzs);
+    float sB, invSB;
+    pow2_scale(wave_max_pos(fmaxf(cs0, cs1) * mq), sB, invSB);
+    const float f0 = cs0 * sB, f1 = cs1 * sB;
+    wave_sync();  // the previous tile's LDS reads are issued before these writes
+#pragma unroll
+    for (int qh = 0; qh < 4; ++qh) {
+      const float a0 = f0 * qr[qh][0], a1 = f1 * qr[qh][1];
+      const uint32_t hv = pack_f16(a0, a1);
+      const uint32_t lv = pack_f16(a0 - f16lo(hv), a1 - f16hi(hv));
+      bop[(wbase + ((2 * qh) ^ wswz)) * 4 + kk_m] = hv;
+      bop[(wbase + ((2 * qh + 1) ^ wswz)) * 4 + kk_m] = lv;
+    }
+    wl.vf[2 * wm][nbm] = make_float2(f16lo(vcs) * f16lo(vss), f16lo(vcs) * f16lo(vzs));
+    wl.vf[2 * wm + 1][nbm] = make_float2(f16hi(vcs) * f16hi(vss), f16hi(vcs) * f16hi(vzs));
+    float bp[4];
+#pragma unroll
+    for (int qh = 0; qh < 4; ++qh) bp[qh] = fmaf(qr[qh][0], cz0, qr[qh][1] * cz1);
+    const float bq = reduce4(bp, c) * qscale;
+    wave_sync();
+
+    // ---- scores: S = sum_j q_tj a_j for the lane's 8 (or 16) tokens and query head c/2 % 4
+    h8v bk[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int unit = (s * 4 + g) * 8 + ((c & 7) ^ ((2 * s + (g >> 1)) & 7));
+      bk[s] = __builtin_bit_cast(h8v, wl.bop[unit]);
+    }
+    const float K1 = qscale * invSB;
+    float lsc[NMB][4];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const uint32_t x0 = kc[mb].x, x1 = kc[mb].y;
+      const uint32_t e0 = x0 & kNib, o0 = (x0 >> 2) & kNib, e1 = x1 & kNib, o1 = (x1 >> 2) & kNib;
+      f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      h8v av0 = as_h8(cvt2<0>(e0), cvt2<0>(o0), cvt2<1>(e0), cvt2<1>(o0));
+      h8v av1 = as_h8(cvt2<2>(e0), cvt2<2>(o0), cvt2<3>(e0), cvt2<3>(o0));
+      h8v av2 = as_h8(cvt2<0>(e1), cvt2<0>(o1), cvt2<1>(e1), cvt2<1>(o1));
+      h8v av3 = as_h8(cvt2<2>(e1), cvt2<2>(o1), cvt2<3>(e1), cvt2<3>(o1));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bk[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bk[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av2, bk[2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av3, bk[3], acc, 0, 0, 0);
+      asm volatile("" : "+v"(acc) : "v"(av0), "v"(av1), "v"(av2), "v"(av3), "v"(bk[0]), "v"(bk[1]), "v"(bk[2]),
+                   "v"(bk[3]));
+      const uint4 rr = kr[mb >> 1];
+      const uint32_t rd[2] = {(mb & 1) ? rr.y : rr.x, (mb & 1) ? rr.w : rr.z};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float S = acc[i] + dppf<kQx1>(acc[i]);  // hi + lo columns
+        const uint32_t rw = rd[i >> 1];
+        const float r = (i & 1) ? f16hi(rw) : f16lo(rw);
+        lsc[mb][i] = fmaf(S, K1, bq) * r;
       }
     }
-    __syncthreads();
-    // B: scores; thread = (token, code word `part`: channels 16m + 2 part + d in slot 8d + m)
-    {
-      const int part = tid & 7;
-      for (int tok = tid >> 3; tok < G; tok += 32) {
-        const uint32_t cw = *reinterpret_cast<const uint32_t*>(rk + tok * 32 + 4 * part);
-        float d[GM];
-        for (int gi = 0; gi < GM; ++gi) d[gi] = 0.0f;
-        for (int k = 0; k < 16; ++k) {
-          const float qq = (float)((cw >> (2 * k)) & 3u);
-          const int j = 16 * (k & 7) + 2 * part + (k >> 3);
-          for (int gi = 0; gi < grp; ++gi) d[gi] = fmaf(sh.av[gi][j], qq, d[gi]);
-        }
-        const float rt = (float)*reinterpret_cast<const _Float16*>(rk + ro + 2 * tok);
-        for (int gi = 0; gi < grp; ++gi) {
-          float v = d[gi];
-          v += xshfl<1>(v);
-          v += xshfl<2>(v);
-          v += xshfl<4>(v);
-          if (part == 0) sh.sc[gi][tok] = scale * rt * (v + (sh.bpart[0][gi] + sh.bpart[1][gi]));
-        }
+
+    // ---- online softmax (query head c/2 % 4; all 4 rows hold the same head)
+    float tmax = lsc[0][0];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = vmax(tmax, lsc[mb][i]);
+    tmax = rows_max(tmax);
+    const float mnew = vmax(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+    float psum = 0.0f, wsum = 0.0f, wmx = 0.0f;
+    float pr[NMB][4];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const uint4 rr = vr[mb >> 1];
+      const uint32_t rd[2] = {(mb & 1) ? rr.y : rr.x, (mb & 1) ? rr.w : rr.z};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(lsc[mb][i] - mnew);
+        const uint32_t rw = rd[i >> 1];
+        const float r = (i & 1) ? f16hi(rw) : f16lo(rw);
+        psum += p;
+        pr[mb][i] = p * r;
+        wsum += pr[mb][i];
+        wmx = fmaxf(wmx, pr[mb][i]);
       }
     }
-    __syncthreads();
-    // C: online softmax (wave 0); V token scales folded into the weights
-    if (wave == 0) {
-      float rvv = 0.0f;
-      if (lane < G) rvv = (float)*reinterpret_cast<const _Float16*>(rvp + ro + 2 * lane);
-      for (int gi = 0; gi < grp; ++gi) {
-        const float x = lane < G ? sh.sc[gi][lane] : -INFINITY;
-        float mt = x;
-        for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
-        const float mn = fmaxf(m[gi], mt);
-        const float al = __expf(m[gi] - mn);
-        const float p = lane < G ? __expf(x - mn) : 0.0f;
-        const float w = p * rvv;
-        float ps = p, ws = w;
-        for (int o = 32; o >= 1; o >>= 1) {
-          ps += __shfl_xor(ps, o);
-          ws += __shfl_xor(ws, o);
-        }
-        sh.wts[gi][lane] = w;
-        l[gi] = l[gi] * al + ps;
-        m[gi] = mn;
-        if (lane == 0) {
-          sh.alpha[gi] = al;
-          sh.sumw[gi] = ws;
-        }
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = mnew;
+    wsum = rows_sum(wsum);
+    float sV, invSV;
+    pow2_scale(wave_max_pos(wmx), sV, invSV);
+
+    // ---- V: weights (hi or lo part by column parity) against the codes
+    h8v aw1[NKB], aw2[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      uint32_t d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float w0 = pr[2 * kb][i] * sV, w1 = pr[2 * kb + 1][i] * sV;
+        const uint32_t hv = pack_f16(w0, w1);
+        d[i] = pack_f16(fmaf(-partf, f16lo(hv), w0), fmaf(-partf, f16hi(hv), w1));
+      }
+      const h8v wv = as_h8(d[0], d[1], d[2], d[3]);
+      const h8v zv = as_h8(0u, 0u, 0u, 0u);
+      aw1[kb] = rows_lo ? wv : zv;
+      aw2[kb] = rows_lo ? zv : wv;
+    }
+    f4v cv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t x = vq[i][kb];
+        const uint32_t e = x & kNib, od = (x >> 2) & kNib;
+        const h8v b1 = as_h8(cvt2<0>(e), cvt2<0>(od), cvt2<1>(e), cvt2<1>(od));
+        const h8v b2 = as_h8(cvt2<2>(e), cvt2<2>(od), cvt2<3>(e), cvt2<3>(od));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw1[kb], b1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw2[kb], b2, acc, 0, 0, 0);
+        asm volatile("" : "+v"(acc) : "v"(aw1[kb]), "v"(aw2[kb]), "v"(b1), "v"(b2));
+      }
+      cv[i] = acc;
+    }
+
+    // ---- fold: o += (c s) acc + (c z) W for query heads 2 (g%2) + {0, 1}
+    const float wb0 = dppf<kNewBcast + 0>(wsum), wb2 = dppf<kNewBcast + 2>(wsum);
+    const float wb4 = dppf<kNewBcast + 4>(wsum), wb6 = dppf<kNewBcast + 6>(wsum);
+    const float wf[2] = {sh_g1 ? wb4 : wb0, sh_g1 ? wb6 : wb2};
+    if (__builtin_amdgcn_ballot_w64(alpha < 1.0f)) {
+      const float ab0 = dppf<kNewBcast + 0>(alpha), ab2 = dppf<kNewBcast + 2>(alpha);
+      const float ab4 = dppf<kNewBcast + 4>(alpha), ab6 = dppf<kNewBcast + 6>(alpha);
+      const float af0 = sh_g1 ? ab4 : ab0, af1 = sh_g1 ? ab6 : ab2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[0][i] *= af0;
+        o[1][i] *= af1;
       }
     }
-    __syncthreads();
-    // D: V accumulation; thread = (channel j, half of the tokens)
-    {
-      const int j = tid >> 1, half = tid & 1;
-      const int nb = G / 4;  // bytes per channel
-      float acc[GM];
-      for (int gi = 0; gi < GM; ++gi) acc[gi] = 0.0f;
-      for (int wq = 0; wq < nb / 8; ++wq) {  // 16 tokens per dword
-        const int dw = half * (nb / 8) + wq;
-        const uint32_t cw = *reinterpret_cast<const uint32_t*>(rvp + j * nb + 4 * dw);
-        for (int k = 0; k < 16; ++k) {
-          const float qq = (float)((cw >> (2 * k)) & 3u);
-          for (int gi = 0; gi < grp; ++gi) acc[gi] = fmaf(sh.wts[gi][16 * dw + k], qq, acc[gi]);
-        }
-      }
-      for (int gi = 0; gi < grp; ++gi) acc[gi] += xshfl<1>(acc[gi]);
-      if (half == 0) {
-        const float c = (float)*reinterpret_cast<const _Float16*>(rvp + co + 2 * j);
-        const float s = (float)*reinterpret_cast<const _Float16*>(rvp + so + 2 * j);
-        const float z = (float)*reinterpret_cast<const _Float16*>(rvp + zo + 2 * j);
-        for (int gi = 0; gi < grp; ++gi)
-          orot[gi] = orot[gi] * sh.alpha[gi] + c * fmaf(s, acc[gi], z * sh.sumw[gi]);
-      }
+    const float4* vfp = reinterpret_cast<const float4*>(&wl.vf[c][4 * (g >> 1)]);
+    const float4 f01 = vfp[0], f23 = vfp[1];
+    const float fcs[4] = {f01.x, f01.z, f23.x, f23.z}, fcz[4] = {f01.y, f01.w, f23.y, f23.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float csv = fcs[i] * invSV;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+        o[qq][i] = fmaf(csv, cv[i][2 * qq] + cv[i][2 * qq + 1], fmaf(fcz[i], wf[qq], o[qq][i]));
     }
-    __syncthreads();
   }
 
-  if (do_tail) {
-    const uint8_t* tk = a.cache + L.tail_row(b, h, 0, 0);
-    const uint8_t* tv = a.cache + L.tail_row(b, h, 1, 0);
-    {
-      const int part = tid & 7;
-      for (int tok = tid >> 3; tok < G; tok += 32) {
-        float d[GM];
-        for (int gi = 0; gi < GM; ++gi) d[gi] = 0.0f;
-        if (tok < ntail) {
-          const uint4* kp = reinterpret_cast<const uint4*>(tk + tok * 2 * kD + 32 * part);
-          float kv[16];
-          const uint4 w0 = kp[0], w1 = kp[1];
-          const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-          for (int k = 0; k < 8; ++k) {
-            kv[2 * k] = f16lo(ws[k]);
-            kv[2 * k + 1] = f16hi(ws[k]);
-          }
-          for (int k = 0; k < 16; ++k)
-            for (int gi = 0; gi < grp; ++gi) d[gi] = fmaf(sh.qorig[gi][16 * part + k], kv[k], d[gi]);
-        }
-        for (int gi = 0; gi < grp; ++gi) {
-          float v = d[gi];
-          v += xshfl<1>(v);
-          v += xshfl<2>(v);
-          v += xshfl<4>(v);
-          if (part == 0) sh.sc[gi][tok] = scale * v;
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      for (int gi = 0; gi < grp; ++gi) {
-        const float x = lane < ntail ? sh.sc[gi][lane] : -INFINITY;
-        float mt = x;
-        for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
-        const float mn = fmaxf(m[gi], mt);
-        const float al = __expf(m[gi] - mn);
-        const float p = lane < ntail ? __expf(x - mn) : 0.0f;
-        float ps = p;
-        for (int o = 32; o >= 1; o >>= 1) ps += __shfl_xor(ps, o);
-        sh.wts[gi][lane] = p;
-        l[gi] = l[gi] * al + ps;
-        m[gi] = mn;
-        if (lane == 0) sh.alpha[gi] = al;
-      }
-    }
-    __syncthreads();
-    {
-      const int j = tid >> 1, half = tid & 1;
-      float acc[GM];
-      for (int gi = 0; gi < GM; ++gi) acc[gi] = 0.0f;
-      for (int tok = half; tok < ntail; tok += 2) {
-        const float vv = (float)*reinterpret_cast<const _Float16*>(tv + tok * 2 * kD + 2 * j);
-        for (int gi = 0; gi < grp; ++gi) acc[gi] = fmaf(sh.wts[gi][tok], vv, acc[gi]);
-      }
-      for (int gi = 0; gi < grp; ++gi) acc[gi] += xshfl<1>(acc[gi]);
-      if (half == 0) {
-        for (int gi = 0; gi < grp; ++gi) {
-          orot[gi] *= sh.alpha[gi];
-          oorig[gi] = oorig[gi] * sh.alpha[gi] + acc[gi];
-        }
-      }
-    }
+  // --- merge the 4 waves of the span (fixed order), one partial per query head
+  l_run = rows_sum(l_run);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) sh.u.oo[wave][2 * (g & 1) + qq][16 * (i + 4 * (g >> 1)) + c] = o[qq][i];
+  if (g == 0 && c < 8 && (c & 1) == 0) {
+    sh.mm[wave][c >> 1] = m_run;
+    sh.ll[wave][c >> 1] = l_run;
   }
-
-  // partials: m and l live in wave 0, o_rot / o_orig in the even threads
-  for (int gi = 0; gi < grp; ++gi) {
-    float* w = a.ws + (((long long)b * a.Hq + h * grp + gi) * a.n_split + split) * kWs;
-    if (tid == 0) {
-      w[0] = m[gi];
-      w[1] = l[gi];
+  __syncthreads();
+  const int qh = threadIdx.x >> 6, j = 2 * lane;
+  if (q0 + qh < a.grp) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.mm[w][qh]);
+    float Ls = 0.0f, O0 = 0.0f, O1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sh.mm[w][qh];
+      if (mw == -INFINITY) continue;  // a wave without tiles
+      const float f = __builtin_amdgcn_exp2f(mw - M);
+      Ls = fmaf(f, sh.ll[w][qh], Ls);
+      O0 = fmaf(f, sh.u.oo[w][qh][j], O0);
+      O1 = fmaf(f, sh.u.oo[w][qh][j + 1], O1);
     }
-    if ((tid & 1) == 0) {
-      w[2 + (tid >> 1)] = orot[gi];
-      w[2 + kD + (tid >> 1)] = oorig[gi];
+    float* dst = a.ws + (((long long)b * a.Hq + h * a.grp + q0 + qh) * a.nspan + span) * kPart;
+    if (lane == 0) {
+      dst[0] = M;
+      dst[1] = Ls;
     }
+    *reinterpret_cast<float2*>(dst + 4 + j) = make_float2(O0, O1);
   }
 }
 
-// One 16-lane row per (b, q head): combine splits in index order, un-rotate, normalize.
+// One 16-lane row per (b, q head): combine the spans in index order, add the tail
+// tokens, un-rotate the V part, normalize.
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, rg = lane >> 4, cg = lane & 15;
-  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + rg;  // b * Hq + g
+  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + rg;  // b * Hq + q head
   const long long nrows = (long long)a.L.B * a.Hq;
   const bool live = row < nrows;
   const long long rr = live ? row : 0;
-  const float* w = a.ws + rr * a.n_split * kWs;
+  const int b = (int)(rr / a.Hq), qhead = (int)(rr % a.Hq), h = qhead / a.grp;
+  const int G = a.L.G;
+  const int n = *reinterpret_cast<const int32_t*>(a.cache + a.L.len_off(b, h, 0));
+  const int nfull = n / G, nt = n - nfull * G;
+  const int nsp = (nfull + 4 * a.tpw - 1) / (4 * a.tpw);
+  const float* w = a.ws + rr * a.nspan * kPart;
   float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, w[s * kWs]);
-  float Lsum = 0.0f, orot[8] = {0, 0, 0, 0, 0, 0, 0, 0}, oorig[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s = 0; s < a.n_split; ++s) {
-    const float* p = w + s * kWs;
-    if (!(p[1] > 0.0f)) continue;
-    const float f = __expf(p[0] - M);
-    Lsum += f * p[1];
-    for (int e = 0; e < 8; ++e) {
-      orot[e] = fmaf(f, p[2 + 8 * cg + e], orot[e]);
-      oorig[e] = fmaf(f, p[2 + kD + 8 * cg + e], oorig[e]);
-    }
+  for (int s = 0; s < nsp; ++s) M = fmaxf(M, w[s * kPart]);
+  float Ls = 0.0f, orot[8] = {0, 0, 0, 0, 0, 0, 0, 0}, oorig[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < nsp; ++s) {
+    const float* p = w + s * kPart;
+    const float f = __builtin_amdgcn_exp2f(p[0] - M);
+    Ls = fmaf(f, p[1], Ls);
+    const float4 x0 = *reinterpret_cast<const float4*>(p + 4 + 8 * cg);
+    const float4 x1 = *reinterpret_cast<const float4*>(p + 8 + 8 * cg);
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) orot[e] = fmaf(f, xs[e], orot[e]);
   }
   float sg[8];
   load_sigma(a.cache, cg, sg);
+  if (nt > 0) {  // uniform over the row
+    float qv[8];
+    const uint4 qw = *reinterpret_cast<const uint4*>(a.q + rr * kD + 8 * cg);
+    const uint32_t ws[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qv[2 * k] = bf16lo(ws[k]);
+      qv[2 * k + 1] = bf16hi(ws[k]);
+    }
+    if (a.flags & KVARN_Q_PREROTATED) {  // q = q_rot H_D^T
+      fwht128(qv, cg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] *= kInvSqrtD * sg[e];
+    }
+    const float qs = kLog2e * a.scale;
+    const uint8_t* tk = a.cache + a.L.tail_row(b, h, 0, 0);
+    const uint8_t* tv = a.cache + a.L.tail_row(b, h, 1, 0);
+    for (int t = 0; t < nt; ++t) {
+      const uint4 kw = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
+      const uint4 vw = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
+      const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+      float d = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d = fmaf(qv[2 * k], f16lo(kk[k]), fmaf(qv[2 * k + 1], f16hi(kk[k]), d));
+      const float lt = row16_sum(d) * qs;
+      const float mn = fmaxf(M, lt);
+      const float al = __builtin_amdgcn_exp2f(M - mn), p = __builtin_amdgcn_exp2f(lt - mn);
+      Ls = fmaf(Ls, al, p);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        orot[2 * k] *= al;
+        orot[2 * k + 1] *= al;
+        oorig[2 * k] = fmaf(oorig[2 * k], al, p * f16lo(vv[k]));
+        oorig[2 * k + 1] = fmaf(oorig[2 * k + 1], al, p * f16hi(vv[k]));
+      }
+      M = mn;
+    }
+  }
   fwht128(orot, cg);  // all 16 lanes of the row take part, live or not
   if (!live) return;
   float o[8];
-  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+#pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (orot[e] * kInvSqrtD * sg[e] + oorig[e]) * inv;
   store8f(a.out + rr * kD + 8 * cg, o);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((long long)a.L.B * a.L.Hkv * a.n_split));
-  if (a.grp <= 1)
-    hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(256), 0, st, a);
-  else if (a.grp <= 2)
-    hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(256), 0, st, a);
-  else if (a.grp <= 4)
-    hipLaunchKernelGGL(attn_kernel<4>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_kernel<8>, grid, dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const long long blocks = (long long)a.L.B * a.L.Hkv * a.nqg * a.nspan;
+  if (blocks > 0) {
+    if (a.L.G == 32)
+      hipLaunchKernelGGL(attn_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const long long rows = (long long)a.L.B * a.Hq;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, a);
   return hipGetLastError();

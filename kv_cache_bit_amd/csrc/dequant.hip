@@ -65,13 +65,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     load_sigma(a.cache, cg, sg);
     float w[8][8];
     if (s == 0) {
-      // channel j = 8cg + e sits in word (j%16)/2 = 4(cg%2) + e/2, slot 8(e%2) + cg/2
+      // channel j = 8cg + e = 16m + 2w + d (m = cg/2, w = 4(cg%2) + e/2, d = e%2) sits in
+      // word w at slot 4(m/2) + m%2 + 2d
+      const int sbase = 2 * (4 * (cg >> 2) + ((cg >> 1) & 1));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint4 q4 = *reinterpret_cast<const uint4*>(rec + (tw0 + i) * 32 + 16 * (cg & 1));
         const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[i][e] = (float)((qw[e >> 1] >> (2 * (8 * (e & 1) + (cg >> 1)))) & 3u);
+        for (int e = 0; e < 8; ++e) w[i][e] = (float)((qw[e >> 1] >> (sbase + 4 * (e & 1))) & 3u);
       }
     } else {
 #pragma unroll

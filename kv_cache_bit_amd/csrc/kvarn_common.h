@@ -54,7 +54,42 @@ inline __host__ Layout make_layout(const kvarn_geom& g) {
 }
 
 #if defined(__HIPCC__)
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+
 // ----------------------------------------------------------------------------- lane exchange
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane ^ 7 within the row), row_mirror (lane ^ 15), row_ror:8 (lane ^ 8),
+// row_newbcast:n (lane n of the row to all 16)
+constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140, kRor8 = 0x128, kNewBcast = 0x150;
+
+// Cross-lane min/max on values the compiler cannot prove canonical (they come
+// through DPP / permlane as integers): plain v_min/v_max, no NaN quieting needed
+// for the finite values that reach them.
+__device__ __forceinline__ float vmin(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Orders LDS traffic of one wave against itself: LDS operations of a wave complete in
+// issue order, so a compiler fence at wavefront scope is all a wave-private buffer needs.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // xor-partner exchange inside a wave. Masks 1 and 2 use DPP quad permutes (no LDS
 // traffic); 4, 8 and 16 use ds_swizzle's bit-mask mode (within 32 lanes); 32 uses
 // ds_bpermute.

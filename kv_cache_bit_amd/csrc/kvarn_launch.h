@@ -46,9 +46,11 @@ struct AttnArgs {
   Layout L;
   const uint8_t* cache;
   const uint16_t* q;  // bf16 [B][Hq][D]
-  float* ws;          // [B][Hq][n_split][2 + 2D]
+  float* ws;          // [B][Hq][nspan][4 + D]: m, l, pad, pad, o_rot
   float* out;         // [B][Hq][D]
-  int Hq, grp, n_split, tiles_per_split;
+  int Hq, grp;        // query heads; query heads per kv head
+  int nqg;            // groups of up to 4 query heads per kv head
+  int nspan, tpw;     // spans of 4 * tpw tiles per sequence; tiles per wave
   float scale;
   uint32_t flags;
 };

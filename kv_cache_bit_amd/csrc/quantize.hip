@@ -27,31 +27,6 @@
 
 namespace kvarn {
 
-typedef _Float16 h8v __attribute__((ext_vector_type(8)));
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-// ----------------------------------------------------------------------------- lane exchange
-template <int CTRL>
-__device__ __forceinline__ float dppf(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-// DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
-// row_half_mirror (lane ^ 7 within the row), row_mirror (lane ^ 15), row_newbcast:n
-constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140, kNewBcast = 0x150;
-
-// Cross-lane min/max on values the compiler cannot prove canonical (they come
-// through DPP / permlane as integers): plain v_min/v_max, no NaN quieting needed
-// for the finite values that reach them.
-__device__ __forceinline__ float vmin(float a, float b) {
-  float r;
-  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float vmax(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
 struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
 struct OpMin { __device__ float operator()(float a, float b) const { return vmin(a, b); } };
 struct OpMax { __device__ float operator()(float a, float b) const { return vmax(a, b); } };
@@ -262,8 +237,7 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
 template <int NW>
 __device__ __forceinline__ void tile_sync() {
   if constexpr (NW == 1) {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    wave_sync();
   } else {
     __syncthreads();
   }
@@ -302,7 +276,7 @@ __device__ __forceinline__ void chan_reduce(const float (&v)[8], float (&own)[2]
 
 // ----------------------------------------------------------------------------- codes
 // Writes the 2-bit codes of this wave's block into the record in LDS.
-// K: word w = c/2 of token t holds channel 16nb + c in slot 8(c%2) + nb.
+// K: word w = c/2 of token t holds channel 16nb + c in slot 4(nb/2) + nb%2 + 2(c%2).
 // V: byte j*G/4 + t/4 holds tokens 4(t/4) .. +3 of channel j, token t%4 in slot t%4.
 template <int NW, bool CLAMP>
 __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (&al)[8], const float (&ga)[8],
@@ -315,17 +289,23 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
     return (uint32_t)__float_as_int(t + 12582912.0f);  // 1.5 * 2^23
   };
   if (stream == 0) {
+    // lane c's channel 16nb + c goes to word c/2, slot 4(nb/2) + nb%2 + 2(c%2): the even
+    // lane assembles bits 8(nb/2) + 2(nb%2) (blocks 0..3 in bytes 0..1, 4..7 in bytes
+    // 2..3, one byte permute), the odd lane's pattern lands 4 bits higher.
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t h = 0;
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) h |= code(acc[mb][nb][i], nb) << (2 * nb);
-        h &= 0xFFFFu;
+        for (int nb = 0; nb < 4; ++nb) {
+          lo |= code(acc[mb][nb][i], nb) << (8 * (nb >> 1) + 2 * (nb & 1));
+          hi |= code(acc[mb][nb + 4][i], nb + 4) << (8 * (nb >> 1) + 2 * (nb & 1));
+        }
+        const uint32_t h = __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // bytes lo.0 lo.1 hi.0 hi.1
         const uint32_t hp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, kQx1, 0xF, 0xF, false);
         if ((c & 1) == 0)
-          *reinterpret_cast<uint32_t*>(sh.rec + (ttile0 + 16 * mb + i) * 32 + 2 * c) = h | (hp << 16);
+          *reinterpret_cast<uint32_t*>(sh.rec + (ttile0 + 16 * mb + i) * 32 + 2 * c) = h | (hp << 4);
       }
   } else {
 #pragma unroll
@@ -493,7 +473,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
 
   // codes, q = clamp(rne(u), 0, 3): 1.5 * 2^23 + u rounds half to even with q left in
   // bits 0..1 and zeros in bits 2..21; shifted into its 2-bit slot, the junk above bit 21
-  // falls outside the masked half-word / byte. The clamp is needed only where u can
+  // falls outside the bytes kept (permute) / the byte stored. The clamp is needed only where u can
   // leave (-0.5, 3.5): with normal s16 and max(|Y|) <= 200 s16 the fp16 rounding of z
   // and s moves u by less than 0.1, so a wave whose channels all satisfy that skips it.
   const bool need_clamp = __any(need_clamp_own);

@@ -220,8 +220,10 @@ def record_bytes(g: int, d: int) -> int:
 
 def k_code_position(j: int) -> tuple[int, int]:
     """K stream: (32-bit word w, 2-bit slot p) holding channel j of a token.
-    Word w holds the 16 channels {16 m + 2 w + d : m < 8, d < 2} at slot p = 8 d + m."""
-    return (j % 16) // 2, 8 * (j % 2) + j // 16
+    Word w holds the 16 channels {16 m + 2 w + d : m < 8, d < 2} at slot
+    p = 4 (m // 2) + m % 2 + 2 d, so byte k of the word holds m in {2k, 2k+1}, both d."""
+    m, w, d = j // 16, (j % 16) // 2, j % 2
+    return w, 4 * (m // 2) + m % 2 + 2 * d
 
 
 def pack_codes(q, stream: int) -> np.ndarray:
