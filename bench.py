@@ -145,9 +145,8 @@ def copy_ceiling(torch, gib=4):
     return dict(bytes=2 * n, ms=round(ms, 3), GBps=round(2 * n / (ms * 1e-3) / 1e9, 1))
 
 
-def cpu_baseline(synth, tokens):
-    """The oracle's prefill on layer 0 of the prefill workload, first `tokens` tokens (host cores)."""
-    import numpy as np
+def cpu_baseline(synth, tokens, layers):
+    """The oracle's prefill on the first `layers` layers of the prefill workload (host cores)."""
     from oracle import kvarn_ref as R
     try:
         from threadpoolctl import threadpool_info
@@ -155,15 +154,54 @@ def cpu_baseline(synth, tokens):
     except Exception:  # pragma: no cover
         blas = 1
     H, G = 8, 32
-    k, v = synth.kv_host(synth.sub_seed(2, 0, 0), 1, tokens, H)
-    c = R.Cache(R.Geom(1, H, 128, tokens, G, 3, 2), synth.sign_vector(0))
-    t0 = time.perf_counter()
-    R.quantize_prefill(c, k, v, tokens)
-    dt = time.perf_counter() - t0
-    gbs = 2 * 2 * tokens * H * 128 / dt / 1e9
+    dt = 0.0
+    for l in range(layers):
+        k, v = synth.kv_host(synth.sub_seed(2, l, 0), 1, tokens, H)
+        c = R.Cache(R.Geom(1, H, 128, tokens, G, 3, 2), synth.sign_vector(0))
+        t0 = time.perf_counter()
+        R.quantize_prefill(c, k, v, tokens)
+        dt += time.perf_counter() - t0
+    gbs = layers * 2 * 2 * tokens * H * 128 / dt / 1e9
     return dict(value=round(gbs, 5), unit="GB/s", cores=int(blas), kind="oracle",
-                sample=f"layer 0 of the prefill workload, {tokens} tokens x 8 KV heads x K and V "
-                       f"({2 * H * tokens // G} tiles), {dt:.1f} s; NumPy fp64, BLAS threads = cores")
+                sample=f"layers 0..{layers - 1} of the prefill workload, {tokens} tokens x 8 KV heads x K and V "
+                       f"each ({layers * 2 * H * tokens // G} tiles), {dt:.1f} s of oracle time; NumPy fp64, "
+                       "BLAS threads = cores")
+
+
+# HBM traffic of a kernel from committed rocprofv3 counter summaries: FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch) scaled by what the same counters read for a 4 GiB device
+# copy. The figures stand only while the kernel sources hash to the digest recorded
+# with them; otherwise traffic is reported as null.
+KERNEL_SOURCES = ["kv_cache_bit_amd/csrc/kvarn_common.h", "kv_cache_bit_amd/csrc/kvarn_launch.h"]
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in files:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(profile, sources):
+    """Bytes per launch from a profiles/ counter summary, or None if stale or absent."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", profile)
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_digest") != source_digest(sources + KERNEL_SOURCES):
+            return None
+        fetch = float(kv["FETCH_SIZE_KiB"]) * float(kv["fetch_scale"])
+        write = float(kv["WRITE_SIZE_KiB"]) * float(kv["write_scale"])
+        return int(round((fetch + write) * 1024))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -175,6 +213,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-layers", type=int, default=5, help="layers of the prefill workload the oracle runs")
     ap.add_argument("--no-copy", action="store_true", help="skip the 4 GiB device copy ceiling")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -210,7 +249,10 @@ def main():
                    "varn_iters": pf["n_it"], "bits": 2, "input": "bf16, outlier channels x20, 5% lognormal tokens"},
         "hbm_frac_step": round(total_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic("prefill_kernel_llama8b_32k_pmc.txt",
+                                                ["kv_cache_bit_amd/csrc/quantize.hip"]),
+                     "traffic_unit": "bytes/launch",
                      "kernel": "prefill_kernel<1,false>", "bytes_per_launch": pf["bytes_in"] + pf["bytes_out"],
                      "avg_launch_us": round(avg_launch * 1e3, 2), "median_launch_us": round(lm[len(lm) // 2] * 1e3, 2)},
         "flags": pf["flags"],
@@ -229,11 +271,18 @@ def main():
             "layers": dc["layers"], "batch": dc["B"], "kv_heads": dc["H"], "q_heads": dc["Hq"],
             "context_at_start": dc["ctx_start"], "attn_avg_us": round(a_avg * 1e3, 2),
             "attn_GBps": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9, 1),
-            "attn_frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "flags": dc["flags"]}
+            "attn_frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "flags": dc["flags"],
+            "roofline": {"bound": "hbm", "kernel": "attn_kernel<32> + merge_kernel",
+                         "achieved": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": dc["attn_bytes"],
+                         "traffic": counted_traffic("attn_kernel_phi4_decode_pmc.txt",
+                                                    ["kv_cache_bit_amd/csrc/attn.hip"]),
+                         "traffic_unit": "bytes/launch (tile pass)"}}
         log(f"decode: {tok_s:.1f} tok/s, attn {a_avg * 1e3:.1f} us/layer-step")
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
-        res["cpu_baseline"] = cpu_baseline(synth, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(synth, args.cpu_tokens, args.cpu_layers)
     print(json.dumps(res), flush=True)
 
 

@@ -229,7 +229,8 @@ def run_attn(gc, q_bits, Hq, scale=0.0, flags=0):
     return out.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("T,Hq,H", [(256, 4, 1), (250, 8, 2), (1, 1, 1), (20, 4, 2), (1000, 4, 2), (33, 2, 2)])
+@pytest.mark.parametrize("T,Hq,H", [(256, 4, 1), (250, 8, 2), (1, 1, 1), (20, 4, 2), (1000, 4, 2), (33, 2, 2),
+                                    (300, 16, 2), (100, 6, 2)])
 def test_attention_parity(T, Hq, H):
     say("attn", T, Hq, H)
     B = 2
