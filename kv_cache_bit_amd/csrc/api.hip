@@ -49,7 +49,9 @@ kvarn_status prefill_impl(const kvarn_geom* g, void* cache, const void* k, const
   a.v = static_cast<const uint16_t*>(v);
   a.T = T;
   a.nfull = T / g->group;
-  a.jobs = (long long)g->batch * g->num_kv_heads * a.nfull * 2;
+  a.jobs = g->batch * g->num_kv_heads * a.nfull * 2;
+  a.dhkv = make_fastdiv((uint32_t)g->num_kv_heads);
+  a.dnfull = make_fastdiv((uint32_t)a.nfull);
   a.wk = wk;
   a.wv = wv;
   a.yk = yk;

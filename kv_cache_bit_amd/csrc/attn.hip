@@ -68,10 +68,10 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // max over the 64 lanes of non-negative floats (compared as integers), wave-uniform
 __device__ __forceinline__ uint32_t wave_max_pos(float x) {
   uint32_t u = (uint32_t)__float_as_int(x);
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kQx1, 0xF, 0xF, false));
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kQx2, 0xF, 0xF, false));
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kHalfMirror, 0xF, 0xF, false));
-  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, kMirror, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, kQx1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, kQx2, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, kHalfMirror, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, kMirror, 0xF, 0xF, true));
   const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)u, 0), (uint32_t)__builtin_amdgcn_readlane((int)u, 16));
   const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)u, 32), (uint32_t)__builtin_amdgcn_readlane((int)u, 48));
   return max(a, b);
@@ -420,37 +420,59 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 }
 
 // One 16-lane row per (b, q head): combine the spans in index order, add the tail
-// tokens, un-rotate the V part, normalize.
+// tokens, un-rotate the V part, normalize. Loads are issued in independent batches (span
+// maxima spread over the row's lanes, spans and tail tokens four at a time), so the
+// kernel waits on memory a few times rather than once per span or token.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, xshfl<1>(v));
+  v = fmaxf(v, xshfl<2>(v));
+  v = fmaxf(v, xshfl<4>(v));
+  return fmaxf(v, xshfl<8>(v));
+}
+
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, rg = lane >> 4, cg = lane & 15;
   const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + rg;  // b * Hq + q head
   const long long nrows = (long long)a.L.B * a.Hq;
   const bool live = row < nrows;
-  const long long rr = live ? row : 0;
-  const int b = (int)(rr / a.Hq), qhead = (int)(rr % a.Hq), h = qhead / a.grp;
+  const int rr = live ? (int)row : 0;
+  const int b = rr / a.Hq, qhead = rr - b * a.Hq, h = qhead / a.grp;
   const int G = a.L.G;
   const int n = *reinterpret_cast<const int32_t*>(a.cache + a.L.len_off(b, h, 0));
   const int nfull = n / G, nt = n - nfull * G;
   const int nsp = (nfull + 4 * a.tpw - 1) / (4 * a.tpw);
-  const float* w = a.ws + rr * a.nspan * kPart;
+  const float* w = a.ws + (long long)rr * a.nspan * kPart;
+  // span maxima: lane cg looks at spans cg, cg + 16, ...
   float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, w[s * kPart]);
+  for (int s = cg; s < nsp; s += 16) M = fmaxf(M, w[s * kPart]);
+  M = row16_max(M);
   float Ls = 0.0f, orot[8] = {0, 0, 0, 0, 0, 0, 0, 0}, oorig[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s = 0; s < nsp; ++s) {
-    const float* p = w + s * kPart;
-    const float f = __builtin_amdgcn_exp2f(p[0] - M);
-    Ls = fmaf(f, p[1], Ls);
-    const float4 x0 = *reinterpret_cast<const float4*>(p + 4 + 8 * cg);
-    const float4 x1 = *reinterpret_cast<const float4*>(p + 8 + 8 * cg);
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  for (int s0 = 0; s0 < nsp; s0 += 4) {
+    float ml[4][2];
+    float4 x[4][2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) orot[e] = fmaf(f, xs[e], orot[e]);
+    for (int k = 0; k < 4; ++k) {
+      const int s = min(s0 + k, nsp - 1);
+      const float* p = w + s * kPart;
+      ml[k][0] = p[0];
+      ml[k][1] = p[1];
+      x[k][0] = *reinterpret_cast<const float4*>(p + 4 + 8 * cg);
+      x[k][1] = *reinterpret_cast<const float4*>(p + 8 + 8 * cg);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float f = (s0 + k < nsp) ? __builtin_amdgcn_exp2f(ml[k][0] - M) : 0.0f;
+      Ls = fmaf(f, ml[k][1], Ls);
+      const float xs[8] = {x[k][0].x, x[k][0].y, x[k][0].z, x[k][0].w, x[k][1].x, x[k][1].y, x[k][1].z, x[k][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) orot[e] = fmaf(f, xs[e], orot[e]);
+    }
   }
   float sg[8];
   load_sigma(a.cache, cg, sg);
   if (nt > 0) {  // uniform over the row
     float qv[8];
-    const uint4 qw = *reinterpret_cast<const uint4*>(a.q + rr * kD + 8 * cg);
+    const uint4 qw = *reinterpret_cast<const uint4*>(a.q + (long long)rr * kD + 8 * cg);
     const uint32_t ws[4] = {qw.x, qw.y, qw.z, qw.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -465,23 +487,41 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const float qs = kLog2e * a.scale;
     const uint8_t* tk = a.cache + a.L.tail_row(b, h, 0, 0);
     const uint8_t* tv = a.cache + a.L.tail_row(b, h, 1, 0);
-    for (int t = 0; t < nt; ++t) {
-      const uint4 kw = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
-      const uint4 vw = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
-      const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
-      float d = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) d = fmaf(qv[2 * k], f16lo(kk[k]), fmaf(qv[2 * k + 1], f16hi(kk[k]), d));
-      const float lt = row16_sum(d) * qs;
-      const float mn = fmaxf(M, lt);
-      const float al = __builtin_amdgcn_exp2f(M - mn), p = __builtin_amdgcn_exp2f(lt - mn);
-      Ls = fmaf(Ls, al, p);
+    for (int t0 = 0; t0 < nt; t0 += 4) {  // four tail tokens per step, one softmax update
+      uint4 kw[4], vw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        orot[2 * k] *= al;
-        orot[2 * k + 1] *= al;
-        oorig[2 * k] = fmaf(oorig[2 * k], al, p * f16lo(vv[k]));
-        oorig[2 * k + 1] = fmaf(oorig[2 * k + 1], al, p * f16hi(vv[k]));
+        const int t = min(t0 + k, nt - 1);
+        kw[k] = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
+        vw[k] = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
+      }
+      float lt[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t kk[4] = {kw[k].x, kw[k].y, kw[k].z, kw[k].w};
+        float d = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d = fmaf(qv[2 * e], f16lo(kk[e]), fmaf(qv[2 * e + 1], f16hi(kk[e]), d));
+        lt[k] = t0 + k < nt ? row16_sum(d) * qs : -INFINITY;
+      }
+      const float mn = fmaxf(M, fmaxf(fmaxf(lt[0], lt[1]), fmaxf(lt[2], lt[3])));
+      const float al = __builtin_amdgcn_exp2f(M - mn);
+      Ls *= al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        orot[e] *= al;
+        oorig[e] *= al;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float p = __builtin_amdgcn_exp2f(lt[k] - mn);
+        Ls += p;
+        const uint32_t vv[4] = {vw[k].x, vw[k].y, vw[k].z, vw[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          oorig[2 * e] = fmaf(p, f16lo(vv[e]), oorig[2 * e]);
+          oorig[2 * e + 1] = fmaf(p, f16hi(vv[e]), oorig[2 * e + 1]);
+        }
       }
       M = mn;
     }
@@ -492,7 +532,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (orot[e] * kInvSqrtD * sg[e] + oorig[e]) * inv;
-  store8f(a.out + rr * kD + 8 * cg, o);
+  store8f(a.out + (long long)rr * kD + 8 * cg, o);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {

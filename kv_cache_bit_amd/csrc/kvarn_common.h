@@ -38,6 +38,28 @@ struct Layout {
   }
 };
 
+// Division of a 32-bit unsigned n by a fixed d >= 1 without a divide: with l = ceil(log2 d)
+// and m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l for every n < 2^32
+// (Granlund and Montgomery, "Division by invariant integers using multiplication", 1994).
+// On uniform operands the device side runs on the scalar unit.
+struct FastDiv {
+  uint32_t m;
+  int l;
+  uint32_t d;
+};
+inline __host__ FastDiv make_fastdiv(uint32_t d) {
+  if (d == 0) d = 1;
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{(uint32_t)m, l, d};
+}
+#if defined(__HIPCC__)
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.l);
+}
+#endif
+
 inline __host__ Layout make_layout(const kvarn_geom& g) {
   Layout L;
   L.B = g.batch;
@@ -60,9 +82,10 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 
 // ----------------------------------------------------------------------------- lane exchange
+// Every control used here reads a valid lane for every lane, so no "old" value is needed.
 template <int CTRL>
 __device__ __forceinline__ float dppf(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 // DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
 // row_half_mirror (lane ^ 7 within the row), row_mirror (lane ^ 15), row_ror:8 (lane ^ 8),

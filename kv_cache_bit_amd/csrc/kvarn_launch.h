@@ -22,7 +22,8 @@ struct PrefillArgs {
   const uint16_t* k;  // bf16 [B][T][Hkv][D]
   const uint16_t* v;
   int T, nfull;       // tokens; full tiles per sequence
-  long long jobs;     // B * Hkv * nfull * 2 tile-streams
+  int jobs;           // B * Hkv * nfull * 2 tile-streams (< 2^31, checked on the host)
+  FastDiv dhkv, dnfull;  // division by Hkv and by nfull
   float *wk, *wv, *yk, *yv;  // optional fp32 intermediates [B][nfull*G][Hkv][D]
 };
 

@@ -54,16 +54,16 @@ __device__ __forceinline__ float row_rs8(const float (&v)[8], int c) {
   const float d = keep + dppf<kQx2>(send);
   return d + dppf<kQx1>(d);
 }
-// Token tau's value from its owner lanes (2 tau, 2 tau + 1) to the whole row.
-__device__ __forceinline__ void row_gather8(float own, float (&v)[8]) {
-  v[0] = dppf<kNewBcast + 0>(own);
-  v[1] = dppf<kNewBcast + 2>(own);
-  v[2] = dppf<kNewBcast + 4>(own);
-  v[3] = dppf<kNewBcast + 6>(own);
-  v[4] = dppf<kNewBcast + 8>(own);
-  v[5] = dppf<kNewBcast + 10>(own);
-  v[6] = dppf<kNewBcast + 12>(own);
-  v[7] = dppf<kNewBcast + 14>(own);
+// Token tau's value from its owner lanes (2 tau, 2 tau + 1) to the whole row, through a
+// wave-private LDS slot (a wave's LDS operations complete in issue order).
+__device__ __forceinline__ void row_gather8(float own, float (&v)[8], float* buf, int g, int c) {
+  wave_sync();
+  if ((c & 1) == 0) buf[8 * g + (c >> 1)] = own;
+  wave_sync();
+  const float4 x = *reinterpret_cast<const float4*>(buf + 8 * g);
+  const float4 y = *reinterpret_cast<const float4*>(buf + 8 * g + 4);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
 // Reduce-scatter of 8 per-channel partials (channel blocks nb) over the 4 rows:
@@ -86,18 +86,16 @@ __device__ __forceinline__ void col_rs8(const float (&v)[8], float (&out)[2], Op
     out[q] = op(__int_as_float(s[0]), __int_as_float(s[1]));
   }
 }
-// Inverse: row g holds channel blocks g and 4 + g; every row gets all 8.
-__device__ __forceinline__ void col_gather8(const float (&own)[2], float (&v)[8]) {
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_int(own[q]), __float_as_int(own[q]), false, false);
-    const auto p0 = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
-    const auto p1 = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
-    v[4 * q + 0] = __int_as_float(p0[0]);
-    v[4 * q + 1] = __int_as_float(p0[1]);
-    v[4 * q + 2] = __int_as_float(p1[0]);
-    v[4 * q + 3] = __int_as_float(p1[1]);
-  }
+// Inverse of col_rs8: row g holds channel blocks g and 4 + g; every row gets all 8,
+// through a wave-private LDS slot laid out [c][g][q].
+__device__ __forceinline__ void col_gather8(const float (&own)[2], float (&v)[8], float* buf, int g, int c) {
+  wave_sync();
+  *reinterpret_cast<float2*>(buf + 8 * c + 2 * g) = make_float2(own[0], own[1]);
+  wave_sync();
+  const float4 x = *reinterpret_cast<const float4*>(buf + 8 * c);      // (g0,q0) (g0,q1) (g1,q0) (g1,q1)
+  const float4 y = *reinterpret_cast<const float4*>(buf + 8 * c + 4);  // (g2,q0) (g2,q1) (g3,q0) (g3,q1)
+  v[0] = x.x; v[4] = x.y; v[1] = x.z; v[5] = x.w;
+  v[2] = y.x; v[6] = y.y; v[3] = y.z; v[7] = y.w;
 }
 
 // ----------------------------------------------------------------------------- Hadamard fragments
@@ -109,18 +107,32 @@ __device__ __forceinline__ void col_gather8(const float (&own)[2], float (&v)[8]
 struct Frags {
   h8v v[4];  // F, -F, G, -G
 };
-__device__ __forceinline__ Frags hadamard_frags(int g, int c) {
+// The four fragments of every lane as fp16 bit patterns, computed at compile time:
+// word [lane][4 f + d] holds elements 2d, 2d+1 of fragment f.
+struct FragTable {
+  uint32_t w[64][16];
+};
+constexpr FragTable make_frag_table() {
+  FragTable t{};
+  for (int lane = 0; lane < 64; ++lane) {
+    const int g = lane >> 4, c = lane & 15;
+    for (int e = 0; e < 8; ++e) {
+      int pc = (g & 1) & (c >> 3);
+      for (int b = 0; b < 3; ++b) pc += (e >> b) & (c >> b) & 1;
+      const uint32_t f = (pc & 1) ? 0xBC00u : 0x3C00u;  // -1 / +1
+      const uint32_t gg = (g >> 1) ? f ^ 0x8000u : f;
+      const uint32_t vals[4] = {f, f ^ 0x8000u, gg, gg ^ 0x8000u};
+      for (int q = 0; q < 4; ++q) t.w[lane][4 * q + e / 2] |= vals[q] << (16 * (e & 1));
+    }
+  }
+  return t;
+}
+__device__ const FragTable kFrags = make_frag_table();
+__device__ __forceinline__ Frags hadamard_frags(int lane) {
+  const uint4* p = reinterpret_cast<const uint4*>(kFrags.w[lane]);
   Frags h;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int pc = __builtin_popcount(e & (c & 7)) + ((g & 1) & (c >> 3));
-    const float f = (pc & 1) ? -1.0f : 1.0f;
-    const float gg = (g >> 1) ? -f : f;
-    h.v[0][e] = (_Float16)f;
-    h.v[1][e] = (_Float16)(-f);
-    h.v[2][e] = (_Float16)gg;
-    h.v[3][e] = (_Float16)(-gg);
-  }
+  for (int q = 0; q < 4; ++q) h.v[q] = __builtin_bit_cast(h8v, p[q]);
   return h;
 }
 __device__ __forceinline__ int frag_index(int ks, int nb) {
@@ -250,6 +262,8 @@ struct TileLds {
   uint8_t rec[TR] __attribute__((aligned(16)));
   float red_a[NW][kD];
   float red_b[NW][kD];
+  float gcol[NW][kD] __attribute__((aligned(16)));  // per-wave gather buffers
+  float grow[NW][32] __attribute__((aligned(16)));
 };
 
 // Per-channel reduction of a tile: 4-row reduce-scatter inside the wave, then (G=64)
@@ -303,7 +317,7 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
           hi |= code(acc[mb][nb + 4][i], nb + 4) << (8 * (nb >> 1) + 2 * (nb & 1));
         }
         const uint32_t h = __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // bytes lo.0 lo.1 hi.0 hi.1
-        const uint32_t hp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, kQx1, 0xF, 0xF, false);
+        const uint32_t hp = (uint32_t)__builtin_amdgcn_mov_dpp((int)h, kQx1, 0xF, 0xF, true);
         if ((c & 1) == 0)
           *reinterpret_cast<uint32_t*>(sh.rec + (ttile0 + 16 * mb + i) * 32 + 2 * c) = h | (hp << 4);
       }
@@ -360,7 +374,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
       s_tok = row_rs8(tp, c);
     }
     if (s_tok > 0.0f) v_own = (float)kD * __builtin_amdgcn_rcpf(s_tok);
-    row_gather8(v_own, v);
+    row_gather8(v_own, v, sh.grow[sub], g, c);
     float cp[8];  // channel pass
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
@@ -375,7 +389,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       if (s_ch[q] > 0.0f) u_own[q] = (float)G * __builtin_amdgcn_rcpf(s_ch[q]);
-    col_gather8(u_own, u);
+    col_gather8(u_own, u, sh.gcol[sub], g, c);
   }
 
   // stored scales: fp16, clamped to [2^-14, 65504]
@@ -384,7 +398,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
   if (rc != r_own) flags |= KVARN_FLAG_SCALE_CLAMPED;
   const float r16_own = round_f16(rc);
   float at[8];  // Y = W' / (sqrt(D) r16 c16): per-token factor 1 / (sqrt(D) r16)
-  row_gather8(kInvSqrtD * __builtin_amdgcn_rcpf(r16_own), at);
+  row_gather8(kInvSqrtD * __builtin_amdgcn_rcpf(r16_own), at, sh.grow[sub], g, c);
   float c16_own[2], ic_own[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -409,7 +423,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
   rotate_block(av2, hf, acc);
   if constexpr (DBG) {
     float ic[8];
-    col_gather8(ic_own, ic);
+    col_gather8(ic_own, ic, sh.gcol[sub], g, c);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -468,8 +482,8 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
     ga_own[q] = -z16_own[q] * is;
   }
   float al[8], ga[8];
-  col_gather8(al_own, al);
-  col_gather8(ga_own, ga);
+  col_gather8(al_own, al, sh.gcol[sub], g, c);
+  col_gather8(ga_own, ga, sh.gcol[sub], g, c);
 
   // codes, q = clamp(rne(u), 0, 3): 1.5 * 2^23 + u rounds half to even with q left in
   // bits 0..1 and zeros in bits 2..21; shifted into its 2-bit slot, the junk above bit 21
@@ -547,12 +561,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const Layout& L = a.L;
   uint8_t* hdr = a.cache;
   uint32_t flags = 0;
-  const long long tile_blocks = (a.jobs + TPW - 1) / TPW;
+  const uint32_t tile_blocks = ((uint32_t)a.jobs + TPW - 1) / TPW;
 
-  if ((long long)blockIdx.x >= tile_blocks) {
-    const long long sj = ((long long)blockIdx.x - tile_blocks) * 4 + wave;  // (b, h, s)
-    if (sj >= 2LL * L.B * L.Hkv) return;
-    const int s = (int)(sj % 2), h = (int)((sj / 2) % L.Hkv), b = (int)(sj / 2 / L.Hkv);
+  if (blockIdx.x >= tile_blocks) {
+    const uint32_t sj = (blockIdx.x - tile_blocks) * 4 + wave;  // (b, h, s)
+    if (sj >= 2u * L.B * L.Hkv) return;
+    const uint32_t q = fdiv(sj >> 1, a.dhkv);
+    const int s = (int)(sj & 1u), h = (int)((sj >> 1) - q * (uint32_t)L.Hkv), b = (int)q;
     const uint16_t* src = s ? a.v : a.k;
     for (int t = a.nfull * L.G + g; t < a.T; t += 4) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + (((long long)b * a.T + t) * L.Hkv + h) * kD + 8 * c);
@@ -568,17 +583,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   const int tw = wave / NW, sub = wave % NW;
   TileLds<NW>& sh = sh_all[tw];
-  long long job = (long long)blockIdx.x * TPW + tw;
-  const bool valid = job < a.jobs;
+  uint32_t job = blockIdx.x * TPW + tw;
+  const bool valid = job < (uint32_t)a.jobs;
   if (!valid) job = 0;  // keep the barrier sequence uniform; results are discarded
   // job = ((b * nfull + tile) * 2 + s) * Hkv + h : neighbouring waves read neighbouring heads
-  const int h = (int)(job % L.Hkv);
-  const int s = (int)((job / L.Hkv) % 2);
-  const int tile = (int)((job / L.Hkv / 2) % a.nfull);
-  const int b = (int)(job / L.Hkv / 2 / a.nfull);
+  const uint32_t q1 = fdiv(job, a.dhkv), q2 = q1 >> 1, q3 = fdiv(q2, a.dnfull);
+  const int h = (int)(job - q1 * (uint32_t)L.Hkv);
+  const int s = (int)(q1 & 1u);
+  const int tile = (int)(q2 - q3 * (uint32_t)a.nfull);
+  const int b = (int)q3;
   const uint16_t* src = s ? a.v : a.k;
   const int t0 = tile * L.G + sub * 32;  // first token of this wave's block
-  const Frags hf = hadamard_frags(g, c);
+  const Frags hf = hadamard_frags(lane);
 
   // A rows are tokens t0 + 16mb + c; K chunk 4ks + g holds channels 8(4ks + g) .. +7
   const uint16_t* rows = src + (((long long)b * a.T + t0 + c) * L.Hkv + h) * kD + 8 * g;
@@ -658,7 +674,7 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
     *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, pos % G) + 16 * c) = pack8_f16(xin);
   }
   if ((pos + 1) % G == 0) {
-    const Frags hf = hadamard_frags(g, c);
+    const Frags hf = hadamard_frags(lane);
     h8v av[2][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
