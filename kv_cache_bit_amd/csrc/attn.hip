@@ -38,8 +38,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kNib = 0x33333333u;
 
 struct WaveLds {
-  uint4 bop[128];   // K-side B operand, unit (s, g, n8 ^ swz(s, g)) = 4 dwords
-  float2 vf[16][8]; // V fold factors (c s, c z) of channel 16 blk + n at [n][blk]
+  uint4 bop[128];    // K-side B operand, unit (s, g, n8 ^ swz(s, g)) = 4 dwords
+  float vf[16][20];  // V fold factors (c s, c z) of channel 16 blk + n at [n][2 blk], rows
+                     // padded to 80 B so the 16 lanes of a row read distinct banks
 };
 struct AttnLds {
   float qrot[4][kD];
@@ -198,6 +199,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     krow[mb] = 32 * (mb >> 1) + 8 * (c >> 2) + (c & 1) + 4 * ((c >> 1) & 1) + 2 * (mb & 1);
   const float partf = (float)(c & 1);
   const bool rows_lo = c < 8;
+  // byte permutes building (even-block token, odd-block token) f16 pairs from this lane's
+  // pair `mine` (bytes 0..3) and the partner's `theirs` (bytes 4..7)
+  const uint32_t sel_lo = rows_lo ? 0x05040100u : 0x01000504u;
+  const uint32_t sel_hi = rows_lo ? 0x07060302u : 0x03020706u;
   const uint32_t sh_g1 = (uint32_t)(g & 1);
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -249,8 +254,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       bop[(wbase + ((2 * qh) ^ wswz)) * 4 + kk_m] = hv;
       bop[(wbase + ((2 * qh + 1) ^ wswz)) * 4 + kk_m] = lv;
     }
-    wl.vf[2 * wm][nbm] = make_float2(f16lo(vcs) * f16lo(vss), f16lo(vcs) * f16lo(vzs));
-    wl.vf[2 * wm + 1][nbm] = make_float2(f16hi(vcs) * f16hi(vss), f16hi(vcs) * f16hi(vzs));
+    *reinterpret_cast<float2*>(&wl.vf[2 * wm][2 * nbm]) = make_float2(f16lo(vcs) * f16lo(vss), f16lo(vcs) * f16lo(vzs));
+    *reinterpret_cast<float2*>(&wl.vf[2 * wm + 1][2 * nbm]) =
+        make_float2(f16hi(vcs) * f16hi(vss), f16hi(vcs) * f16hi(vzs));
     float bp[4];
 #pragma unroll
     for (int qh = 0; qh < 4; ++qh) bp[qh] = fmaf(qr[qh][0], cz0, qr[qh][1] * cz1);
@@ -265,75 +271,91 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       bk[s] = __builtin_bit_cast(h8v, wl.bop[unit]);
     }
     const float K1 = qscale * invSB;
-    float lsc[NMB][4];
+    // Columns 8..15 repeat 0..7, so from here lane c < 8 takes the even 16-token blocks
+    // (mb % 2 = 0) and lane c + 8 the odd ones; partial sums meet through row_ror:8.
+    float lsc[NKB][4];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const uint32_t x0 = kc[mb].x, x1 = kc[mb].y;
-      const uint32_t e0 = x0 & kNib, o0 = (x0 >> 2) & kNib, e1 = x1 & kNib, o1 = (x1 >> 2) & kNib;
-      f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      h8v av0 = as_h8(cvt2<0>(e0), cvt2<0>(o0), cvt2<1>(e0), cvt2<1>(o0));
-      h8v av1 = as_h8(cvt2<2>(e0), cvt2<2>(o0), cvt2<3>(e0), cvt2<3>(o0));
-      h8v av2 = as_h8(cvt2<0>(e1), cvt2<0>(o1), cvt2<1>(e1), cvt2<1>(o1));
-      h8v av3 = as_h8(cvt2<2>(e1), cvt2<2>(o1), cvt2<3>(e1), cvt2<3>(o1));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bk[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bk[1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av2, bk[2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av3, bk[3], acc, 0, 0, 0);
-      asm volatile("" : "+v"(acc) : "v"(av0), "v"(av1), "v"(av2), "v"(av3), "v"(bk[0]), "v"(bk[1]), "v"(bk[2]),
-                   "v"(bk[3]));
-      const uint4 rr = kr[mb >> 1];
-      const uint32_t rd[2] = {(mb & 1) ? rr.y : rr.x, (mb & 1) ? rr.w : rr.z};
+    for (int kb = 0; kb < NKB; ++kb) {
+      f4v sc[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t x0 = kc[2 * kb + h2].x, x1 = kc[2 * kb + h2].y;
+        const uint32_t e0 = x0 & kNib, o0 = (x0 >> 2) & kNib, e1 = x1 & kNib, o1 = (x1 >> 2) & kNib;
+        f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        h8v av0 = as_h8(cvt2<0>(e0), cvt2<0>(o0), cvt2<1>(e0), cvt2<1>(o0));
+        h8v av1 = as_h8(cvt2<2>(e0), cvt2<2>(o0), cvt2<3>(e0), cvt2<3>(o0));
+        h8v av2 = as_h8(cvt2<0>(e1), cvt2<0>(o1), cvt2<1>(e1), cvt2<1>(o1));
+        h8v av3 = as_h8(cvt2<2>(e1), cvt2<2>(o1), cvt2<3>(e1), cvt2<3>(o1));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bk[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bk[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av2, bk[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av3, bk[3], acc, 0, 0, 0);
+        asm volatile("" : "+v"(acc) : "v"(av0), "v"(av1), "v"(av2), "v"(av3), "v"(bk[0]), "v"(bk[1]), "v"(bk[2]),
+                     "v"(bk[3]));
+        sc[h2] = acc;
+      }
+      // r of this lane's tokens 32 kb + 8 g + tau(2 i + parity): dwords 2 (i/2) + parity
+      const uint4 rr = kr[kb];
+      const uint32_t rd[2] = {rows_lo ? rr.x : rr.y, rows_lo ? rr.z : rr.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float S = acc[i] + dppf<kQx1>(acc[i]);  // hi + lo columns
+        const float x = rows_lo ? sc[0][i] : sc[1][i];
+        const float S = x + dppf<kQx1>(x);  // hi + lo columns
         const uint32_t rw = rd[i >> 1];
         const float r = (i & 1) ? f16hi(rw) : f16lo(rw);
-        lsc[mb][i] = fmaf(S, K1, bq) * r;
+        lsc[kb][i] = fmaf(S, K1, bq) * r;
       }
     }
 
     // ---- online softmax (query head c/2 % 4; all 4 rows hold the same head)
     float tmax = lsc[0][0];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = vmax(tmax, lsc[mb][i]);
+      for (int i = 0; i < 4; ++i) tmax = vmax(tmax, lsc[kb][i]);
+    tmax = vmax(tmax, dppf<kRor8>(tmax));
     tmax = rows_max(tmax);
     const float mnew = vmax(m_run, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
     float psum = 0.0f, wsum = 0.0f, wmx = 0.0f;
-    float pr[NMB][4];
+    float pr[NKB][4];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const uint4 rr = vr[mb >> 1];
-      const uint32_t rd[2] = {(mb & 1) ? rr.y : rr.x, (mb & 1) ? rr.w : rr.z};
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint4 rr = vr[kb];
+      const uint32_t rd[2] = {rows_lo ? rr.x : rr.y, rows_lo ? rr.z : rr.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(lsc[mb][i] - mnew);
+        const float p = __builtin_amdgcn_exp2f(lsc[kb][i] - mnew);
         const uint32_t rw = rd[i >> 1];
         const float r = (i & 1) ? f16hi(rw) : f16lo(rw);
         psum += p;
-        pr[mb][i] = p * r;
-        wsum += pr[mb][i];
-        wmx = fmaxf(wmx, pr[mb][i]);
+        pr[kb][i] = p * r;
+        wsum += pr[kb][i];
+        wmx = fmaxf(wmx, pr[kb][i]);
       }
     }
-    l_run = fmaf(l_run, alpha, psum);
+    l_run = fmaf(l_run, alpha, psum);  // this lane's blocks; the partner's half joins at the end
     m_run = mnew;
+    wsum += dppf<kRor8>(wsum);
     wsum = rows_sum(wsum);
     float sV, invSV;
     pow2_scale(wave_max_pos(wmx), sV, invSV);
 
-    // ---- V: weights (hi or lo part by column parity) against the codes
+    // ---- V: weights (hi or lo part by column parity) against the codes. Each lane packs
+    // its own tokens in pairs (i, i+1); the A operand wants (even block, odd block) of the
+    // same i, so the pairs are merged with the partner's by byte permutes.
     h8v aw1[NKB], aw2[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       uint32_t d[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float w0 = pr[2 * kb][i] * sV, w1 = pr[2 * kb + 1][i] * sV;
+      for (int pp = 0; pp < 2; ++pp) {
+        const float w0 = pr[kb][2 * pp] * sV, w1 = pr[kb][2 * pp + 1] * sV;
         const uint32_t hv = pack_f16(w0, w1);
-        d[i] = pack_f16(fmaf(-partf, f16lo(hv), w0), fmaf(-partf, f16hi(hv), w1));
+        const uint32_t mine = pack_f16(fmaf(-partf, f16lo(hv), w0), fmaf(-partf, f16hi(hv), w1));
+        const uint32_t theirs = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, kRor8, 0xF, 0xF, true);
+        d[2 * pp] = __builtin_amdgcn_perm(theirs, mine, sel_lo);
+        d[2 * pp + 1] = __builtin_amdgcn_perm(theirs, mine, sel_hi);
       }
       const h8v wv = as_h8(d[0], d[1], d[2], d[3]);
       const h8v zv = as_h8(0u, 0u, 0u, 0u);
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         o[1][i] *= af1;
       }
     }
-    const float4* vfp = reinterpret_cast<const float4*>(&wl.vf[c][4 * (g >> 1)]);
+    const float4* vfp = reinterpret_cast<const float4*>(&wl.vf[c][8 * (g >> 1)]);
     const float4 f01 = vfp[0], f23 = vfp[1];
     const float fcs[4] = {f01.x, f01.z, f23.x, f23.z}, fcz[4] = {f01.y, f01.w, f23.y, f23.w};
 #pragma unroll
@@ -384,6 +406,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 
   // --- merge the 4 waves of the span (fixed order), one partial per query head
+  l_run += dppf<kRor8>(l_run);
   l_run = rows_sum(l_run);
   __syncthreads();
 #pragma unroll
