@@ -66,6 +66,30 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
 }
 
+// Exact product of two fp16 values taken from the same half (low: HI = 0, high: HI = 1)
+// of two packed registers, one v_fma_mix_f32 (an fp16 x fp16 product fits fp32 exactly).
+template <int HI>
+__device__ __forceinline__ float mul_f16(uint32_t a, uint32_t b) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// x - m * (fp16 half HI of h), one v_fma_mix_f32: the residual of an fp16 rounding
+// (exact, as x and the rounded value are within a factor of two of each other)
+template <int HI>
+__device__ __forceinline__ float sub_f16(float x, uint32_t h, float m) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(-m), "v"(x));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(-m), "v"(x));
+  return r;
+}
+
 // max over the 64 lanes of non-negative floats (compared as integers), wave-uniform
 __device__ __forceinline__ uint32_t wave_max_pos(float x) {
   uint32_t u = (uint32_t)__float_as_int(x);
@@ -240,8 +264,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
 
     // ---- K-side factors of this lane's channel pair; per-tile scale of the a-values
-    const float cs0 = f16lo(kcs) * f16lo(kss), cs1 = f16hi(kcs) * f16hi(kss);
-    const float cz0 = f16lo(kcs) * f16lo(kzs), cz1 = f16hi(kcs) * f16hi(kzs);
+    const float cs0 = mul_f16<0>(kcs, kss), cs1 = mul_f16<1>(kcs, kss);
+    const float cz0 = mul_f16<0>(kcs, kzs), cz1 = mul_f16<1>(kcs, kzs);
     float sB, invSB;
     pow2_scale(wave_max_pos(fmaxf(cs0, cs1) * mq), sB, invSB);
     const float f0 = cs0 * sB, f1 = cs1 * sB;
@@ -250,13 +274,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int qh = 0; qh < 4; ++qh) {
       const float a0 = f0 * qr[qh][0], a1 = f1 * qr[qh][1];
       const uint32_t hv = pack_f16(a0, a1);
-      const uint32_t lv = pack_f16(a0 - f16lo(hv), a1 - f16hi(hv));
+      const uint32_t lv = pack_f16(sub_f16<0>(a0, hv, 1.0f), sub_f16<1>(a1, hv, 1.0f));
       bop[(wbase + ((2 * qh) ^ wswz)) * 4 + kk_m] = hv;
       bop[(wbase + ((2 * qh + 1) ^ wswz)) * 4 + kk_m] = lv;
     }
-    *reinterpret_cast<float2*>(&wl.vf[2 * wm][2 * nbm]) = make_float2(f16lo(vcs) * f16lo(vss), f16lo(vcs) * f16lo(vzs));
-    *reinterpret_cast<float2*>(&wl.vf[2 * wm + 1][2 * nbm]) =
-        make_float2(f16hi(vcs) * f16hi(vss), f16hi(vcs) * f16hi(vzs));
+    *reinterpret_cast<float2*>(&wl.vf[2 * wm][2 * nbm]) = make_float2(mul_f16<0>(vcs, vss), mul_f16<0>(vcs, vzs));
+    *reinterpret_cast<float2*>(&wl.vf[2 * wm + 1][2 * nbm]) = make_float2(mul_f16<1>(vcs, vss), mul_f16<1>(vcs, vzs));
     float bp[4];
 #pragma unroll
     for (int qh = 0; qh < 4; ++qh) bp[qh] = fmaf(qr[qh][0], cz0, qr[qh][1] * cz1);
@@ -352,7 +375,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int pp = 0; pp < 2; ++pp) {
         const float w0 = pr[kb][2 * pp] * sV, w1 = pr[kb][2 * pp + 1] * sV;
         const uint32_t hv = pack_f16(w0, w1);
-        const uint32_t mine = pack_f16(fmaf(-partf, f16lo(hv), w0), fmaf(-partf, f16hi(hv), w1));
+        const uint32_t mine = pack_f16(sub_f16<0>(w0, hv, partf), sub_f16<1>(w1, hv, partf));
         const uint32_t theirs = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, kRor8, 0xF, 0xF, true);
         d[2 * pp] = __builtin_amdgcn_perm(theirs, mine, sel_lo);
         d[2 * pp + 1] = __builtin_amdgcn_perm(theirs, mine, sel_hi);
