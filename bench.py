@@ -112,6 +112,38 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     attn_ms = [a.elapsed_time(b) for a, b in evs]
+    # one append launch per layer-step, timed the same way
+    ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+    for i, (e0, e1) in enumerate(ea):
+        s = warmup + steps + i
+        e0.record(stream)
+        K.kvarn_append_decode(g, caches[0], kp[s % pool], vp[s % pool], stream)
+        e1.record(stream)
+        for l in range(1, layers):
+            K.kvarn_append_decode(g, caches[l], kp[s % pool], vp[s % pool], stream)
+        for l in range(layers):
+            K.kvarn_attn_decode(g, caches[l], qp[s % pool], Hq, 0.0, 0, ws, nws, out, stream)
+    torch.cuda.synchronize()
+    append_ms = [a.elapsed_time(b) for a, b in ea]
+    # the same step as one HIP graph: 40 x (append + attention) replayed, the step's inputs
+    # copied into the captured buffers first (inside the timed region)
+    k_in, v_in, q_in = torch.empty_like(kp[0]), torch.empty_like(vp[0]), torch.empty_like(qp[0])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l in range(layers):
+            K.kvarn_append_decode(g, caches[l], k_in, v_in)
+            K.kvarn_attn_decode(g, caches[l], q_in, Hq, 0.0, 0, ws, nws, out)
+    torch.cuda.synchronize()
+    s0 = warmup + steps + len(ea)
+    t0 = time.perf_counter()
+    for s in range(s0, s0 + steps):
+        k_in.copy_(kp[s % pool])
+        v_in.copy_(vp[s % pool])
+        q_in.copy_(qp[s % pool])
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_wall = time.perf_counter() - t0
+    del graph
     flags = K.kvarn_cache_flags(caches[0])
     ctx_mid = T0 + warmup + steps // 2
     # attention bytes per layer-step: K and V records of the full tiles + tail rows + q + out
@@ -120,7 +152,39 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
     del caches
     torch.cuda.empty_cache()
     return dict(wall=wall, steps=steps, B=B, layers=layers, attn_ms=attn_ms, attn_bytes=attn_bytes, flags=flags,
-                ctx_start=T0 + warmup, H=H, Hq=Hq)
+                ctx_start=T0 + warmup, H=H, Hq=Hq, graph_wall=graph_wall, append_ms=append_ms)
+
+
+def bench_bf16_decode(torch, steps=8, warmup=2, layers=40, B=32, H=10, Hq=40, T=16384):
+    """Plain bf16 decode attention over a bf16 KV cache of the same shapes (no quantization):
+    per layer scores = q K^T (K stored transposed, [B][H][D][T]), fp32 softmax, out = p V,
+    as batched matrix products whose right operands are contiguous."""
+    grp = Hq // H
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    kt = [torch.randn(B, H, 128, T, generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(layers)]
+    vv = [torch.randn(B, H, T, 128, generator=gen, device="cuda", dtype=torch.bfloat16) for _ in range(layers)]
+    q = torch.randn(B, H, grp, 128, generator=gen, device="cuda", dtype=torch.bfloat16)
+    scale = 1.0 / 128 ** 0.5
+
+    def step():
+        for l in range(layers):
+            sc = torch.matmul(q, kt[l]).float() * scale
+            p = torch.softmax(sc, dim=-1).to(torch.bfloat16)
+            torch.matmul(p, vv[l])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cache_bytes = layers * 2 * B * H * T * 128 * 2
+    del kt, vv
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=round(wall * 1e3 / steps, 3), tokens_per_s=round(B * steps / wall, 1),
+                cache_GB=round(cache_bytes / 1e9, 2), context=T)
 
 
 def copy_ceiling(torch, gib=4):
@@ -215,6 +279,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--cpu-layers", type=int, default=5, help="layers of the prefill workload the oracle runs")
     ap.add_argument("--no-copy", action="store_true", help="skip the 4 GiB device copy ceiling")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the plain bf16 decode-attention baseline")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -279,7 +344,18 @@ def main():
                          "traffic": counted_traffic("attn_kernel_phi4_decode_pmc.txt",
                                                     ["kv_cache_bit_amd/csrc/attn.hip"]),
                          "traffic_unit": "bytes/launch (tile pass)"}}
-        log(f"decode: {tok_s:.1f} tok/s, attn {a_avg * 1e3:.1f} us/layer-step")
+        ap = sorted(dc["append_ms"])
+        res["decode"]["graph_tokens_per_s"] = round(dc["B"] * dc["steps"] / dc["graph_wall"], 1)
+        res["decode"]["graph_ms_per_step"] = round(dc["graph_wall"] * 1e3 / dc["steps"], 3)
+        res["decode"]["append_us"] = round(ap[len(ap) // 2] * 1e3, 2)
+        res["decode"]["append_share"] = round(ap[len(ap) // 2] / (ap[len(ap) // 2] + a_avg), 4)
+        log(f"decode: {tok_s:.1f} tok/s eager, {res['decode']['graph_tokens_per_s']} tok/s as a graph; "
+            f"attn {a_avg * 1e3:.1f} us, append {res['decode']['append_us']} us per layer-step")
+        if not args.no_bf16:
+            bf = bench_bf16_decode(torch)
+            res["decode"]["bf16_baseline"] = dict(bf, kind="plain bf16 KV cache, torch batched products, same shapes")
+            res["decode"]["speedup_vs_bf16"] = round(res["decode"]["graph_tokens_per_s"] / bf["tokens_per_s"], 2)
+            log(f"bf16 baseline: {bf}")
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(synth, args.cpu_tokens, args.cpu_layers)
