@@ -49,6 +49,13 @@ SCALE_MIN = 2.0 ** -14      # smallest normal fp16; lower clamp of r and c
 HEADER_FIXED = 512          # len[] starts here
 SIGMA_OFFSET = 64
 FLAGS_OFFSET = 36
+VARIANT_OFFSET = 40
+# Ablation variants ([AP] section 5, ablations: Hadamard only, VarN only, VarN along one
+# axis only). A bit set removes one component; 0 is the method as defined.
+VARIANT_NO_ROTATION = 1       # H_D replaced by the identity ("VarN only")
+VARIANT_NO_CHANNEL_PASS = 2   # VarN keeps the token-axis passes only
+VARIANT_NO_TOKEN_PASS = 4     # VarN keeps the channel-axis passes only
+VARIANT_CENTERED = 8          # "variance" about the mean instead of the mean square
 
 
 def align256(n: int) -> int:
@@ -121,8 +128,25 @@ def unrotate(w, sigma) -> np.ndarray:
     return np.asarray(w, dtype=np.float64) @ rotation_matrix(sigma).T
 
 
+def apply_rotation(x, sigma, variant: int = 0) -> np.ndarray:
+    """x H_D, or x itself for the "VarN only" ablation (VARIANT_NO_ROTATION)."""
+    return np.asarray(x, dtype=np.float64) if variant & VARIANT_NO_ROTATION else rotate(x, sigma)
+
+
+def undo_rotation(w, sigma, variant: int = 0) -> np.ndarray:
+    """w H_D^T, or w itself for the "VarN only" ablation."""
+    return np.asarray(w, dtype=np.float64) if variant & VARIANT_NO_ROTATION else unrotate(w, sigma)
+
+
 # ----------------------------------------------------------------------------- VarN ([AP] 3.2)
-def varn(w, n_it: int) -> tuple[np.ndarray, np.ndarray]:
+def _spread(y, axis: int, centered: bool) -> np.ndarray:
+    """Mean square of y along `axis`; with `centered`, the variance about the mean."""
+    if centered:
+        y = y - np.mean(y, axis=axis, keepdims=True)
+    return np.mean(y * y, axis=axis)
+
+
+def varn(w, n_it: int, variant: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """Dual-axis variance normalization of tile(s) w[..., G, D]; returns (r[..., G], c[..., D]).
 
     [AP] 3.2: (1) normalize along the token axis so each token's variance is 1,
@@ -132,17 +156,23 @@ def varn(w, n_it: int) -> tuple[np.ndarray, np.ndarray]:
     the scales are cumulative and multiplicative, Y = W / (r_t c_j), starting at 1;
     one iteration is a token pass followed by a channel pass; a pass leaves the
     scale unchanged where the mean square is 0 (all-zero row or column).
+    Ablations ([AP] section 5): VARIANT_NO_CHANNEL_PASS / VARIANT_NO_TOKEN_PASS drop
+    one of the two passes (the other then reaches its fixed point after one pass),
+    VARIANT_CENTERED measures the variance about the mean.
     """
     w = np.asarray(w, dtype=np.float64)
     r = np.ones(w.shape[:-1])
     c = np.ones(w.shape[:-2] + w.shape[-1:])
+    centered = bool(variant & VARIANT_CENTERED)
     for _ in range(n_it):
-        y = w / (r[..., :, None] * c[..., None, :])
-        ms_t = np.mean(y * y, axis=-1)                       # token axis: one value per token
-        r = np.where(ms_t > 0, r * np.sqrt(ms_t), r)
-        y = w / (r[..., :, None] * c[..., None, :])
-        ms_j = np.mean(y * y, axis=-2)                       # channel axis: one value per channel
-        c = np.where(ms_j > 0, c * np.sqrt(ms_j), c)
+        if not variant & VARIANT_NO_TOKEN_PASS:
+            y = w / (r[..., :, None] * c[..., None, :])
+            ms_t = _spread(y, -1, centered)                  # token axis: one value per token
+            r = np.where(ms_t > 0, r * np.sqrt(ms_t), r)
+        if not variant & VARIANT_NO_CHANNEL_PASS:
+            y = w / (r[..., :, None] * c[..., None, :])
+            ms_j = _spread(y, -2, centered)                  # channel axis: one value per channel
+            c = np.where(ms_j > 0, c * np.sqrt(ms_j), c)
     return r, c
 
 
@@ -194,9 +224,9 @@ def pre_rounding(y, s16, z16) -> np.ndarray:
     return (np.asarray(y) - z) / np.where(s == 0, 1.0, s)
 
 
-def quantize_tile(w, n_it: int) -> dict:
+def quantize_tile(w, n_it: int, variant: int = 0) -> dict:
     """Rotated tile(s) w[..., G, D] -> stored scales, grid, codes (steps of [AP] 3.2)."""
-    r, c = varn(w, n_it)
+    r, c = varn(w, n_it, variant)
     r16, c16, clamped = stored_scales(r, c)
     y = normalize(w, r16, c16)
     s16, z16, sat = grid(y)
@@ -274,11 +304,13 @@ def unpack_record(rec, g: int, d: int, stream: int) -> dict:
 
 # ----------------------------------------------------------------------------- cache buffer (format v1)
 class Geom:
-    """batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits."""
+    """batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant (VARIANT_* bits)."""
 
-    def __init__(self, batch, num_kv_heads, head_dim=128, capacity=0, group=32, varn_iters=3, bits=2):
+    def __init__(self, batch, num_kv_heads, head_dim=128, capacity=0, group=32, varn_iters=3, bits=2,
+                 variant=0):
         self.batch, self.num_kv_heads, self.head_dim = batch, num_kv_heads, head_dim
         self.capacity, self.group, self.varn_iters, self.bits = capacity, group, varn_iters, bits
+        self.variant = variant
 
     def as_tuple(self):
         return (self.batch, self.num_kv_heads, self.head_dim, self.capacity, self.group,
@@ -323,6 +355,7 @@ class Cache:
         hdr[0:4].view(np.uint32)[0] = MAGIC
         hdr[4:8].view(np.uint32)[0] = VERSION
         hdr[8:36].view(np.int32)[:] = geom.as_tuple()
+        hdr[VARIANT_OFFSET:VARIANT_OFFSET + 4].view(np.uint32)[0] = geom.variant
         hdr[SIGMA_OFFSET:SIGMA_OFFSET + geom.head_dim].view(np.int8)[:] = np.asarray(sigma, np.int8)
 
     # header fields
@@ -376,8 +409,8 @@ def _quantize_stream(x, sigma, g: Geom, stream: int):
     """x[..., n_tiles*G, D] canonical fp64 tokens -> (records [..., n_tiles, TR], flags)."""
     lead = x.shape[:-2]
     nt = x.shape[-2] // g.group
-    w = rotate(x, sigma).reshape(lead + (nt, g.group, g.head_dim))
-    t = quantize_tile(w, g.varn_iters)
+    w = apply_rotation(x, sigma, g.variant).reshape(lead + (nt, g.group, g.head_dim))
+    t = quantize_tile(w, g.varn_iters, g.variant)
     recs = np.zeros(lead + (nt, g.tr), dtype=np.uint8)
     for idx in np.ndindex(*(lead + (nt,))):
         recs[idx] = pack_record(t["q"][idx], t["r16"][idx], t["c16"][idx], t["s16"][idx],
@@ -449,10 +482,10 @@ def stream_values(cache: Cache, b: int, h: int, s: int, rotated: bool = False) -
     for tile in range(nfull):
         u = unpack_record(cache.record(b, h, tile, s), g.group, g.head_dim, s)
         w = dequantize_tile(u["q"], u["r16"], u["c16"], u["s16"], u["z16"])
-        out[tile * g.group:(tile + 1) * g.group] = w if rotated else unrotate(w, cache.sigma)
+        out[tile * g.group:(tile + 1) * g.group] = w if rotated else undo_rotation(w, cache.sigma, g.variant)
     tail = cache.tail(b, h, s).astype(np.float64)
     for t in range(nfull * g.group, n):
-        out[t] = rotate(tail[t % g.group], cache.sigma) if rotated else tail[t % g.group]
+        out[t] = apply_rotation(tail[t % g.group], cache.sigma, g.variant) if rotated else tail[t % g.group]
     return out
 
 
@@ -485,7 +518,7 @@ def attn_decode(cache: Cache, q_bits, num_q_heads: int, softmax_scale: float = 0
     scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
     q = bf16_to_f64(q_bits)                                     # [B][Hq][D]
     if flags & Q_PREROTATED:
-        q = unrotate(q, cache.sigma)
+        q = undo_rotation(q, cache.sigma, g.variant)
     grp = num_q_heads // g.num_kv_heads
     out = np.zeros((g.batch, num_q_heads, d))
     todo = pairs if pairs is not None else [(b, h) for b in range(g.batch) for h in range(g.num_kv_heads)]
