@@ -27,7 +27,8 @@
  *   header  align256(512 + 8*B*Hkv) bytes:
  *           u32 magic 0x4E52564B, u32 version 1, i32 geom[7] (batch, num_kv_heads,
  *           head_dim, capacity, group, varn_iters, bits), u32 flags (sticky),
- *           i8 sigma[D] at byte 64, i32 len[B][Hkv][2] at byte 512;
+ *           u32 variant at byte 40, i8 sigma[D] at byte 64, i32 len[B][Hkv][2]
+ *           at byte 512;
  *   tiles   [B][Hkv][capacity/G][2 (K,V)][TR] tile records, region padded to 256 B;
  *   tail    [B][Hkv][2][G][D] fp16, unrotated tokens of the group being filled,
  *           slot = token index mod G.
@@ -74,7 +75,8 @@ typedef enum {
 } kvarn_status;
 
 /* Geometry of one layer cache. v1 supports head_dim = 128, group in {32, 64},
- * bits = 2, 0 <= varn_iters <= 8, capacity a positive multiple of group. */
+ * bits = 2, 0 <= varn_iters <= 8, capacity a positive multiple of group,
+ * variant a combination of the KVARN_VARIANT_* bits below (0 = the method). */
 typedef struct {
     int32_t batch;          /* B   sequences                                   */
     int32_t num_kv_heads;   /* Hkv                                             */
@@ -83,7 +85,18 @@ typedef struct {
     int32_t group;          /* G   tokens per tile (the pages' 32 or 64)       */
     int32_t varn_iters;     /* VarN iterations (token pass + channel pass)     */
     int32_t bits;           /* code width (2)                                  */
+    int32_t variant;        /* ablation bits, 0 for KVarN as defined           */
 } kvarn_geom;
+
+/* Ablation variants (ai-paper-analysis page, section 5: Hadamard only = varn_iters 0,
+ * VarN only, VarN along one axis only). The variant is written into the header at
+ * byte 40 by kvarn_cache_init; every call on a cache must pass the geometry it was
+ * initialized with. A cache with KVARN_VARIANT_NO_ROTATION uses the identity in
+ * place of H_D everywhere (quantization, dequantization and attention; sigma is
+ * stored but unused, and KVARN_Q_PREROTATED changes nothing). */
+enum { KVARN_VARIANT_NO_ROTATION = 1u,      /* H_D = I: "VarN only"                            */
+       KVARN_VARIANT_NO_CHANNEL_PASS = 2u,  /* VarN keeps the token-axis passes only: c = 1     */
+       KVARN_VARIANT_NO_TOKEN_PASS = 4u     /* VarN keeps the channel-axis passes only: r = 1   */ };
 
 enum { KVARN_OUT_F32 = 0, KVARN_OUT_BF16 = 1 };            /* dequantize output dtype     */
 enum { KVARN_Q_PREROTATED = 1u };                          /* attention: q is already q H_D */

@@ -18,6 +18,8 @@ kvarn_status check_geom(const kvarn_geom* g) {
     return KVARN_ERR_GEOM;
   if (g->head_dim != kD || (g->group != 32 && g->group != 64) || g->bits != 2 || g->varn_iters > 8)
     return KVARN_ERR_UNSUPPORTED;
+  if (g->variant & ~(int32_t)(KVARN_VARIANT_NO_ROTATION | KVARN_VARIANT_NO_CHANNEL_PASS | KVARN_VARIANT_NO_TOKEN_PASS))
+    return KVARN_ERR_UNSUPPORTED;
   if (g->capacity % g->group != 0) return KVARN_ERR_GEOM;
   // keep every element index of a [B][capacity][Hkv][D] tensor and every tile count in range
   if ((long long)g->batch * g->capacity * g->num_kv_heads * kD >= (1LL << 40)) return KVARN_ERR_RANGE;
@@ -71,7 +73,7 @@ const char* kvarn_status_str(kvarn_status s) {
     case KVARN_ERR_NULL: return "null pointer";
     case KVARN_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case KVARN_ERR_GEOM: return "inconsistent geometry";
-    case KVARN_ERR_UNSUPPORTED: return "unsupported geometry (v1: head_dim 128, group 32/64, 2 bits, <= 8 VarN iterations)";
+    case KVARN_ERR_UNSUPPORTED: return "unsupported geometry (v1: head_dim 128, group 32/64, 2 bits, <= 8 VarN iterations, variant bits 1|2|4)";
     case KVARN_ERR_RANGE: return "size out of range";
     case KVARN_ERR_DEVICE: return "HIP runtime error";
   }
@@ -102,6 +104,7 @@ kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* si
   a.geom[4] = g->group;
   a.geom[5] = g->varn_iters;
   a.geom[6] = g->bits;
+  a.variant = (uint32_t)g->variant;
   memcpy(a.sigma, signs_host, kD);
   a.n_len = 2LL * g->batch * g->num_kv_heads;
   a.hdr_bytes = make_layout(*g).header;
@@ -204,6 +207,7 @@ kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const voi
   attn_split(g, a.grp, &a.tpw, &a.nspan);
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)kD);
   a.flags = flags;
+  a.idr = (g->variant & KVARN_VARIANT_NO_ROTATION) != 0;
   return dev(launch_attn(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         qv[2 * k + 1] = bf16hi(ws[k]);
       }
     }
-    if (!(a.flags & KVARN_Q_PREROTATED)) {
+    if (!(a.flags & KVARN_Q_PREROTATED) && !a.idr) {
       float sg[8];
       load_sigma(a.cache, c, sg);
 #pragma unroll
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       qv[2 * k] = bf16lo(ws[k]);
       qv[2 * k + 1] = bf16hi(ws[k]);
     }
-    if (a.flags & KVARN_Q_PREROTATED) {  // q = q_rot H_D^T
+    if ((a.flags & KVARN_Q_PREROTATED) && !a.idr) {  // q = q_rot H_D^T
       fwht128(qv, cg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[e] *= kInvSqrtD * sg[e];
@@ -572,12 +572,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       M = mn;
     }
   }
-  fwht128(orot, cg);  // all 16 lanes of the row take part, live or not
+  if (!a.idr) fwht128(orot, cg);  // all 16 lanes of the row take part, live or not
   if (!live) return;
   float o[8];
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (orot[e] * kInvSqrtD * sg[e] + oorig[e]) * inv;
+  for (int e = 0; e < 8; ++e) o[e] = (orot[e] * (a.idr ? 1.0f : kInvSqrtD * sg[e]) + oorig[e]) * inv;
   store8f(a.out + (long long)rr * kD + 8 * cg, o);
 }
 

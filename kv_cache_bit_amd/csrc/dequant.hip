@@ -83,13 +83,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         for (int i = 0; i < 8; ++i) w[i][e] = (float)((hq >> (2 * i)) & 3u);
       }
     }
+    const bool idr = (L.variant & KVARN_VARIANT_NO_ROTATION) != 0;  // uniform
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[i][e] = (ri[i] * cj[e]) * fmaf(sj[e], w[i][e], zj[e]);
-      fwht128(w[i], cg);
+      if (!idr) {
+        fwht128(w[i], cg);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[i][e] *= kInvSqrtD * sg[e];
+        for (int e = 0; e < 8; ++e) w[i][e] *= kInvSqrtD * sg[e];
+      }
       store_row(blk * 32 + rg * 8 + i, w[i]);
     }
   } else {
@@ -117,9 +120,10 @@ __global__ void init_kernel(InitArgs a) {
     h32[1] = kVersion;
     for (int k = 0; k < 7; ++k) h32[2 + k] = (uint32_t)a.geom[k];
     h32[9] = 0;  // flags
+    h32[10] = a.variant;
   }
-  for (int k = t; k < 128; k += blockDim.x) {  // bytes 40..511: pad, sigma, pad
-    const int off = 40 + 4 * k;
+  for (int k = t; k < 128; k += blockDim.x) {  // bytes 44..511: pad, sigma, pad
+    const int off = 44 + 4 * k;
     if (off >= kHdrFixed) break;
     uint32_t w = 0;
     for (int q = 0; q < 4; ++q) {

@@ -24,6 +24,7 @@ inline __host__ __device__ long long align256(long long n) { return (n + 255) / 
 // Byte layout of one layer cache (format v1), computed on the host and passed by value.
 struct Layout {
   int B, Hkv, cap, G, n_it, tiles;  // tiles = cap / G
+  int variant;                      // KVARN_VARIANT_* bits
   int tr;                           // tile record bytes
   long long header, tail_off, total;
 
@@ -67,6 +68,7 @@ inline __host__ Layout make_layout(const kvarn_geom& g) {
   L.cap = g.capacity;
   L.G = g.group;
   L.n_it = g.varn_iters;
+  L.variant = g.variant;
   L.tiles = g.capacity / g.group;
   L.tr = g.group * kD / 4 + 2 * g.group + 6 * kD;
   L.header = align256(kHdrFixed + 8LL * g.batch * g.num_kv_heads);

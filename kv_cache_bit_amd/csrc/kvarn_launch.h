@@ -11,6 +11,7 @@ namespace kvarn {
 struct InitArgs {
   uint8_t* cache;
   int32_t geom[7];
+  uint32_t variant;  // header byte 40
   int8_t sigma[kD];
   long long n_len;  // entries of len[]
   long long hdr_bytes;  // header size; everything past len[] is zeroed
@@ -54,6 +55,7 @@ struct AttnArgs {
   int nspan, tpw;     // spans of 4 * tpw tiles per sequence; tiles per wave
   float scale;
   uint32_t flags;
+  int idr;            // identity in place of H_D (KVARN_VARIANT_NO_ROTATION)
 };
 
 hipError_t launch_init(const InitArgs& a, hipStream_t st);

@@ -138,6 +138,24 @@ __device__ __forceinline__ Frags hadamard_frags(int lane) {
 __device__ __forceinline__ int frag_index(int ks, int nb) {
   return ((nb & 1) << 1) | (__builtin_popcount(ks & (nb >> 1)) & 1);
 }
+// Identity in place of H_syl (the "VarN only" ablation): block nb takes the single K-step
+// ks = nb/2, whose B fragment is one-hot: lane (g, c) holds 1 at e = c%8 iff
+// 8g + e = 16(nb%2) + c, i.e. g = 2(nb%2) + c/8. v[P] is the fragment for nb%2 = P.
+__device__ __forceinline__ Frags identity_frags(int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  Frags h;
+#pragma unroll
+  for (int P = 0; P < 2; ++P) {
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      w[d] = (g == 2 * P + (c >> 3) && d == ((c & 7) >> 1)) ? 0x3C00u << (16 * (c & 1)) : 0u;
+    h.v[P] = __builtin_bit_cast(h8v, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  h.v[2] = h.v[0];
+  h.v[3] = h.v[1];
+  return h;
+}
 
 // ----------------------------------------------------------------------------- inputs
 typedef float f2v __attribute__((ext_vector_type(2)));
@@ -192,22 +210,28 @@ __device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp1
                                             w.z ^ ((m.lo[2] >> 16) | m.hi[2]), w.w ^ ((m.lo[3] >> 16) | m.hi[3])));
 }
 
-// W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]
+// W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]; with ID the
+// identity fragments make W' = A (one MFMA per block).
 //
 // An MFMA whose destination shares registers with its A or B source reads clobbered
 // rows on this hardware. After each accumulation chain an empty asm takes the chain's
 // result as read-write and all its A and B fragments as inputs: the data dependency
 // pins it after the chain's MFMAs, so every source is still live when each of them
 // issues and the register allocator cannot hand a source's registers to the result.
+template <bool ID>
 __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& hf, f4v (&acc)[2][8]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (ID) {
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+      }
       asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
                    "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
       acc[mb][nb] = s;
@@ -218,6 +242,7 @@ __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& 
 // Rotation fused with the squares and the first token-axis sums (u = 1): each chain's
 // W' block is squared as soon as it is complete, so the fp32 block is never held whole.
 // Returns the row total of the lane's own token (see row_rs8).
+template <bool ID>
 __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, float (&p)[2][8][4],
                                                 int c) {
   float tp[8];
@@ -228,9 +253,13 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (ID) {
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+      }
       asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
                    "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
 #pragma unroll
@@ -241,6 +270,42 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
     }
   }
   return row_rs8(tp, c);
+}
+
+// Dispatch for the ablation build (ABL): the identity rotation is a runtime choice there;
+// the standard build compiles the Hadamard path only.
+template <bool ABL>
+__device__ __forceinline__ float rotate_squares_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
+                                                  float (&p)[2][8][4], int c) {
+  if constexpr (ABL) {
+    if (idr) return rotate_squares<true>(a, hf, p, c);
+  }
+  return rotate_squares<false>(a, hf, p, c);
+}
+template <bool ABL>
+__device__ __forceinline__ void rotate_block_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
+                                               f4v (&acc)[2][8]) {
+  if constexpr (ABL) {
+    if (idr) {
+      rotate_block<true>(a, hf, acc);
+      return;
+    }
+  }
+  rotate_block<false>(a, hf, acc);
+}
+template <bool ABL>
+__device__ __forceinline__ SigMask masks_v(bool idr, const uint8_t* hdr, int chunk) {
+  if constexpr (ABL) {
+    if (idr) return SigMask{};  // no sign flips without the rotation
+  }
+  return sigma_masks(hdr, chunk);
+}
+template <bool ABL>
+__device__ __forceinline__ Frags frags_v(bool idr, int lane) {
+  if constexpr (ABL) {
+    if (idr) return identity_frags(lane);
+  }
+  return hadamard_frags(lane);
 }
 
 // ----------------------------------------------------------------------------- LDS
@@ -346,59 +411,73 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
 // an all-zero line keeps its scale. Each lane owns one token (c/2 of its row's 8) and
 // two channels (16g + c, 64 + 16g + c): their scalars are computed once, by the owner,
 // and broadcast back.
-template <int NW, bool DBG>
+//
+// ABL builds the ablation variants (var = KVARN_VARIANT_* bits, uniform): with the
+// identity rotation W' = W (k = 1 instead of sqrt(D)): v and u keep their form, only r
+// becomes sqrt(S'_t) / (k sqrt(D)) and the start value v = 1/k^2; a dropped pass keeps
+// its scale at 1 (the other pass then repeats the same sums every iteration).
+template <int NW, bool DBG, bool ABL>
 __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2][8][4], float st_own, int lane,
-                            int sub, int stream, int n_it, TileLds<NW>& sh, uint32_t& flags, float* dbg_w,
+                            int sub, int stream, int n_it, int var, TileLds<NW>& sh, uint32_t& flags, float* dbg_w,
                             float* dbg_y, long long dstride) {
   constexpr int G = 32 * NW;
   const int g = lane >> 4, c = lane & 15;
   const int tau_own = c >> 1;  // own token: mb = tau/4, i = tau%4
+  const bool idr = ABL && (var & KVARN_VARIANT_NO_ROTATION);
+  const bool tok = !ABL || !(var & KVARN_VARIANT_NO_TOKEN_PASS);
+  const bool chp = !ABL || !(var & KVARN_VARIANT_NO_CHANNEL_PASS);
+  const float inv_k = idr ? 1.0f : kInvSqrtD;   // 1/k
+  const float r_k = idr ? kInvSqrtD : 1.0f / kD;  // 1/(k sqrt(D))
 
   float u[8], v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) u[k] = 1.0f;
-  float v_own = 1.0f / kD, s_tok = st_own;
+  float v_own = idr ? 1.0f : 1.0f / kD, s_tok = st_own;
   float u_own[2] = {1.0f, 1.0f}, s_ch[2] = {0.0f, 0.0f};
   for (int it = 0; it < n_it; ++it) {
-    if (it > 0) {  // token pass (the first one arrives precomputed)
-      float tp[8];
+    if (tok) {
+      if (it > 0) {  // token pass (the first one arrives precomputed)
+        float tp[8];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float t = 0.0f;
+          for (int i = 0; i < 4; ++i) {
+            float t = 0.0f;
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) t = fmaf(p[mb][nb][i], u[nb], t);
-          tp[4 * mb + i] = t;
-        }
-      s_tok = row_rs8(tp, c);
+            for (int nb = 0; nb < 8; ++nb) t = fmaf(p[mb][nb][i], u[nb], t);
+            tp[4 * mb + i] = t;
+          }
+        s_tok = row_rs8(tp, c);
+      }
+      if (s_tok > 0.0f) v_own = (float)kD * __builtin_amdgcn_rcpf(s_tok);
     }
-    if (s_tok > 0.0f) v_own = (float)kD * __builtin_amdgcn_rcpf(s_tok);
-    row_gather8(v_own, v, sh.grow[sub], g, c);
-    float cp[8];  // channel pass
+    if (chp) {
+      row_gather8(v_own, v, sh.grow[sub], g, c);
+      float cp[8];  // channel pass
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      float t = 0.0f;
+      for (int nb = 0; nb < 8; ++nb) {
+        float t = 0.0f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t = fmaf(p[mb][nb][i], v[4 * mb + i], t);
-      cp[nb] = t;
+          for (int i = 0; i < 4; ++i) t = fmaf(p[mb][nb][i], v[4 * mb + i], t);
+        cp[nb] = t;
+      }
+      chan_reduce<NW>(cp, s_ch, sh, g, c, sub, sh.red_a, OpAdd());
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (s_ch[q] > 0.0f) u_own[q] = (float)G * __builtin_amdgcn_rcpf(s_ch[q]);
+      col_gather8(u_own, u, sh.gcol[sub], g, c);
     }
-    chan_reduce<NW>(cp, s_ch, sh, g, c, sub, sh.red_a, OpAdd());
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (s_ch[q] > 0.0f) u_own[q] = (float)G * __builtin_amdgcn_rcpf(s_ch[q]);
-    col_gather8(u_own, u, sh.gcol[sub], g, c);
   }
 
   // stored scales: fp16, clamped to [2^-14, 65504]
-  const float r_own = (n_it > 0 && s_tok > 0.0f) ? __builtin_amdgcn_sqrtf(s_tok) * (1.0f / kD) : 1.0f;
+  const float r_own = (n_it > 0 && tok && s_tok > 0.0f) ? __builtin_amdgcn_sqrtf(s_tok) * r_k : 1.0f;
   const float rc = fminf(fmaxf(r_own, kScaleMin), kFp16Max);
   if (rc != r_own) flags |= KVARN_FLAG_SCALE_CLAMPED;
   const float r16_own = round_f16(rc);
-  float at[8];  // Y = W' / (sqrt(D) r16 c16): per-token factor 1 / (sqrt(D) r16)
-  row_gather8(kInvSqrtD * __builtin_amdgcn_rcpf(r16_own), at, sh.grow[sub], g, c);
+  float at[8];  // Y = W' / (k r16 c16): per-token factor 1 / (k r16)
+  row_gather8(inv_k * __builtin_amdgcn_rcpf(r16_own), at, sh.grow[sub], g, c);
   float c16_own[2], ic_own[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -420,7 +499,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
       asm volatile("" : "+v"(av2[mb][ks]) : "v"(s_tok), "v"(s_ch[0]), "v"(s_ch[1]));
     }
   f4v acc[2][8];
-  rotate_block(av2, hf, acc);
+  rotate_block_v<ABL>(idr, av2, hf, acc);
   if constexpr (DBG) {
     float ic[8];
     col_gather8(ic_own, ic, sh.gcol[sub], g, c);
@@ -431,11 +510,11 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           const long long off = (16 * mb + 4 * g + i) * dstride + 16 * nb + c;
-          if (dbg_w) dbg_w[off] = acc[mb][nb][i] * kInvSqrtD;
+          if (dbg_w) dbg_w[off] = acc[mb][nb][i] * inv_k;
           if (dbg_y) dbg_y[off] = (acc[mb][nb][i] * at[4 * mb + i]) * ic[nb];
         }
   }
-  // Y' = W' / (sqrt(D) r16) = Y c16 (the positive c16 is applied to the channel's min/max)
+  // Y' = W' / (k r16) = Y c16 (the positive c16 is applied to the channel's min/max)
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -551,7 +630,7 @@ __device__ __forceinline__ uint32_t sat_flag(float amax) {
 // ----------------------------------------------------------------------------- prefill
 // Work-groups [0, tile_blocks) quantize full tiles, 4/NW tiles per work-group; the
 // remaining work-groups write the fp16 tail and len[], one (b, h, s) per wave.
-template <int NW, bool DBG>
+template <int NW, bool DBG, bool ABL>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   constexpr int TPW = 4 / NW;
   __shared__ TileLds<NW> sh_all[TPW];
@@ -594,7 +673,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int b = (int)q3;
   const uint16_t* src = s ? a.v : a.k;
   const int t0 = tile * L.G + sub * 32;  // first token of this wave's block
-  const Frags hf = hadamard_frags(lane);
+  const bool idr = ABL && (L.variant & KVARN_VARIANT_NO_ROTATION);
+  const Frags hf = frags_v<ABL>(idr, lane);
 
   // A rows are tokens t0 + 16mb + c; K chunk 4ks + g holds channels 8(4ks + g) .. +7
   const uint16_t* rows = src + (((long long)b * a.T + t0 + c) * L.Hkv + h) * kD + 8 * g;
@@ -610,21 +690,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int ks = 0; ks < 4; ++ks) raw[mb][ks] = *reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const SigMask m = sigma_masks(hdr, 4 * ks + g);
+      const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) av[mb][ks] = canon_a<false>(raw[mb][ks], m);
     }
   }
-  st = rotate_squares(av, hf, p, c);
+  st = rotate_squares_v<ABL>(idr, av, hf, p, c);
   if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion): redo saturating
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const SigMask m = sigma_masks(hdr, 4 * ks + g);
+      const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         av[mb][ks] = canon_a<true>(*reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks), m);
     }
-    st = rotate_squares(av, hf, p, c);
+    st = rotate_squares_v<ABL>(idr, av, hf, p, c);
     flags |= KVARN_FLAG_SATURATED;
   }
 
@@ -640,7 +720,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     dw = (valid && pw) ? pw + doff : nullptr;
     dy = (valid && py) ? py + doff : nullptr;
   }
-  tile_finish<NW, DBG>(av, hf, p, st, lane, sub, s, L.n_it, sh, flags, dw, dy, dstride);
+  tile_finish<NW, DBG, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, dw, dy, dstride);
   if (valid) {
     copy_record<NW>(sh, a.cache + L.record(b, h, tile, s), lane, sub);
     raise_flags(hdr, flags);
@@ -650,7 +730,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 // ----------------------------------------------------------------------------- append
 // One work-group (G/32 waves) per (b, h, s). The token goes to tail slot len mod G;
 // when it completes a group, the group is quantized into the next tile record.
-template <int NW>
+template <int NW, bool ABL>
 __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
   constexpr int G = 32 * NW;
   __shared__ TileLds<NW> sh;
@@ -674,11 +754,12 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
     *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, pos % G) + 16 * c) = pack8_f16(xin);
   }
   if ((pos + 1) % G == 0) {
-    const Frags hf = hadamard_frags(lane);
+    const bool idr = ABL && (L.variant & KVARN_VARIANT_NO_ROTATION);
+    const Frags hf = frags_v<ABL>(idr, lane);
     h8v av[2][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const SigMask m = sigma_masks(hdr, 4 * ks + g);
+      const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int t = sub * 32 + 16 * mb + c;  // token of this A row inside the tile
@@ -694,8 +775,8 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
       }
     }
     float p[2][8][4];
-    const float st = rotate_squares(av, hf, p, c);
-    tile_finish<NW, false>(av, hf, p, st, lane, sub, s, L.n_it, sh, flags, nullptr, nullptr, 0);
+    const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
+    tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, nullptr, nullptr, 0);
     copy_record<NW>(sh, a.cache + L.record(b, h, (pos + 1) / G - 1, s), lane, sub);
   }
   raise_flags(hdr, flags);
@@ -710,26 +791,35 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const long long tail_blocks = (2LL * a.L.B * a.L.Hkv + 3) / 4;
   const dim3 grid((unsigned)(tile_blocks + tail_blocks));
   const bool dbg = a.wk || a.wv || a.yk || a.yv;
-  if (a.L.G == 32) {
-    if (dbg)
-      hipLaunchKernelGGL((prefill_kernel<1, true>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel<1, false>), grid, dim3(256), 0, st, a);
-  } else {
-    if (dbg)
-      hipLaunchKernelGGL((prefill_kernel<2, true>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel<2, false>), grid, dim3(256), 0, st, a);
+  const bool abl = a.L.variant != 0;
+  const int which = (a.L.G == 32 ? 0 : 4) + (dbg ? 2 : 0) + (abl ? 1 : 0);
+  switch (which) {
+    case 0: hipLaunchKernelGGL((prefill_kernel<1, false, false>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<1, false, true>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<1, true, false>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((prefill_kernel<1, true, true>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<2, false, false>), grid, dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((prefill_kernel<2, false, true>), grid, dim3(256), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((prefill_kernel<2, true, false>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((prefill_kernel<2, true, true>), grid, dim3(256), 0, st, a); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(2LL * a.L.B * a.L.Hkv));
-  if (a.L.G == 32)
-    hipLaunchKernelGGL(append_kernel<1>, grid, dim3(64), 0, st, a);
-  else
-    hipLaunchKernelGGL(append_kernel<2>, grid, dim3(128), 0, st, a);
+  const bool abl = a.L.variant != 0;
+  if (a.L.G == 32) {
+    if (abl)
+      hipLaunchKernelGGL((append_kernel<1, true>), grid, dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((append_kernel<1, false>), grid, dim3(64), 0, st, a);
+  } else {
+    if (abl)
+      hipLaunchKernelGGL((append_kernel<2, true>), grid, dim3(128), 0, st, a);
+    else
+      hipLaunchKernelGGL((append_kernel<2, false>), grid, dim3(128), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ KVARN_ERR_UNSUPPORTED, KVARN_ERR_RANGE, KVARN_ERR_DEVICE = 4, 5, 6
 KVARN_OUT_F32, KVARN_OUT_BF16 = 0, 1
 KVARN_Q_PREROTATED = 1
 KVARN_FLAG_CAPACITY, KVARN_FLAG_SATURATED, KVARN_FLAG_SCALE_CLAMPED = 1, 2, 4
+KVARN_VARIANT_NO_ROTATION, KVARN_VARIANT_NO_CHANNEL_PASS, KVARN_VARIANT_NO_TOKEN_PASS = 1, 2, 4
 
 EXPORTS = ("kvarn_format_version", "kvarn_cache_bytes", "kvarn_cache_init", "kvarn_quantize_prefill",
            "kvarn_append_decode", "kvarn_dequantize", "kvarn_attn_workspace_bytes", "kvarn_attn_decode",
@@ -31,14 +32,14 @@ class KvarnError(RuntimeError):
 
 class kvarn_geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "num_kv_heads", "head_dim", "capacity", "group", "varn_iters", "bits")]
+                ("batch", "num_kv_heads", "head_dim", "capacity", "group", "varn_iters", "bits", "variant")]
 
     def __repr__(self):
         return "kvarn_geom(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
-def geom(batch, num_kv_heads, capacity, group=32, varn_iters=3, head_dim=128, bits=2) -> kvarn_geom:
-    return kvarn_geom(batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits)
+def geom(batch, num_kv_heads, capacity, group=32, varn_iters=3, head_dim=128, bits=2, variant=0) -> kvarn_geom:
+    return kvarn_geom(batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant)
 
 
 def _load():

@@ -53,9 +53,9 @@ def close_rowwise(got, ref, rel, axis=-1):
 class GpuCache:
     """One layer cache in device memory plus host copies for the oracle."""
 
-    def __init__(self, B, H, cap, G=32, n_it=3, seed_sigma=0):
-        self.g = K.geom(B, H, cap, G, n_it)
-        self.og = R.Geom(B, H, 128, cap, G, n_it, 2)
+    def __init__(self, B, H, cap, G=32, n_it=3, seed_sigma=0, variant=0):
+        self.g = K.geom(B, H, cap, G, n_it, variant=variant)
+        self.og = R.Geom(B, H, 128, cap, G, n_it, 2, variant)
         self.sigma = synth.sign_vector(seed_sigma, 128)
         self.buf = K.alloc_cache(self.g, self.sigma)
 
@@ -78,6 +78,7 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
     # header
     assert hc.buf[0:4].view(np.uint32)[0] == R.MAGIC
     assert hc.buf[8:36].view(np.int32).tolist() == list(og.as_tuple())
+    assert hc.buf[R.VARIANT_OFFSET:R.VARIANT_OFFSET + 4].view(np.uint32)[0] == og.variant
     assert np.array_equal(hc.sigma, gc.sigma.astype(np.float64))
     assert np.all(hc.lens == T), hc.lens
     nfull = T // G
@@ -86,7 +87,7 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
     for s, bits in enumerate((k_bits, v_bits)):
         for (b, h, tile) in tiles:
             x, _ = R.canonicalize(bits[b, tile * G:(tile + 1) * G, h])       # [G][D]
-            w_ref = R.rotate(x, gc.sigma)
+            w_ref = R.apply_rotation(x, gc.sigma, og.variant)
             if w is not None:
                 ok, worst = close_rowwise(w[s][b, tile * G:(tile + 1) * G, h], w_ref, 1e-5)
                 assert ok, ("W", s, b, h, tile, worst)
@@ -94,7 +95,7 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
             u = R.unpack_record(rec, G, 128, s)
             # layout: the oracle's packing of the GPU's own fields is the GPU record
             assert np.array_equal(R.pack_record(u["q"], u["r16"], u["c16"], u["s16"], u["z16"], s), rec)
-            t_ref = R.quantize_tile(w_ref, og.varn_iters)
+            t_ref = R.quantize_tile(w_ref, og.varn_iters, og.variant)
             dr = fp16_ulp_dist(u["r16"], t_ref["r16"])
             dc = fp16_ulp_dist(u["c16"], t_ref["c16"])
             assert dr.max() <= 1 and dc.max() <= 1, ("r/c ulp", s, b, h, tile, dr.max(), dc.max())

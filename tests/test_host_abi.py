@@ -39,6 +39,13 @@ def test_cache_bytes_match_oracle_layout(B, H, cap, G):
     assert K.kvarn_cache_bytes(K.geom(B, H, cap, G, 3)) == R.Geom(B, H, 128, cap, G, 3, 2).total
 
 
+def test_variants_accepted():
+    """Every combination of the three GPU variant bits is a valid geometry, same size."""
+    n0 = K.kvarn_cache_bytes(K.geom(2, 3, 256, 64, 2))
+    for var in range(8):
+        assert K.kvarn_cache_bytes(K.geom(2, 3, 256, 64, 2, variant=var)) == n0
+
+
 def test_workspace_bytes():
     g = K.geom(32, 10, 17408, 32, 3)
     n = K.kvarn_attn_workspace_bytes(g, 40)
@@ -62,9 +69,11 @@ def test_workspace_bytes():
     (dict(capacity=100), K.KVARN_ERR_GEOM),
     (dict(capacity=0), K.KVARN_ERR_GEOM),
     (dict(batch=0), K.KVARN_ERR_GEOM),
+    (dict(variant=8), K.KVARN_ERR_UNSUPPORTED),   # centered variance: oracle only
+    (dict(variant=-1), K.KVARN_ERR_UNSUPPORTED),
 ])
 def test_geometry_rejected(kw, status):
-    base = dict(batch=1, num_kv_heads=2, head_dim=128, capacity=128, group=32, varn_iters=3, bits=2)
+    base = dict(batch=1, num_kv_heads=2, head_dim=128, capacity=128, group=32, varn_iters=3, bits=2, variant=0)
     base.update(kw)
     g = K.kvarn_geom(*[base[n] for n, _ in K.kvarn_geom._fields_])
     with pytest.raises(K.KvarnError) as e:
