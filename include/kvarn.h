@@ -96,7 +96,8 @@ typedef struct {
  * stored but unused, and KVARN_Q_PREROTATED changes nothing). */
 enum { KVARN_VARIANT_NO_ROTATION = 1u,      /* H_D = I: "VarN only"                            */
        KVARN_VARIANT_NO_CHANNEL_PASS = 2u,  /* VarN keeps the token-axis passes only: c = 1     */
-       KVARN_VARIANT_NO_TOKEN_PASS = 4u     /* VarN keeps the channel-axis passes only: r = 1   */ };
+       KVARN_VARIANT_NO_TOKEN_PASS = 4u,    /* VarN keeps the channel-axis passes only: r = 1   */
+       KVARN_VARIANT_CENTERED = 8u          /* "variance" about the mean, not the mean square   */ };
 
 enum { KVARN_OUT_F32 = 0, KVARN_OUT_BF16 = 1 };            /* dequantize output dtype     */
 enum { KVARN_Q_PREROTATED = 1u };                          /* attention: q is already q H_D */

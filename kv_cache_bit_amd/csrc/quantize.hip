@@ -353,6 +353,80 @@ __device__ __forceinline__ void chan_reduce(const float (&v)[8], float (&own)[2]
   }
 }
 
+// VarN with the centered reading of "variance" (an ablation): explicit cumulative scales,
+// y = W / (r c), and per pass var = mean(y^2) - mean(y)^2 along the axis; a pass leaves
+// the scale unchanged where the variance is not positive. Needs W itself, so the
+// rotation is recomputed here (the ablation build only). r_own, c_own: the owner
+// lane's token and channel scales, in units of W.
+template <int NW, bool ABL>
+__device__ void centered_varn(const h8v (&av)[2][4], const Frags& hf, bool idr, bool tok, bool chp, int n_it,
+                              float inv_k, int lane, int sub, TileLds<NW>& sh, float& r_own, float (&c_own)[2]) {
+  constexpr int G = 32 * NW;
+  const int g = lane >> 4, c = lane & 15;
+  f4v w[2][8];
+  rotate_block_v<ABL>(idr, av, hf, w);
+  float ir[8], ic[8];  // 1/(k r) per lane token, 1/c per lane channel block
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    ir[k] = inv_k;
+    ic[k] = 1.0f;
+  }
+  r_own = 1.0f;
+  c_own[0] = c_own[1] = 1.0f;
+  for (int it = 0; it < n_it; ++it) {
+    if (tok) {
+      float s1[8], s2[8];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = 0.0f, b = 0.0f;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const float y = w[mb][nb][i] * ir[4 * mb + i] * ic[nb];
+            a += y;
+            b = fmaf(y, y, b);
+          }
+          s1[4 * mb + i] = a;
+          s2[4 * mb + i] = b;
+        }
+      const float m1 = row_rs8(s1, c) * (1.0f / kD), m2 = row_rs8(s2, c) * (1.0f / kD);
+      const float vr = m2 - m1 * m1;
+      if (vr > 0.0f) r_own *= __builtin_amdgcn_sqrtf(vr);
+      row_gather8(inv_k / r_own, ir, sh.grow[sub], g, c);
+    }
+    if (chp) {
+      float s1[8], s2[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        float a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = w[mb][nb][i] * ir[4 * mb + i] * ic[nb];
+            a += y;
+            b = fmaf(y, y, b);
+          }
+        s1[nb] = a;
+        s2[nb] = b;
+      }
+      float m1[2], m2[2];
+      chan_reduce<NW>(s1, m1, sh, g, c, sub, sh.red_a, OpAdd());
+      chan_reduce<NW>(s2, m2, sh, g, c, sub, sh.red_b, OpAdd());
+      float icn[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float mean = m1[q] * (1.0f / G);
+        const float vr = m2[q] * (1.0f / G) - mean * mean;
+        if (vr > 0.0f) c_own[q] *= __builtin_amdgcn_sqrtf(vr);
+        icn[q] = 1.0f / c_own[q];
+      }
+      col_gather8(icn, ic, sh.gcol[sub], g, c);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- codes
 // Writes the 2-bit codes of this wave's block into the record in LDS.
 // K: word w = c/2 of token t holds channel 16nb + c in slot 4(nb/2) + nb%2 + 2(c%2).
@@ -415,7 +489,8 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
 // ABL builds the ablation variants (var = KVARN_VARIANT_* bits, uniform): with the
 // identity rotation W' = W (k = 1 instead of sqrt(D)): v and u keep their form, only r
 // becomes sqrt(S'_t) / (k sqrt(D)) and the start value v = 1/k^2; a dropped pass keeps
-// its scale at 1 (the other pass then repeats the same sums every iteration).
+// its scale at 1 (the other pass then repeats the same sums every iteration). The
+// centered reading of "variance" runs its own loop (centered_varn).
 template <int NW, bool DBG, bool ABL>
 __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2][8][4], float st_own, int lane,
                             int sub, int stream, int n_it, int var, TileLds<NW>& sh, uint32_t& flags, float* dbg_w,
@@ -426,15 +501,17 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
   const bool idr = ABL && (var & KVARN_VARIANT_NO_ROTATION);
   const bool tok = !ABL || !(var & KVARN_VARIANT_NO_TOKEN_PASS);
   const bool chp = !ABL || !(var & KVARN_VARIANT_NO_CHANNEL_PASS);
+  const bool cen = ABL && (var & KVARN_VARIANT_CENTERED);
   const float inv_k = idr ? 1.0f : kInvSqrtD;   // 1/k
   const float r_k = idr ? kInvSqrtD : 1.0f / kD;  // 1/(k sqrt(D))
+  const int n_std = cen ? 0 : n_it;              // iterations of the mean-square loop
 
   float u[8], v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) u[k] = 1.0f;
   float v_own = idr ? 1.0f : 1.0f / kD, s_tok = st_own;
   float u_own[2] = {1.0f, 1.0f}, s_ch[2] = {0.0f, 0.0f};
-  for (int it = 0; it < n_it; ++it) {
+  for (int it = 0; it < n_std; ++it) {
     if (tok) {
       if (it > 0) {  // token pass (the first one arrives precomputed)
         float tp[8];
@@ -472,7 +549,14 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
   }
 
   // stored scales: fp16, clamped to [2^-14, 65504]
-  const float r_own = (n_it > 0 && tok && s_tok > 0.0f) ? __builtin_amdgcn_sqrtf(s_tok) * r_k : 1.0f;
+  float r_own = (n_std > 0 && tok && s_tok > 0.0f) ? __builtin_amdgcn_sqrtf(s_tok) * r_k : 1.0f;
+  float c_own[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    c_own[q] = (n_std > 0 && s_ch[q] > 0.0f) ? __builtin_amdgcn_sqrtf(s_ch[q] * (1.0f / G)) : 1.0f;
+  if constexpr (ABL) {
+    if (cen) centered_varn<NW, ABL>(av, hf, idr, tok, chp, n_it, inv_k, lane, sub, sh, r_own, c_own);
+  }
   const float rc = fminf(fmaxf(r_own, kScaleMin), kFp16Max);
   if (rc != r_own) flags |= KVARN_FLAG_SCALE_CLAMPED;
   const float r16_own = round_f16(rc);
@@ -481,7 +565,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
   float c16_own[2], ic_own[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const float cv = (n_it > 0 && s_ch[q] > 0.0f) ? __builtin_amdgcn_sqrtf(s_ch[q] * (1.0f / G)) : 1.0f;
+    const float cv = c_own[q];
     const float x = fminf(fmaxf(cv, kScaleMin), kFp16Max);
     if (x != cv) flags |= KVARN_FLAG_SCALE_CLAMPED;
     c16_own[q] = round_f16(x);

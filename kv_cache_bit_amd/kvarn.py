@@ -18,6 +18,7 @@ KVARN_OUT_F32, KVARN_OUT_BF16 = 0, 1
 KVARN_Q_PREROTATED = 1
 KVARN_FLAG_CAPACITY, KVARN_FLAG_SATURATED, KVARN_FLAG_SCALE_CLAMPED = 1, 2, 4
 KVARN_VARIANT_NO_ROTATION, KVARN_VARIANT_NO_CHANNEL_PASS, KVARN_VARIANT_NO_TOKEN_PASS = 1, 2, 4
+KVARN_VARIANT_CENTERED = 8
 
 EXPORTS = ("kvarn_format_version", "kvarn_cache_bytes", "kvarn_cache_init", "kvarn_quantize_prefill",
            "kvarn_append_decode", "kvarn_dequantize", "kvarn_attn_workspace_bytes", "kvarn_attn_decode",

@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 VARIANTS = [K.KVARN_VARIANT_NO_ROTATION, K.KVARN_VARIANT_NO_CHANNEL_PASS, K.KVARN_VARIANT_NO_TOKEN_PASS,
             K.KVARN_VARIANT_NO_ROTATION | K.KVARN_VARIANT_NO_CHANNEL_PASS,
             K.KVARN_VARIANT_NO_ROTATION | K.KVARN_VARIANT_NO_TOKEN_PASS,
-            K.KVARN_VARIANT_NO_CHANNEL_PASS | K.KVARN_VARIANT_NO_TOKEN_PASS]
+            K.KVARN_VARIANT_NO_CHANNEL_PASS | K.KVARN_VARIANT_NO_TOKEN_PASS,
+            K.KVARN_VARIANT_CENTERED, K.KVARN_VARIANT_CENTERED | K.KVARN_VARIANT_NO_ROTATION,
+            K.KVARN_VARIANT_CENTERED | K.KVARN_VARIANT_NO_CHANNEL_PASS]
 
 
 def say(*a):
@@ -37,7 +39,8 @@ def test_prefill_variant_parity(variant, G, n_it, T):
     say("stats", st)
 
 
-@pytest.mark.parametrize("variant", [K.KVARN_VARIANT_NO_ROTATION, K.KVARN_VARIANT_NO_TOKEN_PASS])
+@pytest.mark.parametrize("variant", [K.KVARN_VARIANT_NO_ROTATION, K.KVARN_VARIANT_NO_TOKEN_PASS,
+                                     K.KVARN_VARIANT_CENTERED])
 @pytest.mark.parametrize("G,n_it", [(32, 3), (64, 2)])
 def test_append_equals_prefill_variant(variant, G, n_it):
     T = 2 * G + 5

@@ -40,9 +40,9 @@ def test_cache_bytes_match_oracle_layout(B, H, cap, G):
 
 
 def test_variants_accepted():
-    """Every combination of the three GPU variant bits is a valid geometry, same size."""
+    """Every combination of the four variant bits is a valid geometry, same size."""
     n0 = K.kvarn_cache_bytes(K.geom(2, 3, 256, 64, 2))
-    for var in range(8):
+    for var in range(16):
         assert K.kvarn_cache_bytes(K.geom(2, 3, 256, 64, 2, variant=var)) == n0
 
 
@@ -69,7 +69,7 @@ def test_workspace_bytes():
     (dict(capacity=100), K.KVARN_ERR_GEOM),
     (dict(capacity=0), K.KVARN_ERR_GEOM),
     (dict(batch=0), K.KVARN_ERR_GEOM),
-    (dict(variant=8), K.KVARN_ERR_UNSUPPORTED),   # centered variance: oracle only
+    (dict(variant=16), K.KVARN_ERR_UNSUPPORTED),
     (dict(variant=-1), K.KVARN_ERR_UNSUPPORTED),
 ])
 def test_geometry_rejected(kw, status):
