@@ -140,9 +140,10 @@ KVARN_API kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, con
 KVARN_API kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_out, void* v_out,
                               int32_t max_tokens, int32_t out_dtype, void* stream);
 
-/* Workspace bytes kvarn_attn_decode needs for num_q_heads query heads. Host only.
- * The workspace holds one f32 partial (m, l, 2 pad, o[D]) per (batch, query head,
- * span); a span is 4 x tpw tiles, tpw in [2, 16] chosen from the geometry alone. */
+/* Workspace bytes kvarn_attn_decode and kvarn_append_attn_decode need for num_q_heads
+ * query heads. Host only. The workspace holds one f32 partial (m, l, 2 pad, o[D]) per
+ * (batch, query head, span), a span being 4 x tpw tiles with tpw in [2, 16] chosen from
+ * the geometry alone, followed by one i32 per (batch, kv head) (padded to 16 bytes). */
 KVARN_API kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes);
 
 /* Single-query decode attention over every cached token:
@@ -160,6 +161,20 @@ KVARN_API kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t n
 KVARN_API kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const void* q_bf16,
                                int32_t num_q_heads, float softmax_scale, uint32_t flags,
                                void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/* One decode step of a layer: append k, v (as kvarn_append_decode) and attend with q
+ * over the cache including the new token (as kvarn_attn_decode), in the two launches of
+ * the attention: the append runs inside the merge launch. Same arguments and layouts as
+ * those two calls. The result equals kvarn_append_decode followed by kvarn_attn_decode,
+ * except on a step whose token completes a group of G: the attention then reads that
+ * group as the fp16 values it is quantized from (the tile is written for later steps).
+ * A full sequence drops the token (KVARN_FLAG_CAPACITY) and attends without it.
+ * (ai-paper-analysis page, section 3.2: the group being filled is kept until complete;
+ * section 3.1: the query is rotated like the keys.) */
+KVARN_API kvarn_status kvarn_append_attn_decode(const kvarn_geom* g, void* cache, const void* k_bf16,
+                                      const void* v_bf16, const void* q_bf16, int32_t num_q_heads,
+                                      float softmax_scale, uint32_t flags, void* workspace,
+                                      size_t workspace_bytes, float* out, void* stream);
 
 /* Read the sticky flags into *flags_host. Synchronizes `stream`. */
 KVARN_API kvarn_status kvarn_cache_flags(const void* cache, void* stream, uint32_t* flags_host);

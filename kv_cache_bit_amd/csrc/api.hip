@@ -173,26 +173,35 @@ static void attn_split(const kvarn_geom* g, int grp, int* tpw, int* nspan) {
   *nspan = (int)((tiles + 4 * t - 1) / (4 * t));
 }
 
+// Workspace: the span partials [B][Hq][nspan][4 + D] f32, then len [B][Hkv] i32 as the
+// tile pass saw it.
+static size_t attn_partial_bytes(const kvarn_geom* g, int32_t num_q_heads) {
+  int tpw, nspan;
+  attn_split(g, num_q_heads / g->num_kv_heads, &tpw, &nspan);
+  return (size_t)g->batch * num_q_heads * nspan * (4 + kD) * sizeof(float);
+}
+
 kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes) {
   kvarn_status st = check_geom(g);
   if (st != KVARN_OK) return st;
   if (!bytes) return KVARN_ERR_NULL;
   if (num_q_heads <= 0 || num_q_heads % g->num_kv_heads != 0) return KVARN_ERR_GEOM;
   if (num_q_heads / g->num_kv_heads > 8) return KVARN_ERR_UNSUPPORTED;
-  int tpw, nspan;
-  attn_split(g, num_q_heads / g->num_kv_heads, &tpw, &nspan);
-  *bytes = (size_t)g->batch * num_q_heads * nspan * (4 + kD) * sizeof(float);
+  const size_t lens = ((size_t)g->batch * g->num_kv_heads * sizeof(int32_t) + 15) / 16 * 16;
+  *bytes = attn_partial_bytes(g, num_q_heads) + lens;
   return KVARN_OK;
 }
 
-kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const void* q_bf16, int32_t num_q_heads,
-                               float softmax_scale, uint32_t flags, void* workspace, size_t workspace_bytes,
-                               float* out, void* stream) {
+static kvarn_status attn_impl(const kvarn_geom* g, const void* cache, const void* q_bf16, int32_t num_q_heads,
+                              float softmax_scale, uint32_t flags, void* workspace, size_t workspace_bytes,
+                              float* out, void* cache_rw, const void* k_bf16, const void* v_bf16, void* stream) {
   size_t need = 0;
   kvarn_status st = kvarn_attn_workspace_bytes(g, num_q_heads, &need);
   if (st != KVARN_OK) return st;
   if (!cache || !q_bf16 || !workspace || !out) return KVARN_ERR_NULL;
   if (!aligned16(cache) || !aligned16(q_bf16) || !aligned16(workspace) || !aligned16(out)) return KVARN_ERR_ALIGN;
+  if (cache_rw && (!k_bf16 || !v_bf16)) return KVARN_ERR_NULL;
+  if (cache_rw && (!aligned16(k_bf16) || !aligned16(v_bf16))) return KVARN_ERR_ALIGN;
   if (workspace_bytes < need) return KVARN_ERR_RANGE;
   if ((flags & ~(uint32_t)KVARN_Q_PREROTATED) != 0) return KVARN_ERR_UNSUPPORTED;
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVARN_ERR_RANGE;
@@ -209,7 +218,26 @@ kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const voi
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)kD);
   a.flags = flags;
   a.idr = (g->variant & KVARN_VARIANT_NO_ROTATION) != 0;
+  a.lens_ws = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + attn_partial_bytes(g, num_q_heads));
+  a.cache_rw = static_cast<uint8_t*>(cache_rw);
+  a.kn = static_cast<const uint16_t*>(k_bf16);
+  a.vn = static_cast<const uint16_t*>(v_bf16);
   return dev(launch_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const void* q_bf16, int32_t num_q_heads,
+                               float softmax_scale, uint32_t flags, void* workspace, size_t workspace_bytes,
+                               float* out, void* stream) {
+  return attn_impl(g, cache, q_bf16, num_q_heads, softmax_scale, flags, workspace, workspace_bytes, out, nullptr,
+                   nullptr, nullptr, stream);
+}
+
+kvarn_status kvarn_append_attn_decode(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
+                                      const void* q_bf16, int32_t num_q_heads, float softmax_scale, uint32_t flags,
+                                      void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  if (!cache) return KVARN_ERR_NULL;
+  return attn_impl(g, cache, q_bf16, num_q_heads, softmax_scale, flags, workspace, workspace_bytes, out, cache, k_bf16,
+                   v_bf16, stream);
 }
 
 kvarn_status kvarn_cache_flags(const void* cache, void* stream, uint32_t* flags_host) {

@@ -28,8 +28,15 @@
 // query head and span goes to the workspace. The merge kernel combines the spans in
 // index order (log-sum-exp), adds the fp16 tail tokens (unrotated, scored in original
 // space), rotates the V part back by H_D^T and normalizes. Scores live in log2 units.
+//
+// Fused decode step (append + attention): the tile pass records each sequence's length
+// in the workspace; the merge launch then also runs the append jobs (tail write, group
+// quantization, len update) as extra work-groups. Its rows take the call's new token
+// from the input, read only tail slots below the recorded length, and never read len
+// or tile records, so they do not race with the append jobs of the same launch.
 #include "kvarn_common.h"
 #include "kvarn_launch.h"
+#include "quantize_dev.h"
 
 namespace kvarn {
 
@@ -168,6 +175,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   bid /= a.nqg;
   const int h = bid % L.Hkv, b = bid / L.Hkv;
   const int n = *reinterpret_cast<const int32_t*>(a.cache + L.len_off(b, h, 0));
+  if (span == 0 && qg == 0 && threadIdx.x == 0) a.lens_ws[b * L.Hkv + h] = n;  // for the merge
   const int nfull = n / G;
   const int t0 = span * 4 * a.tpw;
   if (t0 >= nfull) return;  // uniform over the work-group
@@ -476,16 +484,33 @@ __device__ __forceinline__ float row16_max(float v) {
   return fmaxf(v, xshfl<8>(v));
 }
 
+// FUSED: work-groups past the rows' ones run the append jobs (one (b, h, s) each, on
+// G/32 waves; the other waves exit).
+template <bool FUSED, int NW, bool ABL>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+  const long long nrows = (long long)a.L.B * a.Hq;
+  if constexpr (FUSED) {
+    const long long row_blocks = (nrows + 15) / 16;
+    if ((long long)blockIdx.x >= row_blocks) {
+      __shared__ TileLds<NW> sh;
+      const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      if (wave >= NW) return;
+      const AppendArgs ap{a.L, a.cache_rw, a.kn, a.vn};
+      append_job<NW, ABL>(ap, (int)(blockIdx.x - row_blocks), wave, threadIdx.x & 63, sh);
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63, rg = lane >> 4, cg = lane & 15;
   const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + rg;  // b * Hq + q head
-  const long long nrows = (long long)a.L.B * a.Hq;
   const bool live = row < nrows;
   const int rr = live ? (int)row : 0;
   const int b = rr / a.Hq, qhead = rr - b * a.Hq, h = qhead / a.grp;
   const int G = a.L.G;
-  const int n = *reinterpret_cast<const int32_t*>(a.cache + a.L.len_off(b, h, 0));
-  const int nfull = n / G, nt = n - nfull * G;
+  // a fused call reads the length the tile pass saw; its append jobs move len meanwhile
+  const int n = FUSED ? a.lens_ws[b * a.L.Hkv + h] : *reinterpret_cast<const int32_t*>(a.cache + a.L.len_off(b, h, 0));
+  const int nfull = n / G, nt_old = n - nfull * G;
+  // the call's own token (fused, unless the sequence is full) follows the tail
+  const int nt = nt_old + ((FUSED && n < a.L.cap) ? 1 : 0);
   const int nsp = (nfull + 4 * a.tpw - 1) / (4 * a.tpw);
   const float* w = a.ws + (long long)rr * a.nspan * kPart;
   // span maxima: lane cg looks at spans cg, cg + 16, ...
@@ -538,8 +563,17 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int t = min(t0 + k, nt - 1);
-        kw[k] = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
-        vw[k] = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
+        if (FUSED && t == nt_old) {  // the new token, canonicalized as the append stores it
+          const long long src = ((long long)b * a.L.Hkv + h) * kD + 8 * cg;
+          float xk[8], xv[8], amax = 0.0f;
+          canon8_bf16(*reinterpret_cast<const uint4*>(a.kn + src), xk, amax);
+          canon8_bf16(*reinterpret_cast<const uint4*>(a.vn + src), xv, amax);
+          kw[k] = pack8_f16(xk);
+          vw[k] = pack8_f16(xv);
+        } else {
+          kw[k] = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
+          vw[k] = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
+        }
       }
       float lt[4];
 #pragma unroll
@@ -592,7 +626,24 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const long long rows = (long long)a.L.B * a.Hq;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, a);
+  const long long row_blocks = (rows + 15) / 16;
+  if (!a.kn) {
+    hipLaunchKernelGGL((merge_kernel<false, 1, false>), dim3((unsigned)row_blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)(row_blocks + 2LL * a.L.B * a.L.Hkv));
+  const bool abl = a.L.variant != 0;
+  if (a.L.G == 32) {
+    if (abl)
+      hipLaunchKernelGGL((merge_kernel<true, 1, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<true, 1, false>), grid, dim3(256), 0, st, a);
+  } else {
+    if (abl)
+      hipLaunchKernelGGL((merge_kernel<true, 2, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<true, 2, false>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -56,6 +56,12 @@ struct AttnArgs {
   float scale;
   uint32_t flags;
   int idr;            // identity in place of H_D (KVARN_VARIANT_NO_ROTATION)
+  int32_t* lens_ws;   // [B][Hkv] len at the tile pass, for the merge of a fused call
+  // fused append + attention: the call's new token (bf16 [B][Hkv][D]) and the writable
+  // cache; kn == nullptr for a plain attention call
+  const uint16_t* kn;
+  const uint16_t* vn;
+  uint8_t* cache_rw;
 };
 
 hipError_t launch_init(const InitArgs& a, hipStream_t st);

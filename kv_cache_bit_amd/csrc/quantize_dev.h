@@ -1,0 +1,777 @@
+// KVarN write path on gfx950: prefill quantization and decode append.
+//
+// Method (KVarN pages, ai-paper-analysis page): rotate tokens by a randomized
+// Hadamard matrix along head_dim (section 3.1), then VarN -- token-axis and
+// channel-axis variance normalization repeated a few times, Sinkhorn-Knopp style,
+// with grouped scales undone at dequantization (section 3.2) -- then uniform 2-bit
+// quantization with four codes per byte.
+//
+// Work mapping. A tile (G tokens x 128 channels of one batch row, kv head and
+// stream) is handled by G/32 waves, one 32-token block each.
+//   * Rotation on the matrix cores: the canonical inputs are exact in fp16 and the
+//     Sylvester matrix is +-1, so W' = (x * sigma) H_syl is computed exactly by
+//     v_mfma_f32_16x16x32_f16 with fp32 accumulation (2 token blocks x 8 channel
+//     blocks x 4 K-steps). H_syl's 32x16 blocks are one of four register fragments
+//     (+-F, +-G), so the 32 KiB matrix never leaves registers.
+//   * The MFMA output leaves lane (g = lane/16, c = lane%16) with tokens 16mb + 4g + i
+//     (mb < 2, i < 4) and channels 16nb + c (nb < 8): a token-axis sum is 8 in-lane
+//     terms plus a DPP reduction over the 16 lanes of a row; a channel-axis sum is 8
+//     in-lane terms plus permlane16/32 swaps across the 4 rows (and an LDS exchange
+//     between the two waves of a G=64 tile).
+//   * The 2-bit codes are formed with the magic-number trick: after clamping to
+//     [0, 3] the value is added to 1.5 * 2^23, so fp32 round-half-to-even leaves the
+//     code in mantissa bits 0..1 (bits 2..21 zero); it is then shifted into its slot.
+// Reductions have a fixed order, so results are bit-identical run to run.
+//
+// This header holds the device code of the write path (rotation, VarN, grid, codes,
+// the tile core and the decode append job); quantize.hip instantiates the kernels, and
+// the attention merge launch reuses the append job for the fused decode step.
+#pragma once
+
+#include "kvarn_common.h"
+#include "kvarn_launch.h"
+
+namespace kvarn {
+
+struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpMin { __device__ float operator()(float a, float b) const { return vmin(a, b); } };
+struct OpMax { __device__ float operator()(float a, float b) const { return vmax(a, b); } };
+
+// Reduce-scatter of 8 per-token partials over the 16 lanes of a row. Stages pair
+// lane c with c^15, c^7, c^2, c^1 (row_mirror, row_half_mirror, quad perms); at each
+// stage a lane keeps half of its tokens (chosen by bits 3, 2, 1 of c) and adds the
+// partner's partial of the same tokens. Lane c ends with the row total of token
+// c/2 (identical in lanes c and c^1).
+__device__ __forceinline__ float row_rs8(const float (&v)[8], int c) {
+  const bool b3 = c & 8, b2 = c & 4, b1 = c & 2;
+  float a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float send = b3 ? v[k] : v[k + 4], keep = b3 ? v[k + 4] : v[k];
+    a[k] = keep + dppf<kMirror>(send);
+  }
+  float bb[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float send = b2 ? a[k] : a[k + 2], keep = b2 ? a[k + 2] : a[k];
+    bb[k] = keep + dppf<kHalfMirror>(send);
+  }
+  const float send = b1 ? bb[0] : bb[1], keep = b1 ? bb[1] : bb[0];
+  const float d = keep + dppf<kQx2>(send);
+  return d + dppf<kQx1>(d);
+}
+// Token tau's value from its owner lanes (2 tau, 2 tau + 1) to the whole row, through a
+// wave-private LDS slot (a wave's LDS operations complete in issue order).
+__device__ __forceinline__ void row_gather8(float own, float (&v)[8], float* buf, int g, int c) {
+  wave_sync();
+  if ((c & 1) == 0) buf[8 * g + (c >> 1)] = own;
+  wave_sync();
+  const float4 x = *reinterpret_cast<const float4*>(buf + 8 * g);
+  const float4 y = *reinterpret_cast<const float4*>(buf + 8 * g + 4);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+
+// Reduce-scatter of 8 per-channel partials (channel blocks nb) over the 4 rows:
+// permlane16_swap of two channel registers leaves rows 0+1 / 2+3 partials of one
+// channel in rows 0, 2 and of the other in rows 1, 3; permlane32_swap then combines
+// the halves. Row g ends with channel block g in out[0] and 4 + g in out[1].
+template <typename Op>
+__device__ __forceinline__ void col_rs8(const float (&v)[8], float (&out)[2], Op op) {
+  float y[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_int(v[2 * p]), __float_as_int(v[2 * p + 1]),
+                                                    false, false);
+    y[p] = op(__int_as_float(s[0]), __int_as_float(s[1]));
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(y[2 * q]), __float_as_int(y[2 * q + 1]),
+                                                    false, false);
+    out[q] = op(__int_as_float(s[0]), __int_as_float(s[1]));
+  }
+}
+// Inverse of col_rs8: row g holds channel blocks g and 4 + g; every row gets all 8,
+// through a wave-private LDS slot laid out [c][g][q].
+__device__ __forceinline__ void col_gather8(const float (&own)[2], float (&v)[8], float* buf, int g, int c) {
+  wave_sync();
+  *reinterpret_cast<float2*>(buf + 8 * c + 2 * g) = make_float2(own[0], own[1]);
+  wave_sync();
+  const float4 x = *reinterpret_cast<const float4*>(buf + 8 * c);      // (g0,q0) (g0,q1) (g1,q0) (g1,q1)
+  const float4 y = *reinterpret_cast<const float4*>(buf + 8 * c + 4);  // (g2,q0) (g2,q1) (g3,q0) (g3,q1)
+  v[0] = x.x; v[4] = x.y; v[1] = x.z; v[5] = x.w;
+  v[2] = y.x; v[6] = y.y; v[3] = y.z; v[7] = y.w;
+}
+
+// ----------------------------------------------------------------------------- Hadamard fragments
+// B operand of the 16x16x32 MFMA for K-step ks (channels 32ks..32ks+31) and channel
+// block nb: lane (g, c) holds H_syl[32ks + 8g + e][16nb + c], e < 8. With
+// popcount((32ks + 8g + e) & (16nb + c)) = pc(e & c%8) + (g%2)(c/8) + (g/2)(nb%2)
+// + pc(ks & nb/2), the fragment is F (nb even) or G = F * (-1)^(g/2) (nb odd), times
+// the uniform sign (-1)^pc(ks & nb/2).
+struct Frags {
+  h8v v[4];  // F, -F, G, -G
+};
+// The four fragments of every lane as fp16 bit patterns, computed at compile time:
+// word [lane][4 f + d] holds elements 2d, 2d+1 of fragment f.
+struct FragTable {
+  uint32_t w[64][16];
+};
+constexpr FragTable make_frag_table() {
+  FragTable t{};
+  for (int lane = 0; lane < 64; ++lane) {
+    const int g = lane >> 4, c = lane & 15;
+    for (int e = 0; e < 8; ++e) {
+      int pc = (g & 1) & (c >> 3);
+      for (int b = 0; b < 3; ++b) pc += (e >> b) & (c >> b) & 1;
+      const uint32_t f = (pc & 1) ? 0xBC00u : 0x3C00u;  // -1 / +1
+      const uint32_t gg = (g >> 1) ? f ^ 0x8000u : f;
+      const uint32_t vals[4] = {f, f ^ 0x8000u, gg, gg ^ 0x8000u};
+      for (int q = 0; q < 4; ++q) t.w[lane][4 * q + e / 2] |= vals[q] << (16 * (e & 1));
+    }
+  }
+  return t;
+}
+static __device__ const FragTable kFrags = make_frag_table();
+__device__ __forceinline__ Frags hadamard_frags(int lane) {
+  const uint4* p = reinterpret_cast<const uint4*>(kFrags.w[lane]);
+  Frags h;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) h.v[q] = __builtin_bit_cast(h8v, p[q]);
+  return h;
+}
+__device__ __forceinline__ int frag_index(int ks, int nb) {
+  return ((nb & 1) << 1) | (__builtin_popcount(ks & (nb >> 1)) & 1);
+}
+// Identity in place of H_syl (the "VarN only" ablation): block nb takes the single K-step
+// ks = nb/2, whose B fragment is one-hot: lane (g, c) holds 1 at e = c%8 iff
+// 8g + e = 16(nb%2) + c, i.e. g = 2(nb%2) + c/8. v[P] is the fragment for nb%2 = P.
+__device__ __forceinline__ Frags identity_frags(int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  Frags h;
+#pragma unroll
+  for (int P = 0; P < 2; ++P) {
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      w[d] = (g == 2 * P + (c >> 3) && d == ((c & 7) >> 1)) ? 0x3C00u << (16 * (c & 1)) : 0u;
+    h.v[P] = __builtin_bit_cast(h8v, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  h.v[2] = h.v[0];
+  h.v[3] = h.v[1];
+  return h;
+}
+
+// ----------------------------------------------------------------------------- inputs
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// Sign masks for the 8 channels of chunk `chunk` (channels 8 chunk .. +7): bit 31 of
+// lo[d] / hi[d] is set where sigma of channel 2d / 2d+1 is -1.
+struct SigMask {
+  uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ SigMask sigma_masks(const uint8_t* hdr, int chunk) {
+  const uint2 s = *reinterpret_cast<const uint2*>(hdr + kSigmaOff + 8 * chunk);
+  SigMask m;
+  m.lo[0] = (s.x & 0x80u) << 24;
+  m.hi[0] = (s.x & 0x8000u) << 16;
+  m.lo[1] = (s.x & 0x800000u) << 8;
+  m.hi[1] = s.x & 0x80000000u;
+  m.lo[2] = (s.y & 0x80u) << 24;
+  m.hi[2] = (s.y & 0x8000u) << 16;
+  m.lo[3] = (s.y & 0x800000u) << 8;
+  m.hi[3] = s.y & 0x80000000u;
+  return m;
+}
+
+// two fp32 -> packed fp16 pair, round half to even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, h2v));
+}
+
+// 8 bf16 -> 8 canonical fp16 (round half to even), times sigma: the sign flip rides on
+// the bf16 -> fp32 unpack ((w << 16) + bit31 flips bit 31; (w & hi16) ^ bit31 too).
+// Without clamping a value beyond fp16 becomes inf, which the caller detects and then
+// redoes with CLAMP.
+template <bool CLAMP>
+__device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    float lo = __int_as_float((int)((ws[d] << 16) + m.lo[d]));
+    float hi = __int_as_float((int)((ws[d] & 0xFFFF0000u) ^ m.hi[d]));
+    if constexpr (CLAMP) {
+      lo = __builtin_amdgcn_fmed3f(lo, -kFp16Max, kFp16Max);
+      hi = __builtin_amdgcn_fmed3f(hi, -kFp16Max, kFp16Max);
+    }
+    o[d] = pack_f16x2(lo, hi);
+  }
+  return __builtin_bit_cast(h8v, make_uint4(o[0], o[1], o[2], o[3]));
+}
+__device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp16 input
+  return __builtin_bit_cast(h8v, make_uint4(w.x ^ ((m.lo[0] >> 16) | m.hi[0]), w.y ^ ((m.lo[1] >> 16) | m.hi[1]),
+                                            w.z ^ ((m.lo[2] >> 16) | m.hi[2]), w.w ^ ((m.lo[3] >> 16) | m.hi[3])));
+}
+
+// W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]; with ID the
+// identity fragments make W' = A (one MFMA per block).
+//
+// An MFMA whose destination shares registers with its A or B source reads clobbered
+// rows on this hardware. After each accumulation chain an empty asm takes the chain's
+// result as read-write and all its A and B fragments as inputs: the data dependency
+// pins it after the chain's MFMAs, so every source is still live when each of them
+// issues and the register allocator cannot hand a source's registers to the result.
+template <bool ID>
+__device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& hf, f4v (&acc)[2][8]) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (ID) {
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+      }
+      asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
+                   "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
+      acc[mb][nb] = s;
+    }
+  }
+}
+
+// Rotation fused with the squares and the first token-axis sums (u = 1): each chain's
+// W' block is squared as soon as it is complete, so the fp32 block is never held whole.
+// Returns the row total of the lane's own token (see row_rs8).
+template <bool ID>
+__device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, float (&p)[2][8][4],
+                                                int c) {
+  float tp[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) tp[k] = 0.0f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (ID) {
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+      }
+      asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
+                   "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[mb][nb][i] = s[i] * s[i];
+        tp[4 * mb + i] += p[mb][nb][i];
+      }
+    }
+  }
+  return row_rs8(tp, c);
+}
+
+// Dispatch for the ablation build (ABL): the identity rotation is a runtime choice there;
+// the standard build compiles the Hadamard path only.
+template <bool ABL>
+__device__ __forceinline__ float rotate_squares_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
+                                                  float (&p)[2][8][4], int c) {
+  if constexpr (ABL) {
+    if (idr) return rotate_squares<true>(a, hf, p, c);
+  }
+  return rotate_squares<false>(a, hf, p, c);
+}
+template <bool ABL>
+__device__ __forceinline__ void rotate_block_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
+                                               f4v (&acc)[2][8]) {
+  if constexpr (ABL) {
+    if (idr) {
+      rotate_block<true>(a, hf, acc);
+      return;
+    }
+  }
+  rotate_block<false>(a, hf, acc);
+}
+template <bool ABL>
+__device__ __forceinline__ SigMask masks_v(bool idr, const uint8_t* hdr, int chunk) {
+  if constexpr (ABL) {
+    if (idr) return SigMask{};  // no sign flips without the rotation
+  }
+  return sigma_masks(hdr, chunk);
+}
+template <bool ABL>
+__device__ __forceinline__ Frags frags_v(bool idr, int lane) {
+  if constexpr (ABL) {
+    if (idr) return identity_frags(lane);
+  }
+  return hadamard_frags(lane);
+}
+
+// ----------------------------------------------------------------------------- LDS
+// A one-wave tile only needs its own LDS writes ordered before its reads (a wave's LDS
+// operations complete in order); a two-wave tile needs the work-group barrier.
+template <int NW>
+__device__ __forceinline__ void tile_sync() {
+  if constexpr (NW == 1) {
+    wave_sync();
+  } else {
+    __syncthreads();
+  }
+}
+
+template <int NW>
+struct TileLds {
+  static constexpr int G = 32 * NW;
+  static constexpr int TR = G * kD / 4 + 2 * G + 6 * kD;
+  uint8_t rec[TR] __attribute__((aligned(16)));
+  float red_a[NW][kD];
+  float red_b[NW][kD];
+  float gcol[NW][kD] __attribute__((aligned(16)));  // per-wave gather buffers
+  float grow[NW][32] __attribute__((aligned(16)));
+};
+
+// Per-channel reduction of a tile: 4-row reduce-scatter inside the wave, then (G=64)
+// the partials of the NW waves through LDS in wave order. own[q] is channel
+// 16 (4q + g) + c. The trailing barrier lets the next call reuse the LDS slots.
+template <int NW, typename Op>
+__device__ __forceinline__ void chan_reduce(const float (&v)[8], float (&own)[2], TileLds<NW>& sh, int g,
+                                            int c, int sub, float (*red)[kD], Op op) {
+  col_rs8(v, own, op);
+  if constexpr (NW > 1) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) red[sub][16 * (4 * q + g) + c] = own[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float t = red[0][16 * (4 * q + g) + c];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) t = op(t, red[w][16 * (4 * q + g) + c]);
+      own[q] = t;
+    }
+    __syncthreads();
+  }
+}
+
+// VarN with the centered reading of "variance" (an ablation): explicit cumulative scales,
+// y = W / (r c), and per pass var = mean(y^2) - mean(y)^2 along the axis; a pass leaves
+// the scale unchanged where the variance is not positive. Needs W itself, so the
+// rotation is recomputed here (the ablation build only). r_own, c_own: the owner
+// lane's token and channel scales, in units of W.
+template <int NW, bool ABL>
+__device__ void centered_varn(const h8v (&av)[2][4], const Frags& hf, bool idr, bool tok, bool chp, int n_it,
+                              float inv_k, int lane, int sub, TileLds<NW>& sh, float& r_own, float (&c_own)[2]) {
+  constexpr int G = 32 * NW;
+  const int g = lane >> 4, c = lane & 15;
+  f4v w[2][8];
+  rotate_block_v<ABL>(idr, av, hf, w);
+  float ir[8], ic[8];  // 1/(k r) per lane token, 1/c per lane channel block
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    ir[k] = inv_k;
+    ic[k] = 1.0f;
+  }
+  r_own = 1.0f;
+  c_own[0] = c_own[1] = 1.0f;
+  for (int it = 0; it < n_it; ++it) {
+    if (tok) {
+      float s1[8], s2[8];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = 0.0f, b = 0.0f;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const float y = w[mb][nb][i] * ir[4 * mb + i] * ic[nb];
+            a += y;
+            b = fmaf(y, y, b);
+          }
+          s1[4 * mb + i] = a;
+          s2[4 * mb + i] = b;
+        }
+      const float m1 = row_rs8(s1, c) * (1.0f / kD), m2 = row_rs8(s2, c) * (1.0f / kD);
+      const float vr = m2 - m1 * m1;
+      if (vr > 0.0f) r_own *= __builtin_amdgcn_sqrtf(vr);
+      row_gather8(inv_k / r_own, ir, sh.grow[sub], g, c);
+    }
+    if (chp) {
+      float s1[8], s2[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        float a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = w[mb][nb][i] * ir[4 * mb + i] * ic[nb];
+            a += y;
+            b = fmaf(y, y, b);
+          }
+        s1[nb] = a;
+        s2[nb] = b;
+      }
+      float m1[2], m2[2];
+      chan_reduce<NW>(s1, m1, sh, g, c, sub, sh.red_a, OpAdd());
+      chan_reduce<NW>(s2, m2, sh, g, c, sub, sh.red_b, OpAdd());
+      float icn[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float mean = m1[q] * (1.0f / G);
+        const float vr = m2[q] * (1.0f / G) - mean * mean;
+        if (vr > 0.0f) c_own[q] *= __builtin_amdgcn_sqrtf(vr);
+        icn[q] = 1.0f / c_own[q];
+      }
+      col_gather8(icn, ic, sh.gcol[sub], g, c);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- codes
+// Writes the 2-bit codes of this wave's block into the record in LDS.
+// K: word w = c/2 of token t holds channel 16nb + c in slot 4(nb/2) + nb%2 + 2(c%2).
+// V: byte j*G/4 + t/4 holds tokens 4(t/4) .. +3 of channel j, token t%4 in slot t%4.
+template <int NW, bool CLAMP>
+__device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (&al)[8], const float (&ga)[8],
+                                           int stream, int sub, int g, int c, TileLds<NW>& sh) {
+  constexpr int G = 32 * NW;
+  const int ttile0 = sub * 32 + 4 * g;  // token of (mb = 0, i = 0) inside the tile
+  auto code = [&](float y, int nb) -> uint32_t {
+    float t = fmaf(y, al[nb], ga[nb]);
+    if constexpr (CLAMP) t = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f);
+    return (uint32_t)__float_as_int(t + 12582912.0f);  // 1.5 * 2^23
+  };
+  if (stream == 0) {
+    // lane c's channel 16nb + c goes to word c/2, slot 4(nb/2) + nb%2 + 2(c%2): the even
+    // lane assembles bits 8(nb/2) + 2(nb%2) (blocks 0..3 in bytes 0..1, 4..7 in bytes
+    // 2..3, one byte permute), the odd lane's pattern lands 4 bits higher.
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          lo |= code(acc[mb][nb][i], nb) << (8 * (nb >> 1) + 2 * (nb & 1));
+          hi |= code(acc[mb][nb + 4][i], nb + 4) << (8 * (nb >> 1) + 2 * (nb & 1));
+        }
+        const uint32_t h = __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // bytes lo.0 lo.1 hi.0 hi.1
+        const uint32_t hp = (uint32_t)__builtin_amdgcn_mov_dpp((int)h, kQx1, 0xF, 0xF, true);
+        if ((c & 1) == 0)
+          *reinterpret_cast<uint32_t*>(sh.rec + (ttile0 + 16 * mb + i) * 32 + 2 * c) = h | (hp << 4);
+      }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        uint32_t h = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h |= code(acc[mb][nb][i], nb) << (2 * i);
+        sh.rec[(16 * nb + c) * (G / 4) + (ttile0 + 16 * mb) / 4] = (uint8_t)h;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------- the tile core
+// From the rotated block W' = sqrt(D) W (acc), its squares p and the first token-axis
+// sum of the lane's own token (u = 1): VarN, stored scales, grid, codes; the record
+// is assembled in sh.rec. Steps follow the ai-paper-analysis page, section 3.2.
+//
+// VarN with cumulative scales (the mean square of W/(r c) along the axis becomes 1):
+//   token pass   S'_t = sum_j W'_tj^2 / c_j^2,   r_t = sqrt(S'_t) / D,  v_t = D / S'_t
+//   channel pass S'_j = sum_t W'_tj^2 v_t,       c_j = sqrt(S'_j / G),  u_j = G / S'_j
+// (with W' = sqrt(D) W these are the oracle's r_t <- r_t sqrt(ms_t), c_j <- c_j sqrt(ms_j));
+// an all-zero line keeps its scale. Each lane owns one token (c/2 of its row's 8) and
+// two channels (16g + c, 64 + 16g + c): their scalars are computed once, by the owner,
+// and broadcast back.
+//
+// ABL builds the ablation variants (var = KVARN_VARIANT_* bits, uniform): with the
+// identity rotation W' = W (k = 1 instead of sqrt(D)): v and u keep their form, only r
+// becomes sqrt(S'_t) / (k sqrt(D)) and the start value v = 1/k^2; a dropped pass keeps
+// its scale at 1 (the other pass then repeats the same sums every iteration). The
+// centered reading of "variance" runs its own loop (centered_varn).
+template <int NW, bool DBG, bool ABL>
+__device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2][8][4], float st_own, int lane,
+                            int sub, int stream, int n_it, int var, TileLds<NW>& sh, uint32_t& flags, float* dbg_w,
+                            float* dbg_y, long long dstride) {
+  constexpr int G = 32 * NW;
+  const int g = lane >> 4, c = lane & 15;
+  const int tau_own = c >> 1;  // own token: mb = tau/4, i = tau%4
+  const bool idr = ABL && (var & KVARN_VARIANT_NO_ROTATION);
+  const bool tok = !ABL || !(var & KVARN_VARIANT_NO_TOKEN_PASS);
+  const bool chp = !ABL || !(var & KVARN_VARIANT_NO_CHANNEL_PASS);
+  const bool cen = ABL && (var & KVARN_VARIANT_CENTERED);
+  const float inv_k = idr ? 1.0f : kInvSqrtD;   // 1/k
+  const float r_k = idr ? kInvSqrtD : 1.0f / kD;  // 1/(k sqrt(D))
+  const int n_std = cen ? 0 : n_it;              // iterations of the mean-square loop
+
+  float u[8], v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) u[k] = 1.0f;
+  float v_own = idr ? 1.0f : 1.0f / kD, s_tok = st_own;
+  float u_own[2] = {1.0f, 1.0f}, s_ch[2] = {0.0f, 0.0f};
+  for (int it = 0; it < n_std; ++it) {
+    if (tok) {
+      if (it > 0) {  // token pass (the first one arrives precomputed)
+        float tp[8];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float t = 0.0f;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) t = fmaf(p[mb][nb][i], u[nb], t);
+            tp[4 * mb + i] = t;
+          }
+        s_tok = row_rs8(tp, c);
+      }
+      if (s_tok > 0.0f) v_own = (float)kD * __builtin_amdgcn_rcpf(s_tok);
+    }
+    if (chp) {
+      row_gather8(v_own, v, sh.grow[sub], g, c);
+      float cp[8];  // channel pass
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        float t = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t = fmaf(p[mb][nb][i], v[4 * mb + i], t);
+        cp[nb] = t;
+      }
+      chan_reduce<NW>(cp, s_ch, sh, g, c, sub, sh.red_a, OpAdd());
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (s_ch[q] > 0.0f) u_own[q] = (float)G * __builtin_amdgcn_rcpf(s_ch[q]);
+      col_gather8(u_own, u, sh.gcol[sub], g, c);
+    }
+  }
+
+  // stored scales: fp16, clamped to [2^-14, 65504]
+  float r_own = (n_std > 0 && tok && s_tok > 0.0f) ? __builtin_amdgcn_sqrtf(s_tok) * r_k : 1.0f;
+  float c_own[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    c_own[q] = (n_std > 0 && s_ch[q] > 0.0f) ? __builtin_amdgcn_sqrtf(s_ch[q] * (1.0f / G)) : 1.0f;
+  if constexpr (ABL) {
+    if (cen) centered_varn<NW, ABL>(av, hf, idr, tok, chp, n_it, inv_k, lane, sub, sh, r_own, c_own);
+  }
+  const float rc = fminf(fmaxf(r_own, kScaleMin), kFp16Max);
+  if (rc != r_own) flags |= KVARN_FLAG_SCALE_CLAMPED;
+  const float r16_own = round_f16(rc);
+  float at[8];  // Y = W' / (k r16 c16): per-token factor 1 / (k r16)
+  row_gather8(inv_k * __builtin_amdgcn_rcpf(r16_own), at, sh.grow[sub], g, c);
+  float c16_own[2], ic_own[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float cv = c_own[q];
+    const float x = fminf(fmaxf(cv, kScaleMin), kFp16Max);
+    if (x != cv) flags |= KVARN_FLAG_SCALE_CLAMPED;
+    c16_own[q] = round_f16(x);
+    ic_own[q] = __builtin_amdgcn_rcpf(c16_own[q]);
+  }
+  // W' again, from the kept fp16 inputs: the matrix cores redo the exact rotation so the
+  // 64 fp32 values need not stay in registers through VarN (the asm ties the inputs to
+  // the last VarN sums, so the recomputation is not hoisted back into VarN)
+  h8v av2[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      av2[mb][ks] = av[mb][ks];
+      asm volatile("" : "+v"(av2[mb][ks]) : "v"(s_tok), "v"(s_ch[0]), "v"(s_ch[1]));
+    }
+  f4v acc[2][8];
+  rotate_block_v<ABL>(idr, av2, hf, acc);
+  if constexpr (DBG) {
+    float ic[8];
+    col_gather8(ic_own, ic, sh.gcol[sub], g, c);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const long long off = (16 * mb + 4 * g + i) * dstride + 16 * nb + c;
+          if (dbg_w) dbg_w[off] = acc[mb][nb][i] * inv_k;
+          if (dbg_y) dbg_y[off] = (acc[mb][nb][i] * at[4 * mb + i]) * ic[nb];
+        }
+  }
+  // Y' = W' / (k r16) = Y c16 (the positive c16 is applied to the channel's min/max)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mb][nb][i] *= at[4 * mb + i];
+
+  // per-channel asymmetric min/max 2-bit grid over the tile's G tokens
+  float mnl[8], mxl[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    float lo = acc[0][nb][0], hi = acc[0][nb][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo = fminf(lo, acc[mb][nb][i]);
+        hi = fmaxf(hi, acc[mb][nb][i]);
+      }
+    mnl[nb] = lo;
+    mxl[nb] = hi;
+  }
+  float mn_own[2], mx_own[2];
+  chan_reduce<NW>(mnl, mn_own, sh, g, c, sub, sh.red_a, OpMin());
+  chan_reduce<NW>(mxl, mx_own, sh, g, c, sub, sh.red_b, OpMax());
+  float s16_own[2], z16_own[2], al_own[2], ga_own[2];
+  bool need_clamp_own = false;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float lo = mn_own[q] * ic_own[q], hi = mx_own[q] * ic_own[q];
+    const float sr = (hi - lo) * (1.0f / 3.0f);
+    const float sc = fminf(sr, kFp16Max);
+    const float zc = fminf(fmaxf(lo, -kFp16Max), kFp16Max);
+    if (sc != sr || zc != lo) {
+      flags |= KVARN_FLAG_SCALE_CLAMPED;
+      need_clamp_own = true;
+    }
+    const float big = fmaxf(fabsf(lo), fabsf(hi));
+    if (sc != 0.0f && (!(sc >= kScaleMin) || !(big <= 200.0f * sc))) need_clamp_own = true;
+    s16_own[q] = round_f16(sc);
+    z16_own[q] = round_f16(zc);
+    const float is = s16_own[q] > 0.0f ? __builtin_amdgcn_rcpf(s16_own[q]) : 0.0f;
+    al_own[q] = ic_own[q] * is;  // u = (Y - z)/s = Y' (ic/s) - z/s
+    ga_own[q] = -z16_own[q] * is;
+  }
+  float al[8], ga[8];
+  col_gather8(al_own, al, sh.gcol[sub], g, c);
+  col_gather8(ga_own, ga, sh.gcol[sub], g, c);
+
+  // codes, q = clamp(rne(u), 0, 3): 1.5 * 2^23 + u rounds half to even with q left in
+  // bits 0..1 and zeros in bits 2..21; shifted into its 2-bit slot, the junk above bit 21
+  // falls outside the bytes kept (permute) / the byte stored. The clamp is needed only where u can
+  // leave (-0.5, 3.5): with normal s16 and max(|Y|) <= 200 s16 the fp16 rounding of z
+  // and s moves u by less than 0.1, so a wave whose channels all satisfy that skips it.
+  const bool need_clamp = __any(need_clamp_own);
+  if (need_clamp)
+    emit_codes<NW, true>(acc, al, ga, stream, sub, g, c, sh);
+  else
+    emit_codes<NW, false>(acc, al, ga, stream, sub, g, c, sh);
+  const int ttile0 = sub * 32 + 4 * g;
+  constexpr int RO = G * kD / 4, CO = RO + 2 * G, SO = CO + 2 * kD, ZO = SO + 2 * kD;
+  if ((c & 1) == 0) {
+    const int t = ttile0 + 16 * (tau_own >> 2) + (tau_own & 3);
+    *reinterpret_cast<uint16_t*>(sh.rec + RO + 2 * t) = (uint16_t)f16bits(r16_own);
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = 16 * (4 * q + g) + c;
+      *reinterpret_cast<uint16_t*>(sh.rec + CO + 2 * j) = (uint16_t)f16bits(c16_own[q]);
+      *reinterpret_cast<uint16_t*>(sh.rec + SO + 2 * j) = (uint16_t)f16bits(s16_own[q]);
+      *reinterpret_cast<uint16_t*>(sh.rec + ZO + 2 * j) = (uint16_t)f16bits(z16_own[q]);
+    }
+  }
+  tile_sync<NW>();
+}
+
+template <int NW>
+__device__ __forceinline__ void copy_record(const TileLds<NW>& sh, uint8_t* dst, int lane, int sub) {
+  constexpr int N16 = TileLds<NW>::TR / 16;
+  const uint4* s = reinterpret_cast<const uint4*>(sh.rec);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  for (int k = sub * 64 + lane; k < N16; k += 64 * NW) d[k] = s[k];
+}
+
+__device__ __forceinline__ void raise_flags(uint8_t* hdr, uint32_t f) {
+  if (f) atomicOr(reinterpret_cast<uint32_t*>(hdr + kFlagsOff), f);
+}
+
+__device__ __forceinline__ uint4 pack8_f16(const float (&x)[8]) {
+  uint4 o;
+  o.x = pack_f16x2(x[0], x[1]);
+  o.y = pack_f16x2(x[2], x[3]);
+  o.z = pack_f16x2(x[4], x[5]);
+  o.w = pack_f16x2(x[6], x[7]);
+  return o;
+}
+// bf16 x 8 -> canonical fp16 values (saturating), largest magnitude into amax
+__device__ __forceinline__ void canon8_bf16(const uint4 w, float (&x)[8], float& amax) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = bf16lo(ws[k]), hi = bf16hi(ws[k]);
+    amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+    x[2 * k] = round_f16(fminf(fmaxf(lo, -kFp16Max), kFp16Max));
+    x[2 * k + 1] = round_f16(fminf(fmaxf(hi, -kFp16Max), kFp16Max));
+  }
+}
+__device__ __forceinline__ uint32_t sat_flag(float amax) {
+  return amax > kFp16Max ? (uint32_t)KVARN_FLAG_SATURATED : 0u;
+}
+
+// ----------------------------------------------------------------------------- append
+// Decode append of one (b, h, s) = job (s fastest, then h) by the G/32 waves
+// sub = 0 .. NW-1 of a work-group; any further waves of the work-group must have exited
+// (the barriers then wait on these waves only). The token goes to tail slot len mod G;
+// when it completes a group, the group is quantized into the next tile record.
+template <int NW, bool ABL>
+__device__ void append_job(const AppendArgs& a, int job, int sub, int lane, TileLds<NW>& sh) {
+  constexpr int G = 32 * NW;
+  const int g = lane >> 4, c = lane & 15;
+  const Layout& L = a.L;
+  uint8_t* hdr = a.cache;
+  const int s = job % 2, h = (job / 2) % L.Hkv, b = job / 2 / L.Hkv;
+  int32_t* lenp = reinterpret_cast<int32_t*>(a.cache + L.len_off(b, h, s));
+  const int pos = *lenp;
+  if (pos >= L.cap) {
+    if (sub == 0 && lane == 0) raise_flags(hdr, KVARN_FLAG_CAPACITY);
+    return;
+  }
+  uint32_t flags = 0;
+  const uint16_t* src = (s ? a.v : a.k) + ((long long)b * L.Hkv + h) * kD;
+  if (sub == 0 && g == 0) {  // the new token into the fp16 tail (16 lanes x 8 channels)
+    float xin[8], amax = 0.0f;
+    canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * c), xin, amax);
+    flags |= sat_flag(amax);
+    *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, pos % G) + 16 * c) = pack8_f16(xin);
+  }
+  if ((pos + 1) % G == 0) {
+    const bool idr = ABL && (L.variant & KVARN_VARIANT_NO_ROTATION);
+    const Frags hf = frags_v<ABL>(idr, lane);
+    h8v av[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int t = sub * 32 + 16 * mb + c;  // token of this A row inside the tile
+        uint4 w;
+        if (t == G - 1) {  // the token just written: take it from the input, not from memory
+          float x[8], amax = 0.0f;
+          canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * (4 * ks + g)), x, amax);
+          w = pack8_f16(x);
+        } else {
+          w = *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, t) + 16 * (4 * ks + g));
+        }
+        av[mb][ks] = sign_a(w, m);
+      }
+    }
+    float p[2][8][4];
+    const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
+    tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, nullptr, nullptr, 0);
+    copy_record<NW>(sh, a.cache + L.record(b, h, (pos + 1) / G - 1, s), lane, sub);
+  }
+  raise_flags(hdr, flags);
+  __syncthreads();  // every wave has read len before it moves
+  if (sub == 0 && lane == 0) *lenp = pos + 1;
+}
+
+}  // namespace kvarn

@@ -535,6 +535,42 @@ def attn_decode(cache: Cache, q_bits, num_q_heads: int, softmax_scale: float = 0
     return out
 
 
+def append_attn_decode(cache: Cache, k_bits, v_bits, q_bits, num_q_heads: int, softmax_scale: float = 0.0,
+                       flags: int = 0) -> np.ndarray:
+    """One decode step: attend with q over the stored tokens plus the new one, then append it.
+    The stored tokens are read as in attn_decode (tiles dequantized, the tail as fp16);
+    the new token is its canonical fp16 value, which is also what a group completed by
+    this token holds before it is quantized ([AP] 3.2: the group being filled is kept
+    until it is complete). A full sequence attends without the token, which the append
+    then drops."""
+    g = cache.g
+    d = g.head_dim
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
+    q = bf16_to_f64(q_bits)
+    if flags & Q_PREROTATED:
+        q = undo_rotation(q, cache.sigma, g.variant)
+    kn, _ = canonicalize(k_bits)                                # [B][Hkv][D]
+    vn, _ = canonicalize(v_bits)
+    grp = num_q_heads // g.num_kv_heads
+    out = np.zeros((g.batch, num_q_heads, d))
+    for b in range(g.batch):
+        for h in range(g.num_kv_heads):
+            k = stream_values(cache, b, h, 0)
+            v = stream_values(cache, b, h, 1)
+            if int(cache.lens[b, h, 0]) < g.capacity:
+                k = np.vstack([k, kn[b, h][None]])
+                v = np.vstack([v, vn[b, h][None]])
+            if k.shape[0] == 0:
+                continue
+            for gi in range(h * grp, (h + 1) * grp):
+                logits = scale * (k @ q[b, gi])
+                p = np.exp(logits - logits.max())
+                p /= p.sum()
+                out[b, gi] = p @ v
+    append_decode(cache, k_bits, v_bits)
+    return out
+
+
 # ----------------------------------------------------------------------------- diagnostics ([AP] section 2)
 def error_split(x, xhat) -> tuple[np.ndarray, np.ndarray]:
     """Magnitude and direction parts of eps = xhat - x ([AP] section 2, error equation):

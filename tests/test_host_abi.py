@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(K.lib, n), n
     assert sorted(K.EXPORTS) == names
@@ -50,8 +50,8 @@ def test_workspace_bytes():
     g = K.geom(32, 10, 17408, 32, 3)
     n = K.kvarn_attn_workspace_bytes(g, 40)
     # one partial (m, l, 2 pad, o[128]) per (b, q head, span); at this geometry a span is
-    # 4 waves x 16 tiles, so 544 tiles give 9 spans
-    assert n == 32 * 40 * 9 * (4 + 128) * 4
+    # 4 waves x 16 tiles, so 544 tiles give 9 spans; then len per (b, kv head), 16-B padded
+    assert n == 32 * 40 * 9 * (4 + 128) * 4 + 32 * 10 * 4
     with pytest.raises(K.KvarnError) as e:
         K.kvarn_attn_workspace_bytes(g, 41)
     assert e.value.status == K.KVARN_ERR_GEOM
@@ -116,6 +116,12 @@ def test_argument_errors_return_before_any_launch():
     assert _code(K.kvarn_attn_decode, g, A, A2, 4, 0.0, 8, A, ws, A2, 0) == K.KVARN_ERR_UNSUPPORTED
     assert _code(K.kvarn_attn_decode, g, A, A2, 4, float("nan"), 0, A, ws, A2, 0) == K.KVARN_ERR_RANGE
     assert _code(K.kvarn_attn_decode, g, A, 0, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_NULL
+    # fused decode step: the attention's checks plus the appended token's pointers
+    assert _code(K.kvarn_append_attn_decode, g, A, A2, A2, A2, 4, 0.0, 0, A, ws - 1, A2, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_append_attn_decode, g, A, 0, A2, A2, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_append_attn_decode, g, A, A2, MIS, A2, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_append_attn_decode, g, 0, A2, A2, A2, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_append_attn_decode, g, A, A2, A2, A2, 4, 0.0, 2, A, ws, A2, 0) == K.KVARN_ERR_UNSUPPORTED
     assert _code(K.kvarn_cache_flags, 0, 0) == K.KVARN_ERR_NULL
     bad = K.geom(1, 2, 100, 32, 3)
     assert _code(K.kvarn_quantize_prefill, bad, A, A, A2, 10, 0) == K.KVARN_ERR_GEOM

@@ -174,3 +174,63 @@ def test_quality_guard_varn_beats_hadamard_only():
         errs[n_it] = np.mean(e)
     assert errs[3] < 0.2
     assert errs[3] < 0.1 * errs[0]
+
+
+def _fresh(T, G=32, cap=96, B=2, H=2, seed=31):
+    k, v = synth.kv_host(seed, B, T + 1, H)
+    c = R.Cache(R.Geom(B, H, 128, cap, G, 3, 2), synth.sign_vector(4))
+    R.quantize_prefill(c, k, v, T)
+    return c, k, v
+
+
+@pytest.mark.parametrize("T", [40, 0, 17])
+def test_append_attn_step_equals_append_then_attend(T):
+    """A step whose token does not complete a group: the fused step is the append
+    followed by the attention, on the same bytes."""
+    a, k, v = _fresh(T)
+    b, _, _ = _fresh(T)
+    q = synth.q_host(5, 2, 4)
+    fused = R.append_attn_decode(a, k[:, T], v[:, T], q, 4)
+    R.append_decode(b, k[:, T], v[:, T])
+    assert np.array_equal(fused, R.attn_decode(b, q, 4))
+    assert np.array_equal(a.buf, b.buf)
+
+
+def test_append_attn_step_completing_a_group_reads_fp16():
+    """A step whose token completes a group (T = 63, G = 32): the attention reads tile 0
+    from its record and the 32 tokens of the completed group as fp16 (the 31 tail tokens,
+    then the new token); afterwards the cache equals the plain append's, and attending
+    again reads the group quantized, which differs."""
+    T = 63
+    a, k, v = _fresh(T)
+    before, _, _ = _fresh(T)
+    b, _, _ = _fresh(T)
+    q = synth.q_host(6, 2, 4)
+    fused = R.append_attn_decode(a, k[:, T], v[:, T], q, 4)
+    qq = R.bf16_to_f64(q)
+    for bb in range(2):
+        for h in range(2):
+            kv = []
+            for s, bits in ((0, k), (1, v)):
+                rec = R.unpack_record(before.record(bb, h, 0, s), 32, 128, s)
+                tile0 = R.unrotate(R.dequantize_tile(rec["q"], rec["r16"], rec["c16"], rec["s16"], rec["z16"]),
+                                   before.sigma)
+                tail = before.tail(bb, h, s)[:31].astype(np.float64)
+                new = R.fp16_round(R.bf16_to_f64(bits[bb, T, h]))
+                kv.append(np.vstack([tile0, tail, new[None]]))
+            for gi in range(2 * h, 2 * h + 2):
+                lg = kv[0] @ qq[bb, gi] / np.sqrt(128)
+                p = np.exp(lg - lg.max())
+                assert np.allclose(fused[bb, gi], (p / p.sum()) @ kv[1], rtol=1e-12, atol=1e-12)
+    R.append_decode(b, k[:, T], v[:, T])
+    assert np.array_equal(a.buf, b.buf)
+    assert not np.allclose(fused, R.attn_decode(b, q, 4), rtol=1e-6)
+
+
+def test_append_attn_step_on_full_sequence():
+    a, k, v = _fresh(96, cap=96)
+    q = synth.q_host(7, 2, 4)
+    b, _, _ = _fresh(96, cap=96)
+    fused = R.append_attn_decode(a, k[:, 95], v[:, 95], q, 4)
+    assert np.array_equal(fused, R.attn_decode(b, q, 4))
+    assert a.flags & R.FLAG_CAPACITY and np.all(a.lens == 96)
