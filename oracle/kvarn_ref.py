@@ -43,6 +43,7 @@ VERSION = 1
 FLAG_CAPACITY = 1           # an append found the cache full (token dropped)
 FLAG_SATURATED = 2          # an input value was outside the fp16 range and was saturated
 FLAG_SCALE_CLAMPED = 4      # a stored scale hit the fp16 clamp range
+FLAG_UNMAPPED = 8           # a paged cache had no page for a tile that was written
 Q_PREROTATED = 1            # attention flag: the query is already rotated (q H)
 FP16_MAX = 65504.0
 SCALE_MIN = 2.0 ** -14      # smallest normal fp16; lower clamp of r and c
@@ -304,13 +305,15 @@ def unpack_record(rec, g: int, d: int, stream: int) -> dict:
 
 # ----------------------------------------------------------------------------- cache buffer (format v1)
 class Geom:
-    """batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant (VARIANT_* bits)."""
+    """batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant (VARIANT_* bits),
+    num_pages (0: tiles stored per sequence; > 0: a pool of pages found through a page map)."""
 
     def __init__(self, batch, num_kv_heads, head_dim=128, capacity=0, group=32, varn_iters=3, bits=2,
-                 variant=0):
+                 variant=0, num_pages=0):
         self.batch, self.num_kv_heads, self.head_dim = batch, num_kv_heads, head_dim
         self.capacity, self.group, self.varn_iters, self.bits = capacity, group, varn_iters, bits
         self.variant = variant
+        self.num_pages = num_pages
 
     def as_tuple(self):
         return (self.batch, self.num_kv_heads, self.head_dim, self.capacity, self.group,
@@ -322,23 +325,45 @@ class Geom:
         return record_bytes(self.group, self.head_dim)
 
     @property
+    def paged(self):
+        return self.num_pages > 0
+
+    @property
+    def map_offset(self):
+        """Page map int32 [B][capacity/G] (paged caches): right after len[]."""
+        return HEADER_FIXED + 8 * self.batch * self.num_kv_heads
+
+    @property
     def header(self):
-        return align256(HEADER_FIXED + 8 * self.batch * self.num_kv_heads)
+        extra = 4 * self.batch * self.tiles_per_seq if self.paged else 0
+        return align256(HEADER_FIXED + 8 * self.batch * self.num_kv_heads + extra)
 
     @property
     def tiles_per_seq(self):
         return self.capacity // self.group
 
     @property
+    def pool_bytes(self):
+        """Records: one page = the K and V records of every kv head for one group of G tokens
+        of one sequence ([Hkv][2][TR]); per-sequence storage is [B][Hkv][capacity/G][2][TR]."""
+        if self.paged:
+            return self.num_pages * self.num_kv_heads * 2 * self.tr
+        return self.batch * self.num_kv_heads * self.tiles_per_seq * 2 * self.tr
+
+    @property
     def tail_offset(self):
-        return self.header + align256(self.batch * self.num_kv_heads * self.tiles_per_seq * 2 * self.tr)
+        return self.header + align256(self.pool_bytes)
 
     @property
     def total(self):
         return self.tail_offset + align256(self.batch * self.num_kv_heads * 2 * self.group * self.head_dim * 2)
 
     def record_offset(self, b, h, tile, s):
+        assert not self.paged
         return self.header + ((((b * self.num_kv_heads + h) * self.tiles_per_seq + tile) * 2 + s) * self.tr)
+
+    def page_offset(self, page, h, s):
+        return self.header + ((page * self.num_kv_heads + h) * 2 + s) * self.tr
 
     def tail_slot_offset(self, b, h, s, slot):
         return self.tail_offset + ((((b * self.num_kv_heads + h) * 2 + s) * self.group + slot)
@@ -357,6 +382,8 @@ class Cache:
         hdr[8:36].view(np.int32)[:] = geom.as_tuple()
         hdr[VARIANT_OFFSET:VARIANT_OFFSET + 4].view(np.uint32)[0] = geom.variant
         hdr[SIGMA_OFFSET:SIGMA_OFFSET + geom.head_dim].view(np.int8)[:] = np.asarray(sigma, np.int8)
+        if geom.paged:
+            self.page_map[:] = -1                               # no page yet
 
     # header fields
     @property
@@ -377,10 +404,34 @@ class Cache:
         return self.buf[HEADER_FIXED:HEADER_FIXED + 4 * n].view(np.int32).reshape(
             self.g.batch, self.g.num_kv_heads, 2)
 
+    @property
+    def page_map(self) -> np.ndarray:
+        """int32 [B][capacity/G]: the page holding each tile of each sequence (-1: none)."""
+        g = self.g
+        n = g.batch * g.tiles_per_seq
+        return self.buf[g.map_offset:g.map_offset + 4 * n].view(np.int32).reshape(g.batch, g.tiles_per_seq)
+
+    def set_pages(self, pages, tile_first: int = 0):
+        """Map tiles [tile_first, tile_first + n) of every sequence: pages int32 [B][n]."""
+        pages = np.asarray(pages, dtype=np.int32)
+        self.page_map[:, tile_first:tile_first + pages.shape[1]] = pages
+
     # records and tail
-    def record(self, b, h, tile, s) -> np.ndarray:
-        o = self.g.record_offset(b, h, tile, s)
-        return self.buf[o:o + self.g.tr]
+    def record(self, b, h, tile, s):
+        """The tile's record bytes, or None for a paged cache without a valid page there."""
+        g = self.g
+        if g.paged:
+            page = int(self.page_map[b, tile])
+            if not 0 <= page < g.num_pages:
+                return None
+            o = g.page_offset(page, h, s)
+        else:
+            o = g.record_offset(b, h, tile, s)
+        return self.buf[o:o + g.tr]
+
+    def record_offset(self, b, h, tile, s):
+        r = self.record(b, h, tile, s)
+        return None if r is None else int(r.ctypes.data - self.buf.ctypes.data)
 
     def tail(self, b, h, s) -> np.ndarray:
         """fp16 view [G][D] of one tail."""
@@ -398,8 +449,9 @@ class Cache:
                 for s in range(2):
                     n = int(self.lens[b, h, s])
                     for tile in range(n // g.group):
-                        o = g.record_offset(b, h, tile, s)
-                        m[o:o + g.tr] = True
+                        o = self.record_offset(b, h, tile, s)
+                        if o is not None:
+                            m[o:o + g.tr] = True
                     o = g.tail_slot_offset(b, h, s, 0)
                     m[o:o + (n % g.group) * g.head_dim * 2] = True
         return m
@@ -437,7 +489,11 @@ def quantize_prefill(cache: Cache, k_bits, v_bits, num_tokens: int) -> None:
             for b in range(g.batch):
                 for h in range(g.num_kv_heads):
                     for tile in range(nfull):
-                        cache.record(b, h, tile, s)[:] = recs[b, h, tile]
+                        rec = cache.record(b, h, tile, s)
+                        if rec is None:
+                            cache.or_flags(FLAG_UNMAPPED)
+                        else:
+                            rec[:] = recs[b, h, tile]
         for b in range(g.batch):
             for h in range(g.num_kv_heads):
                 tail = cache.tail(b, h, s)
@@ -446,16 +502,21 @@ def quantize_prefill(cache: Cache, k_bits, v_bits, num_tokens: int) -> None:
     cache.lens[:] = T
 
 
-def append_decode(cache: Cache, k_bits, v_bits) -> None:
+def append_decode(cache: Cache, k_bits, v_bits, mask=None) -> None:
     """Append one token per (batch, kv head) (bf16 bits [B][Hkv][D]) through the fp16 tail.
     When a group of G fills, it is rotated, normalized and quantized into the next
-    tile record ([AP] 3.2: statistics of the current group are updated as tokens arrive)."""
+    tile record ([AP] 3.2: statistics of the current group are updated as tokens arrive).
+    `mask` (bool [B]) restricts the append to the sequences it selects."""
     g = cache.g
     for s, bits in enumerate((k_bits, v_bits)):
-        x, sat = canonicalize(bits)                              # [B][Hkv][D]
+        sel = [b for b in range(g.batch) if mask is None or mask[b]]
+        x, sat = canonicalize(np.asarray(bits)[sel])             # [len(sel)][Hkv][D]
         if sat:
             cache.or_flags(FLAG_SATURATED)
-        for b in range(g.batch):
+        x_all = np.zeros((g.batch,) + x.shape[1:])
+        x_all[sel] = x
+        x = x_all
+        for b in sel:
             for h in range(g.num_kv_heads):
                 pos = int(cache.lens[b, h, s])
                 if pos >= g.capacity:
@@ -466,27 +527,50 @@ def append_decode(cache: Cache, k_bits, v_bits) -> None:
                 if (pos + 1) % g.group == 0:
                     tile_x = tail.astype(np.float64)[None]         # [1][G][D]
                     recs, f = _quantize_stream(tile_x, cache.sigma, g, s)
-                    cache.or_flags(f)
-                    cache.record(b, h, (pos + 1) // g.group - 1, s)[:] = recs[0]
+                    rec = cache.record(b, h, (pos + 1) // g.group - 1, s)
+                    if rec is None:
+                        cache.or_flags(FLAG_UNMAPPED)
+                    else:
+                        cache.or_flags(f)
+                        rec[:] = recs[0]
                 cache.lens[b, h, s] = pos + 1
 
 
-def stream_values(cache: Cache, b: int, h: int, s: int, rotated: bool = False) -> np.ndarray:
+def append_tokens(cache: Cache, k_bits, v_bits, counts=None) -> None:
+    """Append counts[b] tokens (bf16 bits [B][T][Hkv][D], the first counts[b] rows of
+    sequence b; all T when counts is None) to every sequence after its stored tokens:
+    the same as that many single-token appends in order. Covers a chunk of a prefill into
+    a non-empty cache, ragged batches and per-sequence append masks (counts 0 or 1)."""
+    k_bits, v_bits = np.asarray(k_bits), np.asarray(v_bits)
+    T = k_bits.shape[1]
+    counts = np.full(cache.g.batch, T) if counts is None else np.asarray(counts)
+    for t in range(int(counts.max(initial=0))):
+        append_decode(cache, k_bits[:, t], v_bits[:, t], mask=counts > t)
+
+
+def stream_values(cache: Cache, b: int, h: int, s: int, rotated: bool = False, with_mask: bool = False):
     """All stored tokens of one stream, dequantized, in original space (fp64 [len][D]).
     With rotated=True the tile tokens are returned in rotated space and tail tokens
-    are rotated too (used for checks that work in the rotated basis)."""
+    are rotated too (used for checks that work in the rotated basis). Tokens of a tile
+    without a page (paged cache) are absent: 0 here, and False in the mask returned
+    with with_mask=True."""
     g = cache.g
     n = int(cache.lens[b, h, s])
     out = np.zeros((n, g.head_dim))
+    present = np.ones(n, dtype=bool)
     nfull = n // g.group
     for tile in range(nfull):
-        u = unpack_record(cache.record(b, h, tile, s), g.group, g.head_dim, s)
+        rec = cache.record(b, h, tile, s)
+        if rec is None:
+            present[tile * g.group:(tile + 1) * g.group] = False
+            continue
+        u = unpack_record(rec, g.group, g.head_dim, s)
         w = dequantize_tile(u["q"], u["r16"], u["c16"], u["s16"], u["z16"])
         out[tile * g.group:(tile + 1) * g.group] = w if rotated else undo_rotation(w, cache.sigma, g.variant)
     tail = cache.tail(b, h, s).astype(np.float64)
     for t in range(nfull * g.group, n):
         out[t] = apply_rotation(tail[t % g.group], cache.sigma, g.variant) if rotated else tail[t % g.group]
-    return out
+    return (out, present) if with_mask else out
 
 
 def dequantize(cache: Cache, max_tokens: int) -> tuple[np.ndarray, np.ndarray]:
@@ -523,8 +607,9 @@ def attn_decode(cache: Cache, q_bits, num_q_heads: int, softmax_scale: float = 0
     out = np.zeros((g.batch, num_q_heads, d))
     todo = pairs if pairs is not None else [(b, h) for b in range(g.batch) for h in range(g.num_kv_heads)]
     for b, h in todo:
-        k = stream_values(cache, b, h, 0)
+        k, present = stream_values(cache, b, h, 0, with_mask=True)
         v = stream_values(cache, b, h, 1)
+        k, v = k[present], v[present]                            # tiles without a page are skipped
         if k.shape[0] == 0:
             continue
         for gi in range(h * grp, (h + 1) * grp):
@@ -555,8 +640,9 @@ def append_attn_decode(cache: Cache, k_bits, v_bits, q_bits, num_q_heads: int, s
     out = np.zeros((g.batch, num_q_heads, d))
     for b in range(g.batch):
         for h in range(g.num_kv_heads):
-            k = stream_values(cache, b, h, 0)
+            k, present = stream_values(cache, b, h, 0, with_mask=True)
             v = stream_values(cache, b, h, 1)
+            k, v = k[present], v[present]
             if int(cache.lens[b, h, 0]) < g.capacity:
                 k = np.vstack([k, kn[b, h][None]])
                 v = np.vstack([v, vn[b, h][None]])
