@@ -30,6 +30,14 @@
  *           u32 variant at byte 40, i8 sigma[D] at byte 64, i32 len[B][Hkv][2]
  *           at byte 512;
  *   tiles   [B][Hkv][capacity/G][2 (K,V)][TR] tile records, region padded to 256 B;
+ *           paged caches (num_pages > 0) instead hold a pool of num_pages pages,
+ *           [num_pages][Hkv][2][TR] (one page = one group of G tokens of one sequence,
+ *           every kv head, K and V), and the header grows by a page map int32
+ *           [B][capacity/G] at byte 512 + 8*B*Hkv naming each tile's page (-1 = none,
+ *           the state after kvarn_cache_init): header = align256(512 + 8*B*Hkv +
+ *           4*B*capacity/G). A tile whose map entry is not a valid page is dropped by
+ *           writers (KVARN_FLAG_UNMAPPED) and skipped by readers (attention leaves its
+ *           tokens out, dequantization writes zeros).
  *   tail    [B][Hkv][2][G][D] fp16, unrotated tokens of the group being filled,
  *           slot = token index mod G.
  *   Tile record TR = G*D/4 + 2G + 6D bytes (1856 at G=32, 2944 at G=64):
@@ -76,7 +84,8 @@ typedef enum {
 
 /* Geometry of one layer cache. v1 supports head_dim = 128, group in {32, 64},
  * bits = 2, 0 <= varn_iters <= 8, capacity a positive multiple of group,
- * variant a combination of the KVARN_VARIANT_* bits below (0 = the method). */
+ * variant a combination of the KVARN_VARIANT_* bits below (0 = the method),
+ * num_pages >= 0 (see the paged layout above). */
 typedef struct {
     int32_t batch;          /* B   sequences                                   */
     int32_t num_kv_heads;   /* Hkv                                             */
@@ -86,6 +95,7 @@ typedef struct {
     int32_t varn_iters;     /* VarN iterations (token pass + channel pass)     */
     int32_t bits;           /* code width (2)                                  */
     int32_t variant;        /* ablation bits, 0 for KVarN as defined           */
+    int32_t num_pages;      /* 0: records stored per sequence; > 0: paged      */
 } kvarn_geom;
 
 /* Ablation variants (ai-paper-analysis page, section 5: Hadamard only = varn_iters 0,
@@ -103,7 +113,8 @@ enum { KVARN_OUT_F32 = 0, KVARN_OUT_BF16 = 1 };            /* dequantize output 
 enum { KVARN_Q_PREROTATED = 1u };                          /* attention: q is already q H_D */
 enum { KVARN_FLAG_CAPACITY = 1u,      /* an append found a full sequence; token dropped      */
        KVARN_FLAG_SATURATED = 2u,     /* an input had |x| > 65504 and was saturated          */
-       KVARN_FLAG_SCALE_CLAMPED = 4u  /* r or c hit [2^-14, 65504], or s/z saturated        */ };
+       KVARN_FLAG_SCALE_CLAMPED = 4u, /* r or c hit [2^-14, 65504], or s/z saturated        */
+       KVARN_FLAG_UNMAPPED = 8u       /* a paged cache had no page for a tile being written  */ };
 
 /* Format version of the cache buffer (1). */
 KVARN_API int kvarn_format_version(void);
@@ -132,6 +143,25 @@ KVARN_API kvarn_status kvarn_quantize_prefill(const kvarn_geom* g, void* cache, 
  * and sets KVARN_FLAG_CAPACITY. */
 KVARN_API kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, const void* k_bf16,
                                  const void* v_bf16, void* stream);
+
+/* Append counts[b] tokens to sequence b after its stored ones: k_bf16, v_bf16 device
+ * bf16 [B][num_tokens][Hkv][D] (sequence b's tokens are its first counts[b] rows);
+ * counts: device int32[B], each clamped to [0, num_tokens], or NULL for num_tokens
+ * everywhere. The result is that of counts[b] single-token appends in order (and so,
+ * from an empty sequence, of a prefill): a chunk of a prefill into a non-empty cache,
+ * a ragged batch, or a per-sequence append mask (counts 0 or 1). Tokens past the
+ * capacity are dropped (KVARN_FLAG_CAPACITY). 0 <= num_tokens <= capacity. Two launches.
+ * (ai-paper-analysis page, section 3.2: a group is quantized once it is complete.) */
+KVARN_API kvarn_status kvarn_append_tokens(const kvarn_geom* g, void* cache, const void* k_bf16,
+                                 const void* v_bf16, int32_t num_tokens, const int32_t* counts,
+                                 void* stream);
+
+/* Paged caches only (num_pages > 0): tiles [tile_first, tile_first + num_tiles) of every
+ * sequence take the pages in pages (device int32 [B][num_tiles]); an entry outside
+ * [0, num_pages) unmaps the tile. The caller owns the pool: two tiles written into one
+ * page overwrite each other. Layout of the map: see the cache format above. */
+KVARN_API kvarn_status kvarn_cache_set_pages(const kvarn_geom* g, void* cache, const int32_t* pages,
+                                   int32_t tile_first, int32_t num_tiles, void* stream);
 
 /* Dequantize into k_out, v_out: device [B][max_tokens][Hkv][D], f32 or bf16 per
  * out_dtype. Tile tokens undo grid and scales and rotate back by H_D^T

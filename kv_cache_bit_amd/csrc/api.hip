@@ -14,7 +14,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 kvarn_status check_geom(const kvarn_geom* g) {
   if (!g) return KVARN_ERR_NULL;
   if (g->batch <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0 || g->capacity <= 0 || g->group <= 0 ||
-      g->varn_iters < 0 || g->bits <= 0)
+      g->varn_iters < 0 || g->bits <= 0 || g->num_pages < 0)
     return KVARN_ERR_GEOM;
   if (g->head_dim != kD || (g->group != 32 && g->group != 64) || g->bits != 2 || g->varn_iters > 8)
     return KVARN_ERR_UNSUPPORTED;
@@ -25,6 +25,7 @@ kvarn_status check_geom(const kvarn_geom* g) {
   // keep every element index of a [B][capacity][Hkv][D] tensor and every tile count in range
   if ((long long)g->batch * g->capacity * g->num_kv_heads * kD >= (1LL << 40)) return KVARN_ERR_RANGE;
   if ((long long)g->batch * g->num_kv_heads * (g->capacity / g->group) * 2 >= (1LL << 31)) return KVARN_ERR_RANGE;
+  if ((long long)g->num_pages * g->num_kv_heads * 2 >= (1LL << 31)) return KVARN_ERR_RANGE;
   return KVARN_OK;
 }
 
@@ -108,7 +109,10 @@ kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* si
   a.variant = (uint32_t)g->variant;
   memcpy(a.sigma, signs_host, kD);
   a.n_len = 2LL * g->batch * g->num_kv_heads;
-  a.hdr_bytes = make_layout(*g).header;
+  const Layout L = make_layout(*g);
+  a.hdr_bytes = L.header;
+  a.map_off = L.map_off;
+  a.map_end = g->num_pages > 0 ? L.map_off + 4LL * g->batch * L.tiles : L.map_off;
   return dev(launch_init(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -135,6 +139,47 @@ kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, const void* k
   a.k = static_cast<const uint16_t*>(k_bf16);
   a.v = static_cast<const uint16_t*>(v_bf16);
   return dev(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_append_tokens(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
+                                 int32_t num_tokens, const int32_t* counts, void* stream) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (!cache || ((!k_bf16 || !v_bf16) && num_tokens > 0)) return KVARN_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(k_bf16) || !aligned16(v_bf16) || ((uintptr_t)counts & 3u)) return KVARN_ERR_ALIGN;
+  if (num_tokens < 0 || num_tokens > g->capacity) return KVARN_ERR_RANGE;
+  if (num_tokens == 0) return KVARN_OK;
+  TokensArgs a{};
+  a.L = make_layout(*g);
+  a.cache = static_cast<uint8_t*>(cache);
+  a.k = static_cast<const uint16_t*>(k_bf16);
+  a.v = static_cast<const uint16_t*>(v_bf16);
+  a.counts = counts;
+  a.T = num_tokens;
+  a.max_tiles = (g->group - 1 + num_tokens) / g->group;
+  const long long jobs = (long long)g->batch * a.max_tiles * 2 * g->num_kv_heads;
+  if (jobs >= (1LL << 31)) return KVARN_ERR_RANGE;
+  a.jobs = (int)jobs;
+  return dev(launch_tokens(a, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_cache_set_pages(const kvarn_geom* g, void* cache, const int32_t* pages, int32_t tile_first,
+                                   int32_t num_tiles, void* stream) {
+  kvarn_status st = check_geom(g);
+  if (st != KVARN_OK) return st;
+  if (g->num_pages == 0) return KVARN_ERR_GEOM;
+  if (!cache || (!pages && num_tiles > 0)) return KVARN_ERR_NULL;
+  if (!aligned16(cache) || ((uintptr_t)pages & 3u)) return KVARN_ERR_ALIGN;
+  const int tiles = g->capacity / g->group;
+  if (tile_first < 0 || num_tiles < 0 || tile_first > tiles || num_tiles > tiles - tile_first) return KVARN_ERR_RANGE;
+  if (num_tiles == 0) return KVARN_OK;
+  SetPagesArgs a{};
+  a.L = make_layout(*g);
+  a.cache = static_cast<uint8_t*>(cache);
+  a.pages = pages;
+  a.tile_first = tile_first;
+  a.n = num_tiles;
+  return dev(launch_set_pages(a, static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_out, void* v_out, int32_t max_tokens,

@@ -243,7 +243,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int k = 0; k < 4; ++k) o[0][k] = o[1][k] = 0.0f;
 
   for (int tile = t0 + wave; tile < t1; tile += 4) {
-    const uint8_t* rk = a.cache + L.record(b, h, tile, 0);
+    const long long roff = record_at(a.cache, L, b, h, tile, 0);
+    if (roff < 0) continue;  // paged cache, no page for this tile: its tokens are left out
+    const uint8_t* rk = a.cache + roff;
     const uint8_t* rv = rk + L.tr;
     // ---- loads
     uint2 kc[NMB];

@@ -52,8 +52,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     }
   };
   const int tile = (blk * 32) / L.G;
-  if (tile < nfull) {
-    const uint8_t* rec = a.cache + L.record(b, h, tile, s);
+  const long long roff = tile < nfull ? record_at(a.cache, L, b, h, tile, s) : 0;
+  if (tile < nfull && roff < 0) {  // paged cache without a page for this tile: zeros
+    const float zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) store_row(blk * 32 + rg * 8 + i, zero);
+  } else if (tile < nfull) {
+    const uint8_t* rec = a.cache + roff;
     const int G = L.G;
     const int ro = G * kD / 4, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
     const int tw0 = (blk * 32) % G + rg * 8;
@@ -132,12 +137,29 @@ __global__ void init_kernel(InitArgs a) {
     }
     h32[off / 4] = w;
   }
-  for (long long k = kHdrFixed / 4 + t; k < a.hdr_bytes / 4; k += blockDim.x) h32[k] = 0;  // len[] and padding
+  for (long long k = kHdrFixed / 4 + t; k < a.hdr_bytes / 4; k += blockDim.x)  // len[], page map, padding
+    h32[k] = (k >= a.map_off / 4 && k < a.map_end / 4) ? 0xFFFFFFFFu : 0u;
+}
+
+// ----------------------------------------------------------------------------- page map
+// Tiles [tile_first, tile_first + n) of every sequence take the pages given (no check of
+// the values: readers and writers check each entry when they use it).
+__global__ void set_pages_kernel(SetPagesArgs a) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)a.L.B * a.n) return;
+  const long long b = i / a.n, t = i - b * a.n;
+  reinterpret_cast<int32_t*>(a.cache + a.L.map_off)[b * a.L.tiles + a.tile_first + t] = a.pages[i];
 }
 
 // ----------------------------------------------------------------------------- launchers
 hipError_t launch_init(const InitArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(init_kernel, dim3(1), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_pages(const SetPagesArgs& a, hipStream_t st) {
+  const long long n = (long long)a.L.B * a.n;
+  hipLaunchKernelGGL(set_pages_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

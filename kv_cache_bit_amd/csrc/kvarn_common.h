@@ -22,14 +22,21 @@ constexpr float kInvSqrtD = 0.08838834764831845f;      // 1/sqrt(128), fp32-roun
 inline __host__ __device__ long long align256(long long n) { return (n + 255) / 256 * 256; }
 
 // Byte layout of one layer cache (format v1), computed on the host and passed by value.
+// Records are stored per sequence ([B][Hkv][tiles][2][TR]) or, for a paged cache
+// (num_pages > 0), in a pool of pages [num_pages][Hkv][2][TR] named by the page map
+// int32 [B][tiles] at map_off; record_at resolves either.
 struct Layout {
   int B, Hkv, cap, G, n_it, tiles;  // tiles = cap / G
   int variant;                      // KVARN_VARIANT_* bits
+  int num_pages;                    // 0: per-sequence records
   int tr;                           // tile record bytes
-  long long header, tail_off, total;
+  long long header, map_off, tail_off, total;
 
-  __host__ __device__ long long record(int b, int h, int tile, int s) const {
+  __host__ __device__ long long record_seq(int b, int h, int tile, int s) const {
     return header + ((((long long)b * Hkv + h) * tiles + tile) * 2 + s) * tr;
+  }
+  __host__ __device__ long long page_record(int page, int h, int s) const {
+    return header + (((long long)page * Hkv + h) * 2 + s) * tr;
   }
   __host__ __device__ long long tail_row(int b, int h, int s, int slot) const {
     return tail_off + ((((long long)b * Hkv + h) * 2 + s) * G + slot) * (kD * 2);
@@ -69,15 +76,29 @@ inline __host__ Layout make_layout(const kvarn_geom& g) {
   L.G = g.group;
   L.n_it = g.varn_iters;
   L.variant = g.variant;
+  L.num_pages = g.num_pages;
   L.tiles = g.capacity / g.group;
   L.tr = g.group * kD / 4 + 2 * g.group + 6 * kD;
-  L.header = align256(kHdrFixed + 8LL * g.batch * g.num_kv_heads);
-  L.tail_off = L.header + align256((long long)g.batch * g.num_kv_heads * L.tiles * 2 * L.tr);
+  L.map_off = kHdrFixed + 8LL * g.batch * g.num_kv_heads;
+  L.header = align256(L.map_off + (g.num_pages > 0 ? 4LL * g.batch * L.tiles : 0));
+  const long long pool = g.num_pages > 0 ? (long long)g.num_pages * g.num_kv_heads * 2 * L.tr
+                                         : (long long)g.batch * g.num_kv_heads * L.tiles * 2 * L.tr;
+  L.tail_off = L.header + align256(pool);
   L.total = L.tail_off + align256((long long)g.batch * g.num_kv_heads * 2 * g.group * kD * 2);
   return L;
 }
 
 #if defined(__HIPCC__)
+// Byte offset of the record of (b, h, tile, s), or -1 when a paged cache names no valid
+// page for that tile (writers then drop the tile, readers skip it).
+__device__ __forceinline__ long long record_at(const uint8_t* cache, const Layout& L, int b, int h, int tile,
+                                               int s) {
+  if (L.num_pages == 0) return L.record_seq(b, h, tile, s);
+  const int page = reinterpret_cast<const int32_t*>(cache + L.map_off)[(long long)b * L.tiles + tile];
+  if (page < 0 || page >= L.num_pages) return -1;
+  return L.page_record(page, h, s);
+}
+
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));

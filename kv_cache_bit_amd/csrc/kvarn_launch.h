@@ -14,7 +14,27 @@ struct InitArgs {
   uint32_t variant;  // header byte 40
   int8_t sigma[kD];
   long long n_len;  // entries of len[]
-  long long hdr_bytes;  // header size; everything past len[] is zeroed
+  long long hdr_bytes;  // header size; everything past byte 512 is zeroed except the page map
+  long long map_off, map_end;  // page map bytes (set to -1); empty for per-sequence caches
+};
+
+struct SetPagesArgs {
+  Layout L;
+  uint8_t* cache;
+  const int32_t* pages;  // [B][n]
+  int tile_first, n;
+};
+
+// Multi-token append: counts[b] (or T) tokens of k, v per sequence after its stored ones.
+struct TokensArgs {
+  Layout L;
+  uint8_t* cache;
+  const uint16_t* k;       // bf16 [B][T][Hkv][D]
+  const uint16_t* v;
+  const int32_t* counts;   // [B] or nullptr
+  int T;
+  int max_tiles;           // groups one sequence can complete: (G - 1 + T) / G
+  int jobs;                // B * max_tiles * 2 * Hkv tile jobs
 };
 
 struct PrefillArgs {
@@ -68,6 +88,8 @@ hipError_t launch_init(const InitArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);
+hipError_t launch_set_pages(const SetPagesArgs& a, hipStream_t st);
+hipError_t launch_tokens(const TokensArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
 }  // namespace kvarn

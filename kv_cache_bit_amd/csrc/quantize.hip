@@ -99,7 +99,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
   tile_finish<NW, DBG, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, dw, dy, dstride);
   if (valid) {
-    copy_record<NW>(sh, a.cache + L.record(b, h, tile, s), lane, sub);
+    const long long ro = record_at(a.cache, L, b, h, tile, s);
+    if (ro >= 0)
+      copy_record<NW>(sh, a.cache + ro, lane, sub);
+    else
+      flags |= KVARN_FLAG_UNMAPPED;
     raise_flags(hdr, flags);
   }
 }
@@ -110,6 +114,103 @@ template <int NW, bool ABL>
 __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
   __shared__ TileLds<NW> sh;
   append_job<NW, ABL>(a, blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63, sh);
+}
+
+// ----------------------------------------------------------------------------- multi-token append
+// counts[b] tokens (T when counts is null) go after each sequence's stored ones, as that
+// many single-token appends would place them. Tile pass: each group the new tokens
+// complete is quantized from its stored tail tokens and the new input rows; job
+// (b, j, s, h) takes the j-th such group, 4/NW jobs per work-group, and jobs past the
+// sequence's last completed group run on clamped inputs and store nothing (the
+// work-group's barriers stay uniform). Tail pass, a second launch so that the tail is read
+// before it is overwritten: the new tokens after the last complete group go to the tail
+// and len moves on.
+__device__ __forceinline__ void tokens_range(const TokensArgs& a, int b, int h, int s, int& l0, int& l1,
+                                             bool& dropped) {
+  l0 = *reinterpret_cast<const int32_t*>(a.cache + a.L.len_off(b, h, s));
+  const int cnt = min(max(a.counts ? a.counts[b] : a.T, 0), a.T);
+  l1 = min(l0 + cnt, a.L.cap);
+  dropped = l0 + cnt > a.L.cap;
+}
+
+template <int NW, bool ABL>
+__global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
+  constexpr int TPW = 4 / NW;
+  constexpr int G = 32 * NW;
+  __shared__ TileLds<NW> sh_all[TPW];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int tw = wave / NW, sub = wave % NW;
+  TileLds<NW>& sh = sh_all[tw];
+  const Layout& L = a.L;
+  uint8_t* hdr = a.cache;
+  int job = blockIdx.x * TPW + tw;
+  const bool in_grid = job < a.jobs;
+  if (!in_grid) job = 0;
+  const int h = job % L.Hkv, s = (job / L.Hkv) % 2, j = (job / L.Hkv / 2) % a.max_tiles;
+  const int b = job / L.Hkv / 2 / a.max_tiles;
+  int l0, l1;
+  bool dropped;
+  tokens_range(a, b, h, s, l0, l1, dropped);
+  const int tile = l0 / G + j;
+  const bool valid = in_grid && tile < l1 / G;
+  const bool idr = ABL && (L.variant & KVARN_VARIANT_NO_ROTATION);
+  const Frags hf = frags_v<ABL>(idr, lane);
+  const uint16_t* src = (s ? a.v : a.k) + ((long long)b * a.T * L.Hkv + h) * kD;  // + row * Hkv * D
+  uint32_t flags = 0;
+  h8v av[2][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int tt = tile * G + sub * 32 + 16 * mb + c;  // token of this A row in the sequence
+      uint4 w;
+      if (tt < l0) {  // stored in the tail
+        w = *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, tt % G) + 16 * (4 * ks + g));
+      } else {        // a new token
+        const int row = min(tt - l0, a.T - 1);
+        float x[8], amax = 0.0f;
+        canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)row * L.Hkv * kD + 8 * (4 * ks + g)), x, amax);
+        if (valid) flags |= sat_flag(amax);
+        w = pack8_f16(x);
+      }
+      av[mb][ks] = sign_a(w, m);
+    }
+  }
+  float p[2][8][4];
+  const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
+  tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, nullptr, nullptr, 0);
+  if (valid) {
+    const long long ro = record_at(a.cache, L, b, h, tile, s);
+    if (ro >= 0)
+      copy_record<NW>(sh, a.cache + ro, lane, sub);
+    else
+      flags |= KVARN_FLAG_UNMAPPED;
+    raise_flags(hdr, flags);
+  }
+}
+
+// One wave per (b, h, s): 4 tokens per step, 16 lanes x 8 channels each.
+__global__ __launch_bounds__(256) void tokens_tail_kernel(TokensArgs a) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const Layout& L = a.L;
+  const long long sj = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sj >= 2LL * L.B * L.Hkv) return;
+  const int s = (int)(sj % 2), h = (int)((sj / 2) % L.Hkv), b = (int)(sj / 2 / L.Hkv);
+  int l0, l1;
+  bool dropped;
+  tokens_range(a, b, h, s, l0, l1, dropped);
+  uint32_t flags = dropped ? (uint32_t)KVARN_FLAG_CAPACITY : 0u;
+  const uint16_t* src = (s ? a.v : a.k) + ((long long)b * a.T * L.Hkv + h) * kD;
+  for (int t = max(l0, l1 / L.G * L.G) + g; t < l1; t += 4) {
+    float x[8], amax = 0.0f;
+    canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)(t - l0) * L.Hkv * kD + 8 * c), x, amax);
+    flags |= sat_flag(amax);
+    *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = pack8_f16(x);
+  }
+  raise_flags(a.cache, flags);
+  if (lane == 0) *reinterpret_cast<int32_t*>(a.cache + L.len_off(b, h, s)) = l1;  // the wave read len first
 }
 
 // ----------------------------------------------------------------------------- launchers
@@ -148,6 +249,30 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
     else
       hipLaunchKernelGGL((append_kernel<2, false>), grid, dim3(128), 0, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_tokens(const TokensArgs& a, hipStream_t st) {
+  const int tpw = 4 / (a.L.G / 32);
+  if (a.jobs > 0) {
+    const dim3 grid((unsigned)((a.jobs + tpw - 1) / tpw));
+    const bool abl = a.L.variant != 0;
+    if (a.L.G == 32) {
+      if (abl)
+        hipLaunchKernelGGL((tokens_tile_kernel<1, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((tokens_tile_kernel<1, false>), grid, dim3(256), 0, st, a);
+    } else {
+      if (abl)
+        hipLaunchKernelGGL((tokens_tile_kernel<2, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((tokens_tile_kernel<2, false>), grid, dim3(256), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long streams = 2LL * a.L.B * a.L.Hkv;
+  hipLaunchKernelGGL(tokens_tail_kernel, dim3((unsigned)((streams + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

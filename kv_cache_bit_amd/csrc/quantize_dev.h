@@ -767,7 +767,11 @@ __device__ void append_job(const AppendArgs& a, int job, int sub, int lane, Tile
     float p[2][8][4];
     const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
     tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, nullptr, nullptr, 0);
-    copy_record<NW>(sh, a.cache + L.record(b, h, (pos + 1) / G - 1, s), lane, sub);
+    const long long ro = record_at(a.cache, L, b, h, (pos + 1) / G - 1, s);
+    if (ro >= 0)
+      copy_record<NW>(sh, a.cache + ro, lane, sub);
+    else
+      flags |= KVARN_FLAG_UNMAPPED;
   }
   raise_flags(hdr, flags);
   __syncthreads();  // every wave has read len before it moves

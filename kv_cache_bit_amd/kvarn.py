@@ -16,13 +16,14 @@ KVARN_OK, KVARN_ERR_NULL, KVARN_ERR_ALIGN, KVARN_ERR_GEOM = 0, 1, 2, 3
 KVARN_ERR_UNSUPPORTED, KVARN_ERR_RANGE, KVARN_ERR_DEVICE = 4, 5, 6
 KVARN_OUT_F32, KVARN_OUT_BF16 = 0, 1
 KVARN_Q_PREROTATED = 1
-KVARN_FLAG_CAPACITY, KVARN_FLAG_SATURATED, KVARN_FLAG_SCALE_CLAMPED = 1, 2, 4
+KVARN_FLAG_CAPACITY, KVARN_FLAG_SATURATED, KVARN_FLAG_SCALE_CLAMPED, KVARN_FLAG_UNMAPPED = 1, 2, 4, 8
 KVARN_VARIANT_NO_ROTATION, KVARN_VARIANT_NO_CHANNEL_PASS, KVARN_VARIANT_NO_TOKEN_PASS = 1, 2, 4
 KVARN_VARIANT_CENTERED = 8
 
 EXPORTS = ("kvarn_format_version", "kvarn_cache_bytes", "kvarn_cache_init", "kvarn_quantize_prefill",
            "kvarn_append_decode", "kvarn_dequantize", "kvarn_attn_workspace_bytes", "kvarn_attn_decode",
-           "kvarn_cache_flags", "kvarn_status_str", "kvarn_debug_prefill", "kvarn_append_attn_decode")
+           "kvarn_cache_flags", "kvarn_status_str", "kvarn_debug_prefill", "kvarn_append_attn_decode",
+           "kvarn_append_tokens", "kvarn_cache_set_pages")
 
 
 class KvarnError(RuntimeError):
@@ -33,14 +34,16 @@ class KvarnError(RuntimeError):
 
 class kvarn_geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "num_kv_heads", "head_dim", "capacity", "group", "varn_iters", "bits", "variant")]
+                ("batch", "num_kv_heads", "head_dim", "capacity", "group", "varn_iters", "bits", "variant",
+                 "num_pages")]
 
     def __repr__(self):
         return "kvarn_geom(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
-def geom(batch, num_kv_heads, capacity, group=32, varn_iters=3, head_dim=128, bits=2, variant=0) -> kvarn_geom:
-    return kvarn_geom(batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant)
+def geom(batch, num_kv_heads, capacity, group=32, varn_iters=3, head_dim=128, bits=2, variant=0,
+         num_pages=0) -> kvarn_geom:
+    return kvarn_geom(batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant, num_pages)
 
 
 def _load():
@@ -59,6 +62,8 @@ def _load():
         "kvarn_attn_workspace_bytes": ([G, I32, S], ctypes.c_int),
         "kvarn_attn_decode": ([G, P, P, I32, F32, U32, P, ctypes.c_size_t, P, P], ctypes.c_int),
         "kvarn_append_attn_decode": ([G, P, P, P, P, I32, F32, U32, P, ctypes.c_size_t, P, P], ctypes.c_int),
+        "kvarn_append_tokens": ([G, P, P, P, I32, P, P], ctypes.c_int),
+        "kvarn_cache_set_pages": ([G, P, P, I32, I32, P], ctypes.c_int),
         "kvarn_cache_flags": ([P, P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
         "kvarn_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "kvarn_debug_prefill": ([G, P, P, P, I32, P, P, P, P, P], ctypes.c_int),
@@ -157,6 +162,16 @@ def kvarn_append_attn_decode(g: kvarn_geom, cache, k, v, q, num_q_heads: int, so
     _check(lib.kvarn_append_attn_decode(ctypes.byref(g), _ptr(cache), _ptr(k), _ptr(v), _ptr(q), num_q_heads,
                                         softmax_scale, flags, _ptr(workspace), workspace_bytes, _ptr(out),
                                         _stream(stream)), "kvarn_append_attn_decode")
+
+
+def kvarn_append_tokens(g: kvarn_geom, cache, k, v, num_tokens: int, counts=None, stream=None) -> None:
+    _check(lib.kvarn_append_tokens(ctypes.byref(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _ptr(counts),
+                                   _stream(stream)), "kvarn_append_tokens")
+
+
+def kvarn_cache_set_pages(g: kvarn_geom, cache, pages, tile_first: int, num_tiles: int, stream=None) -> None:
+    _check(lib.kvarn_cache_set_pages(ctypes.byref(g), _ptr(cache), _ptr(pages), tile_first, num_tiles,
+                                     _stream(stream)), "kvarn_cache_set_pages")
 
 
 def kvarn_cache_flags(cache, stream=None) -> int:

@@ -506,32 +506,33 @@ def append_decode(cache: Cache, k_bits, v_bits, mask=None) -> None:
     """Append one token per (batch, kv head) (bf16 bits [B][Hkv][D]) through the fp16 tail.
     When a group of G fills, it is rotated, normalized and quantized into the next
     tile record ([AP] 3.2: statistics of the current group are updated as tokens arrive).
-    `mask` (bool [B]) restricts the append to the sequences it selects."""
+    `mask` (bool [B]) restricts the append to the sequences it selects. Flags: a token
+    dropped at capacity is not read (no saturation flag from it); a group quantized for a
+    tile without a page still raises its scale flags."""
     g = cache.g
-    for s, bits in enumerate((k_bits, v_bits)):
-        sel = [b for b in range(g.batch) if mask is None or mask[b]]
-        x, sat = canonicalize(np.asarray(bits)[sel])             # [len(sel)][Hkv][D]
-        if sat:
-            cache.or_flags(FLAG_SATURATED)
-        x_all = np.zeros((g.batch,) + x.shape[1:])
-        x_all[sel] = x
-        x = x_all
-        for b in sel:
+    bits_s = (np.asarray(k_bits), np.asarray(v_bits))
+    for s in range(2):
+        for b in range(g.batch):
+            if mask is not None and not mask[b]:
+                continue
             for h in range(g.num_kv_heads):
                 pos = int(cache.lens[b, h, s])
                 if pos >= g.capacity:
                     cache.or_flags(FLAG_CAPACITY)
                     continue
+                x, sat = canonicalize(bits_s[s][b, h])
+                if sat:
+                    cache.or_flags(FLAG_SATURATED)
                 tail = cache.tail(b, h, s)
-                tail[pos % g.group] = x[b, h].astype(np.float16)
+                tail[pos % g.group] = x.astype(np.float16)
                 if (pos + 1) % g.group == 0:
                     tile_x = tail.astype(np.float64)[None]         # [1][G][D]
                     recs, f = _quantize_stream(tile_x, cache.sigma, g, s)
+                    cache.or_flags(f)
                     rec = cache.record(b, h, (pos + 1) // g.group - 1, s)
                     if rec is None:
                         cache.or_flags(FLAG_UNMAPPED)
                     else:
-                        cache.or_flags(f)
                         rec[:] = recs[0]
                 cache.lens[b, h, s] = pos + 1
 

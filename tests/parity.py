@@ -137,8 +137,10 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
 
 
 def gpu_prefill(gc: GpuCache, k_bits, v_bits, T, debug=False):
-    k = from_u16(k_bits)
-    v = from_u16(v_bits)
+    """Prefill with the first T tokens of k_bits, v_bits (uint16 [B][>= T][H][D]): the
+    library reads a contiguous [B][T][H][D] input, so longer arrays are cut first."""
+    k = from_u16(k_bits[:, :T])
+    v = from_u16(v_bits[:, :T])
     B, H = gc.og.batch, gc.og.num_kv_heads
     tf = (T // gc.og.group) * gc.og.group
     if debug:

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(K.lib, n), n
     assert sorted(K.EXPORTS) == names
@@ -37,6 +37,12 @@ def test_format_version_and_status_strings():
                                        (32, 10, 17408, 32), (3, 5, 640, 64)])
 def test_cache_bytes_match_oracle_layout(B, H, cap, G):
     assert K.kvarn_cache_bytes(K.geom(B, H, cap, G, 3)) == R.Geom(B, H, 128, cap, G, 3, 2).total
+
+
+def test_paged_sizes_match_oracle():
+    for B, H, cap, G, pages in [(2, 3, 256, 64, 7), (4, 8, 1024, 32, 100), (1, 1, 32, 32, 1)]:
+        assert K.kvarn_cache_bytes(K.geom(B, H, cap, G, 2, num_pages=pages)) == \
+            R.Geom(B, H, 128, cap, G, 2, 2, 0, pages).total
 
 
 def test_variants_accepted():
@@ -73,7 +79,8 @@ def test_workspace_bytes():
     (dict(variant=-1), K.KVARN_ERR_UNSUPPORTED),
 ])
 def test_geometry_rejected(kw, status):
-    base = dict(batch=1, num_kv_heads=2, head_dim=128, capacity=128, group=32, varn_iters=3, bits=2, variant=0)
+    base = dict(batch=1, num_kv_heads=2, head_dim=128, capacity=128, group=32, varn_iters=3, bits=2, variant=0,
+                num_pages=0)
     base.update(kw)
     g = K.kvarn_geom(*[base[n] for n, _ in K.kvarn_geom._fields_])
     with pytest.raises(K.KvarnError) as e:
@@ -116,6 +123,21 @@ def test_argument_errors_return_before_any_launch():
     assert _code(K.kvarn_attn_decode, g, A, A2, 4, 0.0, 8, A, ws, A2, 0) == K.KVARN_ERR_UNSUPPORTED
     assert _code(K.kvarn_attn_decode, g, A, A2, 4, float("nan"), 0, A, ws, A2, 0) == K.KVARN_ERR_RANGE
     assert _code(K.kvarn_attn_decode, g, A, 0, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_NULL
+    # multi-token append and the page map
+    assert _code(K.kvarn_append_tokens, g, A, A, A2, 129, None, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_append_tokens, g, A, A, A2, -1, None, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_append_tokens, g, A, 0, A2, 3, None, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_append_tokens, g, A, MIS, A2, 3, None, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_append_tokens, g, A, A, A2, 3, A + 2, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_append_tokens, g, A, A, A2, 0, None, 0) == K.KVARN_OK   # nothing to do
+    assert _code(K.kvarn_cache_set_pages, g, A, A2, 0, 1, 0) == K.KVARN_ERR_GEOM  # not paged
+    gp = K.geom(2, 2, 128, 32, 3, num_pages=5)
+    assert _code(K.kvarn_cache_set_pages, gp, A, A2, 3, 2, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_cache_set_pages, gp, A, A2, -1, 1, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_cache_set_pages, gp, A, 0, 0, 1, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_cache_set_pages, gp, A, A2 + 1, 0, 1, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_cache_set_pages, gp, A, A2, 4, 0, 0) == K.KVARN_OK
+    assert _code(K.kvarn_cache_bytes, K.geom(2, 2, 128, 32, 3, num_pages=-1)) == K.KVARN_ERR_GEOM
     # fused decode step: the attention's checks plus the appended token's pointers
     assert _code(K.kvarn_append_attn_decode, g, A, A2, A2, A2, 4, 0.0, 0, A, ws - 1, A2, 0) == K.KVARN_ERR_RANGE
     assert _code(K.kvarn_append_attn_decode, g, A, 0, A2, A2, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_NULL
