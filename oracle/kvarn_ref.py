@@ -194,27 +194,28 @@ def normalize(w, r16, c16) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- 2-bit grid
-def grid(y) -> tuple[np.ndarray, np.ndarray, bool]:
+def grid(y, bits: int = 2) -> tuple[np.ndarray, np.ndarray, bool]:
     """Uniform 2-bit grid, one per channel over the tile's G tokens ([AP] 3.2: one scale
     per group of 32 or 64 entries; [RP]: a scale shared across tokens is what outlier
     tokens stretch). Reading: asymmetric min/max, levels z + s*{0,1,2,3},
-    s = (max - min)/3, both stored as fp16 (RNE, saturating)."""
+    s = (max - min)/3, both stored as fp16 (RNE, saturating). With bits = 3 or 4 (the
+    widths beyond the pages' 2) the same grid has 2^bits levels, s = (max - min)/(2^bits - 1)."""
     y = np.asarray(y, dtype=np.float64)
     mn = y.min(axis=-2)
     mx = y.max(axis=-2)
-    s16, sat_s = fp16_saturate((mx - mn) / 3.0)
+    s16, sat_s = fp16_saturate((mx - mn) / (2 ** bits - 1))
     z16, sat_z = fp16_saturate(mn)
     return s16, z16, bool(sat_s.any() or sat_z.any())
 
 
-def codes(y, s16, z16) -> np.ndarray:
-    """q = clamp(round_half_even((Y - z) / s), 0, 3); q = 0 in a channel whose s is 0."""
+def codes(y, s16, z16, bits: int = 2) -> np.ndarray:
+    """q = clamp(round_half_even((Y - z) / s), 0, 2^bits - 1); q = 0 in a channel whose s is 0."""
     y = np.asarray(y, dtype=np.float64)
     s = np.asarray(s16)[..., None, :]
     z = np.asarray(z16)[..., None, :]
     safe = np.where(s == 0, 1.0, s)
     u = (y - z) / safe
-    q = np.clip(np.rint(u), 0, 3)               # np.rint rounds half to even
+    q = np.clip(np.rint(u), 0, 2 ** bits - 1)   # np.rint rounds half to even
     return np.where(s == 0, 0, q).astype(np.uint8)
 
 
@@ -225,13 +226,13 @@ def pre_rounding(y, s16, z16) -> np.ndarray:
     return (np.asarray(y) - z) / np.where(s == 0, 1.0, s)
 
 
-def quantize_tile(w, n_it: int, variant: int = 0) -> dict:
+def quantize_tile(w, n_it: int, variant: int = 0, bits: int = 2) -> dict:
     """Rotated tile(s) w[..., G, D] -> stored scales, grid, codes (steps of [AP] 3.2)."""
     r, c = varn(w, n_it, variant)
     r16, c16, clamped = stored_scales(r, c)
     y = normalize(w, r16, c16)
-    s16, z16, sat = grid(y)
-    q = codes(y, s16, z16)
+    s16, z16, sat = grid(y, bits)
+    q = codes(y, s16, z16, bits)
     return dict(r=r, c=c, r16=r16, c16=c16, y=y, s16=s16, z16=z16, q=q,
                 flags=(FLAG_SCALE_CLAMPED if (clamped or sat) else 0))
 
@@ -244,9 +245,9 @@ def dequantize_tile(q, r16, c16, s16, z16) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- tile record (format v1)
-def record_bytes(g: int, d: int) -> int:
-    """codes G*D/4 | r fp16[G] | c fp16[D] | s fp16[D] | z fp16[D]."""
-    return g * d // 4 + 2 * g + 6 * d
+def record_bytes(g: int, d: int, bits: int = 2) -> int:
+    """codes G*D*bits/8 | r fp16[G] | c fp16[D] | s fp16[D] | z fp16[D]."""
+    return g * d * bits // 8 + 2 * g + 6 * d
 
 
 def k_code_position(j: int) -> tuple[int, int]:
@@ -257,7 +258,79 @@ def k_code_position(j: int) -> tuple[int, int]:
     return w, 4 * (m // 2) + m % 2 + 2 * d
 
 
-def pack_codes(q, stream: int) -> np.ndarray:
+def pack_codes(q, stream: int, bits: int = 2) -> np.ndarray:
+    """Codes of `bits` bits as bit planes: plane A (bits 0-1 of every code) in the 2-bit
+    layout below, then for bits = 4 plane B (bits 2-3) in the same 2-bit layout, or for
+    bits = 3 plane B (bit 2) in the 1-bit layout of pack_bit_plane."""
+    q = np.asarray(q, dtype=np.uint8)
+    if bits == 2:
+        return pack_2bit(q, stream)
+    plane_b = pack_2bit(q >> 2, stream) if bits == 4 else pack_bit_plane(q >> 2, stream)
+    return np.concatenate([pack_2bit(q & 3, stream), plane_b])
+
+
+def unpack_codes(b, g: int, d: int, stream: int, bits: int = 2) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    if bits == 2:
+        return unpack_2bit(b, g, d, stream)
+    n = g * d // 4
+    hi = unpack_2bit(b[n:], g, d, stream) if bits == 4 else unpack_bit_plane(b[n:], g, d, stream)
+    return (unpack_2bit(b[:n], g, d, stream) | (hi << 2)).astype(np.uint8)
+
+
+def k_bit_position(j: int) -> tuple[int, int]:
+    """1-bit plane, K stream: (32-bit word u, bit p) of channel j of a token. Word u pairs the
+    2-bit layout's words 2u and 2u + 1: the channel in word w, slot k sits at bit
+    4 (k // 2) + k % 2 + 2 (w % 2) of word w // 2."""
+    w, k = k_code_position(j)
+    return w // 2, 4 * (k // 2) + k % 2 + 2 * (w % 2)
+
+
+def v_bit_position(t: int, j: int, g: int) -> tuple[int, int]:
+    """1-bit plane, V stream: (32-bit word index, bit) of code (t, j). With j = 16 blk + c,
+    blk = i + 4 hh (i < 4), i = 2 ip + ii and t = 8 o + 2 n + par: word
+    (16 ip + c) * G/8 + o, bit 4 (n + 4 hh) + par + 2 ii. A word holds the 8 tokens of an
+    octet for the four channels c + 16 {2ip, 2ip + 1, 2ip + 4, 2ip + 5}."""
+    blk, c = j // 16, j % 16
+    i, hh = blk % 4, blk // 4
+    ip, ii = i // 2, i % 2
+    o, u = t // 8, t % 8
+    n, par = u // 2, u % 2
+    return (16 * ip + c) * (g // 8) + o, 4 * (n + 4 * hh) + par + 2 * ii
+
+
+def pack_bit_plane(qb, stream: int) -> np.ndarray:
+    """One bit per code, 32 per little-endian word: K token t owns words 4t .. 4t + 3
+    (k_bit_position); V words as v_bit_position. G*D/8 bytes either way."""
+    qb = np.asarray(qb, dtype=np.uint32) & 1
+    g, d = qb.shape
+    words = np.zeros(g * d // 32, dtype=np.uint32)
+    for t in range(g):
+        for j in range(d):
+            if stream == 0:
+                u, p = k_bit_position(j)
+                words[(d // 32) * t + u] |= np.uint32(qb[t, j] << p)
+            else:
+                wi, p = v_bit_position(t, j, g)
+                words[wi] |= np.uint32(qb[t, j] << p)
+    return words.view(np.uint8)
+
+
+def unpack_bit_plane(b, g: int, d: int, stream: int) -> np.ndarray:
+    words = np.asarray(b, dtype=np.uint8).view(np.uint32)
+    q = np.zeros((g, d), dtype=np.uint8)
+    for t in range(g):
+        for j in range(d):
+            if stream == 0:
+                u, p = k_bit_position(j)
+                q[t, j] = (words[(d // 32) * t + u] >> p) & 1
+            else:
+                wi, p = v_bit_position(t, j, g)
+                q[t, j] = (words[wi] >> p) & 1
+    return q
+
+
+def pack_2bit(q, stream: int) -> np.ndarray:
     """Four 2-bit codes per byte, slot k of a byte at bits 2k..2k+1 (little-endian words).
     K (stream 0): token t owns bytes t*D/4 .. t*D/4 + D/4 - 1, read as D/16 words;
                   channel j sits in word w, slot p (k_code_position): byte t*D/4 + 4w + p//4,
@@ -276,7 +349,7 @@ def pack_codes(q, stream: int) -> np.ndarray:
     return b.reshape(-1)
 
 
-def unpack_codes(b, g: int, d: int, stream: int) -> np.ndarray:
+def unpack_2bit(b, g: int, d: int, stream: int) -> np.ndarray:
     b = np.asarray(b, dtype=np.uint8)
     if stream == 0:
         rows = b.reshape(g, d // 4)
@@ -289,17 +362,17 @@ def unpack_codes(b, g: int, d: int, stream: int) -> np.ndarray:
     return parts.reshape(d, g).T.astype(np.uint8)
 
 
-def pack_record(q, r16, c16, s16, z16, stream: int) -> np.ndarray:
-    return np.concatenate([pack_codes(q, stream),
+def pack_record(q, r16, c16, s16, z16, stream: int, bits: int = 2) -> np.ndarray:
+    return np.concatenate([pack_codes(q, stream, bits),
                            fp16_bits(r16).view(np.uint8), fp16_bits(c16).view(np.uint8),
                            fp16_bits(s16).view(np.uint8), fp16_bits(z16).view(np.uint8)])
 
 
-def unpack_record(rec, g: int, d: int, stream: int) -> dict:
+def unpack_record(rec, g: int, d: int, stream: int, bits: int = 2) -> dict:
     rec = np.asarray(rec, dtype=np.uint8)
-    n = g * d // 4
+    n = g * d * bits // 8
     f = lambda off, k: fp16_from_bits(rec[off:off + 2 * k].view(np.uint16))  # noqa: E731
-    return dict(q=unpack_codes(rec[:n], g, d, stream), r16=f(n, g), c16=f(n + 2 * g, d),
+    return dict(q=unpack_codes(rec[:n], g, d, stream, bits), r16=f(n, g), c16=f(n + 2 * g, d),
                 s16=f(n + 2 * g + 2 * d, d), z16=f(n + 2 * g + 4 * d, d))
 
 
@@ -322,7 +395,7 @@ class Geom:
     # layout
     @property
     def tr(self):
-        return record_bytes(self.group, self.head_dim)
+        return record_bytes(self.group, self.head_dim, self.bits)
 
     @property
     def paged(self):
@@ -462,11 +535,11 @@ def _quantize_stream(x, sigma, g: Geom, stream: int):
     lead = x.shape[:-2]
     nt = x.shape[-2] // g.group
     w = apply_rotation(x, sigma, g.variant).reshape(lead + (nt, g.group, g.head_dim))
-    t = quantize_tile(w, g.varn_iters, g.variant)
+    t = quantize_tile(w, g.varn_iters, g.variant, g.bits)
     recs = np.zeros(lead + (nt, g.tr), dtype=np.uint8)
     for idx in np.ndindex(*(lead + (nt,))):
         recs[idx] = pack_record(t["q"][idx], t["r16"][idx], t["c16"][idx], t["s16"][idx],
-                                t["z16"][idx], stream)
+                                t["z16"][idx], stream, g.bits)
     return recs, t["flags"]
 
 
@@ -565,7 +638,7 @@ def stream_values(cache: Cache, b: int, h: int, s: int, rotated: bool = False, w
         if rec is None:
             present[tile * g.group:(tile + 1) * g.group] = False
             continue
-        u = unpack_record(rec, g.group, g.head_dim, s)
+        u = unpack_record(rec, g.group, g.head_dim, s, g.bits)
         w = dequantize_tile(u["q"], u["r16"], u["c16"], u["s16"], u["z16"])
         out[tile * g.group:(tile + 1) * g.group] = w if rotated else undo_rotation(w, cache.sigma, g.variant)
     tail = cache.tail(b, h, s).astype(np.float64)
