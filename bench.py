@@ -30,12 +30,12 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def record_bytes(g: int) -> int:
-    return g * 128 // 4 + 2 * g + 6 * 128
+def record_bytes(g: int, bits: int = 2) -> int:
+    return g * 128 * bits // 8 + 2 * g + 6 * 128
 
 
-def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32, n_it=3):
-    g = K.geom(1, H, T, G, n_it)
+def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32, n_it=3, bits=2):
+    g = K.geom(1, H, T, G, n_it, bits=bits)
     sig = synth.sign_vector(0)
     log(f"prefill workload: {layers} layers x B=1 x T={T} x Hkv={H}, G={G}, iters={n_it}")
     ks, vs, caches = [], [], []
@@ -64,7 +64,7 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
     wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     bytes_in = 2 * 2 * T * H * 128                       # K and V, bf16
-    bytes_out = 2 * H * (T // G) * record_bytes(G)       # tile records
+    bytes_out = 2 * H * (T // G) * record_bytes(G, bits)  # tile records
     flags = K.kvarn_cache_flags(caches[0])
     del ks, vs, caches
     torch.cuda.empty_cache()
@@ -73,8 +73,8 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
 
 
 def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40, T0=16384, cap=17408, G=32,
-                 n_it=3, pool=128):
-    g = K.geom(B, H, cap, G, n_it)
+                 n_it=3, pool=128, bits=2):
+    g = K.geom(B, H, cap, G, n_it, bits=bits)
     sig = synth.sign_vector(0)
     log(f"decode workload: {layers} layers x B={B} x Hkv={H} x Hq={Hq}, {T0} prior tokens, {steps} timed steps")
     k0, v0 = synth.kv_device(synth.sub_seed(4, 0, 0), B, T0, H)
@@ -178,7 +178,7 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
     ctx_mid = T0 + warmup + steps // 2
     # attention bytes per layer-step: K and V records of the full tiles + tail rows + q + out
     nfull = ctx_mid // G
-    attn_bytes = B * H * (2 * nfull * record_bytes(G) + 2 * (ctx_mid % G) * 256) + B * Hq * (256 + 512)
+    attn_bytes = B * H * (2 * nfull * record_bytes(G, bits) + 2 * (ctx_mid % G) * 256) + B * Hq * (256 + 512)
     del caches
     torch.cuda.empty_cache()
     return dict(wall=wall, steps=steps, B=B, layers=layers, attn_ms=attn_ms, attn_bytes=attn_bytes, flags=flags,
@@ -313,6 +313,8 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=5, help="layers of the prefill workload the oracle runs")
     ap.add_argument("--no-copy", action="store_true", help="skip the 4 GiB device copy ceiling")
     ap.add_argument("--no-bf16", action="store_true", help="skip the plain bf16 decode-attention baseline")
+    ap.add_argument("--bits", type=int, default=2, choices=(2, 3, 4),
+                    help="code width of both workloads (the pages' method, and the headline, use 2)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -329,7 +331,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     log("device", torch.cuda.get_device_name(0))
-    pf = bench_prefill(K, synth, torch, args.steps, args.warmup)
+    pf = bench_prefill(K, synth, torch, args.steps, args.warmup, bits=args.bits)
     ms_step = pf["wall"] * 1e3 / args.steps
     value = pf["layers"] * pf["bytes_in"] / (ms_step * 1e-3) / 1e9
     total_gbs = pf["layers"] * (pf["bytes_in"] + pf["bytes_out"]) / (ms_step * 1e-3) / 1e9
@@ -344,13 +346,15 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "llama3.1-8b-shaped KV prefill quantize", "layers": pf["layers"], "batch": 1,
                    "tokens": pf["T"], "kv_heads": pf["H"], "head_dim": 128, "group": pf["G"],
-                   "varn_iters": pf["n_it"], "bits": 2, "input": "bf16, outlier channels x20, 5% lognormal tokens"},
+                   "varn_iters": pf["n_it"], "bits": args.bits,
+                   "input": "bf16, outlier channels x20, 5% lognormal tokens"},
         "hbm_frac_step": round(total_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES),
+                     "traffic": (counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES)
+                                 if args.bits == 2 else None),
                      "traffic_unit": "bytes/launch",
-                     "kernel": "prefill_kernel<1,false,false>", "bytes_per_launch": pf["bytes_in"] + pf["bytes_out"],
+                     "kernel": "prefill_kernel<1,false,false>" if args.bits == 2 else "prefill_kernel<1,false,true>", "bytes_per_launch": pf["bytes_in"] + pf["bytes_out"],
                      "avg_launch_us": round(avg_launch * 1e3, 2), "median_launch_us": round(lm[len(lm) // 2] * 1e3, 2)},
         "flags": pf["flags"],
     }
@@ -358,7 +362,7 @@ def main():
         res["copy_ceiling"] = copy_ceiling(torch)
         log(f"copy ceiling: {res['copy_ceiling']}")
     if not args.no_decode:
-        dc = bench_decode(K, synth, torch, args.decode_steps)
+        dc = bench_decode(K, synth, torch, args.decode_steps, bits=args.bits)
         tok_s = dc["B"] * dc["steps"] / dc["wall"]
         am = sorted(dc["attn_ms"])
         a_avg = sum(am) / len(am)
@@ -369,11 +373,12 @@ def main():
             "context_at_start": dc["ctx_start"], "attn_avg_us": round(a_avg * 1e3, 2),
             "attn_GBps": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9, 1),
             "attn_frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "flags": dc["flags"],
-            "roofline": {"bound": "hbm", "kernel": "attn_kernel<32> + merge_kernel",
+            "roofline": {"bound": "hbm", "kernel": f"attn_kernel<32, {args.bits}> + merge_kernel",
                          "achieved": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "bytes_per_launch": dc["attn_bytes"],
-                         "traffic": counted_traffic("attn_kernel_phi4_decode_pmc.txt", ATTN_SOURCES),
+                         "traffic": (counted_traffic("attn_kernel_phi4_decode_pmc.txt", ATTN_SOURCES)
+                                     if args.bits == 2 else None),
                          "traffic_unit": "bytes/launch (tile pass)"}}
         ap = sorted(dc["append_ms"])
         res["decode"]["graph_tokens_per_s"] = round(dc["B"] * dc["steps"] / dc["graph_wall"], 1)

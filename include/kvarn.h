@@ -21,7 +21,8 @@
  *   one (batch, kv head, stream); r (per token) and c (per channel) are stored as
  *   fp16 clamped to [2^-14, 65504]; the 2-bit grid is per channel over the tile's
  *   G tokens, asymmetric min/max, levels z + s*{0,1,2,3}, s and z fp16;
- *   codes round half to even and clamp to [0, 3].
+ *   codes round half to even and clamp to [0, 3] (3- and 4-bit codes: 2^bits levels,
+ *   s = (max - min)/(2^bits - 1), clamp to [0, 2^bits - 1]).
  *
  * Cache buffer, format v1 (one caller-owned buffer per layer, 256-B aligned regions):
  *   header  align256(512 + 8*B*Hkv) bytes:
@@ -40,14 +41,21 @@
  *           tokens out, dequantization writes zeros).
  *   tail    [B][Hkv][2][G][D] fp16, unrotated tokens of the group being filled,
  *           slot = token index mod G.
- *   Tile record TR = G*D/4 + 2G + 6D bytes (1856 at G=32, 2944 at G=64):
- *     codes  G*D/4 B, four 2-bit codes per byte, slot k of a byte at bits 2k..2k+1:
+ *   Tile record TR = G*D*bits/8 + 2G + 6D bytes (2 bits: 1856 at G=32, 2944 at G=64):
+ *     codes  G*D*bits/8 B. 2-bit codes: four per byte, slot k of a byte at bits 2k..2k+1:
  *            K: token t owns the D/4 bytes from t*D/4 on, read as D/16 little-endian
  *               32-bit words; channel j = 16m + 2w + d (m < 8, d < 2) sits in word w
  *               at slot 4(m/2) + m%2 + 2d, i.e. byte t*D/4 + 4w + m/2, bits
  *               2(m%2 + 2d): each byte holds the channel pairs (2i, 2i+1) of two
  *               channel blocks of 16;
  *            V: code(t,j) in byte j*G/4 + t/4, bits 2*(t%4) (tokens fastest);
+ *            3- and 4-bit codes q = qA + 4 qB: plane A (qA = bits 0..1) in the 2-bit
+ *            layout above, then plane B. 4-bit: qB (bits 2..3) in the 2-bit layout.
+ *            3-bit: qB (bit 2) one bit per code, 32-bit words: K: channel j of token
+ *            t, in word w slot k of the 2-bit layout, at word 4t + w/2, bit
+ *            4(k/2) + k%2 + 2(w%2); V: code (t = 8o + 2n + par, j = 16 blk + c with
+ *            blk = i + 4hh, i = 2ip + ii) at word (16 ip + c) G/8 + o, bit
+ *            4(n + 4hh) + par + 2ii. The grid has 2^bits levels.
  *     r fp16[G], c fp16[D], s fp16[D], z fp16[D].
  *   A tile token dequantizes as x_hat = (r_t c_j (z_j + s_j q_tj))_j H_D^T.
  *
@@ -83,7 +91,7 @@ typedef enum {
 } kvarn_status;
 
 /* Geometry of one layer cache. v1 supports head_dim = 128, group in {32, 64},
- * bits = 2, 0 <= varn_iters <= 8, capacity a positive multiple of group,
+ * bits in {2, 3, 4}, 0 <= varn_iters <= 8, capacity a positive multiple of group,
  * variant a combination of the KVARN_VARIANT_* bits below (0 = the method),
  * num_pages >= 0 (see the paged layout above). */
 typedef struct {
@@ -93,7 +101,7 @@ typedef struct {
     int32_t capacity;       /* max tokens per sequence                         */
     int32_t group;          /* G   tokens per tile (the pages' 32 or 64)       */
     int32_t varn_iters;     /* VarN iterations (token pass + channel pass)     */
-    int32_t bits;           /* code width (2)                                  */
+    int32_t bits;           /* code width: 2 (the pages'), 3 or 4              */
     int32_t variant;        /* ablation bits, 0 for KVarN as defined           */
     int32_t num_pages;      /* 0: records stored per sequence; > 0: paged      */
 } kvarn_geom;

@@ -16,7 +16,7 @@ kvarn_status check_geom(const kvarn_geom* g) {
   if (g->batch <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0 || g->capacity <= 0 || g->group <= 0 ||
       g->varn_iters < 0 || g->bits <= 0 || g->num_pages < 0)
     return KVARN_ERR_GEOM;
-  if (g->head_dim != kD || (g->group != 32 && g->group != 64) || g->bits != 2 || g->varn_iters > 8)
+  if (g->head_dim != kD || (g->group != 32 && g->group != 64) || g->bits < 2 || g->bits > 4 || g->varn_iters > 8)
     return KVARN_ERR_UNSUPPORTED;
   if (g->variant & ~(int32_t)(KVARN_VARIANT_NO_ROTATION | KVARN_VARIANT_NO_CHANNEL_PASS | KVARN_VARIANT_NO_TOKEN_PASS |
                               KVARN_VARIANT_CENTERED))
@@ -75,7 +75,7 @@ const char* kvarn_status_str(kvarn_status s) {
     case KVARN_ERR_NULL: return "null pointer";
     case KVARN_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case KVARN_ERR_GEOM: return "inconsistent geometry";
-    case KVARN_ERR_UNSUPPORTED: return "unsupported geometry (v1: head_dim 128, group 32/64, 2 bits, <= 8 VarN iterations, variant bits 1|2|4|8)";
+    case KVARN_ERR_UNSUPPORTED: return "unsupported geometry (v1: head_dim 128, group 32/64, 2-4 bits, <= 8 VarN iterations, variant bits 1|2|4|8)";
     case KVARN_ERR_RANGE: return "size out of range";
     case KVARN_ERR_DEVICE: return "HIP runtime error";
   }

@@ -64,6 +64,13 @@ template <int BY>
 __device__ __forceinline__ uint32_t cvt2(uint32_t plane) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(plane, 2.0f, BY));
 }
+// The same for plane B of 3- and 4-bit codes, worth 4x: a nibble q_B (0..3, or 0..1 for
+// the 1-bit plane) is the e2m1 value q_B/2, converted with scale 8 to 4 q_B.
+template <int BY>
+__device__ __forceinline__ uint32_t cvt2_hi(uint32_t plane) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(plane, 8.0f, BY));
+}
+constexpr uint32_t kBit = 0x11111111u;  // bit 0 of each nibble
 __device__ __forceinline__ h8v as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint4 v = make_uint4(a, b, c, d);
   return __builtin_bit_cast(h8v, v);
@@ -158,11 +165,17 @@ __device__ __forceinline__ float reduce4(const float (&v)[4], int c) {
 //  * V MFMA i (i < 4): columns = channels 16 i + c (rows 0..7 of A) and 16 (i+4) + c
 //    (rows 8..15), lane (c, g) folds rows 4 (g%2) .. +3 of block i + 4 (g/2), i.e. query
 //    heads 2 (g%2) + {0, 1} of channel 16 (i + 4 (g/2)) + c.
-template <int G>
+//
+// BITS = 3 or 4: the codes are plane A (bits 0..1, the 2-bit layout) plus 4 x plane B
+// (4-bit: the 2-bit layout at PB; 3-bit: the 1-bit layout, whose words give the nibble
+// planes of two 2-bit words by shifts and masks). Plane B runs through the same MFMAs
+// with codes worth 4 q_B, accumulated into the same sums.
+template <int G, int BITS>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int NKB = G / 32;  // 32-token blocks per tile
   constexpr int NMB = 2 * NKB; // 16-token K blocks per tile
-  constexpr int RO = G * kD / 4, CO = RO + 2 * G, SO = CO + 2 * kD, ZO = SO + 2 * kD;
+  constexpr int PB = G * kD / 4;  // plane B of 3- and 4-bit codes
+  constexpr int RO = G * kD * BITS / 8, CO = RO + 2 * G, SO = CO + 2 * kD, ZO = SO + 2 * kD;
   __shared__ AttnLds sh;
   const Layout& L = a.L;
   const int lane = threadIdx.x & 63;
@@ -251,6 +264,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     uint2 kc[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) kc[mb] = *reinterpret_cast<const uint2*>(rk + krow[mb] * 32 + 8 * g);
+    uint2 kcb[BITS > 2 ? NMB : 1];  // plane B: two 2-bit words (BITS 4) or one 1-bit word in .x
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) kcb[mb] = *reinterpret_cast<const uint2*>(rk + PB + krow[mb] * 32 + 8 * g);
+    } else if constexpr (BITS == 3) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+        kcb[mb] = make_uint2(*reinterpret_cast<const uint32_t*>(rk + PB + krow[mb] * 16 + 4 * g), 0u);
+    }
     const uint32_t kcs = *reinterpret_cast<const uint32_t*>(rk + CO + 4 * lane);
     const uint32_t kss = *reinterpret_cast<const uint32_t*>(rk + SO + 4 * lane);
     const uint32_t kzs = *reinterpret_cast<const uint32_t*>(rk + ZO + 4 * lane);
@@ -272,6 +294,25 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const uint32_t hi = *reinterpret_cast<const uint16_t*>(rv + (16 * (i + 4) + c) * (G / 4) + 2 * (4 * kb + g));
         vq[i][kb] = lo | (hi << 16);
       }
+    // plane B of V: BITS 4 as vq; BITS 3 one 1-bit word per channel pair {i, i + 1} (i even)
+    uint32_t vqb[BITS > 2 ? 4 : 1][NKB];
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(rv + PB + (16 * i + c) * (G / 4) + 2 * (4 * kb + g));
+          const uint32_t hi =
+              *reinterpret_cast<const uint16_t*>(rv + PB + (16 * (i + 4) + c) * (G / 4) + 2 * (4 * kb + g));
+          vqb[i][kb] = lo | (hi << 16);
+        }
+    } else if constexpr (BITS == 3) {
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          vqb[ip][kb] = *reinterpret_cast<const uint32_t*>(rv + PB + 4 * ((16 * ip + c) * (G / 8) + 4 * kb + g));
+    }
 
     // ---- K-side factors of this lane's channel pair; per-tile scale of the a-values
     const float cs0 = mul_f16<0>(kcs, kss), cs1 = mul_f16<1>(kcs, kss);
@@ -325,6 +366,26 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av3, bk[3], acc, 0, 0, 0);
         asm volatile("" : "+v"(acc) : "v"(av0), "v"(av1), "v"(av2), "v"(av3), "v"(bk[0]), "v"(bk[1]), "v"(bk[2]),
                      "v"(bk[3]));
+        if constexpr (BITS > 2) {
+          uint32_t eb0, ob0, eb1, ob1;  // nibble planes of plane B, as e0, o0, e1, o1 above
+          if constexpr (BITS == 4) {
+            const uint32_t y0 = kcb[2 * kb + h2].x, y1 = kcb[2 * kb + h2].y;
+            eb0 = y0 & kNib, ob0 = (y0 >> 2) & kNib, eb1 = y1 & kNib, ob1 = (y1 >> 2) & kNib;
+          } else {
+            const uint32_t y = kcb[2 * kb + h2].x;
+            eb0 = y & kBit, ob0 = (y >> 1) & kBit, eb1 = (y >> 2) & kBit, ob1 = (y >> 3) & kBit;
+          }
+          const h8v bv0 = as_h8(cvt2_hi<0>(eb0), cvt2_hi<0>(ob0), cvt2_hi<1>(eb0), cvt2_hi<1>(ob0));
+          const h8v bv1 = as_h8(cvt2_hi<2>(eb0), cvt2_hi<2>(ob0), cvt2_hi<3>(eb0), cvt2_hi<3>(ob0));
+          const h8v bv2 = as_h8(cvt2_hi<0>(eb1), cvt2_hi<0>(ob1), cvt2_hi<1>(eb1), cvt2_hi<1>(ob1));
+          const h8v bv3 = as_h8(cvt2_hi<2>(eb1), cvt2_hi<2>(ob1), cvt2_hi<3>(eb1), cvt2_hi<3>(ob1));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv0, bk[0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv1, bk[1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv2, bk[2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv3, bk[3], acc, 0, 0, 0);
+          asm volatile("" : "+v"(acc) : "v"(bv0), "v"(bv1), "v"(bv2), "v"(bv3), "v"(bk[0]), "v"(bk[1]),
+                       "v"(bk[2]), "v"(bk[3]));
+        }
         sc[h2] = acc;
       }
       // r of this lane's tokens 32 kb + 8 g + tau(2 i + parity): dwords 2 (i/2) + parity
@@ -408,6 +469,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw1[kb], b1, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw2[kb], b2, acc, 0, 0, 0);
         asm volatile("" : "+v"(acc) : "v"(aw1[kb]), "v"(aw2[kb]), "v"(b1), "v"(b2));
+        if constexpr (BITS > 2) {
+          uint32_t eb, odb;
+          if constexpr (BITS == 4) {
+            const uint32_t y = vqb[i][kb];
+            eb = y & kNib, odb = (y >> 2) & kNib;
+          } else {
+            const uint32_t y = vqb[i >> 1][kb] >> (2 * (i & 1));
+            eb = y & kBit, odb = (y >> 1) & kBit;
+          }
+          const h8v c1 = as_h8(cvt2_hi<0>(eb), cvt2_hi<0>(odb), cvt2_hi<1>(eb), cvt2_hi<1>(odb));
+          const h8v c2 = as_h8(cvt2_hi<2>(eb), cvt2_hi<2>(odb), cvt2_hi<3>(eb), cvt2_hi<3>(odb));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw1[kb], c1, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw2[kb], c2, acc, 0, 0, 0);
+          asm volatile("" : "+v"(acc) : "v"(aw1[kb]), "v"(aw2[kb]), "v"(c1), "v"(c2));
+        }
       }
       cv[i] = acc;
     }
@@ -620,10 +696,16 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   const long long blocks = (long long)a.L.B * a.L.Hkv * a.nqg * a.nspan;
   if (blocks > 0) {
-    if (a.L.G == 32)
-      hipLaunchKernelGGL(attn_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    const dim3 grid((unsigned)blocks);
+    const int which = (a.L.G == 32 ? 0 : 3) + (a.L.bits - 2);
+    switch (which) {
+      case 0: hipLaunchKernelGGL((attn_kernel<32, 2>), grid, dim3(256), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((attn_kernel<32, 3>), grid, dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((attn_kernel<32, 4>), grid, dim3(256), 0, st, a); break;
+      case 3: hipLaunchKernelGGL((attn_kernel<64, 2>), grid, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((attn_kernel<64, 3>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((attn_kernel<64, 4>), grid, dim3(256), 0, st, a); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -634,7 +716,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(row_blocks + 2LL * a.L.B * a.L.Hkv));
-  const bool abl = a.L.variant != 0;
+  const bool abl = a.L.variant != 0 || a.L.bits != 2;  // the extended build
   if (a.L.G == 32) {
     if (abl)
       hipLaunchKernelGGL((merge_kernel<true, 1, true>), grid, dim3(256), 0, st, a);

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   } else if (tile < nfull) {
     const uint8_t* rec = a.cache + roff;
     const int G = L.G;
-    const int ro = G * kD / 4, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
+    const int ro = G * kD * L.bits / 8, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
     const int tw0 = (blk * 32) % G + rg * 8;
     float cj[8], sj[8], zj[8], ri[8], sg[8];
     widen8_f16(*reinterpret_cast<const uint4*>(rec + co + 16 * cg), cj);
@@ -86,6 +86,55 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         const uint32_t hq = *reinterpret_cast<const uint16_t*>(rec + (8 * cg + e) * (G / 4) + tw0 / 4);
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[i][e] = (float)((hq >> (2 * i)) & 3u);
+      }
+    }
+    // plane B of 3- and 4-bit codes (the code is plane A + 4 * plane B)
+    const uint8_t* pb = rec + G * kD / 4;
+    if (L.bits == 4) {  // the 2-bit layout again
+      if (s == 0) {
+        const int sbase = 2 * (4 * (cg >> 2) + ((cg >> 1) & 1));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 q4 = *reinterpret_cast<const uint4*>(pb + (tw0 + i) * 32 + 16 * (cg & 1));
+          const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[i][e] += 4.0f * (float)((qw[e >> 1] >> (sbase + 4 * (e & 1))) & 3u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hq = *reinterpret_cast<const uint16_t*>(pb + (8 * cg + e) * (G / 4) + tw0 / 4);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i][e] += 4.0f * (float)((hq >> (2 * i)) & 3u);
+        }
+      }
+    } else if (L.bits == 3) {  // the 1-bit layout
+      if (s == 0) {
+        // channel 8cg + e: 2-bit word wd = 4(cg%2) + e/2, slot k = 4(m/2) + m%2 + 2(e%2) with
+        // m = cg/2; its bit: word wd/2 of the token's four, bit 4(k/2) + k%2 + 2(wd%2)
+        const int m = cg >> 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 q4 = *reinterpret_cast<const uint4*>(pb + (tw0 + i) * 16);
+          const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int wd = 4 * (cg & 1) + (e >> 1), k = 4 * (m >> 1) + (m & 1) + 2 * (e & 1);
+            const int bit = 4 * (k >> 1) + (k & 1) + 2 * (wd & 1);
+            w[i][e] += 4.0f * (float)((qw[wd >> 1] >> bit) & 1u);
+          }
+        }
+      } else {
+        // token t = 8o + 2n + par of channel 16 blk + c (blk = i4 + 4hh, i4 = 2ip + ii): word
+        // (16 ip + c) G/8 + o, bit 4(n + 4hh) + par + 2ii; this lane's 8 tokens are one octet
+        const int blk = cg >> 1, i4 = blk & 3, hh = blk >> 2, ip = i4 >> 1, ii = i4 & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int cc = 8 * (cg & 1) + e;
+          const uint32_t word = *reinterpret_cast<const uint32_t*>(pb + 4 * ((16 * ip + cc) * (G / 8) + tw0 / 8));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i][e] += 4.0f * (float)((word >> (4 * ((i >> 1) + 4 * hh) + (i & 1) + 2 * ii)) & 1u);
+        }
       }
     }
     const bool idr = (L.variant & KVARN_VARIANT_NO_ROTATION) != 0;  // uniform

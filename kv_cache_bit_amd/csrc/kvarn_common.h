@@ -29,6 +29,7 @@ struct Layout {
   int B, Hkv, cap, G, n_it, tiles;  // tiles = cap / G
   int variant;                      // KVARN_VARIANT_* bits
   int num_pages;                    // 0: per-sequence records
+  int bits;                         // code width: 2, 3 or 4
   int tr;                           // tile record bytes
   long long header, map_off, tail_off, total;
 
@@ -77,8 +78,9 @@ inline __host__ Layout make_layout(const kvarn_geom& g) {
   L.n_it = g.varn_iters;
   L.variant = g.variant;
   L.num_pages = g.num_pages;
+  L.bits = g.bits;
   L.tiles = g.capacity / g.group;
-  L.tr = g.group * kD / 4 + 2 * g.group + 6 * kD;
+  L.tr = g.group * kD * g.bits / 8 + 2 * g.group + 6 * kD;
   L.map_off = kHdrFixed + 8LL * g.batch * g.num_kv_heads;
   L.header = align256(L.map_off + (g.num_pages > 0 ? 4LL * g.batch * L.tiles : 0));
   const long long pool = g.num_pages > 0 ? (long long)g.num_pages * g.num_kv_heads * 2 * L.tr

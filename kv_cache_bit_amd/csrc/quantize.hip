@@ -97,11 +97,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     dw = (valid && pw) ? pw + doff : nullptr;
     dy = (valid && py) ? py + doff : nullptr;
   }
-  tile_finish<NW, DBG, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, dw, dy, dstride);
+  tile_finish<NW, DBG, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, dw, dy, dstride);
   if (valid) {
     const long long ro = record_at(a.cache, L, b, h, tile, s);
     if (ro >= 0)
-      copy_record<NW>(sh, a.cache + ro, lane, sub);
+      copy_record<NW>(sh, a.cache + ro, lane, sub, L.tr);
     else
       flags |= KVARN_FLAG_UNMAPPED;
     raise_flags(hdr, flags);
@@ -180,11 +180,11 @@ __global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
   }
   float p[2][8][4];
   const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
-  tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, nullptr, nullptr, 0);
+  tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr, nullptr, 0);
   if (valid) {
     const long long ro = record_at(a.cache, L, b, h, tile, s);
     if (ro >= 0)
-      copy_record<NW>(sh, a.cache + ro, lane, sub);
+      copy_record<NW>(sh, a.cache + ro, lane, sub, L.tr);
     else
       flags |= KVARN_FLAG_UNMAPPED;
     raise_flags(hdr, flags);
@@ -220,7 +220,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const long long tail_blocks = (2LL * a.L.B * a.L.Hkv + 3) / 4;
   const dim3 grid((unsigned)(tile_blocks + tail_blocks));
   const bool dbg = a.wk || a.wv || a.yk || a.yv;
-  const bool abl = a.L.variant != 0;
+  const bool abl = a.L.variant != 0 || a.L.bits != 2;  // the extended build
   const int which = (a.L.G == 32 ? 0 : 4) + (dbg ? 2 : 0) + (abl ? 1 : 0);
   switch (which) {
     case 0: hipLaunchKernelGGL((prefill_kernel<1, false, false>), grid, dim3(256), 0, st, a); break;
@@ -237,7 +237,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(2LL * a.L.B * a.L.Hkv));
-  const bool abl = a.L.variant != 0;
+  const bool abl = a.L.variant != 0 || a.L.bits != 2;  // the extended build
   if (a.L.G == 32) {
     if (abl)
       hipLaunchKernelGGL((append_kernel<1, true>), grid, dim3(64), 0, st, a);
@@ -256,7 +256,7 @@ hipError_t launch_tokens(const TokensArgs& a, hipStream_t st) {
   const int tpw = 4 / (a.L.G / 32);
   if (a.jobs > 0) {
     const dim3 grid((unsigned)((a.jobs + tpw - 1) / tpw));
-    const bool abl = a.L.variant != 0;
+    const bool abl = a.L.variant != 0 || a.L.bits != 2;  // the extended build
     if (a.L.G == 32) {
       if (abl)
         hipLaunchKernelGGL((tokens_tile_kernel<1, true>), grid, dim3(256), 0, st, a);

@@ -329,7 +329,7 @@ __device__ __forceinline__ void tile_sync() {
 template <int NW>
 struct TileLds {
   static constexpr int G = 32 * NW;
-  static constexpr int TR = G * kD / 4 + 2 * G + 6 * kD;
+  static constexpr int TR = G * kD / 2 + 2 * G + 6 * kD;  // room for the widest (4-bit) record
   uint8_t rec[TR] __attribute__((aligned(16)));
   float red_a[NW][kD];
   float red_b[NW][kD];
@@ -434,19 +434,15 @@ __device__ void centered_varn(const h8v (&av)[2][4], const Frags& hf, bool idr, 
 }
 
 // ----------------------------------------------------------------------------- codes
-// Writes the 2-bit codes of this wave's block into the record in LDS.
+// The 2-bit layout of one plane of codes, written into `base` (the record in LDS):
 // K: word w = c/2 of token t holds channel 16nb + c in slot 4(nb/2) + nb%2 + 2(c%2).
 // V: byte j*G/4 + t/4 holds tokens 4(t/4) .. +3 of channel j, token t%4 in slot t%4.
-template <int NW, bool CLAMP>
-__device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (&al)[8], const float (&ga)[8],
-                                           int stream, int sub, int g, int c, TileLds<NW>& sh) {
+// code(y, nb) gives the plane's 2-bit value in bits 0..1; bits from 22 up may hold junk
+// (they are shifted out of the bytes kept).
+template <int NW, typename F>
+__device__ __forceinline__ void emit_plane2(const f4v (&acc)[2][8], F code, int stream, int ttile0, int c,
+                                            uint8_t* base) {
   constexpr int G = 32 * NW;
-  const int ttile0 = sub * 32 + 4 * g;  // token of (mb = 0, i = 0) inside the tile
-  auto code = [&](float y, int nb) -> uint32_t {
-    float t = fmaf(y, al[nb], ga[nb]);
-    if constexpr (CLAMP) t = __builtin_amdgcn_fmed3f(t, 0.0f, 3.0f);
-    return (uint32_t)__float_as_int(t + 12582912.0f);  // 1.5 * 2^23
-  };
   if (stream == 0) {
     // lane c's channel 16nb + c goes to word c/2, slot 4(nb/2) + nb%2 + 2(c%2): the even
     // lane assembles bits 8(nb/2) + 2(nb%2) (blocks 0..3 in bytes 0..1, 4..7 in bytes
@@ -464,7 +460,7 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
         const uint32_t h = __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // bytes lo.0 lo.1 hi.0 hi.1
         const uint32_t hp = (uint32_t)__builtin_amdgcn_mov_dpp((int)h, kQx1, 0xF, 0xF, true);
         if ((c & 1) == 0)
-          *reinterpret_cast<uint32_t*>(sh.rec + (ttile0 + 16 * mb + i) * 32 + 2 * c) = h | (hp << 4);
+          *reinterpret_cast<uint32_t*>(base + (ttile0 + 16 * mb + i) * 32 + 2 * c) = h | (hp << 4);
       }
   } else {
 #pragma unroll
@@ -474,9 +470,82 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
         uint32_t h = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) h |= code(acc[mb][nb][i], nb) << (2 * i);
-        sh.rec[(16 * nb + c) * (G / 4) + (ttile0 + 16 * mb) / 4] = (uint8_t)h;
+        base[(16 * nb + c) * (G / 4) + (ttile0 + 16 * mb) / 4] = (uint8_t)h;
       }
   }
+}
+
+// The 1-bit plane of 3-bit codes (their bit 2), ORed into the zeroed plane at `base`:
+// K: channel j of token t sits in the 2-bit layout's word w, slot k; its bit goes to word
+//    4t + w/2, bit 4(k/2) + k%2 + 2(w%2). For lane c's channel 16nb + c that is word
+//    4t + c/4, bit 8(nb/2) + nb%2 + 4(c%2) + 2((c/2)%2).
+// V: token t = 8o + 2n + par of channel 16 blk + c, blk = i + 4hh, i = 2ip + ii: word
+//    (16 ip + c) G/8 + o, bit 4(n + 4hh) + par + 2ii. This lane's tokens 4(g%2) + i4 of
+//    an octet fill nibbles 2(g%2) + i4/2 (+ 4hh); rows g and g^1 share the word.
+template <int NW, typename F>
+__device__ __forceinline__ void emit_bit_plane(const f4v (&acc)[2][8], F bit, int stream, int ttile0, int g,
+                                               int c, uint8_t* base) {
+  constexpr int G = 32 * NW;
+  if (stream == 0) {
+    const int off = 4 * (c & 1) + 2 * ((c >> 1) & 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) v |= bit(acc[mb][nb][i], nb) << (8 * (nb >> 1) + (nb & 1));
+        atomicOr(reinterpret_cast<uint32_t*>(base + (ttile0 + 16 * mb + i) * 16 + 4 * (c >> 2)), v << off);
+      }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) {
+            const int nb = 2 * ip + ii + 4 * hh;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+              v |= bit(acc[mb][nb][i4], nb) << (4 * (2 * (g & 1) + (i4 >> 1) + 4 * hh) + (i4 & 1) + 2 * ii);
+          }
+        const int o = (ttile0 + 16 * mb) / 8;
+        atomicOr(reinterpret_cast<uint32_t*>(base + 4 * ((16 * ip + c) * (G / 8) + o)), v);
+      }
+  }
+}
+
+// Writes the codes of this wave's block into the record in LDS: 2-bit codes in the layout
+// of emit_plane2; 3- and 4-bit codes as plane A (bits 0..1, that layout) followed by
+// plane B (4-bit: bits 2..3 in the same layout; 3-bit: bit 2, emit_bit_plane).
+template <int NW, bool CLAMP>
+__device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (&al)[8], const float (&ga)[8],
+                                           int stream, int sub, int g, int c, TileLds<NW>& sh, int bits) {
+  constexpr int G = 32 * NW;
+  const int ttile0 = sub * 32 + 4 * g;  // token of (mb = 0, i = 0) inside the tile
+  const float top = bits == 2 ? 3.0f : (float)((1 << bits) - 1);
+  auto code = [&](float y, int nb) -> uint32_t {  // the code in bits 0..bits-1
+    float t = fmaf(y, al[nb], ga[nb]);
+    if constexpr (CLAMP) t = __builtin_amdgcn_fmed3f(t, 0.0f, top);
+    return (uint32_t)__float_as_int(t + 12582912.0f);  // 1.5 * 2^23
+  };
+  if (bits == 2) {
+    emit_plane2<NW>(acc, code, stream, ttile0, c, sh.rec);
+    return;
+  }
+  uint8_t* pb = sh.rec + G * kD / 4;
+  if (bits == 3) {  // plane B is ORed together from several lanes: clear it first
+    reinterpret_cast<uint2*>(pb)[sub * 64 + (g * 16 + c)] = make_uint2(0u, 0u);
+    tile_sync<NW>();
+  }
+  emit_plane2<NW>(acc, [&](float y, int nb) { return code(y, nb) & 3u; }, stream, ttile0, c, sh.rec);
+  if (bits == 4)
+    emit_plane2<NW>(acc, [&](float y, int nb) { return (code(y, nb) >> 2) & 3u; }, stream, ttile0, c, pb);
+  else
+    emit_bit_plane<NW>(acc, [&](float y, int nb) { return (code(y, nb) >> 2) & 1u; }, stream, ttile0, g, c, pb);
 }
 
 // ----------------------------------------------------------------------------- the tile core
@@ -499,9 +568,10 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
 // centered reading of "variance" runs its own loop (centered_varn).
 template <int NW, bool DBG, bool ABL>
 __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2][8][4], float st_own, int lane,
-                            int sub, int stream, int n_it, int var, TileLds<NW>& sh, uint32_t& flags, float* dbg_w,
-                            float* dbg_y, long long dstride) {
+                            int sub, int stream, int n_it, int var, int bits_in, TileLds<NW>& sh, uint32_t& flags,
+                            float* dbg_w, float* dbg_y, long long dstride) {
   constexpr int G = 32 * NW;
+  const int bits = ABL ? bits_in : 2;  // code width; the standard build has 2
   const int g = lane >> 4, c = lane & 15;
   const int tau_own = c >> 1;  // own token: mb = tau/4, i = tau%4
   const bool idr = ABL && (var & KVARN_VARIANT_NO_ROTATION);
@@ -635,7 +705,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const float lo = mn_own[q] * ic_own[q], hi = mx_own[q] * ic_own[q];
-    const float sr = (hi - lo) * (1.0f / 3.0f);
+    const float sr = (hi - lo) * (bits == 2 ? (1.0f / 3.0f) : 1.0f / (float)((1 << bits) - 1));
     const float sc = fminf(sr, kFp16Max);
     const float zc = fminf(fmaxf(lo, -kFp16Max), kFp16Max);
     if (sc != sr || zc != lo) {
@@ -654,18 +724,18 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
   col_gather8(al_own, al, sh.gcol[sub], g, c);
   col_gather8(ga_own, ga, sh.gcol[sub], g, c);
 
-  // codes, q = clamp(rne(u), 0, 3): 1.5 * 2^23 + u rounds half to even with q left in
-  // bits 0..1 and zeros in bits 2..21; shifted into its 2-bit slot, the junk above bit 21
+  // codes, q = clamp(rne(u), 0, 2^bits - 1): 1.5 * 2^23 + u rounds half to even with q left in
+  // bits 0..bits-1 and zeros up to bit 21; shifted into its slot, the junk above bit 21
   // falls outside the bytes kept (permute) / the byte stored. The clamp is needed only where u can
-  // leave (-0.5, 3.5): with normal s16 and max(|Y|) <= 200 s16 the fp16 rounding of z
-  // and s moves u by less than 0.1, so a wave whose channels all satisfy that skips it.
+  // leave (-0.5, 2^bits - 0.5): with normal s16 and max(|Y|) <= 200 s16 the fp16 rounding of
+  // z and s moves u by less than 0.1, so a wave whose channels all satisfy that skips it.
   const bool need_clamp = __any(need_clamp_own);
   if (need_clamp)
-    emit_codes<NW, true>(acc, al, ga, stream, sub, g, c, sh);
+    emit_codes<NW, true>(acc, al, ga, stream, sub, g, c, sh, bits);
   else
-    emit_codes<NW, false>(acc, al, ga, stream, sub, g, c, sh);
+    emit_codes<NW, false>(acc, al, ga, stream, sub, g, c, sh, bits);
   const int ttile0 = sub * 32 + 4 * g;
-  constexpr int RO = G * kD / 4, CO = RO + 2 * G, SO = CO + 2 * kD, ZO = SO + 2 * kD;
+  const int RO = G * kD * bits / 8, CO = RO + 2 * G, SO = CO + 2 * kD, ZO = SO + 2 * kD;
   if ((c & 1) == 0) {
     const int t = ttile0 + 16 * (tau_own >> 2) + (tau_own & 3);
     *reinterpret_cast<uint16_t*>(sh.rec + RO + 2 * t) = (uint16_t)f16bits(r16_own);
@@ -682,12 +752,13 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
   tile_sync<NW>();
 }
 
+// tr: the record's bytes (a multiple of 16 for every supported width and group)
 template <int NW>
-__device__ __forceinline__ void copy_record(const TileLds<NW>& sh, uint8_t* dst, int lane, int sub) {
-  constexpr int N16 = TileLds<NW>::TR / 16;
+__device__ __forceinline__ void copy_record(const TileLds<NW>& sh, uint8_t* dst, int lane, int sub, int tr) {
+  const int n16 = tr / 16;
   const uint4* s = reinterpret_cast<const uint4*>(sh.rec);
   uint4* d = reinterpret_cast<uint4*>(dst);
-  for (int k = sub * 64 + lane; k < N16; k += 64 * NW) d[k] = s[k];
+  for (int k = sub * 64 + lane; k < n16; k += 64 * NW) d[k] = s[k];
 }
 
 __device__ __forceinline__ void raise_flags(uint8_t* hdr, uint32_t f) {
@@ -766,10 +837,10 @@ __device__ void append_job(const AppendArgs& a, int job, int sub, int lane, Tile
     }
     float p[2][8][4];
     const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
-    tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, sh, flags, nullptr, nullptr, 0);
+    tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr, nullptr, 0);
     const long long ro = record_at(a.cache, L, b, h, (pos + 1) / G - 1, s);
     if (ro >= 0)
-      copy_record<NW>(sh, a.cache + ro, lane, sub);
+      copy_record<NW>(sh, a.cache + ro, lane, sub, L.tr);
     else
       flags |= KVARN_FLAG_UNMAPPED;
   }

@@ -53,9 +53,9 @@ def close_rowwise(got, ref, rel, axis=-1):
 class GpuCache:
     """One layer cache in device memory plus host copies for the oracle."""
 
-    def __init__(self, B, H, cap, G=32, n_it=3, seed_sigma=0, variant=0):
-        self.g = K.geom(B, H, cap, G, n_it, variant=variant)
-        self.og = R.Geom(B, H, 128, cap, G, n_it, 2, variant)
+    def __init__(self, B, H, cap, G=32, n_it=3, seed_sigma=0, variant=0, bits=2):
+        self.g = K.geom(B, H, cap, G, n_it, variant=variant, bits=bits)
+        self.og = R.Geom(B, H, 128, cap, G, n_it, bits, variant)
         self.sigma = synth.sign_vector(seed_sigma, 128)
         self.buf = K.alloc_cache(self.g, self.sigma)
 
@@ -92,10 +92,10 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
                 ok, worst = close_rowwise(w[s][b, tile * G:(tile + 1) * G, h], w_ref, 1e-5)
                 assert ok, ("W", s, b, h, tile, worst)
             rec = hc.record(b, h, tile, s)
-            u = R.unpack_record(rec, G, 128, s)
+            u = R.unpack_record(rec, G, 128, s, og.bits)
             # layout: the oracle's packing of the GPU's own fields is the GPU record
-            assert np.array_equal(R.pack_record(u["q"], u["r16"], u["c16"], u["s16"], u["z16"], s), rec)
-            t_ref = R.quantize_tile(w_ref, og.varn_iters, og.variant)
+            assert np.array_equal(R.pack_record(u["q"], u["r16"], u["c16"], u["s16"], u["z16"], s, og.bits), rec)
+            t_ref = R.quantize_tile(w_ref, og.varn_iters, og.variant, og.bits)
             dr = fp16_ulp_dist(u["r16"], t_ref["r16"])
             dc = fp16_ulp_dist(u["c16"], t_ref["c16"])
             assert dr.max() <= 1 and dc.max() <= 1, ("r/c ulp", s, b, h, tile, dr.max(), dc.max())
@@ -107,16 +107,16 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
             if y is not None:
                 ok, worst = close_rowwise(y[s][b, tile * G:(tile + 1) * G, h], y_ref, 1e-5)
                 assert ok, ("Y", s, b, h, tile, worst)
-            s_ref, z_ref, _ = R.grid(y_ref)
+            s_ref, z_ref, _ = R.grid(y_ref, og.bits)
             ds = fp16_ulp_dist(u["s16"], s_ref)
             dz = fp16_ulp_dist(u["z16"], z_ref)
             assert ds.max() <= 1 and dz.max() <= 1, ("s/z ulp", s, b, h, tile)
             stats["s_mis"] += int((ds > 0).sum())
             stats["z_mis"] += int((dz > 0).sum())
-            q_ref = R.codes(y_ref, u["s16"], u["z16"])
+            q_ref = R.codes(y_ref, u["s16"], u["z16"], og.bits)
             uu = R.pre_rounding(y_ref, u["s16"], u["z16"])
             frac = uu - np.floor(uu)
-            near_edge = (np.abs(frac - 0.5) < EDGE_BAND) & (uu > -0.5) & (uu < 3.5)
+            near_edge = (np.abs(frac - 0.5) < EDGE_BAND) & (uu > -0.5) & (uu < 2 ** og.bits - 0.5)
             bad = (q_ref != u["q"]) & ~near_edge
             assert not bad.any(), ("codes", s, b, h, tile, int(bad.sum()))
             stats["edge_exempt"] += int(((q_ref != u["q"]) & near_edge).sum())

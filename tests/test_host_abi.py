@@ -39,6 +39,13 @@ def test_cache_bytes_match_oracle_layout(B, H, cap, G):
     assert K.kvarn_cache_bytes(K.geom(B, H, cap, G, 3)) == R.Geom(B, H, 128, cap, G, 3, 2).total
 
 
+def test_bit_width_sizes_match_oracle():
+    for bits in (2, 3, 4):
+        for G in (32, 64):
+            assert K.kvarn_cache_bytes(K.geom(2, 3, 256, G, 2, bits=bits)) == \
+                R.Geom(2, 3, 128, 256, G, 2, bits).total
+
+
 def test_paged_sizes_match_oracle():
     for B, H, cap, G, pages in [(2, 3, 256, 64, 7), (4, 8, 1024, 32, 100), (1, 1, 32, 32, 1)]:
         assert K.kvarn_cache_bytes(K.geom(B, H, cap, G, 2, num_pages=pages)) == \
@@ -69,7 +76,8 @@ def test_workspace_bytes():
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), K.KVARN_ERR_UNSUPPORTED),
     (dict(group=48), K.KVARN_ERR_UNSUPPORTED),
-    (dict(bits=4), K.KVARN_ERR_UNSUPPORTED),
+    (dict(bits=5), K.KVARN_ERR_UNSUPPORTED),
+    (dict(bits=1), K.KVARN_ERR_UNSUPPORTED),
     (dict(varn_iters=9), K.KVARN_ERR_UNSUPPORTED),
     (dict(varn_iters=-1), K.KVARN_ERR_GEOM),
     (dict(capacity=100), K.KVARN_ERR_GEOM),
