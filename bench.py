@@ -4,7 +4,8 @@
 Headline (`value`): prefill quantization throughput in GB/s of bf16 input on the
 Llama-3.1-8B-shaped KV workload -- 32 layers x 8 KV heads x head_dim 128, 32768
 tokens, batch 1, group 32, 3 VarN iterations, 2 bits -- one step = the 32 layer
-caches quantized from 32 distinct input buffers resident in HBM. Beside it:
+caches quantized from 32 distinct input buffers resident in HBM, issued eagerly (the
+same step replayed as one HIP graph is reported beside it). Beside it:
   * roofline of the quantize kernel: algorithmic bytes per launch (bf16 in + tile
     records out) over its average launch time measured with HIP events on the
     launch stream, against the 8 TB/s HBM peak;
@@ -50,9 +51,9 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
         for l in range(layers):
             K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T, stream)
     torch.cuda.synchronize()
+    # per-launch kernel time: every launch bracketed by HIP events on its stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps * layers)]
-    t0 = time.perf_counter()
     i = 0
     for _ in range(steps):
         for l in range(layers):
@@ -61,15 +62,35 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
             ev[i][1].record(stream)
             i += 1
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in ev]
+    # the timed step: issued eagerly, one C-ABI call per layer, nothing between the launches
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for l in range(layers):
+            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the same step as one HIP graph of its layer launches, replayed
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l in range(layers):
+            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_wall = time.perf_counter() - t0
+    del graph
     bytes_in = 2 * 2 * T * H * 128                       # K and V, bf16
     bytes_out = 2 * H * (T // G) * record_bytes(G, bits)  # tile records
     flags = K.kvarn_cache_flags(caches[0])
     del ks, vs, caches
     torch.cuda.empty_cache()
-    return dict(wall=wall, launch_ms=launch_ms, bytes_in=bytes_in, bytes_out=bytes_out, layers=layers,
-                T=T, H=H, G=G, n_it=n_it, flags=flags)
+    return dict(wall=wall, graph_wall=graph_wall, launch_ms=launch_ms, bytes_in=bytes_in, bytes_out=bytes_out,
+                layers=layers, T=T, H=H, G=G, n_it=n_it, flags=flags)
 
 
 def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40, T0=16384, cap=17408, G=32,
@@ -102,27 +123,37 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
             if ev is not None:
                 ev[1].record(stream)
 
-    for s in range(warmup):
-        step(s)
+    sc = 0  # decode steps issued so far (every step appends one token to every sequence)
+    for _ in range(warmup):
+        step(sc)
+        sc += 1
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ctx_start = T0 + sc
     t0 = time.perf_counter()
-    for s in range(steps):
-        step(warmup + s, evs[s])   # one attention launch per step is timed with events
+    for _ in range(steps):  # the timed steps: nothing but the library calls
+        step(sc)
+        sc += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the attention call of the last layer of each of 8 further steps, bracketed by events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
+    ctx_attn = T0 + sc + 4  # context of the middle one
+    for i in range(8):
+        step(sc, evs[i])
+        sc += 1
+    torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     # one append launch per layer-step, timed the same way
     ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
-    for i, (e0, e1) in enumerate(ea):
-        s = warmup + steps + i
+    for e0, e1 in ea:
         e0.record(stream)
-        K.kvarn_append_decode(g, caches[0], kp[s % pool], vp[s % pool], stream)
+        K.kvarn_append_decode(g, caches[0], kp[sc % pool], vp[sc % pool], stream)
         e1.record(stream)
         for l in range(1, layers):
-            K.kvarn_append_decode(g, caches[l], kp[s % pool], vp[s % pool], stream)
+            K.kvarn_append_decode(g, caches[l], kp[sc % pool], vp[sc % pool], stream)
         for l in range(layers):
-            K.kvarn_attn_decode(g, caches[l], qp[s % pool], Hq, 0.0, 0, ws, nws, out, stream)
+            K.kvarn_attn_decode(g, caches[l], qp[sc % pool], Hq, 0.0, 0, ws, nws, out, stream)
+        sc += 1
     torch.cuda.synchronize()
     append_ms = [a.elapsed_time(b) for a, b in ea]
     # the same step as one HIP graph: 40 x (append + attention) replayed, the step's inputs
@@ -134,13 +165,13 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
             K.kvarn_append_decode(g, caches[l], k_in, v_in)
             K.kvarn_attn_decode(g, caches[l], q_in, Hq, 0.0, 0, ws, nws, out)
     torch.cuda.synchronize()
-    s0 = warmup + steps + len(ea)
     t0 = time.perf_counter()
-    for s in range(s0, s0 + steps):
-        k_in.copy_(kp[s % pool])
-        v_in.copy_(vp[s % pool])
-        q_in.copy_(qp[s % pool])
+    for _ in range(steps):
+        k_in.copy_(kp[sc % pool])
+        v_in.copy_(vp[sc % pool])
+        q_in.copy_(qp[sc % pool])
         graph.replay()
+        sc += 1
     torch.cuda.synchronize()
     graph_wall = time.perf_counter() - t0
     del graph
@@ -150,13 +181,14 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
         for l in range(layers):
             K.kvarn_append_attn_decode(g, caches[l], kk, vv, qq, Hq, 0.0, 0, ws, nws, out, stream)
 
-    s1 = s0 + steps
-    for s in range(s1, s1 + 2):
-        fstep(s, kp[s % pool], vp[s % pool], qp[s % pool])
+    for _ in range(2):
+        fstep(sc, kp[sc % pool], vp[sc % pool], qp[sc % pool])
+        sc += 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(s1 + 2, s1 + 2 + steps):
-        fstep(s, kp[s % pool], vp[s % pool], qp[s % pool])
+    for _ in range(steps):
+        fstep(sc, kp[sc % pool], vp[sc % pool], qp[sc % pool])
+        sc += 1
     torch.cuda.synchronize()
     fused_wall = time.perf_counter() - t0
     fgraph = torch.cuda.CUDAGraph()
@@ -164,25 +196,26 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
         for l in range(layers):
             K.kvarn_append_attn_decode(g, caches[l], k_in, v_in, q_in, Hq, 0.0, 0, ws, nws, out)
     torch.cuda.synchronize()
-    s2 = s1 + 2 + steps
     t0 = time.perf_counter()
-    for s in range(s2, s2 + steps):
-        k_in.copy_(kp[s % pool])
-        v_in.copy_(vp[s % pool])
-        q_in.copy_(qp[s % pool])
+    for _ in range(steps):
+        k_in.copy_(kp[sc % pool])
+        v_in.copy_(vp[sc % pool])
+        q_in.copy_(qp[sc % pool])
         fgraph.replay()
+        sc += 1
     torch.cuda.synchronize()
     fused_graph_wall = time.perf_counter() - t0
     del fgraph
+    assert T0 + sc <= cap, "the decode workload outgrew its capacity"
     flags = K.kvarn_cache_flags(caches[0])
-    ctx_mid = T0 + warmup + steps // 2
-    # attention bytes per layer-step: K and V records of the full tiles + tail rows + q + out
-    nfull = ctx_mid // G
-    attn_bytes = B * H * (2 * nfull * record_bytes(G, bits) + 2 * (ctx_mid % G) * 256) + B * Hq * (256 + 512)
+    # attention bytes per call at the event-timed context: K and V records of the full
+    # tiles + tail rows + q + out
+    nfull = ctx_attn // G
+    attn_bytes = B * H * (2 * nfull * record_bytes(G, bits) + 2 * (ctx_attn % G) * 256) + B * Hq * (256 + 512)
     del caches
     torch.cuda.empty_cache()
     return dict(wall=wall, steps=steps, B=B, layers=layers, attn_ms=attn_ms, attn_bytes=attn_bytes, flags=flags,
-                ctx_start=T0 + warmup, H=H, Hq=Hq, graph_wall=graph_wall, append_ms=append_ms, fused_wall=fused_wall,
+                ctx_start=ctx_start, H=H, Hq=Hq, graph_wall=graph_wall, append_ms=append_ms, fused_wall=fused_wall,
                 fused_graph_wall=fused_graph_wall)
 
 
@@ -338,8 +371,9 @@ def main():
     lm = sorted(pf["launch_ms"])
     avg_launch = sum(lm) / len(lm)
     achieved = (pf["bytes_in"] + pf["bytes_out"]) / (avg_launch * 1e-3) / 1e9
-    log(f"prefill: {ms_step:.3f} ms/step, {value:.1f} GB/s bf16-in, {total_gbs:.1f} GB/s total; "
-        f"kernel avg {avg_launch * 1e3:.1f} us -> {achieved:.1f} GB/s")
+    graph_ms = pf["graph_wall"] * 1e3 / args.steps
+    log(f"prefill: {ms_step:.3f} ms/step ({graph_ms:.3f} as a graph), {value:.1f} GB/s bf16-in, "
+        f"{total_gbs:.1f} GB/s total; kernel avg {avg_launch * 1e3:.1f} us -> {achieved:.1f} GB/s")
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -349,6 +383,8 @@ def main():
                    "varn_iters": pf["n_it"], "bits": args.bits,
                    "input": "bf16, outlier channels x20, 5% lognormal tokens"},
         "hbm_frac_step": round(total_gbs / HBM_PEAK_GBS, 4),
+        "step_as_graph": {"ms_per_step": round(graph_ms, 4),
+                          "value": round(pf["layers"] * pf["bytes_in"] / (graph_ms * 1e-3) / 1e9, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES)

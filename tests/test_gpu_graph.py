@@ -63,3 +63,31 @@ def test_decode_step_graph_replay_matches_eager(G, n_it):
         assert not torch.isnan(out_g).any()
     lens = graph_caches[0].host_cache().lens
     assert np.all(lens == T0 + steps), lens
+
+
+def test_prefill_graph_replay_matches_eager():
+    """Prefill launches of several layers captured once and replayed (with eager work between
+    the replays) write the same cache bytes as eager calls."""
+    say("prefill graph")
+    B, H, T, G, layers = 2, 2, 100, 32, 3
+    k, v = synth.kv_host(23, B, T, H)
+    kd, vd = from_u16(k), from_u16(v)
+    gcs = [GpuCache(B, H, 128, G, 3) for _ in range(layers)]
+    ecs = [GpuCache(B, H, 128, G, 3) for _ in range(layers)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in gcs:
+            K.kvarn_quantize_prefill(c.g, c.buf, kd, vd, T)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for c in gcs:  # disturb the lengths between replays: the replay must reset them
+            K.kvarn_append_decode(c.g, c.buf, kd[:, 0].contiguous(), vd[:, 0].contiguous())
+        graph.replay()
+        for c in ecs:
+            K.kvarn_quantize_prefill(c.g, c.buf, kd, vd, T)
+        torch.cuda.synchronize()
+        for a, b in zip(gcs, ecs):
+            ha, hb = a.host_cache(), b.host_cache()
+            m = hb.defined_mask()
+            assert np.array_equal(ha.buf[m], hb.buf[m]) and np.all(ha.lens == T), rep
