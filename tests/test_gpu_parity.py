@@ -321,3 +321,68 @@ def test_full_size_phi4_decode_sampled():
             m = np.abs(ref[b, g]).max()
             assert np.abs(out[b, g] - ref[b, g]).max() <= 2e-3 * m, (b, g)
     assert np.all(np.isfinite(out))
+
+
+def test_full_size_qwen3_prefill_dequant_sampled():
+    """Qwen3-4B-shaped layer: 8 sequences x 8 KV heads x 16384 tokens, 2% of tokens with norm
+    x50, G=64, 2 VarN iterations. Sampled tiles go through the full parity chain, and the bf16
+    dequantization of the whole layer is compared on those tiles with the oracle's
+    dequantization of the same bytes."""
+    say("full-size qwen3 prefill + dequantize")
+    B, H, T, G = 8, 8, 16384, 64
+    kd, vd = synth.kv_device(synth.sub_seed(3, 0, 0), B, T, H, law="spike", p=0.02, factor=50.0)
+    gc = GpuCache(B, H, T, G, 2)
+    K.kvarn_quantize_prefill(gc.g, gc.buf, kd, vd, T)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    picks = sorted({(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(T // G))) for _ in range(40)}
+                   | {(0, 0, 0), (B - 1, H - 1, T // G - 1)})
+    k = np.zeros((B, T, H, 128), dtype=np.uint16)
+    v = np.zeros_like(k)
+    for b, h, t in picks:
+        k[b, t * G:(t + 1) * G, h] = to_u16(kd[b, t * G:(t + 1) * G, h])
+        v[b, t * G:(t + 1) * G, h] = to_u16(vd[b, t * G:(t + 1) * G, h])
+    say("stats", check_prefill(gc, k, v, T, tiles=picks))
+    del kd, vd
+    ko = torch.empty(B, T, H, 128, dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    K.kvarn_dequantize(gc.g, gc.buf, ko, vo, T, K.KVARN_OUT_BF16)
+    hc = gc.host_cache()
+    for b, h, t in picks:
+        for s, out in ((0, ko), (1, vo)):
+            u = R.unpack_record(hc.record(b, h, t, s), G, 128, s)
+            ref = R.unrotate(R.dequantize_tile(u["q"], u["r16"], u["c16"], u["s16"], u["z16"]), hc.sigma)
+            got = out[b, t * G:(t + 1) * G, h].float().cpu().numpy().astype(np.float64)
+            rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+            assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) * 1.01 + 1e-5 * rms + 1e-30), (b, h, t, s)
+
+
+def test_full_size_long_reasoning_decode_sampled():
+    """Long-reasoning stress shape: 64 sequences x 8 KV heads x 32768 prior tokens, Student-t
+    (nu = 3) token norms, 8 outlier channels x30, G=32, 3 iterations, 32 query heads. Prefill,
+    appends across a group boundary, then attention on sampled (batch, kv head) pairs against
+    the oracle on the GPU-written bytes."""
+    say("full-size long-reasoning decode")
+    B, H, Hq, T0, steps = 64, 8, 32, 32768, 40
+    cap = T0 + 64
+    kd, vd = synth.kv_device(synth.sub_seed(5, 0, 0), B, T0, H, n_outlier_ch=8, ch_mult=30.0, law="student_t",
+                             nu=3.0)
+    gc = GpuCache(B, H, cap)
+    K.kvarn_quantize_prefill(gc.g, gc.buf, kd, vd, T0)
+    del kd, vd
+    kn, vn = synth.kv_device(synth.sub_seed(5, 0, 1), B, steps, H, n_outlier_ch=8, ch_mult=30.0, law="student_t",
+                             nu=3.0)
+    for t in range(steps):
+        K.kvarn_append_decode(gc.g, gc.buf, kn[:, t].contiguous(), vn[:, t].contiguous())
+    q = synth.q_host(19, B, Hq)
+    out = run_attn(gc, q, Hq)
+    assert np.all(np.isfinite(out))
+    hc = gc.host_cache()
+    assert np.all(hc.lens == T0 + steps)
+    pairs = [(0, 0), (63, 7), (29, 4)]
+    ref = R.attn_decode(hc, q, Hq, pairs=pairs)
+    grp = Hq // H
+    for b, h in pairs:
+        for g in range(h * grp, (h + 1) * grp):
+            m = np.abs(ref[b, g]).max()
+            assert np.abs(out[b, g] - ref[b, g]).max() <= 2e-3 * m, (b, g)
