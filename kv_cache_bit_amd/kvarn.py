@@ -49,6 +49,10 @@ def geom(batch, num_kv_heads, capacity, group=32, varn_iters=3, head_dim=128, bi
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it first (python -m kv_cache_bit_amd.build)")
+    # torch ships its own HIP runtime (soname libamdhip64.so.7, file name without the .7):
+    # loaded first, it is the one libkvarn binds to; loaded after libkvarn, a second runtime
+    # comes in beside /opt/rocm's and torch's own kernels fail to launch.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, G, S, I32, U32, F32 = (ctypes.c_void_p, ctypes.POINTER(kvarn_geom), ctypes.POINTER(ctypes.c_size_t),
                               ctypes.c_int32, ctypes.c_uint32, ctypes.c_float)

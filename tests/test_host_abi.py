@@ -163,3 +163,18 @@ def test_null_geometry():
     f = K.lib.kvarn_cache_bytes
     n = ctypes.c_size_t()
     assert f(None, ctypes.byref(n)) == K.KVARN_ERR_NULL
+
+
+def test_one_hip_runtime_when_binding_loads_first():
+    """Importing the binding before torch still leaves one HIP runtime in the process (the
+    binding loads torch's before libkvarn): two runtimes make torch's own launches fail."""
+    import subprocess
+    import sys
+    code = ("import kv_cache_bit_amd.kvarn, sys\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "paths = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "print(len(paths), 'torch' in sys.modules)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["1", "True"], out.stdout
