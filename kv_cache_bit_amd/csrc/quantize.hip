@@ -5,11 +5,12 @@
 namespace kvarn {
 
 // ----------------------------------------------------------------------------- prefill
-// Work-groups [0, tile_blocks) quantize full tiles, 4/NW tiles per work-group; the
-// remaining work-groups write the fp16 tail and len[], one (b, h, s) per wave.
-template <int NW, bool DBG, bool ABL>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
-  constexpr int TPW = 4 / NW;
+// Work-groups [0, tile_blocks) quantize full tiles, TPW tiles (NW waves each) per
+// work-group; the remaining work-groups write the fp16 tail and len[], one (b, h, s)
+// per wave.
+template <int NW, bool DBG, bool ABL, int TPW>
+__global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
+  constexpr int WPG = NW * TPW;  // waves per work-group
   __shared__ TileLds<NW> sh_all[TPW];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: job math on the SALU
   const int lane = threadIdx.x & 63;
@@ -20,7 +21,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const uint32_t tile_blocks = ((uint32_t)a.jobs + TPW - 1) / TPW;
 
   if (blockIdx.x >= tile_blocks) {
-    const uint32_t sj = (blockIdx.x - tile_blocks) * 4 + wave;  // (b, h, s)
+    const uint32_t sj = (blockIdx.x - tile_blocks) * WPG + wave;  // (b, h, s)
     if (sj >= 2u * L.B * L.Hkv) return;
     const uint32_t q = fdiv(sj >> 1, a.dhkv);
     const int s = (int)(sj & 1u), h = (int)((sj >> 1) - q * (uint32_t)L.Hkv), b = (int)q;
@@ -215,22 +216,25 @@ __global__ __launch_bounds__(256) void tokens_tail_kernel(TokensArgs a) {
 
 // ----------------------------------------------------------------------------- launchers
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
-  const int tpw = 4 / (a.L.G / 32);
-  const long long tile_blocks = (a.jobs + tpw - 1) / tpw;
-  const long long tail_blocks = (2LL * a.L.B * a.L.Hkv + 3) / 4;
-  const dim3 grid((unsigned)(tile_blocks + tail_blocks));
+  // One tile per work-group: a tile's waves finish on their own schedule, and a slot freed
+  // by one wave (G = 32) can take the next tile at once instead of waiting for three others.
+  constexpr int TPW = 1;
+  const int nw = a.L.G / 32;
+  const long long tile_blocks = (a.jobs + TPW - 1) / TPW;
+  const long long tail_blocks = (2LL * a.L.B * a.L.Hkv + nw * TPW - 1) / (nw * TPW);
+  const dim3 grid((unsigned)(tile_blocks + tail_blocks)), block((unsigned)(64 * nw * TPW));
   const bool dbg = a.wk || a.wv || a.yk || a.yv;
   const bool abl = a.L.variant != 0 || a.L.bits != 2;  // the extended build
   const int which = (a.L.G == 32 ? 0 : 4) + (dbg ? 2 : 0) + (abl ? 1 : 0);
   switch (which) {
-    case 0: hipLaunchKernelGGL((prefill_kernel<1, false, false>), grid, dim3(256), 0, st, a); break;
-    case 1: hipLaunchKernelGGL((prefill_kernel<1, false, true>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<1, true, false>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((prefill_kernel<1, true, true>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<2, false, false>), grid, dim3(256), 0, st, a); break;
-    case 5: hipLaunchKernelGGL((prefill_kernel<2, false, true>), grid, dim3(256), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((prefill_kernel<2, true, false>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((prefill_kernel<2, true, true>), grid, dim3(256), 0, st, a); break;
+    case 0: hipLaunchKernelGGL((prefill_kernel<1, false, false, TPW>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<1, false, true, TPW>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<1, true, false, TPW>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((prefill_kernel<1, true, true, TPW>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<2, false, false, TPW>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((prefill_kernel<2, false, true, TPW>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((prefill_kernel<2, true, false, TPW>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((prefill_kernel<2, true, true, TPW>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
