@@ -390,7 +390,7 @@ def main():
                      "traffic": (counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES)
                                  if args.bits == 2 else None),
                      "traffic_unit": "bytes/launch",
-                     "kernel": "prefill_kernel<1,false,false>" if args.bits == 2 else "prefill_kernel<1,false,true>", "bytes_per_launch": pf["bytes_in"] + pf["bytes_out"],
+                     "kernel": "prefill_kernel<1,false,false,1>" if args.bits == 2 else "prefill_kernel<1,false,true,1>", "bytes_per_launch": pf["bytes_in"] + pf["bytes_out"],
                      "avg_launch_us": round(avg_launch * 1e3, 2), "median_launch_us": round(lm[len(lm) // 2] * 1e3, 2)},
         "flags": pf["flags"],
     }
