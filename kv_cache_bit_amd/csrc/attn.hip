@@ -551,15 +551,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
-// One 16-lane row per (b, q head): combine the spans in index order, add the tail
-// tokens, un-rotate the V part, normalize. Loads are issued in independent batches (span
-// maxima spread over the row's lanes, spans and tail tokens four at a time), so the
-// kernel waits on memory a few times rather than once per span or token.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, xshfl<1>(v));
-  v = fmaxf(v, xshfl<2>(v));
-  v = fmaxf(v, xshfl<4>(v));
-  return fmaxf(v, xshfl<8>(v));
+// Merge: one work-group per (b, q head) row. Its 16 groups of 16 lanes (lane cg holds
+// channels 8cg .. 8cg+7) take spans gi, gi+16, ... and tail tokens gi, gi+16, ...; each
+// group issues all its loads at once and folds its items into one (m, l, o_rot, o_orig)
+// state in log2 units. The 16 states meet in LDS in group order, one thread per output
+// channel; group 0 then applies H_D^T to the rotated part and normalizes. Every result
+// depends only on the data, not on timing.
+struct MergeLds {
+  float m[16], l[16];
+  float o[16][2 * kD];  // per group: o_rot[D], o_orig[D]
+  float fin[2 * kD];
+  float lsum;
+};
+
+// A state folded with scores that may all be -inf: an empty state keeps weight 1
+// (m == mn) and an empty item gets 0.
+__device__ __forceinline__ float rescale(float m, float mn) { return m == mn ? 1.0f : __builtin_amdgcn_exp2f(m - mn); }
+__device__ __forceinline__ float weight(float x, float mn) {
+  return x > -INFINITY ? __builtin_amdgcn_exp2f(x - mn) : 0.0f;
 }
 
 // FUSED: work-groups past the rows' ones run the append jobs (one (b, h, s) each, on
@@ -568,22 +577,24 @@ template <bool FUSED, int NW, bool ABL>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const long long nrows = (long long)a.L.B * a.Hq;
   if constexpr (FUSED) {
-    const long long row_blocks = (nrows + 15) / 16;
-    if ((long long)blockIdx.x >= row_blocks) {
+    if ((long long)blockIdx.x >= nrows) {
       __shared__ TileLds<NW> sh;
       const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
       if (wave >= NW) return;
       const AppendArgs ap{a.L, a.cache_rw, a.kn, a.vn};
-      append_job<NW, ABL>(ap, (int)(blockIdx.x - row_blocks), wave, threadIdx.x & 63, sh);
+      append_job<NW, ABL>(ap, (int)(blockIdx.x - nrows), wave, threadIdx.x & 63, sh);
       return;
     }
   }
-  const int lane = threadIdx.x & 63, rg = lane >> 4, cg = lane & 15;
-  const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + rg;  // b * Hq + q head
-  const bool live = row < nrows;
-  const int rr = live ? (int)row : 0;
+  __shared__ MergeLds sm;
+  const int tid = threadIdx.x, gi = tid >> 4, cg = tid & 15;
+  const int rr = (int)blockIdx.x;  // b * Hq + q head
   const int b = rr / a.Hq, qhead = rr - b * a.Hq, h = qhead / a.grp;
   const int G = a.L.G;
+  // independent of the length: q and sigma
+  const uint4 qw = *reinterpret_cast<const uint4*>(a.q + (long long)rr * kD + 8 * cg);
+  float sg[8];
+  load_sigma(a.cache, cg, sg);
   // a fused call reads the length the tile pass saw; its append jobs move len meanwhile
   const int n = FUSED ? a.lens_ws[b * a.L.Hkv + h] : *reinterpret_cast<const int32_t*>(a.cache + a.L.len_off(b, h, 0));
   const int nfull = n / G, nt_old = n - nfull * G;
@@ -591,42 +602,54 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int nt = nt_old + ((FUSED && n < a.L.cap) ? 1 : 0);
   const int nsp = (nfull + 4 * a.tpw - 1) / (4 * a.tpw);
   const float* w = a.ws + (long long)rr * a.nspan * kPart;
-  // span maxima: lane cg looks at spans cg, cg + 16, ...
-  float M = -INFINITY;
-  for (int s = cg; s < nsp; s += 16) M = fmaxf(M, w[s * kPart]);
-  M = row16_max(M);
-  float Ls = 0.0f, orot[8] = {0, 0, 0, 0, 0, 0, 0, 0}, oorig[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s0 = 0; s0 < nsp; s0 += 4) {
-    float ml[4][2];
-    float4 x[4][2];
+
+  // tail tokens gi + 16k (k < kt), loaded up front; slots past the tail read the last
+  // stored one (finite values) and get -inf scores
+  constexpr int KT = 4;  // G <= 64
+  const int kt = (nt + 15) / 16;  // uniform over the work-group
+  uint4 kw[KT], vw[KT];
+  const uint8_t* tk = a.cache + a.L.tail_row(b, h, 0, 0);
+  const uint8_t* tv = a.cache + a.L.tail_row(b, h, 1, 0);
+  {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = min(s0 + k, nsp - 1);
-      const float* p = w + s * kPart;
-      ml[k][0] = p[0];
-      ml[k][1] = p[1];
-      x[k][0] = *reinterpret_cast<const float4*>(p + 4 + 8 * cg);
-      x[k][1] = *reinterpret_cast<const float4*>(p + 8 + 8 * cg);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float f = (s0 + k < nsp) ? __builtin_amdgcn_exp2f(ml[k][0] - M) : 0.0f;
-      Ls = fmaf(f, ml[k][1], Ls);
-      const float xs[8] = {x[k][0].x, x[k][0].y, x[k][0].z, x[k][0].w, x[k][1].x, x[k][1].y, x[k][1].z, x[k][1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) orot[e] = fmaf(f, xs[e], orot[e]);
+    for (int k = 0; k < KT; ++k) {
+      if (k >= kt) break;
+      const int t = min(gi + 16 * k, nt - 1);
+      if (FUSED && t == nt_old) {  // the new token, canonicalized as the append stores it
+        const long long src = ((long long)b * a.L.Hkv + h) * kD + 8 * cg;
+        float xk[8], xv[8], amax = 0.0f;
+        canon8_bf16(*reinterpret_cast<const uint4*>(a.kn + src), xk, amax);
+        canon8_bf16(*reinterpret_cast<const uint4*>(a.vn + src), xv, amax);
+        kw[k] = pack8_f16(xk);
+        vw[k] = pack8_f16(xv);
+      } else {
+        kw[k] = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
+        vw[k] = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
+      }
     }
   }
-  float sg[8];
-  load_sigma(a.cache, cg, sg);
-  if (nt > 0) {  // uniform over the row
+  // the first span of the group, loaded with the tokens
+  float m = -INFINITY, l = 0.0f, orot[8] = {0, 0, 0, 0, 0, 0, 0, 0}, oorig[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = gi; s < nsp; s += 16) {  // uniform over the group
+    const float* p = w + s * kPart;
+    const float pm = p[0], pl = p[1];
+    const float4 x0 = *reinterpret_cast<const float4*>(p + 4 + 8 * cg);
+    const float4 x1 = *reinterpret_cast<const float4*>(p + 8 + 8 * cg);
+    const float mn = fmaxf(m, pm);
+    const float al = rescale(m, mn), be = __builtin_amdgcn_exp2f(pm - mn);
+    l = fmaf(l, al, pl * be);
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) orot[e] = fmaf(orot[e], al, xs[e] * be);
+    m = mn;
+  }
+  if (nt > 0) {
     float qv[8];
-    const uint4 qw = *reinterpret_cast<const uint4*>(a.q + (long long)rr * kD + 8 * cg);
-    const uint32_t ws[4] = {qw.x, qw.y, qw.z, qw.w};
+    const uint32_t qq[4] = {qw.x, qw.y, qw.z, qw.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      qv[2 * k] = bf16lo(ws[k]);
-      qv[2 * k + 1] = bf16hi(ws[k]);
+      qv[2 * k] = bf16lo(qq[k]);
+      qv[2 * k + 1] = bf16hi(qq[k]);
     }
     if ((a.flags & KVARN_Q_PREROTATED) && !a.idr) {  // q = q_rot H_D^T
       fwht128(qv, cg);
@@ -634,63 +657,77 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) qv[e] *= kInvSqrtD * sg[e];
     }
     const float qs = kLog2e * a.scale;
-    const uint8_t* tk = a.cache + a.L.tail_row(b, h, 0, 0);
-    const uint8_t* tv = a.cache + a.L.tail_row(b, h, 1, 0);
-    for (int t0 = 0; t0 < nt; t0 += 4) {  // four tail tokens per step, one softmax update
-      uint4 kw[4], vw[4];
+    float lt[KT];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int t = min(t0 + k, nt - 1);
-        if (FUSED && t == nt_old) {  // the new token, canonicalized as the append stores it
-          const long long src = ((long long)b * a.L.Hkv + h) * kD + 8 * cg;
-          float xk[8], xv[8], amax = 0.0f;
-          canon8_bf16(*reinterpret_cast<const uint4*>(a.kn + src), xk, amax);
-          canon8_bf16(*reinterpret_cast<const uint4*>(a.vn + src), xv, amax);
-          kw[k] = pack8_f16(xk);
-          vw[k] = pack8_f16(xv);
-        } else {
-          kw[k] = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
-          vw[k] = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
-        }
-      }
-      float lt[4];
+    for (int k = 0; k < KT; ++k) {
+      lt[k] = -INFINITY;
+      if (k >= kt) continue;
+      const uint32_t kk[4] = {kw[k].x, kw[k].y, kw[k].z, kw[k].w};
+      float d = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t kk[4] = {kw[k].x, kw[k].y, kw[k].z, kw[k].w};
-        float d = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d = fmaf(qv[2 * e], f16lo(kk[e]), fmaf(qv[2 * e + 1], f16hi(kk[e]), d));
-        lt[k] = t0 + k < nt ? row16_sum(d) * qs : -INFINITY;
-      }
-      const float mn = fmaxf(M, fmaxf(fmaxf(lt[0], lt[1]), fmaxf(lt[2], lt[3])));
-      const float al = __builtin_amdgcn_exp2f(M - mn);
-      Ls *= al;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        orot[e] *= al;
-        oorig[e] *= al;
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float p = __builtin_amdgcn_exp2f(lt[k] - mn);
-        Ls += p;
-        const uint32_t vv[4] = {vw[k].x, vw[k].y, vw[k].z, vw[k].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          oorig[2 * e] = fmaf(p, f16lo(vv[e]), oorig[2 * e]);
-          oorig[2 * e + 1] = fmaf(p, f16hi(vv[e]), oorig[2 * e + 1]);
-        }
-      }
-      M = mn;
+      for (int e = 0; e < 4; ++e) d = fmaf(qv[2 * e], f16lo(kk[e]), fmaf(qv[2 * e + 1], f16hi(kk[e]), d));
+      d = row16_sum(d);
+      lt[k] = gi + 16 * k < nt ? d * qs : -INFINITY;
     }
-  }
-  if (!a.idr) fwht128(orot, cg);  // all 16 lanes of the row take part, live or not
-  if (!live) return;
-  float o[8];
-  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    float mn = m;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (orot[e] * (a.idr ? 1.0f : kInvSqrtD * sg[e]) + oorig[e]) * inv;
-  store8f(a.out + (long long)rr * kD + 8 * cg, o);
+    for (int k = 0; k < KT; ++k) mn = fmaxf(mn, lt[k]);
+    const float al = rescale(m, mn);
+    l *= al;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      orot[e] *= al;
+      oorig[e] *= al;
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      if (k >= kt) break;
+      const float pw = weight(lt[k], mn);
+      l += pw;
+      const uint32_t vv[4] = {vw[k].x, vw[k].y, vw[k].z, vw[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        oorig[2 * e] = fmaf(pw, f16lo(vv[e]), oorig[2 * e]);
+        oorig[2 * e + 1] = fmaf(pw, f16hi(vv[e]), oorig[2 * e + 1]);
+      }
+    }
+    m = mn;
+  }
+  // the 16 group states, combined in group order by one thread per output channel
+  if (cg == 0) {
+    sm.m[gi] = m;
+    sm.l[gi] = l;
+  }
+  store8f(&sm.o[gi][8 * cg], orot);
+  store8f(&sm.o[gi][kD + 8 * cg], oorig);
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) M = fmaxf(M, sm.m[g]);
+  float acc = 0.0f, L = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    const float f = weight(sm.m[g], M);
+    acc = fmaf(f, sm.o[g][tid], acc);
+    L = fmaf(f, sm.l[g], L);
+  }
+  sm.fin[tid] = acc;
+  if (tid == 0) sm.lsum = L;
+  __syncthreads();
+  if (tid >= 64) return;  // wave 0 finishes; its four groups do the same work, group 0 stores
+  float fr[8], fo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    fr[e] = sm.fin[8 * cg + e];
+    fo[e] = sm.fin[kD + 8 * cg + e];
+  }
+  if (!a.idr) fwht128(fr, cg);
+  const float Ls = sm.lsum;
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (fr[e] * (a.idr ? 1.0f : kInvSqrtD * sg[e]) + fo[e]) * inv;
+  if (gi == 0) store8f(a.out + (long long)rr * kD + 8 * cg, o);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
@@ -709,8 +746,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long long rows = (long long)a.L.B * a.Hq;
-  const long long row_blocks = (rows + 15) / 16;
+  const long long row_blocks = (long long)a.L.B * a.Hq;  // one work-group per (b, q head)
   if (!a.kn) {
     hipLaunchKernelGGL((merge_kernel<false, 1, false>), dim3((unsigned)row_blocks), dim3(256), 0, st, a);
     return hipGetLastError();
