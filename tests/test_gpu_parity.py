@@ -274,6 +274,24 @@ def test_attention_after_appends_many_splits(G, n_it):
     check_attention(run_attn(gc, q, Hq), gc.host_cache(), q, Hq)
 
 
+@pytest.mark.parametrize("G,T,min_spans", [(32, 9000, 33), (64, 9000, 17)])
+def test_attention_more_spans_than_merge_groups(G, T, min_spans):
+    """One sequence, one KV head: the split gives each span few tiles, so a row has more
+    span partials than the merge has lane groups (16) and some groups fold two or three."""
+    say("attn many spans", G, T)
+    B, H, Hq = 1, 1, 2
+    k, v = outlier_kv(17, B, T, H)
+    cap = (T // G + 2) * G
+    gc = GpuCache(B, H, cap, G, 3 if G == 32 else 2)
+    gpu_prefill(gc, k, v, T)
+    ws_bytes = K.kvarn_attn_workspace_bytes(gc.g, Hq)
+    nspan = (ws_bytes - 4 * B * H) // (B * Hq * (4 + 128) * 4)
+    nsp = -(-(T // G) // (-(-(cap // G) // nspan)))  # spans holding the stored full tiles
+    assert nsp >= min_spans, (nspan, nsp)
+    q = synth.q_host(18, B, Hq)
+    check_attention(run_attn(gc, q, Hq), gc.host_cache(), q, Hq)
+
+
 # ----------------------------------------------------------------------------- full-size spot checks
 def test_full_size_llama_layer_prefill_sampled():
     """Llama-3.1-8B-shaped layer (8 KV heads, 32768 tokens, G=32, 3 iterations), the
