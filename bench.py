@@ -11,6 +11,9 @@ same step replayed as one HIP graph is reported beside it). Beside it:
     launch stream, against the 8 TB/s HBM peak;
   * decode: Phi-4-14B-shaped decode (40 layers x 10 KV heads, 40 query heads,
     batch 32, 16384 prior tokens), tokens/s of the append + fused attention loop;
+  * roundtrip: Qwen3-4B-shaped prefill (36 layers x 8 KV heads, batch 8 x 16384
+    tokens, group 64, 2 VarN iterations) followed by a bf16 dequantization of every
+    layer, with both kernels' launch times and algorithmic GB/s;
   * cpu_baseline: the CPU oracle on a bounded sample of the same prefill workload.
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -219,6 +222,69 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
                 fused_graph_wall=fused_graph_wall)
 
 
+def bench_roundtrip(K, synth, torch, steps, warmup=2, layers=36, B=8, T=16384, H=8, G=64, n_it=2, bits=2,
+                    n_inputs=4):
+    """Qwen3-4B-shaped prefill + dequantize round trip: per layer, quantize a batch of 8
+    sequences x 16384 tokens (G = 64, 2 VarN iterations, 2% of tokens with norm x50), then
+    dequantize the whole cache back to bf16. Inputs cycle over n_inputs distinct buffers."""
+    g = K.geom(B, H, T, G, n_it, bits=bits)
+    sig = synth.sign_vector(0)
+    log(f"round-trip workload: {layers} layers x B={B} x T={T} x Hkv={H}, G={G}, iters={n_it}")
+    ins = [synth.kv_device(synth.sub_seed(3, l, 0), B, T, H, law="spike", p=0.02, factor=50.0)
+           for l in range(n_inputs)]
+    caches = [K.alloc_cache(g, sig) for _ in range(layers)]
+    ko = torch.empty(B, T, H, 128, dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for l in range(layers):
+            k, v = ins[l % n_inputs]
+            if ev is not None:
+                ev[l][0].record(stream)
+            K.kvarn_quantize_prefill(g, caches[l], k, v, T, stream)
+            if ev is not None:
+                ev[l][1].record(stream)
+            K.kvarn_dequantize(g, caches[l], ko, vo, T, K.KVARN_OUT_BF16, stream)
+            if ev is not None:
+                ev[l][2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(layers)]
+    step(ev)
+    torch.cuda.synchronize()
+    pf_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    dq_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    flags = K.kvarn_cache_flags(caches[0])
+    bytes_in = 2 * B * T * H * 128 * 2                          # K and V, bf16
+    bytes_rec = 2 * B * H * (T // G) * record_bytes(G, bits)    # tile records
+    del ins, caches, ko, vo
+    torch.cuda.empty_cache()
+    pf_avg, dq_avg = sum(pf_ms) / layers, sum(dq_ms) / layers
+    pf_gbs = (bytes_in + bytes_rec) / (pf_avg * 1e-3) / 1e9
+    dq_gbs = (bytes_rec + bytes_in) / (dq_avg * 1e-3) / 1e9
+    return {
+        "workload": "qwen3-4b-shaped prefill quantize + bf16 dequantize round trip", "layers": layers,
+        "batch": B, "tokens": T, "kv_heads": H, "group": G, "varn_iters": n_it, "bits": bits,
+        "input": "bf16, outlier channels x20, 2% of tokens x50",
+        "ms_per_step": round(wall * 1e3 / steps, 3), "steps": steps,
+        "prefill": {"kernel": f"prefill_kernel<2,false,{'false' if bits == 2 else 'true'},1>",
+                    "avg_launch_us": round(pf_avg * 1e3, 2), "bytes_per_launch": bytes_in + bytes_rec,
+                    "achieved": round(pf_gbs, 1), "frac": round(pf_gbs / HBM_PEAK_GBS, 4), "unit": "GB/s"},
+        "dequantize": {"kernel": "dequant_kernel (bf16 out)", "avg_launch_us": round(dq_avg * 1e3, 2),
+                       "bytes_per_launch": bytes_rec + bytes_in, "achieved": round(dq_gbs, 1),
+                       "frac": round(dq_gbs / HBM_PEAK_GBS, 4), "unit": "GB/s"},
+        "flags": flags,
+    }
+
+
 def bench_bf16_decode(torch, steps=8, warmup=2, layers=40, B=32, H=10, Hq=40, T=16384):
     """Plain bf16 decode attention over a bf16 KV cache of the same shapes (no quantization):
     per layer scores = q K^T (K stored transposed, [B][H][D][T]), fp32 softmax, out = p V,
@@ -341,6 +407,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-roundtrip", action="store_true",
+                    help="skip the Qwen3-4B-shaped prefill + dequantize round trip")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--cpu-layers", type=int, default=5, help="layers of the prefill workload the oracle runs")
@@ -433,6 +501,12 @@ def main():
             best = max(res["decode"]["graph_tokens_per_s"], res["decode"]["fused_graph_tokens_per_s"])
             res["decode"]["speedup_vs_bf16"] = round(best / bf["tokens_per_s"], 2)
             log(f"bf16 baseline: {bf}")
+    if not args.no_roundtrip:
+        rt = bench_roundtrip(K, synth, torch, max(1, args.steps // 3), bits=args.bits)
+        res["roundtrip"] = rt
+        log(f"round trip: {rt['ms_per_step']} ms/step; prefill {rt['prefill']['avg_launch_us']} us "
+            f"({rt['prefill']['achieved']} GB/s), dequantize {rt['dequantize']['avg_launch_us']} us "
+            f"({rt['dequantize']['achieved']} GB/s) per layer")
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(synth, args.cpu_tokens, args.cpu_layers)

@@ -37,37 +37,44 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   const int nfull = n / L.G;
   const int t0 = blk * 32 + rg * 8;
   void* outp = s ? a.vo : a.ko;
-  auto store_row = [&](int t, const float (&y)[8]) {
+  // sgn[d]: sign bits XORed into the output of channels (2d, 2d + 1) of the lane, at bits
+  // 15 and 31 (a packed bf16 pair's sign bits): sigma for rotated tokens, 0 otherwise
+  auto store_row = [&](int t, const float (&y)[8], const uint32_t (&sgn)[4]) {
     if (t >= a.maxT) return;
     const long long off = (((long long)b * a.maxT + t) * L.Hkv + h) * kD + 8 * cg;
-    if (a.bf16out) {
-      uint4 o;
-      o.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
-      o.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
-      o.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
-      o.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(outp) + off) = o;
+    if (a.bf16out) {  // round half to even (v_cvt_pk_bf16_f32), then the sign
+      uint32_t o[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        o[d] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){y[2 * d], y[2 * d + 1]}, bf2v)) ^ sgn[d];
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(outp) + off) = make_uint4(o[0], o[1], o[2], o[3]);
     } else {
-      store8f(reinterpret_cast<float*>(outp) + off, y);
+      float z[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        z[2 * d] = __int_as_float(__float_as_int(y[2 * d]) ^ (int)(sgn[d] << 16));
+        z[2 * d + 1] = __int_as_float(__float_as_int(y[2 * d + 1]) ^ (int)(sgn[d] & 0x80000000u));
+      }
+      store8f(reinterpret_cast<float*>(outp) + off, z);
     }
   };
+  const uint32_t nosign[4] = {0u, 0u, 0u, 0u};
   const int tile = (blk * 32) / L.G;
   const long long roff = tile < nfull ? record_at(a.cache, L, b, h, tile, s) : 0;
   if (tile < nfull && roff < 0) {  // paged cache without a page for this tile: zeros
     const float zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) store_row(blk * 32 + rg * 8 + i, zero);
+    for (int i = 0; i < 8; ++i) store_row(blk * 32 + rg * 8 + i, zero, nosign);
   } else if (tile < nfull) {
     const uint8_t* rec = a.cache + roff;
     const int G = L.G;
     const int ro = G * kD * L.bits / 8, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
     const int tw0 = (blk * 32) % G + rg * 8;
-    float cj[8], sj[8], zj[8], ri[8], sg[8];
+    float cj[8], sj[8], zj[8], ri[8];
     widen8_f16(*reinterpret_cast<const uint4*>(rec + co + 16 * cg), cj);
     widen8_f16(*reinterpret_cast<const uint4*>(rec + so + 16 * cg), sj);
     widen8_f16(*reinterpret_cast<const uint4*>(rec + zo + 16 * cg), zj);
     widen8_f16(*reinterpret_cast<const uint4*>(rec + ro + 2 * tw0), ri);
-    load_sigma(a.cache, cg, sg);
     float w[8][8];
     if (s == 0) {
       // channel j = 8cg + e = 16m + 2w + d (m = cg/2, w = 4(cg%2) + e/2, d = e%2) sits in
@@ -137,17 +144,32 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         }
       }
     }
+    // x = r (c s q + c z) H_syl^T diag(sigma) / sqrt(D): the per-channel factors take
+    // 1/sqrt(D) (the transform is linear), sigma is a sign flip at the store
     const bool idr = (L.variant & KVARN_VARIANT_NO_ROTATION) != 0;  // uniform
+    const float kf = idr ? 1.0f : kInvSqrtD;
+    float csj[8], czj[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      csj[e] = cj[e] * sj[e] * kf;
+      czj[e] = cj[e] * zj[e] * kf;
+    }
+    uint32_t sgn[4] = {0u, 0u, 0u, 0u};
+    if (!idr) {
+      const uint2 sw = *reinterpret_cast<const uint2*>(a.cache + kSigmaOff + 8 * cg);  // int8 sigma
+      const uint32_t sb[2] = {sw.x, sw.y};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t x = sb[d >> 1] >> (16 * (d & 1));  // bytes: sigma of channels 2d, 2d + 1
+        sgn[d] = ((x << 8) & 0x8000u) | ((x << 16) & 0x80000000u);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[i][e] = (ri[i] * cj[e]) * fmaf(sj[e], w[i][e], zj[e]);
-      if (!idr) {
-        fwht128(w[i], cg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[i][e] *= kInvSqrtD * sg[e];
-      }
-      store_row(blk * 32 + rg * 8 + i, w[i]);
+      for (int e = 0; e < 8; ++e) w[i][e] = ri[i] * fmaf(csj[e], w[i][e], czj[e]);
+      if (!idr) fwht128(w[i], cg);
+      store_row(blk * 32 + rg * 8 + i, w[i], sgn);
     }
   } else {
 #pragma unroll
@@ -160,7 +182,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = 0.0f;
       }
-      store_row(t, y);
+      store_row(t, y, nosign);
     }
   }
 }

@@ -105,6 +105,7 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 
 // ----------------------------------------------------------------------------- lane exchange
 // Every control used here reads a valid lane for every lane, so no "old" value is needed.
@@ -199,10 +200,6 @@ __device__ __forceinline__ uint32_t f16bits(float x) {  // RNE, x assumed within
 }
 __device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x; }
 
-__device__ __forceinline__ uint32_t bf16_rne(float x) {  // f32 -> bf16 bits, half to even
-  const uint32_t u = (uint32_t)__float_as_int(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 // ----------------------------------------------------------------------------- Hadamard
 __device__ __forceinline__ void fwht8(float (&a)[8]) {
 #pragma unroll
