@@ -199,7 +199,11 @@ kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_ou
   a.maxT = max_tokens;
   a.bf16out = out_dtype == KVARN_OUT_BF16;
   a.nblk = (max_tokens + 31) / 32;
-  a.jobs = (long long)g->batch * g->num_kv_heads * 2 * a.nblk;
+  const long long jobs = (long long)g->batch * g->num_kv_heads * 2 * a.nblk;
+  if (jobs >= (1LL << 31)) return KVARN_ERR_RANGE;
+  a.jobs = (int)jobs;
+  a.dhkv = make_fastdiv((uint32_t)g->num_kv_heads);
+  a.dnblk = make_fastdiv((uint32_t)a.nblk);
   return dev(launch_dequant(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -23,16 +23,18 @@ __device__ __forceinline__ void widen8_f16(const uint4 w, float (&x)[8]) {
 // ----------------------------------------------------------------------------- dequantize
 // One wave per 32-token block of one (b, h, s): undo grid and scales, rotate back.
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: job math on the SALU
+  const int lane = threadIdx.x & 63;
   const int rg = lane >> 4, cg = lane & 15;
   const Layout& L = a.L;
-  const long long job = (long long)blockIdx.x * 4 + wave;
-  if (job >= a.jobs) return;
+  const uint32_t job = blockIdx.x * 4u + (uint32_t)wave;
+  if (job >= (uint32_t)a.jobs) return;
   // job = ((b * nblk + blk) * 2 + s) * Hkv + h
-  const int h = (int)(job % L.Hkv);
-  const int s = (int)((job / L.Hkv) % 2);
-  const int blk = (int)((job / L.Hkv / 2) % a.nblk);
-  const int b = (int)(job / L.Hkv / 2 / a.nblk);
+  const uint32_t q1 = fdiv(job, a.dhkv), q2 = q1 >> 1, q3 = fdiv(q2, a.dnblk);
+  const int h = (int)(job - q1 * (uint32_t)L.Hkv);
+  const int s = (int)(q1 & 1u);
+  const int blk = (int)(q2 - q3 * (uint32_t)a.nblk);
+  const int b = (int)q3;
   const int n = *reinterpret_cast<const int32_t*>(a.cache + L.len_off(b, h, s));
   const int nfull = n / L.G;
   const int t0 = blk * 32 + rg * 8;

@@ -61,7 +61,8 @@ struct DequantArgs {
   void* ko;
   void* vo;
   int maxT, bf16out, nblk;  // nblk = ceil(maxT / 32)
-  long long jobs;           // B * Hkv * 2 * nblk
+  int jobs;                 // B * Hkv * 2 * nblk (< 2^31)
+  FastDiv dhkv, dnblk;      // division by Hkv and by nblk
 };
 
 struct AttnArgs {
