@@ -41,9 +41,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   void* outp = s ? a.vo : a.ko;
   // sgn[d]: sign bits XORed into the output of channels (2d, 2d + 1) of the lane, at bits
   // 15 and 31 (a packed bf16 pair's sign bits): sigma for rotated tokens, 0 otherwise
+  // output row of this lane's first token (t0), and the step from one token to the next
+  const long long off0 = (((long long)b * a.maxT + t0) * L.Hkv + h) * kD + 8 * cg;
+  const long long tstep = (long long)L.Hkv * kD;
   auto store_row = [&](int t, const float (&y)[8], const uint32_t (&sgn)[4]) {
     if (t >= a.maxT) return;
-    const long long off = (((long long)b * a.maxT + t) * L.Hkv + h) * kD + 8 * cg;
+    const long long off = off0 + (t - t0) * tstep;
     if (a.bf16out) {  // round half to even (v_cvt_pk_bf16_f32), then the sign
       uint32_t o[4];
 #pragma unroll
