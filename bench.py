@@ -11,6 +11,8 @@ same step replayed as one HIP graph is reported beside it). Beside it:
     launch stream, against the 8 TB/s HBM peak;
   * decode: Phi-4-14B-shaped decode (40 layers x 10 KV heads, 40 query heads,
     batch 32, 16384 prior tokens), tokens/s of the append + fused attention loop;
+  * long_decode: the long-reasoning stress shape (32 layers x 8 KV heads, 32 query heads,
+    batch 64 x 32768-token contexts, Student-t token norms), decode tokens/s;
   * roundtrip: Qwen3-4B-shaped prefill (36 layers x 8 KV heads, batch 8 x 16384
     tokens, group 64, 2 VarN iterations) followed by a bf16 dequantization of every
     layer, with both kernels' launch times and algorithmic GB/s;
@@ -97,18 +99,19 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
 
 
 def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40, T0=16384, cap=17408, G=32,
-                 n_it=3, pool=128, bits=2):
+                 n_it=3, pool=128, bits=2, kv_kw=None):
     g = K.geom(B, H, cap, G, n_it, bits=bits)
     sig = synth.sign_vector(0)
+    kv_kw = kv_kw or {}
     log(f"decode workload: {layers} layers x B={B} x Hkv={H} x Hq={Hq}, {T0} prior tokens, {steps} timed steps")
-    k0, v0 = synth.kv_device(synth.sub_seed(4, 0, 0), B, T0, H)
+    k0, v0 = synth.kv_device(synth.sub_seed(4, 0, 0), B, T0, H, **kv_kw)
     caches = []
     for l in range(layers):
         c = K.alloc_cache(g, sig)
         K.kvarn_quantize_prefill(g, c, k0, v0, T0)
         caches.append(c)
     del k0, v0
-    kp, vp = synth.kv_device(synth.sub_seed(4, 0, 1), B, pool, H)     # [B][pool][H][D]
+    kp, vp = synth.kv_device(synth.sub_seed(4, 0, 1), B, pool, H, **kv_kw)  # [B][pool][H][D]
     kp = kp.transpose(0, 1).contiguous()                              # [pool][B][H][D]
     vp = vp.transpose(0, 1).contiguous()
     qp = torch.stack([synth.q_device(synth.sub_seed(4, 0, 2, s), B, Hq) for s in range(pool)])
@@ -407,6 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=32)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-reasoning decode (64 x 32768-token contexts, Llama-3.1-8B KV geometry)")
     ap.add_argument("--no-roundtrip", action="store_true",
                     help="skip the Qwen3-4B-shaped prefill + dequantize round trip")
     ap.add_argument("--no-cpu", action="store_true")
@@ -501,6 +506,25 @@ def main():
             best = max(res["decode"]["graph_tokens_per_s"], res["decode"]["fused_graph_tokens_per_s"])
             res["decode"]["speedup_vs_bf16"] = round(best / bf["tokens_per_s"], 2)
             log(f"bf16 baseline: {bf}")
+    if not args.no_long:
+        torch.cuda.empty_cache()
+        lg = bench_decode(K, synth, torch, 8, warmup=2, layers=32, B=64, H=8, Hq=32, T0=32768, cap=36864,
+                          bits=args.bits, kv_kw=dict(law="student_t", nu=3.0, n_outlier_ch=8, ch_mult=30.0))
+        lam = sorted(lg["attn_ms"])
+        la_avg = sum(lam) / len(lam)
+        res["long_decode"] = {
+            "workload": "long-reasoning stress decode: llama3.1-8b KV geometry, 64 x 32768-token contexts",
+            "layers": lg["layers"], "batch": lg["B"], "kv_heads": lg["H"], "q_heads": lg["Hq"],
+            "context_at_start": lg["ctx_start"], "input": "bf16, Student-t (nu 3) token norms, 8 outlier channels x30",
+            "tokens_per_s": round(lg["B"] * lg["steps"] / lg["wall"], 1),
+            "ms_per_step": round(lg["wall"] * 1e3 / lg["steps"], 3), "steps_timed": lg["steps"],
+            "fused_tokens_per_s": round(lg["B"] * lg["steps"] / lg["fused_wall"], 1),
+            "attn_avg_us": round(la_avg * 1e3, 2),
+            "attn_GBps": round(lg["attn_bytes"] / (la_avg * 1e-3) / 1e9, 1),
+            "attn_frac": round(lg["attn_bytes"] / (la_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "flags": lg["flags"]}
+        log(f"long decode: {res['long_decode']['tokens_per_s']} tok/s eager, "
+            f"{res['long_decode']['fused_tokens_per_s']} fused; attn {res['long_decode']['attn_avg_us']} us "
+            f"({res['long_decode']['attn_GBps']} GB/s) per layer-step")
     if not args.no_roundtrip:
         rt = bench_roundtrip(K, synth, torch, max(1, args.steps // 3), bits=args.bits)
         res["roundtrip"] = rt
