@@ -200,7 +200,7 @@ kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_ou
   a.bf16out = out_dtype == KVARN_OUT_BF16;
   a.nblk = (max_tokens + 31) / 32;
   const long long jobs = (long long)g->batch * g->num_kv_heads * 2 * a.nblk;
-  if (jobs >= (1LL << 31)) return KVARN_ERR_RANGE;
+  if (jobs >= (1LL << 31)) return KVARN_ERR_RANGE;  // defensive: check_geom's bound keeps it below 2^29
   a.jobs = (int)jobs;
   a.dhkv = make_fastdiv((uint32_t)g->num_kv_heads);
   a.dnblk = make_fastdiv((uint32_t)a.nblk);

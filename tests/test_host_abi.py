@@ -125,7 +125,8 @@ def test_argument_errors_return_before_any_launch():
     assert _code(K.kvarn_dequantize, g, A, A, A2, 129, 0, 0) == K.KVARN_ERR_RANGE
     assert _code(K.kvarn_dequantize, g, A, A, A2, 64, 7, 0) == K.KVARN_ERR_UNSUPPORTED
     assert _code(K.kvarn_dequantize, g, A, MIS, A2, 64, 0, 0) == K.KVARN_ERR_ALIGN
-    # 2^31 or more 32-token jobs (B * Hkv * 2 * ceil(T / 32)) are refused before any launch
+    # a geometry past the element-count limit (B * capacity * Hkv * D >= 2^40) is refused
+    # before any launch, which also keeps every kernel's job count below 2^31
     huge = K.geom(1 << 16, 64, 1 << 16, 32, 3)
     assert _code(K.kvarn_dequantize, huge, A, A, A2, 1 << 16, 0, 0) == K.KVARN_ERR_RANGE
     ws = K.kvarn_attn_workspace_bytes(g, 4)
