@@ -181,11 +181,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
-  int bid = blockIdx.x;
+  // Work-group i runs on XCD i % 8, and each XCD has its own L2. The logical job is
+  // remapped so that every XCD takes a contiguous range of jobs, and the query-head groups
+  // of one span are adjacent in it: work-groups that stream the same K/V records run on
+  // one XCD at about the same time and share its L2.
+  int bid;
+  {
+    const int nb = gridDim.x, q = nb >> 3, r = nb & 7, x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    bid = x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+  }
+  const int qg = bid % a.nqg;  // logical job = ((b Hkv + h) nspan + span) nqg + qg
+  bid /= a.nqg;
   const int span = bid % a.nspan;
   bid /= a.nspan;
-  const int qg = bid % a.nqg;
-  bid /= a.nqg;
   const int h = bid % L.Hkv, b = bid / L.Hkv;
   const int n = *reinterpret_cast<const int32_t*>(a.cache + L.len_off(b, h, 0));
   if (span == 0 && qg == 0 && threadIdx.x == 0) a.lens_ws[b * L.Hkv + h] = n;  // for the merge
