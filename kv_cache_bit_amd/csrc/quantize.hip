@@ -66,12 +66,17 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) raw[mb][ks] = *reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks);
+    SigMask m[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
+    for (int ks = 0; ks < 4; ++ks) m[ks] = masks_v<ABL>(idr, hdr, 4 * ks + g);
+    // every input load is issued before any of them is used: one memory round trip per
+    // tile (left to itself the scheduler issues the second token block's loads only after
+    // the first block's rotation has started)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) av[mb][ks] = canon_a<false>(raw[mb][ks], m);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) av[mb][ks] = canon_a<false>(raw[mb][ks], m[ks]);
   }
   st = rotate_squares_v<ABL>(idr, av, hf, p, c);
   if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion): redo saturating
