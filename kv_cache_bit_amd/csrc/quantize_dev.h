@@ -245,15 +245,18 @@ __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& 
   }
 }
 
-// Rotation fused with the squares and the first token-axis sums (u = 1): each chain's
-// W' block is squared as soon as it is complete, so the fp32 block is never held whole.
-// Returns the row total of the lane's own token (see row_rs8).
+// Rotation fused with the squares: each chain's W' block is squared as soon as it is
+// complete, so the fp32 block is never held whole. Returns the first token-axis sum
+// (u = 1) of the lane's own token, 16 (c/8) + 4 g + (c/2) % 4 (identical in lanes c and
+// c ^ 1), from the Gram diagonal instead of the squares: with H_syl H_syl^T = D I the row
+// sum of W'^2 is D times the row sum of x^2 (1 times it for the identity), and diag(X X^T)
+// comes exactly from the matrix cores, since the B operand X^T of the 16x16x32 MFMA is
+// held in the same registers as the A operand X (lane (g, c): token c, channels 8 g ..
+// 8 g + 7 of the K step). Lane (g, c) of the Gram block holds rows 4 g + i at column c:
+// the diagonal sits in lanes c = 4 g + j at element j, and the owner lane fetches it.
 template <bool ID>
 __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, float (&p)[2][8][4],
                                                 int c) {
-  float tp[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) tp[k] = 0.0f;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -269,13 +272,24 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
       asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
                    "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[mb][nb][i] = s[i] * s[i];
-        tp[4 * mb + i] += p[mb][nb][i];
-      }
+      for (int i = 0; i < 4; ++i) p[mb][nb][i] = s[i] * s[i];
     }
   }
-  return row_rs8(tp, c);
+  float d[2];  // this lane's diagonal candidate of each token block (element c % 4)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    f4v gm = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) gm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], a[mb][ks], gm, 0, 0, 0);
+    asm volatile("" : "+v"(gm) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]));
+    const float lo = (c & 1) ? gm[1] : gm[0], hi = (c & 1) ? gm[3] : gm[2];
+    d[mb] = (c & 2) ? hi : lo;
+  }
+  const int g = (int)(threadIdx.x & 63) >> 4;
+  const int src = 4 * (20 * g + ((c >> 1) & 3));  // byte address of lane 16 g + 4 g + (c/2) % 4
+  const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(d[0])));
+  const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(d[1])));
+  return ((c >> 3) ? x1 : x0) * (ID ? 1.0f : (float)kD);
 }
 
 // Dispatch for the ablation build (ABL): the identity rotation is a runtime choice there;
