@@ -85,7 +85,7 @@ typedef enum {
     KVARN_ERR_NULL = 1,         /* a required pointer is NULL                              */
     KVARN_ERR_ALIGN = 2,        /* a device pointer is not 16-byte aligned                 */
     KVARN_ERR_GEOM = 3,         /* inconsistent geometry or sizes                          */
-    KVARN_ERR_UNSUPPORTED = 4,  /* valid request outside what this build implements        */
+    KVARN_ERR_UNSUPPORTED = 4,  /* valid request outside what the library implements       */
     KVARN_ERR_RANGE = 5,        /* token count, head count or buffer size out of range     */
     KVARN_ERR_DEVICE = 6        /* the HIP runtime reported an error                       */
 } kvarn_status;

@@ -9,7 +9,7 @@
 
 namespace kvarn {
 
-constexpr int kD = 128;                     // head_dim supported by this build
+constexpr int kD = 128;                     // the one head_dim the kernels support
 constexpr uint32_t kMagic = 0x4E52564Bu;    // 'K' 'V' 'R' 'N'
 constexpr int kVersion = 1;
 constexpr int kHdrFixed = 512;              // len[] offset

@@ -1,5 +1,4 @@
-"""Pins of the oracle's 3- and 4-bit codes (beyond the pages' 2 bits; the survey's bit-width
-row): the grid's closed form, the codes against brute force, the record layout as bit
+"""Pins of the oracle's 3- and 4-bit codes (an extension beyond the pages' 2 bits): the grid's closed form, the codes against brute force, the record layout as bit
 planes over the pinned 2-bit layout, hand-worked positions of the 1-bit plane, and the
 error falling with each extra bit.
 """
