@@ -9,10 +9,12 @@
 // Work mapping. A tile (G tokens x 128 channels of one batch row, kv head and
 // stream) is handled by G/32 waves, one 32-token block each.
 //   * Rotation on the matrix cores: the canonical inputs are exact in fp16 and the
-//     Sylvester matrix is +-1, so W' = (x * sigma) H_syl is computed exactly by
-//     v_mfma_f32_16x16x32_f16 with fp32 accumulation (2 token blocks x 8 channel
-//     blocks x 4 K-steps). H_syl's 32x16 blocks are one of four register fragments
-//     (+-F, +-G), so the 32 KiB matrix never leaves registers.
+//     Sylvester matrix is +-1, so the products are exact in v_mfma_f32_16x16x32_f16
+//     with fp32 accumulation. H_syl of order 128 is H_4 (x) H_32: each 32-channel K step
+//     goes through H_32 on the matrix cores (its two 32x16 halves are the register
+//     fragments F and G, so no matrix leaves registers), and the four K steps are
+//     combined by the 4-point transform H_4 in registers (16 MFMAs and 128 adds per
+//     32-token block).
 //   * The MFMA output leaves lane (g = lane/16, c = lane%16) with tokens 16mb + 4g + i
 //     (mb < 2, i < 4) and channels 16nb + c (nb < 8): a token-axis sum is 8 in-lane
 //     terms plus a DPP reduction over the 16 lanes of a row; a channel-axis sum is 8
@@ -109,7 +111,9 @@ __device__ __forceinline__ void col_gather8(const float (&own)[2], float (&v)[8]
 // block nb: lane (g, c) holds H_syl[32ks + 8g + e][16nb + c], e < 8. With
 // popcount((32ks + 8g + e) & (16nb + c)) = pc(e & c%8) + (g%2)(c/8) + (g/2)(nb%2)
 // + pc(ks & nb/2), the fragment is F (nb even) or G = F * (-1)^(g/2) (nb odd), times
-// the uniform sign (-1)^pc(ks & nb/2).
+// the uniform sign (-1)^pc(ks & nb/2), which is H_4[ks][nb/2]: the Hadamard path uses F
+// and G (the two halves of H_32) and applies H_4 after the products; the identity
+// ablation fills the four slots with its own one-hot fragments.
 struct Frags {
   h8v v[4];  // F, -F, G, -G
 };
@@ -140,9 +144,6 @@ __device__ __forceinline__ Frags hadamard_frags(int lane) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) h.v[q] = __builtin_bit_cast(h8v, p[q]);
   return h;
-}
-__device__ __forceinline__ int frag_index(int ks, int nb) {
-  return ((nb & 1) << 1) | (__builtin_popcount(ks & (nb >> 1)) & 1);
 }
 // Identity in place of H_syl (the "VarN only" ablation): block nb takes the single K-step
 // ks = nb/2, whose B fragment is one-hot: lane (g, c) holds 1 at e = c%8 iff
@@ -219,28 +220,62 @@ __device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp1
 // W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]; with ID the
 // identity fragments make W' = A (one MFMA per block).
 //
+// H_syl of order 128 is H_4 (x) H_32 (channel 32 q + j), so the Hadamard path takes each
+// K step's 32 channels through H_32 on the matrix cores (F for output half h = nb % 2,
+// G for h = 1: two MFMAs per token block and K step) and combines the four K steps with
+// the 4-point transform H_4 in registers, output block nb = 2 nb' + h:
+//   nb' = 0: y0 + y1 + y2 + y3   nb' = 1: y0 - y1 + y2 - y3
+//   nb' = 2: y0 + y1 - y2 - y3   nb' = 3: y0 - y1 - y2 + y3
+// (16 MFMAs and 128 adds per 32-token block instead of 64 MFMAs).
+//
 // An MFMA whose destination shares registers with its A or B source reads clobbered
-// rows on this hardware. After each accumulation chain an empty asm takes the chain's
+// rows on this hardware. After each MFMA (or accumulation chain) an empty asm takes the
 // result as read-write and all its A and B fragments as inputs: the data dependency
-// pins it after the chain's MFMAs, so every source is still live when each of them
-// issues and the register allocator cannot hand a source's registers to the result.
+// pins it after the MFMAs, so every source is still live when each of them issues and
+// the register allocator cannot hand a source's registers to the result.
+__device__ __forceinline__ void h32_steps(const h8v (&a)[4], const Frags& hf, int h, f4v (&y)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    f4v t = {0.0f, 0.0f, 0.0f, 0.0f};
+    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], hf.v[2 * h], t, 0, 0, 0);
+    asm volatile("" : "+v"(t) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(hf.v[0]), "v"(hf.v[2]));
+    y[ks] = t;
+  }
+}
+// out[nb'] = sum_ks H_4[ks][nb'] y[ks], element by element
+__device__ __forceinline__ void h4_combine(const f4v (&y)[4], f4v (&out)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float s01 = y[0][i] + y[1][i], d01 = y[0][i] - y[1][i];
+    const float s23 = y[2][i] + y[3][i], d23 = y[2][i] - y[3][i];
+    out[0][i] = s01 + s23;
+    out[1][i] = d01 + d23;
+    out[2][i] = s01 - s23;
+    out[3][i] = d01 - d23;
+  }
+}
 template <bool ID>
 __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& hf, f4v (&acc)[2][8]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
+    if constexpr (ID) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (ID) {
+      for (int nb = 0; nb < 8; ++nb) {
+        f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+        asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
+                     "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
+        acc[mb][nb] = s;
       }
-      asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
-                   "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
-      acc[mb][nb] = s;
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f4v y[4], w[4];
+        h32_steps(a[mb], hf, h, y);
+        h4_combine(y, w);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[mb][2 * q + h] = w[q];
+      }
     }
   }
 }
@@ -259,20 +294,27 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
                                                 int c) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
+    if constexpr (ID) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (ID) {
+      for (int nb = 0; nb < 8; ++nb) {
+        f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
-      } else {
+        asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
+                     "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], hf.v[frag_index(ks, nb)], s, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) p[mb][nb][i] = s[i] * s[i];
       }
-      asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
-                   "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
+    } else {  // H_4 (x) H_32, as in rotate_block; each block is squared once combined
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[mb][nb][i] = s[i] * s[i];
+      for (int h = 0; h < 2; ++h) {
+        f4v y[4], w[4];
+        h32_steps(a[mb], hf, h, y);
+        h4_combine(y, w);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[mb][2 * q + h][i] = w[q][i] * w[q][i];
+      }
     }
   }
   float d[2];  // this lane's diagonal candidate of each token block (element c % 4)
