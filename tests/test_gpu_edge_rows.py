@@ -1,0 +1,49 @@
+"""GPU parity on token rows at the edges of the input range: all-zero rows, and rows far
+below fp16's normal range (f16 subnormals after canonicalization), inside tiles of
+ordinary outlier-bearing rows. The first token-axis pass of VarN takes its sums from the
+Gram diagonal (exact products of the canonical inputs on the matrix cores); with one
+iteration those sums fix the token scale r directly. Run on an MI355X: pytest -m gpu.
+"""
+import numpy as np
+import pytest
+
+from kv_cache_bit_amd import kvarn as K
+from kv_cache_bit_amd import synth
+
+from parity import GpuCache, check_prefill, from_u16, gpu_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def edge_rows_kv(seed, B, T, H, span):
+    k, v = synth.kv_host(seed, B, T, H)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    for arr in (k, v):
+        rows = rng.choice(span, size=6, replace=False)
+        tiny = rng.standard_normal((2, B, H, 128)).astype(np.float32)
+        for j in range(2):
+            arr[:, rows[j]] = 0                                                         # all zero
+            arr[:, rows[2 + j]] = synth.f32_to_bf16_bits(tiny[j] * 1e-6)                 # subnormal in fp16
+            arr[:, rows[4 + j]] = synth.f32_to_bf16_bits(tiny[j] * 2.0 ** -22)           # a few fp16 ulps
+    return k, v
+
+
+@pytest.mark.parametrize("G,n_it", [(32, 1), (32, 3), (64, 2)])
+def test_prefill_zero_and_tiny_token_rows(G, n_it):
+    print("[case] zero/tiny token rows", G, n_it, flush=True)
+    B, H = 1, 2
+    T = 2 * G + 5
+    k, v = edge_rows_kv(11, B, T, H, 2 * G)
+    cap = (T // G + 1) * G
+    gc = GpuCache(B, H, cap, G, n_it)
+    gpu_prefill(gc, k, v, T)
+    check_prefill(gc, k, v, T)
+    # the same tokens through single-token appends give the same bytes
+    ap = GpuCache(B, H, cap, G, n_it)
+    gpu_prefill(ap, k, v, 0)
+    kd, vd = from_u16(k), from_u16(v)
+    for t in range(T):
+        K.kvarn_append_decode(ap.g, ap.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+    ha, hb = gc.host_cache(), ap.host_cache()
+    m = ha.defined_mask()
+    assert np.array_equal(ha.buf[m], hb.buf[m])
