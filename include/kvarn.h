@@ -28,8 +28,10 @@
  *   header  align256(512 + 8*B*Hkv) bytes:
  *           u32 magic 0x4E52564B, u32 version 1, i32 geom[7] (batch, num_kv_heads,
  *           head_dim, capacity, group, varn_iters, bits), u32 flags (sticky),
- *           u32 variant at byte 40, i8 sigma[D] at byte 64, i32 len[B][Hkv][2]
- *           at byte 512;
+ *           u32 variant at byte 40, i8 sigma[D] at byte 64, u32 sign words[D/2]
+ *           at byte 192 (word d: bit 15 set iff sigma[2d] = -1, bit 31 set iff
+ *           sigma[2d+1] = -1, the sign bits of a packed pair of 16-bit floats),
+ *           i32 len[B][Hkv][2] at byte 512;
  *   tiles   [B][Hkv][capacity/G][2 (K,V)][TR] tile records, region padded to 256 B;
  *           paged caches (num_pages > 0) instead hold a pool of num_pages pages,
  *           [num_pages][Hkv][2][TR] (one page = one group of G tokens of one sequence,
@@ -130,7 +132,7 @@ KVARN_API int kvarn_format_version(void);
 /* Size in bytes of a cache buffer for geometry *g. Host only. */
 KVARN_API kvarn_status kvarn_cache_bytes(const kvarn_geom* g, size_t* bytes);
 
-/* Write the header (magic, version, geometry, sigma) and zero len[] and flags.
+/* Write the header (magic, version, geometry, sigma and its sign words) and zero len[] and flags.
  * signs_host: host int8[head_dim], each +1 or -1: the random signs of H_D
  * (ai-paper-analysis page, section 3.1: randomized Hadamard matrix).
  * Asynchronous on `stream`; signs_host may be reused once the call returns. */

@@ -203,13 +203,18 @@ __global__ void init_kernel(InitArgs a) {
     h32[9] = 0;  // flags
     h32[10] = a.variant;
   }
-  for (int k = t; k < 128; k += blockDim.x) {  // bytes 44..511: pad, sigma, pad
+  for (int k = t; k < 128; k += blockDim.x) {  // bytes 44..511: pad, sigma, sign words, pad
     const int off = 44 + 4 * k;
     if (off >= kHdrFixed) break;
     uint32_t w = 0;
-    for (int q = 0; q < 4; ++q) {
-      const int byte = off + q;
-      if (byte >= kSigmaOff && byte < kSigmaOff + kD) w |= (uint32_t)(uint8_t)a.sigma[byte - kSigmaOff] << (8 * q);
+    if (off >= kSignOff && off < kSignOff + 2 * kD) {  // word d: signs of channels 2d, 2d + 1
+      const int d = (off - kSignOff) / 4;
+      w = (a.sigma[2 * d] < 0 ? 0x8000u : 0u) | (a.sigma[2 * d + 1] < 0 ? 0x80000000u : 0u);
+    } else {
+      for (int q = 0; q < 4; ++q) {
+        const int byte = off + q;
+        if (byte >= kSigmaOff && byte < kSigmaOff + kD) w |= (uint32_t)(uint8_t)a.sigma[byte - kSigmaOff] << (8 * q);
+      }
     }
     h32[off / 4] = w;
   }

@@ -14,6 +14,8 @@ constexpr uint32_t kMagic = 0x4E52564Bu;    // 'K' 'V' 'R' 'N'
 constexpr int kVersion = 1;
 constexpr int kHdrFixed = 512;              // len[] offset
 constexpr int kSigmaOff = 64;
+constexpr int kSignOff = 192;               // sign words [64]: bit 15 / bit 31 of word d set
+                                            // where sigma of channel 2d / 2d + 1 is -1
 constexpr int kFlagsOff = 36;
 constexpr float kFp16Max = 65504.0f;
 constexpr float kScaleMin = 6.103515625e-05f;          // 2^-14

@@ -168,23 +168,15 @@ __device__ __forceinline__ Frags identity_frags(int lane) {
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
-// Sign masks for the 8 channels of chunk `chunk` (channels 8 chunk .. +7): bit 31 of
-// lo[d] / hi[d] is set where sigma of channel 2d / 2d+1 is -1.
+// Sign words of the 8 channels of chunk `chunk` (channels 8 chunk .. +7), from the
+// header table written at cache init: bit 15 / bit 31 of m[d] is set where sigma of
+// channel 2d / 2d + 1 is -1, i.e. at the sign bits of a packed pair of 16-bit floats.
 struct SigMask {
-  uint32_t lo[4], hi[4];
+  uint32_t m[4];
 };
 __device__ __forceinline__ SigMask sigma_masks(const uint8_t* hdr, int chunk) {
-  const uint2 s = *reinterpret_cast<const uint2*>(hdr + kSigmaOff + 8 * chunk);
-  SigMask m;
-  m.lo[0] = (s.x & 0x80u) << 24;
-  m.hi[0] = (s.x & 0x8000u) << 16;
-  m.lo[1] = (s.x & 0x800000u) << 8;
-  m.hi[1] = s.x & 0x80000000u;
-  m.lo[2] = (s.y & 0x80u) << 24;
-  m.hi[2] = (s.y & 0x8000u) << 16;
-  m.lo[3] = (s.y & 0x800000u) << 8;
-  m.hi[3] = s.y & 0x80000000u;
-  return m;
+  const uint4 s = *reinterpret_cast<const uint4*>(hdr + kSignOff + 16 * chunk);
+  return SigMask{{s.x, s.y, s.z, s.w}};
 }
 
 // two fp32 -> packed fp16 pair, round half to even (v_cvt_pk_f16_f32)
@@ -193,17 +185,18 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 }
 
 // 8 bf16 -> 8 canonical fp16 (round half to even), times sigma: the sign flip rides on
-// the bf16 -> fp32 unpack ((w << 16) + bit31 flips bit 31; (w & hi16) ^ bit31 too).
-// Without clamping a value beyond fp16 becomes inf, which the caller detects and then
-// redoes with CLAMP.
+// the bf16 -> fp32 unpack. (w + m) << 16 flips bit 15 of the low bf16 before it moves up
+// (the carry out of bit 15 and bit 31 of m are shifted out), and (w ^ m) & 0xFFFF0000
+// flips the high one. Without clamping a value beyond fp16 becomes inf, which the
+// caller detects and then redoes with CLAMP.
 template <bool CLAMP>
 __device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    float lo = __int_as_float((int)((ws[d] << 16) + m.lo[d]));
-    float hi = __int_as_float((int)((ws[d] & 0xFFFF0000u) ^ m.hi[d]));
+    float lo = __int_as_float((int)((ws[d] + m.m[d]) << 16));
+    float hi = __int_as_float((int)((ws[d] ^ m.m[d]) & 0xFFFF0000u));
     if constexpr (CLAMP) {
       lo = __builtin_amdgcn_fmed3f(lo, -kFp16Max, kFp16Max);
       hi = __builtin_amdgcn_fmed3f(hi, -kFp16Max, kFp16Max);
@@ -213,8 +206,7 @@ __device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m) {
   return __builtin_bit_cast(h8v, make_uint4(o[0], o[1], o[2], o[3]));
 }
 __device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp16 input
-  return __builtin_bit_cast(h8v, make_uint4(w.x ^ ((m.lo[0] >> 16) | m.hi[0]), w.y ^ ((m.lo[1] >> 16) | m.hi[1]),
-                                            w.z ^ ((m.lo[2] >> 16) | m.hi[2]), w.w ^ ((m.lo[3] >> 16) | m.hi[3])));
+  return __builtin_bit_cast(h8v, make_uint4(w.x ^ m.m[0], w.y ^ m.m[1], w.z ^ m.m[2], w.w ^ m.m[3]));
 }
 
 // W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]; with ID the

@@ -49,6 +49,9 @@ FP16_MAX = 65504.0
 SCALE_MIN = 2.0 ** -14      # smallest normal fp16; lower clamp of r and c
 HEADER_FIXED = 512          # len[] starts here
 SIGMA_OFFSET = 64
+SIGN_WORDS_OFFSET = 192     # uint32[head_dim / 2]: word d has bit 15 set where sigma[2d] = -1
+                            # and bit 31 where sigma[2d + 1] = -1 (sigma restated as the sign
+                            # bits of a packed pair of 16-bit floats)
 FLAGS_OFFSET = 36
 VARIANT_OFFSET = 40
 # Ablation variants ([AP] section 5, ablations: Hadamard only, VarN only, VarN along one
@@ -443,6 +446,15 @@ class Geom:
                                    * self.head_dim * 2)
 
 
+def sign_words(sigma) -> np.ndarray:
+    """The header's restatement of sigma: for each channel pair (2d, 2d + 1) one uint32 with
+    bit 15 set where sigma[2d] = -1 and bit 31 set where sigma[2d + 1] = -1."""
+    neg = np.asarray(sigma, np.float64) < 0
+    lo = np.where(neg[0::2], 0x8000, 0).astype(np.uint64)
+    hi = np.where(neg[1::2], 0x80000000, 0).astype(np.uint64)
+    return (lo | hi).astype(np.uint32)
+
+
 class Cache:
     """A layer's cache as the byte buffer the library keeps in device memory."""
 
@@ -455,6 +467,7 @@ class Cache:
         hdr[8:36].view(np.int32)[:] = geom.as_tuple()
         hdr[VARIANT_OFFSET:VARIANT_OFFSET + 4].view(np.uint32)[0] = geom.variant
         hdr[SIGMA_OFFSET:SIGMA_OFFSET + geom.head_dim].view(np.int8)[:] = np.asarray(sigma, np.int8)
+        hdr[SIGN_WORDS_OFFSET:SIGN_WORDS_OFFSET + 2 * geom.head_dim].view(np.uint32)[:] = sign_words(sigma)
         if geom.paged:
             self.page_map[:] = -1                               # no page yet
 

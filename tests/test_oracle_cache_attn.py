@@ -40,6 +40,25 @@ def test_header_fields():
     assert c.g.header == 768 and c.g.total % 256 == 0
 
 
+def test_header_sign_words():
+    """Bytes 192..447 restate sigma as the sign bits of packed 16-bit pairs: word d has bit 15
+    set iff sigma[2d] = -1 and bit 31 set iff sigma[2d + 1] = -1 (values worked by hand)."""
+    sigma = np.ones(128)
+    sigma[[1, 2, 4, 5, 127]] = -1
+    c = R.Cache(R.Geom(1, 1, 128, 32, 32, 3, 2), sigma)
+    words = c.buf[192:448].view(np.uint32)
+    assert words[0] == 0x80000000            # (+1, -1)
+    assert words[1] == 0x00008000            # (-1, +1)
+    assert words[2] == 0x80008000            # (-1, -1)
+    assert words[3] == 0                     # (+1, +1)
+    assert words[63] == 0x80000000           # (+1, -1): channels 126, 127
+    assert np.count_nonzero(words[4:63]) == 0
+    # and XORed into a packed pair of fp16 values it flips exactly those signs
+    pair = np.array([1.5, -2.25], dtype=np.float16).view(np.uint32)[0]
+    flipped = np.array([pair ^ words[2]], dtype=np.uint32).view(np.float16)
+    assert flipped.tolist() == [-1.5, 2.25]
+
+
 @pytest.mark.parametrize("T", [0, 5, 31, 32, 33, 100])
 def test_prefill_equals_appends(T):
     """prefill(T) and T single-token appends from empty give the same bytes."""
