@@ -365,6 +365,32 @@ def cpu_baseline(synth, tokens, layers):
                        "BLAS threads = cores")
 
 
+def cpu_baseline_decode(synth, T=16384, H=10, Hq=40, layers=40):
+    """The oracle's decode step (append + attention, by definition over the dequantized
+    cache) on one batch row of the Phi-4-shaped decode, extrapolated to the full step."""
+    from oracle import kvarn_ref as R
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    G = 32
+    c = R.Cache(R.Geom(1, H, 128, T + 2 * G, G, 3, 2), synth.sign_vector(0))
+    k, v = synth.kv_host(synth.sub_seed(4, 0, 0), 1, T, H)
+    R.quantize_prefill(c, k, v, T)                      # set-up, not timed
+    kn, vn = synth.kv_host(synth.sub_seed(4, 0, 1), 1, 1, H)
+    q = synth.q_host(synth.sub_seed(4, 0, 2), 1, Hq)
+    t0 = time.perf_counter()
+    R.append_decode(c, kn[:, 0], vn[:, 0])
+    R.attn_decode(c, q, Hq)
+    dt = time.perf_counter() - t0
+    # a step of B rows costs B times one row per layer and yields B tokens
+    return dict(value=round(1.0 / (dt * layers), 6), unit="tokens/s", cores=int(blas), kind="oracle",
+                sample=f"one batch row of the decode workload ({H} KV heads x {Hq} query heads, {T}-token "
+                       f"context): one append + attention step, {dt:.1f} s of oracle time, extrapolated "
+                       f"to {layers} layers; NumPy fp64, BLAS threads = cores")
+
+
 # HBM traffic of a kernel from committed rocprofv3 counter summaries: FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch) scaled by what the same counters read for a 4 GiB device
 # copy. The figures stand only while the kernel sources hash to the digest recorded
@@ -534,6 +560,9 @@ def main():
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(synth, args.cpu_tokens, args.cpu_layers)
+        if "decode" in res:
+            log("cpu baseline, decode step (oracle) ...")
+            res["decode"]["cpu_baseline"] = cpu_baseline_decode(synth)
     print(json.dumps(res), flush=True)
 
 
