@@ -80,6 +80,8 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
     assert hc.buf[8:36].view(np.int32).tolist() == list(og.as_tuple())
     assert hc.buf[R.VARIANT_OFFSET:R.VARIANT_OFFSET + 4].view(np.uint32)[0] == og.variant
     assert np.array_equal(hc.sigma, gc.sigma.astype(np.float64))
+    sw = hc.buf[R.SIGN_WORDS_OFFSET:R.SIGN_WORDS_OFFSET + 2 * og.head_dim].view(np.uint32)
+    assert np.array_equal(sw, R.sign_words(gc.sigma))
     assert np.all(hc.lens == T), hc.lens
     nfull = T // G
     if tiles is None:
