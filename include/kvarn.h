@@ -3,8 +3,9 @@
  *
  * C ABI. Plain pointers and sizes only. Device pointers are HIP device memory
  * owned by the caller; `stream` is a hipStream_t passed as void*. The library
- * never allocates, frees or synchronizes (except kvarn_cache_flags), keeps no
- * global mutable state, and enqueues all work on the caller's stream.
+ * never allocates or frees, keeps no global mutable state, enqueues all work on the
+ * caller's stream, and synchronizes that stream only in kvarn_cache_init and
+ * kvarn_cache_flags.
  *
  * Method (KVarN pages): each K/V token is rotated along head_dim by a randomized
  * Hadamard matrix H with H H^T = I (ai-paper-analysis page, section 3.1); VarN then
@@ -16,7 +17,8 @@
  *
  * Conventions fixed by this library where the pages are silent:
  *   H_D = diag(sigma) H_syl / sqrt(D), H_syl[i][j] = (-1)^popcount(i & j), sigma in {+1,-1}^D;
- *   inputs are canonicalized bf16 -> fp16 (round-half-to-even, saturating at +-65504);
+ *   inputs are canonicalized bf16 -> fp16 (round-half-to-even, saturating at +-65504;
+ *   a NaN input becomes 0 and raises KVARN_FLAG_NAN);
  *   "variance" is the mean square; a tile is G consecutive tokens x D channels of
  *   one (batch, kv head, stream); r (per token) and c (per channel) are stored as
  *   fp16 clamped to [2^-14, 65504]; the 2-bit grid is per channel over the tile's
@@ -24,14 +26,14 @@
  *   codes round half to even and clamp to [0, 3] (3- and 4-bit codes: 2^bits levels,
  *   s = (max - min)/(2^bits - 1), clamp to [0, 2^bits - 1]).
  *
- * Cache buffer, format v1 (one caller-owned buffer per layer, 256-B aligned regions):
+ * Cache buffer, format v2 (one caller-owned buffer per layer, 256-B aligned regions):
  *   header  align256(512 + 8*B*Hkv) bytes:
- *           u32 magic 0x4E52564B, u32 version 1, i32 geom[7] (batch, num_kv_heads,
- *           head_dim, capacity, group, varn_iters, bits), u32 flags (sticky),
- *           u32 variant at byte 40, i8 sigma[D] at byte 64, u32 sign words[D/2]
- *           at byte 192 (word d: bit 15 set iff sigma[2d] = -1, bit 31 set iff
- *           sigma[2d+1] = -1, the sign bits of a packed pair of 16-bit floats),
- *           i32 len[B][Hkv][2] at byte 512;
+ *           u32 magic 0x4E52564B, u32 version 2, i32 geom[7] (batch, num_kv_heads,
+ *           head_dim, capacity, group, varn_iters, bits), u32 flags (sticky) at byte 36,
+ *           u32 variant at byte 40, i32 num_pages at byte 44, i8 sigma[D] at byte 64,
+ *           u32 sign words[D/2] at byte 192 (word d: bit 15 set iff sigma[2d] = -1,
+ *           bit 31 set iff sigma[2d+1] = -1, the sign bits of a packed pair of 16-bit
+ *           floats), i32 len[B][Hkv][2] at byte 512;
  *   tiles   [B][Hkv][capacity/G][2 (K,V)][TR] tile records, region padded to 256 B;
  *           paged caches (num_pages > 0) instead hold a pool of num_pages pages,
  *           [num_pages][Hkv][2][TR] (one page = one group of G tokens of one sequence,
@@ -60,6 +62,9 @@
  *            4(n + 4hh) + par + 2ii. The grid has 2^bits levels.
  *     r fp16[G], c fp16[D], s fp16[D], z fp16[D].
  *   A tile token dequantizes as x_hat = (r_t c_j (z_j + s_j q_tj))_j H_D^T.
+ *   Format history: v1 stored K and V codes alike (channel order, four per byte) and had
+ *   no sign words, variant, num_pages or page map; v2 is the layout above (K channel-pair
+ *   slots, V tokens fastest, sign words at 192, variant at 40, num_pages at 44, page map).
  *
  * Errors: every argument check runs on the host before any HIP call; on error
  * nothing is enqueued and the cache is untouched. A failed launch returns
@@ -92,10 +97,13 @@ typedef enum {
     KVARN_ERR_DEVICE = 6        /* the HIP runtime reported an error                       */
 } kvarn_status;
 
-/* Geometry of one layer cache. v1 supports head_dim = 128, group in {32, 64},
- * bits in {2, 3, 4}, 0 <= varn_iters <= 8, capacity a positive multiple of group,
- * variant a combination of the KVARN_VARIANT_* bits below (0 = the method),
- * num_pages >= 0 (see the paged layout above). */
+/* Geometry of one layer cache: the pages' statement of the problem (K/V as [tokens,
+ * kv_heads, head_dim] with a leading batch, the group of 32 or 64 sharing a scale and
+ * the VarN iterations: ai-paper-analysis page, section 3.2; the 2-bit width:
+ * researchpapers page). This library supports head_dim = 128, group in {32, 64},
+ * bits in {2, 3, 4}, 0 <= varn_iters <= 8, capacity a positive multiple of group.
+ * A caller that fills these seven fields gets the method as defined, with each
+ * sequence's records stored contiguously. */
 typedef struct {
     int32_t batch;          /* B   sequences                                   */
     int32_t num_kv_heads;   /* Hkv                                             */
@@ -103,10 +111,22 @@ typedef struct {
     int32_t capacity;       /* max tokens per sequence                         */
     int32_t group;          /* G   tokens per tile (the pages' 32 or 64)       */
     int32_t varn_iters;     /* VarN iterations (token pass + channel pass)     */
-    int32_t bits;           /* code width: 2 (the pages'), 3 or 4              */
-    int32_t variant;        /* ablation bits, 0 for KVarN as defined           */
-    int32_t num_pages;      /* 0: records stored per sequence; > 0: paged      */
+    int32_t bits;           /* code width: 2 (the pages'), 3 or 4; may carry KVARN_GEOM_EXT */
 } kvarn_geom;
+
+/* Extended geometry, for the ablation variants and paged caches. Every entry point
+ * takes const kvarn_geom*; a caller that needs these fields passes the address of a
+ * kvarn_geom_ext, whose first member is the kvarn_geom, with KVARN_GEOM_EXT ORed into
+ * base.bits and size = sizeof(kvarn_geom_ext). Without the bit the library reads only
+ * the seven fields above and takes variant = 0, num_pages = 0. A size other than
+ * sizeof(kvarn_geom_ext) is refused with KVARN_ERR_GEOM. */
+#define KVARN_GEOM_EXT 0x10000
+typedef struct {
+    kvarn_geom base;        /* base.bits = code width | KVARN_GEOM_EXT         */
+    uint32_t size;          /* sizeof(kvarn_geom_ext)                          */
+    int32_t variant;        /* ablation bits (KVARN_VARIANT_*), 0 for KVarN    */
+    int32_t num_pages;      /* 0: records stored per sequence; > 0: paged      */
+} kvarn_geom_ext;
 
 /* Ablation variants (ai-paper-analysis page, section 5: Hadamard only = varn_iters 0,
  * VarN only, VarN along one axis only). The variant is written into the header at
@@ -124,18 +144,20 @@ enum { KVARN_Q_PREROTATED = 1u };                          /* attention: q is al
 enum { KVARN_FLAG_CAPACITY = 1u,      /* an append found a full sequence; token dropped      */
        KVARN_FLAG_SATURATED = 2u,     /* an input had |x| > 65504 and was saturated          */
        KVARN_FLAG_SCALE_CLAMPED = 4u, /* r or c hit [2^-14, 65504], or s/z saturated        */
-       KVARN_FLAG_UNMAPPED = 8u       /* a paged cache had no page for a tile being written  */ };
+       KVARN_FLAG_UNMAPPED = 8u,      /* a paged cache had no page for a tile being written  */
+       KVARN_FLAG_NAN = 16u           /* an input was NaN; it was stored as 0                */ };
 
-/* Format version of the cache buffer (1). */
+/* Format version of the cache buffer (2). */
 KVARN_API int kvarn_format_version(void);
 
 /* Size in bytes of a cache buffer for geometry *g. Host only. */
 KVARN_API kvarn_status kvarn_cache_bytes(const kvarn_geom* g, size_t* bytes);
 
-/* Write the header (magic, version, geometry, sigma and its sign words) and zero len[] and flags.
+/* Write the header (magic, version, geometry, variant, num_pages, sigma and its sign words),
+ * zero len[] and flags, and clear the page map of a paged cache to -1.
  * signs_host: host int8[head_dim], each +1 or -1: the random signs of H_D
  * (ai-paper-analysis page, section 3.1: randomized Hadamard matrix).
- * Asynchronous on `stream`; signs_host may be reused once the call returns. */
+ * Synchronizes `stream`: the cache is ready when the call returns. */
 KVARN_API kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* signs_host, void* stream);
 
 /* Reset the cache to hold tokens [0, num_tokens) of k and v.
@@ -197,7 +219,8 @@ KVARN_API kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t n
  * per-tile factors split into f16 hi + lo parts); tail tokens in original space.
  * Two launches on `stream`: the tile pass, then the merge over spans and the tail.
  * workspace: device, >= kvarn_attn_workspace_bytes; out: device f32 [B][Hq][D],
- * original space. An empty sequence gives 0. num_q_heads / num_kv_heads <= 8. */
+ * original space. An empty sequence gives 0. num_q_heads must be a multiple of
+ * num_kv_heads. */
 KVARN_API kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache, const void* q_bf16,
                                int32_t num_q_heads, float softmax_scale, uint32_t flags,
                                void* workspace, size_t workspace_bytes, float* out, void* stream);

@@ -11,8 +11,18 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-kvarn_status check_geom(const kvarn_geom* g) {
-  if (!g) return KVARN_ERR_NULL;
+// The seven fields of kvarn_geom, plus variant and num_pages when the caller passed a
+// kvarn_geom_ext (KVARN_GEOM_EXT in bits); then the limits of this library.
+kvarn_status resolve_geom(const kvarn_geom* in, Geo* g) {
+  if (!in) return KVARN_ERR_NULL;
+  *g = Geo{in->batch, in->num_kv_heads, in->head_dim, in->capacity, in->group, in->varn_iters,
+           in->bits & ~KVARN_GEOM_EXT, 0, 0};
+  if (in->bits & KVARN_GEOM_EXT) {
+    const kvarn_geom_ext* e = reinterpret_cast<const kvarn_geom_ext*>(in);
+    if (e->size != sizeof(kvarn_geom_ext)) return KVARN_ERR_GEOM;
+    g->variant = e->variant;
+    g->num_pages = e->num_pages;
+  }
   if (g->batch <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0 || g->capacity <= 0 || g->group <= 0 ||
       g->varn_iters < 0 || g->bits <= 0 || g->num_pages < 0)
     return KVARN_ERR_GEOM;
@@ -29,19 +39,26 @@ kvarn_status check_geom(const kvarn_geom* g) {
   return KVARN_OK;
 }
 
+#define RESOLVE(in, g)                              \
+  Geo g##_v;                                        \
+  {                                                 \
+    const kvarn_status rs = resolve_geom(in, &g##_v); \
+    if (rs != KVARN_OK) return rs;                  \
+  }                                                 \
+  const Geo* g = &g##_v
+
 kvarn_status dev(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_DEVICE; }
 
-kvarn_status check_prefill(const kvarn_geom* g, void* cache, const void* k, const void* v, int32_t T) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
+kvarn_status check_prefill(const Geo* g, void* cache, const void* k, const void* v, int32_t T) {
   if (!cache || ((!k || !v) && T > 0)) return KVARN_ERR_NULL;
   if (!aligned16(cache) || !aligned16(k) || !aligned16(v)) return KVARN_ERR_ALIGN;
   if (T < 0 || T > g->capacity) return KVARN_ERR_RANGE;
   return KVARN_OK;
 }
 
-kvarn_status prefill_impl(const kvarn_geom* g, void* cache, const void* k, const void* v, int32_t T,
+kvarn_status prefill_impl(const kvarn_geom* gin, void* cache, const void* k, const void* v, int32_t T,
                           float* wk, float* wv, float* yk, float* yv, void* stream) {
+  RESOLVE(gin, g);
   kvarn_status st = check_prefill(g, cache, k, v, T);
   if (st != KVARN_OK) return st;
   for (const float* p : {wk, wv, yk, yv})
@@ -75,24 +92,22 @@ const char* kvarn_status_str(kvarn_status s) {
     case KVARN_ERR_NULL: return "null pointer";
     case KVARN_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case KVARN_ERR_GEOM: return "inconsistent geometry";
-    case KVARN_ERR_UNSUPPORTED: return "unsupported geometry (v1: head_dim 128, group 32/64, 2-4 bits, <= 8 VarN iterations, variant bits 1|2|4|8)";
+    case KVARN_ERR_UNSUPPORTED: return "unsupported geometry (head_dim 128, group 32/64, 2-4 bits, <= 8 VarN iterations, variant bits 1|2|4|8)";
     case KVARN_ERR_RANGE: return "size out of range";
     case KVARN_ERR_DEVICE: return "HIP runtime error";
   }
   return "unknown status";
 }
 
-kvarn_status kvarn_cache_bytes(const kvarn_geom* g, size_t* bytes) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
+kvarn_status kvarn_cache_bytes(const kvarn_geom* gin, size_t* bytes) {
+  RESOLVE(gin, g);
   if (!bytes) return KVARN_ERR_NULL;
   *bytes = (size_t)make_layout(*g).total;
   return KVARN_OK;
 }
 
-kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* signs_host, void* stream) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
+kvarn_status kvarn_cache_init(const kvarn_geom* gin, void* cache, const int8_t* signs_host, void* stream) {
+  RESOLVE(gin, g);
   if (!cache || !signs_host) return KVARN_ERR_NULL;
   if (!aligned16(cache)) return KVARN_ERR_ALIGN;
   for (int j = 0; j < kD; ++j)
@@ -107,13 +122,17 @@ kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const int8_t* si
   a.geom[5] = g->varn_iters;
   a.geom[6] = g->bits;
   a.variant = (uint32_t)g->variant;
+  a.num_pages = g->num_pages;
   memcpy(a.sigma, signs_host, kD);
   a.n_len = 2LL * g->batch * g->num_kv_heads;
   const Layout L = make_layout(*g);
   a.hdr_bytes = L.header;
   a.map_off = L.map_off;
   a.map_end = g->num_pages > 0 ? L.map_off + 4LL * g->batch * L.tiles : L.map_off;
-  return dev(launch_init(a, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const kvarn_status st = dev(launch_init(a, hs));
+  if (st != KVARN_OK) return st;
+  return dev(hipStreamSynchronize(hs));
 }
 
 kvarn_status kvarn_quantize_prefill(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
@@ -127,10 +146,9 @@ kvarn_status kvarn_debug_prefill(const kvarn_geom* g, void* cache, const void* k
   return prefill_impl(g, cache, k_bf16, v_bf16, num_tokens, w_k, w_v, y_k, y_v, stream);
 }
 
-kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
+kvarn_status kvarn_append_decode(const kvarn_geom* gin, void* cache, const void* k_bf16, const void* v_bf16,
                                  void* stream) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
+  RESOLVE(gin, g);
   if (!cache || !k_bf16 || !v_bf16) return KVARN_ERR_NULL;
   if (!aligned16(cache) || !aligned16(k_bf16) || !aligned16(v_bf16)) return KVARN_ERR_ALIGN;
   AppendArgs a{};
@@ -141,10 +159,9 @@ kvarn_status kvarn_append_decode(const kvarn_geom* g, void* cache, const void* k
   return dev(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
-kvarn_status kvarn_append_tokens(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
+kvarn_status kvarn_append_tokens(const kvarn_geom* gin, void* cache, const void* k_bf16, const void* v_bf16,
                                  int32_t num_tokens, const int32_t* counts, void* stream) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
+  RESOLVE(gin, g);
   if (!cache || ((!k_bf16 || !v_bf16) && num_tokens > 0)) return KVARN_ERR_NULL;
   if (!aligned16(cache) || !aligned16(k_bf16) || !aligned16(v_bf16) || ((uintptr_t)counts & 3u)) return KVARN_ERR_ALIGN;
   if (num_tokens < 0 || num_tokens > g->capacity) return KVARN_ERR_RANGE;
@@ -163,10 +180,9 @@ kvarn_status kvarn_append_tokens(const kvarn_geom* g, void* cache, const void* k
   return dev(launch_tokens(a, static_cast<hipStream_t>(stream)));
 }
 
-kvarn_status kvarn_cache_set_pages(const kvarn_geom* g, void* cache, const int32_t* pages, int32_t tile_first,
+kvarn_status kvarn_cache_set_pages(const kvarn_geom* gin, void* cache, const int32_t* pages, int32_t tile_first,
                                    int32_t num_tiles, void* stream) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
+  RESOLVE(gin, g);
   if (g->num_pages == 0) return KVARN_ERR_GEOM;
   if (!cache || (!pages && num_tiles > 0)) return KVARN_ERR_NULL;
   if (!aligned16(cache) || ((uintptr_t)pages & 3u)) return KVARN_ERR_ALIGN;
@@ -182,10 +198,9 @@ kvarn_status kvarn_cache_set_pages(const kvarn_geom* g, void* cache, const int32
   return dev(launch_set_pages(a, static_cast<hipStream_t>(stream)));
 }
 
-kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_out, void* v_out, int32_t max_tokens,
+kvarn_status kvarn_dequantize(const kvarn_geom* gin, const void* cache, void* k_out, void* v_out, int32_t max_tokens,
                               int32_t out_dtype, void* stream) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
+  RESOLVE(gin, g);
   if (!cache || ((!k_out || !v_out) && max_tokens > 0)) return KVARN_ERR_NULL;
   if (!aligned16(cache) || !aligned16(k_out) || !aligned16(v_out)) return KVARN_ERR_ALIGN;
   if (max_tokens < 0 || max_tokens > g->capacity) return KVARN_ERR_RANGE;
@@ -211,7 +226,7 @@ kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_ou
 // 4 query heads, span of 4 * tpw tiles). tpw is chosen for about 2048 work-groups over
 // the cache capacity, between 2 and 16 tiles per wave. Depends only on the geometry, so
 // the workspace size is static.
-static void attn_split(const kvarn_geom* g, int grp, int* tpw, int* nspan) {
+static void attn_split(const Geo* g, int grp, int* tpw, int* nspan) {
   const int tiles = g->capacity / g->group;
   const long long units = (long long)g->batch * g->num_kv_heads * ((grp + 3) / 4);
   const long long want = (2048 + units - 1) / units;  // spans wanted per sequence
@@ -224,28 +239,32 @@ static void attn_split(const kvarn_geom* g, int grp, int* tpw, int* nspan) {
 
 // Workspace: the span partials [B][Hq][nspan][4 + D] f32, then len [B][Hkv] i32 as the
 // tile pass saw it.
-static size_t attn_partial_bytes(const kvarn_geom* g, int32_t num_q_heads) {
+static size_t attn_partial_bytes(const Geo* g, int32_t num_q_heads) {
   int tpw, nspan;
   attn_split(g, num_q_heads / g->num_kv_heads, &tpw, &nspan);
   return (size_t)g->batch * num_q_heads * nspan * (4 + kD) * sizeof(float);
 }
 
-kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes) {
-  kvarn_status st = check_geom(g);
-  if (st != KVARN_OK) return st;
-  if (!bytes) return KVARN_ERR_NULL;
+static kvarn_status ws_need(const Geo* g, int32_t num_q_heads, size_t* bytes) {
   if (num_q_heads <= 0 || num_q_heads % g->num_kv_heads != 0) return KVARN_ERR_GEOM;
-  if (num_q_heads / g->num_kv_heads > 8) return KVARN_ERR_UNSUPPORTED;
+  if ((long long)g->batch * num_q_heads >= (1LL << 31)) return KVARN_ERR_RANGE;
   const size_t lens = ((size_t)g->batch * g->num_kv_heads * sizeof(int32_t) + 15) / 16 * 16;
   *bytes = attn_partial_bytes(g, num_q_heads) + lens;
   return KVARN_OK;
 }
 
-static kvarn_status attn_impl(const kvarn_geom* g, const void* cache, const void* q_bf16, int32_t num_q_heads,
+kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* gin, int32_t num_q_heads, size_t* bytes) {
+  RESOLVE(gin, g);
+  if (!bytes) return KVARN_ERR_NULL;
+  return ws_need(g, num_q_heads, bytes);
+}
+
+static kvarn_status attn_impl(const kvarn_geom* gin, const void* cache, const void* q_bf16, int32_t num_q_heads,
                               float softmax_scale, uint32_t flags, void* workspace, size_t workspace_bytes,
                               float* out, void* cache_rw, const void* k_bf16, const void* v_bf16, void* stream) {
+  RESOLVE(gin, g);
   size_t need = 0;
-  kvarn_status st = kvarn_attn_workspace_bytes(g, num_q_heads, &need);
+  kvarn_status st = ws_need(g, num_q_heads, &need);
   if (st != KVARN_OK) return st;
   if (!cache || !q_bf16 || !workspace || !out) return KVARN_ERR_NULL;
   if (!aligned16(cache) || !aligned16(q_bf16) || !aligned16(workspace) || !aligned16(out)) return KVARN_ERR_ALIGN;

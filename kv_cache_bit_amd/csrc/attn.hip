@@ -625,9 +625,10 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       const int t = min(gi + 16 * k, nt - 1);
       if (FUSED && t == nt_old) {  // the new token, canonicalized as the append stores it
         const long long src = ((long long)b * a.L.Hkv + h) * kD + 8 * cg;
-        float xk[8], xv[8], amax = 0.0f;
-        canon8_bf16(*reinterpret_cast<const uint4*>(a.kn + src), xk, amax);
-        canon8_bf16(*reinterpret_cast<const uint4*>(a.vn + src), xv, amax);
+        float xk[8], xv[8];
+        uint32_t seen = 0;  // the append job of this launch raises the token's flags
+        canon8_bf16(*reinterpret_cast<const uint4*>(a.kn + src), xk, seen);
+        canon8_bf16(*reinterpret_cast<const uint4*>(a.vn + src), xv, seen);
         kw[k] = pack8_f16(xk);
         vw[k] = pack8_f16(xv);
       } else {

@@ -200,11 +200,12 @@ __global__ void init_kernel(InitArgs a) {
     h32[0] = kMagic;
     h32[1] = kVersion;
     for (int k = 0; k < 7; ++k) h32[2 + k] = (uint32_t)a.geom[k];
-    h32[9] = 0;  // flags
-    h32[10] = a.variant;
+    h32[kFlagsOff / 4] = 0;  // flags
+    h32[kVariantOff / 4] = a.variant;
+    h32[kNumPagesOff / 4] = (uint32_t)a.num_pages;
   }
-  for (int k = t; k < 128; k += blockDim.x) {  // bytes 44..511: pad, sigma, sign words, pad
-    const int off = 44 + 4 * k;
+  for (int k = t; k < 128; k += blockDim.x) {  // bytes 48..511: pad, sigma, sign words, pad
+    const int off = kNumPagesOff + 4 + 4 * k;
     if (off >= kHdrFixed) break;
     uint32_t w = 0;
     if (off >= kSignOff && off < kSignOff + 2 * kD) {  // word d: signs of channels 2d, 2d + 1

@@ -11,19 +11,27 @@ namespace kvarn {
 
 constexpr int kD = 128;                     // the one head_dim the kernels support
 constexpr uint32_t kMagic = 0x4E52564Bu;    // 'K' 'V' 'R' 'N'
-constexpr int kVersion = 1;
+constexpr int kVersion = 2;
 constexpr int kHdrFixed = 512;              // len[] offset
 constexpr int kSigmaOff = 64;
 constexpr int kSignOff = 192;               // sign words [64]: bit 15 / bit 31 of word d set
                                             // where sigma of channel 2d / 2d + 1 is -1
 constexpr int kFlagsOff = 36;
+constexpr int kVariantOff = 40;
+constexpr int kNumPagesOff = 44;
 constexpr float kFp16Max = 65504.0f;
 constexpr float kScaleMin = 6.103515625e-05f;          // 2^-14
 constexpr float kInvSqrtD = 0.08838834764831845f;      // 1/sqrt(128), fp32-rounded
 
 inline __host__ __device__ long long align256(long long n) { return (n + 255) / 256 * 256; }
 
-// Byte layout of one layer cache (format v1), computed on the host and passed by value.
+// The geometry as the library uses it: kvarn_geom's seven fields (bits without the
+// KVARN_GEOM_EXT marker) and the extension's variant and num_pages (0 without it).
+struct Geo {
+  int32_t batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant, num_pages;
+};
+
+// Byte layout of one layer cache (format v2), computed on the host and passed by value.
 // Records are stored per sequence ([B][Hkv][tiles][2][TR]) or, for a paged cache
 // (num_pages > 0), in a pool of pages [num_pages][Hkv][2][TR] named by the page map
 // int32 [B][tiles] at map_off; record_at resolves either.
@@ -71,7 +79,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 }
 #endif
 
-inline __host__ Layout make_layout(const kvarn_geom& g) {
+inline __host__ Layout make_layout(const Geo& g) {
   Layout L;
   L.B = g.batch;
   L.Hkv = g.num_kv_heads;

@@ -12,6 +12,7 @@ struct InitArgs {
   uint8_t* cache;
   int32_t geom[7];
   uint32_t variant;  // header byte 40
+  int32_t num_pages;  // header byte 44
   int8_t sigma[kD];
   long long n_len;  // entries of len[]
   long long hdr_bytes;  // header size; everything past byte 512 is zeroed except the page map

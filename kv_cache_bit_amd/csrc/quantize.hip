@@ -28,9 +28,8 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
     const uint16_t* src = s ? a.v : a.k;
     for (int t = a.nfull * L.G + g; t < a.T; t += 4) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + (((long long)b * a.T + t) * L.Hkv + h) * kD + 8 * c);
-      float x[8], amax = 0.0f;
-      canon8_bf16(w, x, amax);
-      flags |= sat_flag(amax);
+      float x[8];
+      canon8_bf16(w, x, flags);
       *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = pack8_f16(x);
     }
     if (lane == 0) *reinterpret_cast<int32_t*>(a.cache + L.len_off(b, h, s)) = a.T;
@@ -79,16 +78,15 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
       for (int mb = 0; mb < 2; ++mb) av[mb][ks] = canon_a<false>(raw[mb][ks], m[ks]);
   }
   st = rotate_squares_v<ABL>(idr, av, hf, p, c);
-  if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion): redo saturating
+  if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion) or NaN: redo checked
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-        av[mb][ks] = canon_a<true>(*reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks), m);
+        av[mb][ks] = canon_a<true>(*reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks), m, &flags);
     }
     st = rotate_squares_v<ABL>(idr, av, hf, p, c);
-    flags |= KVARN_FLAG_SATURATED;
   }
 
   float* dw = nullptr;
@@ -176,9 +174,10 @@ __global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
         w = *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, tt % G) + 16 * (4 * ks + g));
       } else {        // a new token
         const int row = min(tt - l0, a.T - 1);
-        float x[8], amax = 0.0f;
-        canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)row * L.Hkv * kD + 8 * (4 * ks + g)), x, amax);
-        if (valid) flags |= sat_flag(amax);
+        float x[8];
+        uint32_t f = 0;
+        canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)row * L.Hkv * kD + 8 * (4 * ks + g)), x, f);
+        if (valid) flags |= f;
         w = pack8_f16(x);
       }
       av[mb][ks] = sign_a(w, m);
@@ -210,9 +209,8 @@ __global__ __launch_bounds__(256) void tokens_tail_kernel(TokensArgs a) {
   uint32_t flags = dropped ? (uint32_t)KVARN_FLAG_CAPACITY : 0u;
   const uint16_t* src = (s ? a.v : a.k) + ((long long)b * a.T * L.Hkv + h) * kD;
   for (int t = max(l0, l1 / L.G * L.G) + g; t < l1; t += 4) {
-    float x[8], amax = 0.0f;
-    canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)(t - l0) * L.Hkv * kD + 8 * c), x, amax);
-    flags |= sat_flag(amax);
+    float x[8];
+    canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)(t - l0) * L.Hkv * kD + 8 * c), x, flags);
     *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = pack8_f16(x);
   }
   raise_flags(a.cache, flags);

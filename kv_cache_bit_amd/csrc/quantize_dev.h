@@ -187,21 +187,29 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 // 8 bf16 -> 8 canonical fp16 (round half to even), times sigma: the sign flip rides on
 // the bf16 -> fp32 unpack. (w + m) << 16 flips bit 15 of the low bf16 before it moves up
 // (the carry out of bit 15 and bit 31 of m are shifted out), and (w ^ m) & 0xFFFF0000
-// flips the high one. Without clamping a value beyond fp16 becomes inf, which the
-// caller detects and then redoes with CLAMP.
-template <bool CLAMP>
-__device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m) {
+// flips the high one. Without CHECK a value beyond fp16 becomes inf and a NaN stays NaN,
+// which the caller detects and then redoes with CHECK: saturation at +-65504
+// (KVARN_FLAG_SATURATED), a NaN as 0 (KVARN_FLAG_NAN).
+template <bool CHECK>
+__device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m, uint32_t* flags = nullptr) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    float lo = __int_as_float((int)((ws[d] + m.m[d]) << 16));
-    float hi = __int_as_float((int)((ws[d] ^ m.m[d]) & 0xFFFF0000u));
-    if constexpr (CLAMP) {
-      lo = __builtin_amdgcn_fmed3f(lo, -kFp16Max, kFp16Max);
-      hi = __builtin_amdgcn_fmed3f(hi, -kFp16Max, kFp16Max);
+    float v[2] = {__int_as_float((int)((ws[d] + m.m[d]) << 16)), __int_as_float((int)((ws[d] ^ m.m[d]) & 0xFFFF0000u))};
+    if constexpr (CHECK) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (!(v[e] == v[e])) {
+          *flags |= KVARN_FLAG_NAN;
+          v[e] = 0.0f;
+        } else if (fabsf(v[e]) > kFp16Max) {
+          *flags |= KVARN_FLAG_SATURATED;
+          v[e] = __builtin_amdgcn_fmed3f(v[e], -kFp16Max, kFp16Max);
+        }
+      }
     }
-    o[d] = pack_f16x2(lo, hi);
+    o[d] = pack_f16x2(v[0], v[1]);
   }
   return __builtin_bit_cast(h8v, make_uint4(o[0], o[1], o[2], o[3]));
 }
@@ -821,19 +829,24 @@ __device__ __forceinline__ uint4 pack8_f16(const float (&x)[8]) {
   o.w = pack_f16x2(x[6], x[7]);
   return o;
 }
-// bf16 x 8 -> canonical fp16 values (saturating), largest magnitude into amax
-__device__ __forceinline__ void canon8_bf16(const uint4 w, float (&x)[8], float& amax) {
+// bf16 x 8 -> canonical fp16 values: saturated at +-65504 (KVARN_FLAG_SATURATED into
+// flags), a NaN stored as 0 (KVARN_FLAG_NAN)
+__device__ __forceinline__ void canon8_bf16(const uint4 w, float (&x)[8], uint32_t& flags) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float amax = 0.0f;
+  bool nan = false;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float lo = bf16lo(ws[k]), hi = bf16hi(ws[k]);
-    amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
-    x[2 * k] = round_f16(fminf(fmaxf(lo, -kFp16Max), kFp16Max));
-    x[2 * k + 1] = round_f16(fminf(fmaxf(hi, -kFp16Max), kFp16Max));
+    const float v[2] = {bf16lo(ws[k]), bf16hi(ws[k])};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      nan |= !(v[e] == v[e]);
+      amax = fmaxf(amax, fabsf(v[e]));  // a NaN operand is ignored
+      x[2 * k + e] = v[e] == v[e] ? round_f16(fminf(fmaxf(v[e], -kFp16Max), kFp16Max)) : 0.0f;
+    }
   }
-}
-__device__ __forceinline__ uint32_t sat_flag(float amax) {
-  return amax > kFp16Max ? (uint32_t)KVARN_FLAG_SATURATED : 0u;
+  if (amax > kFp16Max) flags |= KVARN_FLAG_SATURATED;
+  if (nan) flags |= KVARN_FLAG_NAN;
 }
 
 // ----------------------------------------------------------------------------- append
@@ -857,9 +870,8 @@ __device__ void append_job(const AppendArgs& a, int job, int sub, int lane, Tile
   uint32_t flags = 0;
   const uint16_t* src = (s ? a.v : a.k) + ((long long)b * L.Hkv + h) * kD;
   if (sub == 0 && g == 0) {  // the new token into the fp16 tail (16 lanes x 8 channels)
-    float xin[8], amax = 0.0f;
-    canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * c), xin, amax);
-    flags |= sat_flag(amax);
+    float xin[8];
+    canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * c), xin, flags);
     *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, pos % G) + 16 * c) = pack8_f16(xin);
   }
   if ((pos + 1) % G == 0) {
@@ -874,8 +886,9 @@ __device__ void append_job(const AppendArgs& a, int job, int sub, int lane, Tile
         const int t = sub * 32 + 16 * mb + c;  // token of this A row inside the tile
         uint4 w;
         if (t == G - 1) {  // the token just written: take it from the input, not from memory
-          float x[8], amax = 0.0f;
-          canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * (4 * ks + g)), x, amax);
+          float x[8];
+          uint32_t seen = 0;  // flags of this token were raised with its tail write
+          canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * (4 * ks + g)), x, seen);
           w = pack8_f16(x);
         } else {
           w = *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, t) + 16 * (4 * ks + g));

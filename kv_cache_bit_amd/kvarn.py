@@ -32,18 +32,45 @@ class KvarnError(RuntimeError):
         super().__init__(f"{fn}: {status_str(status)} (status {status})")
 
 
+KVARN_GEOM_EXT = 0x10000
+KVARN_FLAG_NAN = 16
+_BASE_FIELDS = ("batch", "num_kv_heads", "head_dim", "capacity", "group", "varn_iters", "bits")
+
+
 class kvarn_geom(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "num_kv_heads", "head_dim", "capacity", "group", "varn_iters", "bits", "variant",
-                 "num_pages")]
+    """The seven-field geometry of include/kvarn.h (variant 0, records per sequence)."""
+    _fields_ = [(n, ctypes.c_int32) for n in _BASE_FIELDS]
+    variant = 0
+    num_pages = 0
 
     def __repr__(self):
-        return "kvarn_geom(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+        return "kvarn_geom(" + ", ".join(f"{n}={getattr(self, n)}" for n in _BASE_FIELDS) + ")"
+
+
+class kvarn_geom_ext(ctypes.Structure):
+    """kvarn_geom plus the ablation variant and the page pool (KVARN_GEOM_EXT in base.bits)."""
+    _fields_ = [("base", kvarn_geom), ("size", ctypes.c_uint32), ("variant", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+    def __getattr__(self, name):  # batch, group, ... read through to the base fields
+        if name in _BASE_FIELDS:
+            v = getattr(self.base, name)
+            return v & ~KVARN_GEOM_EXT if name == "bits" else v
+        raise AttributeError(name)
+
+    def __repr__(self):
+        return (f"kvarn_geom_ext({self.base!r}, size={self.size}, variant={self.variant}, "
+                f"num_pages={self.num_pages})")
 
 
 def geom(batch, num_kv_heads, capacity, group=32, varn_iters=3, head_dim=128, bits=2, variant=0,
-         num_pages=0) -> kvarn_geom:
-    return kvarn_geom(batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant, num_pages)
+         num_pages=0):
+    """A kvarn_geom, or a kvarn_geom_ext when a variant or a page pool is asked for."""
+    base = kvarn_geom(batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits)
+    if variant == 0 and num_pages == 0:
+        return base
+    base.bits = bits | KVARN_GEOM_EXT
+    return kvarn_geom_ext(base, ctypes.sizeof(kvarn_geom_ext), variant, num_pages)
 
 
 def _load():
@@ -54,7 +81,7 @@ def _load():
     # comes in beside /opt/rocm's and torch's own kernels fail to launch.
     import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
-    P, G, S, I32, U32, F32 = (ctypes.c_void_p, ctypes.POINTER(kvarn_geom), ctypes.POINTER(ctypes.c_size_t),
+    P, G, S, I32, U32, F32 = (ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                               ctypes.c_int32, ctypes.c_uint32, ctypes.c_float)
     sig = {
         "kvarn_format_version": ([], ctypes.c_int),
@@ -83,6 +110,11 @@ lib = _load()
 
 
 # ----------------------------------------------------------------------------- marshalling helpers
+def _g(g) -> int | None:
+    """Address of a kvarn_geom or kvarn_geom_ext (both are passed as const kvarn_geom*)."""
+    return None if g is None else ctypes.addressof(g)
+
+
 def _ptr(t) -> int | None:
     if t is None:
         return None
@@ -116,65 +148,65 @@ def kvarn_format_version() -> int:
 
 def kvarn_cache_bytes(g: kvarn_geom) -> int:
     n = ctypes.c_size_t()
-    _check(lib.kvarn_cache_bytes(ctypes.byref(g), ctypes.byref(n)), "kvarn_cache_bytes")
+    _check(lib.kvarn_cache_bytes(_g(g), ctypes.byref(n)), "kvarn_cache_bytes")
     return n.value
 
 
 def kvarn_cache_init(g: kvarn_geom, cache, signs, stream=None) -> None:
     import numpy as np
     s = np.ascontiguousarray(signs, dtype=np.int8)
-    _check(lib.kvarn_cache_init(ctypes.byref(g), _ptr(cache), s.ctypes.data, _stream(stream)), "kvarn_cache_init")
+    _check(lib.kvarn_cache_init(_g(g), _ptr(cache), s.ctypes.data, _stream(stream)), "kvarn_cache_init")
 
 
 def kvarn_quantize_prefill(g: kvarn_geom, cache, k, v, num_tokens: int, stream=None) -> None:
-    _check(lib.kvarn_quantize_prefill(ctypes.byref(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _stream(stream)),
+    _check(lib.kvarn_quantize_prefill(_g(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _stream(stream)),
            "kvarn_quantize_prefill")
 
 
 def kvarn_debug_prefill(g: kvarn_geom, cache, k, v, num_tokens: int, w_k=None, w_v=None, y_k=None, y_v=None,
                         stream=None) -> None:
-    _check(lib.kvarn_debug_prefill(ctypes.byref(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _ptr(w_k),
+    _check(lib.kvarn_debug_prefill(_g(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _ptr(w_k),
                                    _ptr(w_v), _ptr(y_k), _ptr(y_v), _stream(stream)), "kvarn_debug_prefill")
 
 
 def kvarn_append_decode(g: kvarn_geom, cache, k, v, stream=None) -> None:
-    _check(lib.kvarn_append_decode(ctypes.byref(g), _ptr(cache), _ptr(k), _ptr(v), _stream(stream)),
+    _check(lib.kvarn_append_decode(_g(g), _ptr(cache), _ptr(k), _ptr(v), _stream(stream)),
            "kvarn_append_decode")
 
 
 def kvarn_dequantize(g: kvarn_geom, cache, k_out, v_out, max_tokens: int, out_dtype: int = KVARN_OUT_F32,
                      stream=None) -> None:
-    _check(lib.kvarn_dequantize(ctypes.byref(g), _ptr(cache), _ptr(k_out), _ptr(v_out), max_tokens, out_dtype,
+    _check(lib.kvarn_dequantize(_g(g), _ptr(cache), _ptr(k_out), _ptr(v_out), max_tokens, out_dtype,
                                 _stream(stream)), "kvarn_dequantize")
 
 
 def kvarn_attn_workspace_bytes(g: kvarn_geom, num_q_heads: int) -> int:
     n = ctypes.c_size_t()
-    _check(lib.kvarn_attn_workspace_bytes(ctypes.byref(g), num_q_heads, ctypes.byref(n)),
+    _check(lib.kvarn_attn_workspace_bytes(_g(g), num_q_heads, ctypes.byref(n)),
            "kvarn_attn_workspace_bytes")
     return n.value
 
 
 def kvarn_attn_decode(g: kvarn_geom, cache, q, num_q_heads: int, softmax_scale: float, flags: int, workspace,
                       workspace_bytes: int, out, stream=None) -> None:
-    _check(lib.kvarn_attn_decode(ctypes.byref(g), _ptr(cache), _ptr(q), num_q_heads, softmax_scale, flags,
+    _check(lib.kvarn_attn_decode(_g(g), _ptr(cache), _ptr(q), num_q_heads, softmax_scale, flags,
                                  _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "kvarn_attn_decode")
 
 
 def kvarn_append_attn_decode(g: kvarn_geom, cache, k, v, q, num_q_heads: int, softmax_scale: float, flags: int,
                              workspace, workspace_bytes: int, out, stream=None) -> None:
-    _check(lib.kvarn_append_attn_decode(ctypes.byref(g), _ptr(cache), _ptr(k), _ptr(v), _ptr(q), num_q_heads,
+    _check(lib.kvarn_append_attn_decode(_g(g), _ptr(cache), _ptr(k), _ptr(v), _ptr(q), num_q_heads,
                                         softmax_scale, flags, _ptr(workspace), workspace_bytes, _ptr(out),
                                         _stream(stream)), "kvarn_append_attn_decode")
 
 
 def kvarn_append_tokens(g: kvarn_geom, cache, k, v, num_tokens: int, counts=None, stream=None) -> None:
-    _check(lib.kvarn_append_tokens(ctypes.byref(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _ptr(counts),
+    _check(lib.kvarn_append_tokens(_g(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _ptr(counts),
                                    _stream(stream)), "kvarn_append_tokens")
 
 
 def kvarn_cache_set_pages(g: kvarn_geom, cache, pages, tile_first: int, num_tiles: int, stream=None) -> None:
-    _check(lib.kvarn_cache_set_pages(ctypes.byref(g), _ptr(cache), _ptr(pages), tile_first, num_tiles,
+    _check(lib.kvarn_cache_set_pages(_g(g), _ptr(cache), _ptr(pages), tile_first, num_tiles,
                                      _stream(stream)), "kvarn_cache_set_pages")
 
 

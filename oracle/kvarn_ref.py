@@ -39,11 +39,12 @@ import numpy as np
 # ----------------------------------------------------------------------------- format constants
 # Written out here on purpose: the oracle includes nothing from the library.
 MAGIC = 0x4E52564B          # bytes 'K','V','R','N' little-endian
-VERSION = 1
+VERSION = 2
 FLAG_CAPACITY = 1           # an append found the cache full (token dropped)
 FLAG_SATURATED = 2          # an input value was outside the fp16 range and was saturated
 FLAG_SCALE_CLAMPED = 4      # a stored scale hit the fp16 clamp range
 FLAG_UNMAPPED = 8           # a paged cache had no page for a tile that was written
+FLAG_NAN = 16               # an input value was NaN (stored as 0)
 Q_PREROTATED = 1            # attention flag: the query is already rotated (q H)
 FP16_MAX = 65504.0
 SCALE_MIN = 2.0 ** -14      # smallest normal fp16; lower clamp of r and c
@@ -54,6 +55,7 @@ SIGN_WORDS_OFFSET = 192     # uint32[head_dim / 2]: word d has bit 15 set where 
                             # bits of a packed pair of 16-bit floats)
 FLAGS_OFFSET = 36
 VARIANT_OFFSET = 40
+NUM_PAGES_OFFSET = 44
 # Ablation variants ([AP] section 5, ablations: Hadamard only, VarN only, VarN along one
 # axis only). A bit set removes one component; 0 is the method as defined.
 VARIANT_NO_ROTATION = 1       # H_D replaced by the identity ("VarN only")
@@ -86,13 +88,17 @@ def bf16_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def canonicalize(bits) -> tuple[np.ndarray, bool]:
+def canonicalize(bits) -> tuple[np.ndarray, bool, bool]:
     """Reading: every K/V input token is first brought to fp16, the dtype of the
     decode-time tail, so a token quantizes identically whether it arrives in a
-    prefill or through the tail. bf16 -> fp16 is exact for 2^-14 <= |x| <= 65504;
-    smaller values round (RNE) to the fp16 subnormal grid, larger ones saturate."""
-    v, clamped = fp16_saturate(bf16_to_f64(bits))
-    return v, bool(clamped.any())
+    prefill or through the tail. bf16 -> fp16 is exact for 2^-17 <= |x| <= 65504 (a
+    bf16 value keeps 8 significant bits); smaller values round (RNE) to the fp16
+    subnormal grid, larger ones (and infinities) saturate. The pages assume finite
+    inputs; a NaN is stored as 0 and reported. Returns (values, saturated, had_nan)."""
+    x = bf16_to_f64(bits)
+    nan = np.isnan(x)
+    v, clamped = fp16_saturate(np.where(nan, 0.0, x))
+    return v, bool(clamped.any()), bool(nan.any())
 
 
 def fp16_bits(x) -> np.ndarray:
@@ -247,7 +253,7 @@ def dequantize_tile(q, r16, c16, s16, z16) -> np.ndarray:
             * (np.asarray(z16)[..., None, :] + np.asarray(s16)[..., None, :] * q))
 
 
-# ----------------------------------------------------------------------------- tile record (format v1)
+# ----------------------------------------------------------------------------- tile record (format v2)
 def record_bytes(g: int, d: int, bits: int = 2) -> int:
     """codes G*D*bits/8 | r fp16[G] | c fp16[D] | s fp16[D] | z fp16[D]."""
     return g * d * bits // 8 + 2 * g + 6 * d
@@ -379,7 +385,7 @@ def unpack_record(rec, g: int, d: int, stream: int, bits: int = 2) -> dict:
                 s16=f(n + 2 * g + 2 * d, d), z16=f(n + 2 * g + 4 * d, d))
 
 
-# ----------------------------------------------------------------------------- cache buffer (format v1)
+# ----------------------------------------------------------------------------- cache buffer (format v2)
 class Geom:
     """batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant (VARIANT_* bits),
     num_pages (0: tiles stored per sequence; > 0: a pool of pages found through a page map)."""
@@ -466,6 +472,7 @@ class Cache:
         hdr[4:8].view(np.uint32)[0] = VERSION
         hdr[8:36].view(np.int32)[:] = geom.as_tuple()
         hdr[VARIANT_OFFSET:VARIANT_OFFSET + 4].view(np.uint32)[0] = geom.variant
+        hdr[NUM_PAGES_OFFSET:NUM_PAGES_OFFSET + 4].view(np.int32)[0] = geom.num_pages
         hdr[SIGMA_OFFSET:SIGMA_OFFSET + geom.head_dim].view(np.int8)[:] = np.asarray(sigma, np.int8)
         hdr[SIGN_WORDS_OFFSET:SIGN_WORDS_OFFSET + 2 * geom.head_dim].view(np.uint32)[:] = sign_words(sigma)
         if geom.paged:
@@ -565,9 +572,11 @@ def quantize_prefill(cache: Cache, k_bits, v_bits, num_tokens: int) -> None:
     assert 0 <= T <= g.capacity
     nfull = T // g.group
     for s, bits in enumerate((k_bits, v_bits)):
-        x, sat = canonicalize(np.asarray(bits)[:, :T])          # [B][T][Hkv][D]
+        x, sat, nan = canonicalize(np.asarray(bits)[:, :T])     # [B][T][Hkv][D]
         if sat:
             cache.or_flags(FLAG_SATURATED)
+        if nan:
+            cache.or_flags(FLAG_NAN)
         xt = np.transpose(x, (0, 2, 1, 3))                       # [B][Hkv][T][D]
         if nfull:
             recs, f = _quantize_stream(xt[:, :, :nfull * g.group], cache.sigma, g, s)
@@ -606,9 +615,11 @@ def append_decode(cache: Cache, k_bits, v_bits, mask=None) -> None:
                 if pos >= g.capacity:
                     cache.or_flags(FLAG_CAPACITY)
                     continue
-                x, sat = canonicalize(bits_s[s][b, h])
+                x, sat, nan = canonicalize(bits_s[s][b, h])
                 if sat:
                     cache.or_flags(FLAG_SATURATED)
+                if nan:
+                    cache.or_flags(FLAG_NAN)
                 tail = cache.tail(b, h, s)
                 tail[pos % g.group] = x.astype(np.float16)
                 if (pos + 1) % g.group == 0:
@@ -721,8 +732,8 @@ def append_attn_decode(cache: Cache, k_bits, v_bits, q_bits, num_q_heads: int, s
     q = bf16_to_f64(q_bits)
     if flags & Q_PREROTATED:
         q = undo_rotation(q, cache.sigma, g.variant)
-    kn, _ = canonicalize(k_bits)                                # [B][Hkv][D]
-    vn, _ = canonicalize(v_bits)
+    kn = canonicalize(k_bits)[0]                                # [B][Hkv][D]
+    vn = canonicalize(v_bits)[0]
     grp = num_q_heads // g.num_kv_heads
     out = np.zeros((g.batch, num_q_heads, d))
     for b in range(g.batch):

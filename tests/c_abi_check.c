@@ -16,8 +16,17 @@ static const entry_fn every_entry_point[] = {
     (entry_fn)kvarn_status_str,       (entry_fn)kvarn_debug_prefill,
 };
 
+/* A seven-field geometry followed in memory by values that would select an ablation
+ * variant and a paged layout if the library read past the struct. */
+struct boxed {
+    kvarn_geom g;
+    int32_t after[4];
+};
+
 int main(void) {
     kvarn_geom g;
+    struct boxed bx;
+    kvarn_geom_ext ext;
     size_t bytes = 0, ws = 0;
     kvarn_status st;
     int i;
@@ -44,6 +53,22 @@ int main(void) {
     printf("gqa_not_multiple_status %d\n", (int)kvarn_attn_workspace_bytes(&g, 15, &ws));
     /* a device call with a NULL cache is refused on the host, before any HIP call */
     printf("prefill_null_cache_status %d\n", (int)kvarn_quantize_prefill(&g, NULL, NULL, NULL, 0, NULL));
+    printf("sizeof_geom %d\nsizeof_geom_ext %d\n", (int)sizeof(kvarn_geom), (int)sizeof(kvarn_geom_ext));
+    bx.g = g;
+    bx.after[0] = 40; bx.after[1] = 8; bx.after[2] = 100; bx.after[3] = -1;
+    bytes = 0;
+    st = kvarn_cache_bytes(&bx.g, &bytes);
+    printf("boxed_status %d\nboxed_bytes %zu\n", (int)st, bytes);
+    memset(&ext, 0, sizeof ext);
+    ext.base = g;
+    ext.base.bits = 2 | KVARN_GEOM_EXT;
+    ext.size = (uint32_t)sizeof ext;
+    ext.num_pages = 100;
+    bytes = 0;
+    st = kvarn_cache_bytes(&ext.base, &bytes);
+    printf("ext_status %d\next_bytes %zu\n", (int)st, bytes);
+    ext.size = 36;
+    printf("ext_badsize_status %d\n", (int)kvarn_cache_bytes(&ext.base, &bytes));
     printf("status_str_ok %s\n", kvarn_status_str(KVARN_OK));
     printf("status_str_geom %s\n", kvarn_status_str(KVARN_ERR_GEOM));
     return 0;

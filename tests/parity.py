@@ -77,6 +77,8 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
     stats = dict(edge_exempt=0, codes=0, r_mis=0, c_mis=0, s_mis=0, z_mis=0, n_r=0, n_c=0)
     # header
     assert hc.buf[0:4].view(np.uint32)[0] == R.MAGIC
+    assert hc.buf[4:8].view(np.uint32)[0] == R.VERSION
+    assert hc.buf[R.NUM_PAGES_OFFSET:R.NUM_PAGES_OFFSET + 4].view(np.int32)[0] == og.num_pages
     assert hc.buf[8:36].view(np.int32).tolist() == list(og.as_tuple())
     assert hc.buf[R.VARIANT_OFFSET:R.VARIANT_OFFSET + 4].view(np.uint32)[0] == og.variant
     assert np.array_equal(hc.sigma, gc.sigma.astype(np.float64))
@@ -88,7 +90,7 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
         tiles = [(b, h, t) for b in range(og.batch) for h in range(og.num_kv_heads) for t in range(nfull)]
     for s, bits in enumerate((k_bits, v_bits)):
         for (b, h, tile) in tiles:
-            x, _ = R.canonicalize(bits[b, tile * G:(tile + 1) * G, h])       # [G][D]
+            x = R.canonicalize(bits[b, tile * G:(tile + 1) * G, h])[0]       # [G][D]
             w_ref = R.apply_rotation(x, gc.sigma, og.variant)
             if w is not None:
                 ok, worst = close_rowwise(w[s][b, tile * G:(tile + 1) * G, h], w_ref, 1e-5)

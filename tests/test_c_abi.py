@@ -35,7 +35,7 @@ def c_results(tmp_path_factory):
 
 def test_c_caller_sees_every_entry_point(c_results):
     assert int(c_results["entry_points"]) == len(K.EXPORTS)
-    assert int(c_results["format_version"]) == 1
+    assert int(c_results["format_version"]) == 2
 
 
 def test_c_caller_sizes_match_oracle_and_binding(c_results):
@@ -44,6 +44,19 @@ def test_c_caller_sizes_match_oracle_and_binding(c_results):
     assert int(c_results["cache_bytes"]) == og.total
     assert int(c_results["workspace_status"]) == K.KVARN_OK
     assert int(c_results["workspace_bytes"]) == K.kvarn_attn_workspace_bytes(K.geom(32, 10, 17408), 40)
+
+
+def test_c_caller_with_the_seven_field_struct(c_results):
+    """A caller written to the seven-field geometry gets defined results: the struct is 28
+    bytes, and the library reads no byte past it (the C caller surrounds it with a sentinel
+    that would select a paged layout if it were read)."""
+    assert int(c_results["sizeof_geom"]) == 28
+    assert int(c_results["sizeof_geom_ext"]) == 40
+    assert int(c_results["boxed_status"]) == K.KVARN_OK
+    assert int(c_results["boxed_bytes"]) == R.Geom(32, 10, 128, 17408, 32, 3, 2).total
+    assert int(c_results["ext_status"]) == K.KVARN_OK
+    assert int(c_results["ext_bytes"]) == R.Geom(32, 10, 128, 17408, 32, 3, 2, 0, 100).total
+    assert int(c_results["ext_badsize_status"]) == K.KVARN_ERR_GEOM
 
 
 def test_c_caller_gets_host_side_errors(c_results):

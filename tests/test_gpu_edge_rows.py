@@ -47,3 +47,33 @@ def test_prefill_zero_and_tiny_token_rows(G, n_it):
     ha, hb = gc.host_cache(), ap.host_cache()
     m = ha.defined_mask()
     assert np.array_equal(ha.buf[m], hb.buf[m])
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_non_finite_inputs(G):
+    """NaN inputs are stored as 0 and raise KVARN_FLAG_NAN; infinities saturate at +-65504
+    (KVARN_FLAG_SATURATED). Checked through the parity chain (a full tile and the tail) and
+    through single-token appends, which must give the same bytes and flags."""
+    print("[case] non-finite inputs", G, flush=True)
+    B, H = 1, 2
+    T = 2 * G + 3
+    k, v = synth.kv_host(21, B, T, H)
+    k[0, 3, 0, 9] = 0x7FC0            # NaN in the first tile
+    v[0, G + 1, 1, 100] = 0xFFC1      # -NaN in the second tile
+    k[0, 2 * G + 1, 1, 0] = 0x7FC0    # NaN in the tail
+    v[0, 7, 0, 50] = 0x7F80           # +inf in a tile
+    cap = (T // G + 1) * G
+    gc = GpuCache(B, H, cap, G, 3)
+    gpu_prefill(gc, k, v, T)
+    check_prefill(gc, k, v, T)
+    want = K.KVARN_FLAG_NAN | K.KVARN_FLAG_SATURATED
+    assert K.kvarn_cache_flags(gc.buf) == want
+    ap = GpuCache(B, H, cap, G, 3)
+    gpu_prefill(ap, k, v, 0)
+    kd, vd = from_u16(k), from_u16(v)
+    for t in range(T):
+        K.kvarn_append_decode(ap.g, ap.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+    assert K.kvarn_cache_flags(ap.buf) == want
+    ha, hb = gc.host_cache(), ap.host_cache()
+    m = ha.defined_mask()
+    assert np.array_equal(ha.buf[m], hb.buf[m])

@@ -230,7 +230,7 @@ def run_attn(gc, q_bits, Hq, scale=0.0, flags=0):
 
 
 @pytest.mark.parametrize("T,Hq,H", [(256, 4, 1), (250, 8, 2), (1, 1, 1), (20, 4, 2), (1000, 4, 2), (33, 2, 2),
-                                    (300, 16, 2), (100, 6, 2)])
+                                    (300, 16, 2), (100, 6, 2), (300, 24, 2), (70, 32, 1)])
 def test_attention_parity(T, Hq, H):
     say("attn", T, Hq, H)
     B = 2
@@ -375,28 +375,67 @@ def test_full_size_qwen3_prefill_dequant_sampled():
             assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) * 1.01 + 1e-5 * rms + 1e-30), (b, h, t, s)
 
 
-def test_full_size_long_reasoning_decode_sampled():
+def test_full_size_long_reasoning_quantize_and_decode():
     """Long-reasoning stress shape: 64 sequences x 8 KV heads x 32768 prior tokens, Student-t
-    (nu = 3) token norms, 8 outlier channels x30, G=32, 3 iterations, 32 query heads. Prefill,
-    appends across a group boundary, then attention on sampled (batch, kv head) pairs against
-    the oracle on the GPU-written bytes."""
-    say("full-size long-reasoning decode")
-    B, H, Hq, T0, steps = 64, 8, 32, 32768, 40
+    (nu = 3) token norms, 8 outlier channels x30, G=32, 3 iterations, 32 query heads, in the
+    benchmark's launch configuration. Prefill, then appends that complete one more group per
+    sequence. Every tile whose stored scales hit the fp16 clamp (r or c at 2^-14 or 65504, or
+    s / z saturated; found from the GPU bytes) goes through the full parity chain, with 64
+    random tiles and tiles completed by the appends. Attention on sampled (batch, kv head)
+    pairs against the oracle on the GPU-written bytes."""
+    say("full-size long-reasoning quantize + decode")
+    B, H, Hq, T0, steps, G = 64, 8, 32, 32768, 40, 32
     cap = T0 + 64
-    kd, vd = synth.kv_device(synth.sub_seed(5, 0, 0), B, T0, H, n_outlier_ch=8, ch_mult=30.0, law="student_t",
-                             nu=3.0)
+    law = dict(n_outlier_ch=8, ch_mult=30.0, law="student_t", nu=3.0)
+    kd, vd = synth.kv_device(synth.sub_seed(5, 0, 0), B, T0, H, **law)
     gc = GpuCache(B, H, cap)
     K.kvarn_quantize_prefill(gc.g, gc.buf, kd, vd, T0)
-    del kd, vd
-    kn, vn = synth.kv_device(synth.sub_seed(5, 0, 1), B, steps, H, n_outlier_ch=8, ch_mult=30.0, law="student_t",
-                             nu=3.0)
+    kn, vn = synth.kv_device(synth.sub_seed(5, 0, 1), B, steps, H, **law)
     for t in range(steps):
         K.kvarn_append_decode(gc.g, gc.buf, kn[:, t].contiguous(), vn[:, t].contiguous())
+    torch.cuda.synchronize()
+    T = T0 + steps
+    nfull = T // G
+    og = gc.og
+    # the clamped tiles, from the stored scales of every full tile (scanned on the device)
+    tiles = cap // G
+    rec = gc.buf[og.header:og.header + B * H * tiles * 2 * og.tr].view(B, H, tiles, 2, og.tr)[:, :, :nfull]
+    f16 = lambda lo, n: rec[..., lo:lo + 2 * n].contiguous().view(torch.int16)  # noqa: E731
+    r16, c16 = f16(1024, G), f16(1024 + 2 * G, 128)
+    s16, z16 = f16(1024 + 2 * G + 256, 128), f16(1024 + 2 * G + 512, 128)
+    lo, hi = 0x0400, 0x7BFF  # fp16 bits of 2^-14 and 65504
+    kinds = {"r_low": (r16 == lo).any(-1), "r_high": (r16 == hi).any(-1), "c_low": (c16 == lo).any(-1),
+             "c_high": (c16 == hi).any(-1), "s_sat": (s16 == hi).any(-1),
+             "z_sat": ((z16 & 0x7FFF) == hi).any(-1)}
+    counts = {k: int(v.sum()) for k, v in kinds.items()}
+    clamped = torch.stack(list(kinds.values())).any(0).any(-1)            # [B][H][nfull], either stream
+    idx = torch.nonzero(clamped).cpu().numpy()
+    del rec, r16, c16, s16, z16, kinds, clamped
+    say("clamped records", counts, "tiles", len(idx), "of", B * H * nfull)
+    assert K.kvarn_cache_flags(gc.buf) & K.KVARN_FLAG_SCALE_CLAMPED or len(idx) == 0
+    rng = np.random.default_rng(5)
+    picks = {(int(b), int(h), int(t)) for b, h, t in idx}
+    picks |= {(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(nfull))) for _ in range(64)}
+    picks |= {(int(rng.integers(B)), int(rng.integers(H)), nfull - 1) for _ in range(8)}  # completed by appends
+    picks = sorted(picks)
+    k = np.zeros((B, T, H, 128), dtype=np.uint16)
+    v = np.zeros_like(k)
+    for b, h, t in picks:
+        for arr, dev, newd in ((k, kd, kn), (v, vd, vn)):
+            lo_t, hi_t = t * G, (t + 1) * G
+            if hi_t <= T0:
+                arr[b, lo_t:hi_t, h] = to_u16(dev[b, lo_t:hi_t, h])
+            else:
+                arr[b, lo_t:hi_t, h] = to_u16(newd[b, lo_t - T0:hi_t - T0, h])
+    k[:, nfull * G:T] = to_u16(kn[:, nfull * G - T0:])  # the tail rows
+    v[:, nfull * G:T] = to_u16(vn[:, nfull * G - T0:])
+    del kd, vd
+    st = check_prefill(gc, k, v, T, tiles=picks)
+    say("stats", st, "tiles checked", len(picks))
     q = synth.q_host(19, B, Hq)
     out = run_attn(gc, q, Hq)
     assert np.all(np.isfinite(out))
     hc = gc.host_cache()
-    assert np.all(hc.lens == T0 + steps)
     pairs = [(0, 0), (63, 7), (29, 4)]
     ref = R.attn_decode(hc, q, Hq, pairs=pairs)
     grp = Hq // H

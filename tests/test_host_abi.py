@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_format_version_and_status_strings():
-    assert K.kvarn_format_version() == 1
+    assert K.kvarn_format_version() == R.VERSION == 2
     for s in range(7):
         assert K.status_str(s)
     assert K.status_str(99) == "unknown status"
@@ -68,9 +68,8 @@ def test_workspace_bytes():
     with pytest.raises(K.KvarnError) as e:
         K.kvarn_attn_workspace_bytes(g, 41)
     assert e.value.status == K.KVARN_ERR_GEOM
-    with pytest.raises(K.KvarnError) as e:
-        K.kvarn_attn_workspace_bytes(K.geom(1, 1, 64, 32, 3), 9)
-    assert e.value.status == K.KVARN_ERR_UNSUPPORTED
+    # any whole number of query heads per kv head: groups of 4 query heads per work-group
+    assert K.kvarn_attn_workspace_bytes(K.geom(1, 1, 64, 32, 3), 9) > 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -90,10 +89,38 @@ def test_geometry_rejected(kw, status):
     base = dict(batch=1, num_kv_heads=2, head_dim=128, capacity=128, group=32, varn_iters=3, bits=2, variant=0,
                 num_pages=0)
     base.update(kw)
-    g = K.kvarn_geom(*[base[n] for n, _ in K.kvarn_geom._fields_])
+    g = K.geom(base.pop("batch"), base.pop("num_kv_heads"), base.pop("capacity"), **base)
     with pytest.raises(K.KvarnError) as e:
         K.kvarn_cache_bytes(g)
     assert e.value.status == status
+
+
+def test_seven_field_geometry_is_the_base_of_the_extension():
+    """kvarn_geom has exactly the seven int32 fields of the problem statement (28 bytes); the
+    extension adds size, variant and num_pages after it, and is read only when the marker bit
+    is set in bits. Without the bit, bytes past the seven fields are never read."""
+    assert ctypes.sizeof(K.kvarn_geom) == 28
+    assert [n for n, _ in K.kvarn_geom._fields_] == ["batch", "num_kv_heads", "head_dim", "capacity", "group",
+                                                      "varn_iters", "bits"]
+    assert ctypes.sizeof(K.kvarn_geom_ext) == 40 and K.kvarn_geom_ext.size.offset == 28
+    plain = K.geom(2, 3, 256, 32, 3)
+    assert isinstance(plain, K.kvarn_geom)
+    # garbage after a plain struct does not matter: a buffer whose bytes 28.. say "paged"
+    buf = (ctypes.c_int32 * 10)(2, 3, 128, 256, 32, 3, 2, 40, 0, 7)
+    n = ctypes.c_size_t()
+    assert K.lib.kvarn_cache_bytes(ctypes.addressof(buf), ctypes.byref(n)) == K.KVARN_OK
+    assert n.value == K.kvarn_cache_bytes(plain) == R.Geom(2, 3, 128, 256, 32, 3, 2).total
+    # the same bytes with the marker bit: read as an extension with 7 pages
+    buf[6] = 2 | K.KVARN_GEOM_EXT
+    assert K.lib.kvarn_cache_bytes(ctypes.addressof(buf), ctypes.byref(n)) == K.KVARN_OK
+    assert n.value == R.Geom(2, 3, 128, 256, 32, 3, 2, 0, 7).total
+    # an extension of the wrong size is refused
+    buf[7] = 36
+    assert K.lib.kvarn_cache_bytes(ctypes.addressof(buf), ctypes.byref(n)) == K.KVARN_ERR_GEOM
+    ext = K.geom(2, 3, 256, 32, 3, variant=K.KVARN_VARIANT_CENTERED)
+    assert isinstance(ext, K.kvarn_geom_ext) and ext.bits == 2 and ext.base.bits == 2 | K.KVARN_GEOM_EXT
+    assert K.kvarn_cache_bytes(ext) == n.value - (R.Geom(2, 3, 128, 256, 32, 3, 2, 0, 7).total
+                                                  - R.Geom(2, 3, 128, 256, 32, 3, 2).total)
 
 
 # Fake device addresses: the calls below must fail validation before touching them.

@@ -34,7 +34,7 @@ def sdpa(q, k, v, scale):
 def test_header_fields():
     c, _, _ = make_cache(B=2, H=3, T=70)
     assert c.buf[0:4].view(np.uint32)[0] == R.MAGIC
-    assert c.buf[4:8].view(np.uint32)[0] == 1
+    assert c.buf[4:8].view(np.uint32)[0] == 2
     assert c.buf[8:36].view(np.int32).tolist() == [2, 3, 128, 128, 32, 3, 2]
     assert np.all(c.lens == 70)
     assert c.g.header == 768 and c.g.total % 256 == 0

@@ -70,18 +70,18 @@ def test_bf16_decoding_known_patterns():
 
 def test_canonicalize_range_edges():
     # 65536 does not fit fp16: saturates to 65504 and raises the flag
-    v, sat = R.canonicalize(np.array([0x4780], dtype=np.uint16))
+    v, sat, _ = R.canonicalize(np.array([0x4780], dtype=np.uint16))
     assert v[0] == 65504.0 and sat
-    v, sat = R.canonicalize(np.array([0x477F, 0x3F80], dtype=np.uint16))
+    v, sat, _ = R.canonicalize(np.array([0x477F, 0x3F80], dtype=np.uint16))
     assert v.tolist() == [65280.0, 1.0] and not sat
     # below 2^-14 the fp16 grid is 2^-24: 1.5 * 2^-24 and 2.5 * 2^-24 round to even (2 * 2^-24)
     x = np.array([1.5 * 2.0 ** -24, 2.5 * 2.0 ** -24, 2.0 ** -20 * (1 + 2.0 ** -7)], dtype=np.float32)
-    v, sat = R.canonicalize(synth.f32_to_bf16_bits(x))
+    v, sat, _ = R.canonicalize(synth.f32_to_bf16_bits(x))
     assert v.tolist() == [2 * 2.0 ** -24, 2 * 2.0 ** -24, 2.0 ** -20] and not sat
     # in the normal fp16 range bf16 -> fp16 is exact
     rng = np.random.default_rng(2)
     b = synth.f32_to_bf16_bits(rng.standard_normal(5000).astype(np.float32) * 100)
-    v, _ = R.canonicalize(b)
+    v = R.canonicalize(b)[0]
     assert np.array_equal(v, R.bf16_to_f64(b))
 
 
@@ -99,3 +99,27 @@ def test_sign_vector_splitmix64_reference_values():
     s = synth.sign_vector(0, 128)
     assert s.dtype == np.int8 and set(np.unique(s).tolist()) <= {-1, 1}
     assert s[0] == -1 and s[1] == 1 and s[2] == 1   # top bits of the three values above
+
+
+def test_canonicalize_non_finite_inputs():
+    """Infinities saturate like any value beyond fp16; a NaN (which the pages' finite
+    tensors never hold) is stored as 0 and reported, so one NaN cannot poison a tile's
+    scales: a prefill with a NaN raises FLAG_NAN and quantizes that element as a zero."""
+    bits = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x3F80], dtype=np.uint16)  # +inf -inf nan -nan 1
+    v, sat, nan = R.canonicalize(bits)
+    assert v.tolist() == [65504.0, -65504.0, 0.0, 0.0, 1.0] and sat and nan
+    v, sat, nan = R.canonicalize(np.array([0x3F80, 0xC000], dtype=np.uint16))
+    assert not sat and not nan
+    k, v2 = synth.kv_host(3, 1, 40, 1)
+    k_nan = k.copy()
+    k_nan[0, 5, 0, 17] = 0x7FC0
+    k_zero = k.copy()
+    k_zero[0, 5, 0, 17] = 0x0000
+    a = R.Cache(R.Geom(1, 1, 128, 64, 32, 3, 2), synth.sign_vector(0))
+    b = R.Cache(R.Geom(1, 1, 128, 64, 32, 3, 2), synth.sign_vector(0))
+    R.quantize_prefill(a, k_nan, v2, 40)
+    R.quantize_prefill(b, k_zero, v2, 40)
+    assert a.flags == R.FLAG_NAN and b.flags == 0
+    fl = R.FLAGS_OFFSET
+    a.buf[fl:fl + 4] = 0
+    assert np.array_equal(a.buf, b.buf)
