@@ -7,16 +7,23 @@ tokens, batch 1, group 32, 3 VarN iterations, 2 bits -- one step = the 32 layer
 caches quantized from 32 distinct input buffers resident in HBM, issued eagerly (the
 same step replayed as one HIP graph is reported beside it). Beside it:
   * roofline of the quantize kernel: algorithmic bytes per launch (bf16 in + tile
-    records out) over its average launch time measured with HIP events on the
-    launch stream, against the 8 TB/s HBM peak;
-  * decode: Phi-4-14B-shaped decode (40 layers x 10 KV heads, 40 query heads,
-    batch 32, 16384 prior tokens), tokens/s of the append + fused attention loop;
-  * long_decode: the long-reasoning stress shape (32 layers x 8 KV heads, 32 query heads,
-    batch 64 x 32768-token contexts, Student-t token norms), decode tokens/s;
+    records out) over the launch time, measured with HIP events on the launch stream
+    around the whole timed step loop and divided by the number of launches, against the
+    8 TB/s HBM peak, the 4 GiB copy ceiling and a streaming kernel with the prefill's
+    read/write mix;
+  * long_prefill: the same quantizer on the long-reasoning shape (64 x 32768 tokens per
+    layer, Student-t token norms), 32 launches;
+  * decode: the Phi-4-14B-shaped run as configured (40 layers x 10 KV heads, 40 query
+    heads, batch 32, 16384 -> 17408 tokens: 1024 steps of append + attention, every step
+    timed), eagerly, fused, and as a HIP graph;
+  * long_decode: the long-reasoning run (32 layers x 8 KV heads, 32 query heads, batch 64,
+    32768 -> 36864 tokens: 4096 steps), timed on 16 windows of 8 steps spread evenly over
+    the run; the steps between windows only append;
   * roundtrip: Qwen3-4B-shaped prefill (36 layers x 8 KV heads, batch 8 x 16384
     tokens, group 64, 2 VarN iterations) followed by a bf16 dequantization of every
     layer, with both kernels' launch times and algorithmic GB/s;
-  * cpu_baseline: the CPU oracle on a bounded sample of the same prefill workload.
+  * cpu_baseline: the CPU oracle on a bounded sample of the same workloads, one
+    single-threaded process per host core used (at most --cpu-workers).
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -40,77 +47,99 @@ def record_bytes(g: int, bits: int = 2) -> int:
     return g * 128 * bits // 8 + 2 * g + 6 * 128
 
 
-def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32, n_it=3, bits=2):
-    g = K.geom(1, H, T, G, n_it, bits=bits)
+def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32, n_it=3, bits=2, B=1,
+                  distinct=True, graph=True, law=None, tag="prefill"):
+    """`steps` steps of `layers` prefill launches, issued eagerly with nothing between them.
+    The timed region is bracketed by HIP events on the launch stream (so the per-launch
+    average is the kernel time of the step, gaps included) and by the wall clock."""
+    g = K.geom(B, H, T, G, n_it, bits=bits)
     sig = synth.sign_vector(0)
-    log(f"prefill workload: {layers} layers x B=1 x T={T} x Hkv={H}, G={G}, iters={n_it}")
-    ks, vs, caches = [], [], []
-    for l in range(layers):
-        k, v = synth.kv_device(synth.sub_seed(2, l, 0), 1, T, H)
+    law = law or {}
+    log(f"{tag} workload: {layers} layers x B={B} x T={T} x Hkv={H}, G={G}, iters={n_it}, {law or 'lognormal'}")
+    n_in = layers if distinct else 1
+    ks, vs = [], []
+    for l in range(n_in):
+        k, v = synth.kv_device(synth.sub_seed(2 if B == 1 else 5, l, 0), B, T, H, **law)
         ks.append(k)
         vs.append(v)
-        caches.append(K.alloc_cache(g, sig))
+    caches = [K.alloc_cache(g, sig) for _ in range(layers if distinct else 1)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+
+    def step():
+        for l in range(layers):
+            i = l if distinct else 0
+            K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T, stream)
+
     for _ in range(warmup):
-        for l in range(layers):
-            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T, stream)
+        step()
     torch.cuda.synchronize()
-    # per-launch kernel time: every launch bracketed by HIP events on its stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps * layers)]
-    i = 0
-    for _ in range(steps):
-        for l in range(layers):
-            ev[i][0].record(stream)
-            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T, stream)
-            ev[i][1].record(stream)
-            i += 1
-    torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    # the timed step: issued eagerly, one C-ABI call per layer, nothing between the launches
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for _ in range(steps):
-        for l in range(layers):
-            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T, stream)
+        step()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the same step as one HIP graph of its layer launches, replayed
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for l in range(layers):
-            K.kvarn_quantize_prefill(g, caches[l], ks[l], vs[l], T)
+    region_ms = e0.elapsed_time(e1)
+    # diagnostic only: every launch bracketed by its own event pair (adds a dispatch per launch)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+    for l in range(layers):
+        i = l if distinct else 0
+        ev[l][0].record(stream)
+        K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T, stream)
+        ev[l][1].record(stream)
     torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_wall = time.perf_counter() - t0
-    del graph
-    bytes_in = 2 * 2 * T * H * 128                       # K and V, bf16
-    bytes_out = 2 * H * (T // G) * record_bytes(G, bits)  # tile records
+    isolated_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    graph_wall = None
+    if graph:  # the same step as one HIP graph of its layer launches, replayed
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for l in range(layers):
+                i = l if distinct else 0
+                K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            gr.replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+        del gr
+    bytes_in = B * 2 * 2 * T * H * 128                       # K and V, bf16
+    bytes_out = B * 2 * H * (T // G) * record_bytes(G, bits)  # tile records
     flags = K.kvarn_cache_flags(caches[0])
     del ks, vs, caches
     torch.cuda.empty_cache()
-    return dict(wall=wall, graph_wall=graph_wall, launch_ms=launch_ms, bytes_in=bytes_in, bytes_out=bytes_out,
-                layers=layers, T=T, H=H, G=G, n_it=n_it, flags=flags)
+    return dict(wall=wall, graph_wall=graph_wall, region_ms=region_ms, launches=steps * layers,
+                isolated_ms=isolated_ms, bytes_in=bytes_in, bytes_out=bytes_out, layers=layers, T=T, H=H, G=G,
+                n_it=n_it, B=B, flags=flags)
 
 
-def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40, T0=16384, cap=17408, G=32,
-                 n_it=3, pool=128, bits=2, kv_kw=None):
+def bench_decode(K, synth, torch, run_steps, windows=0, win_steps=8, warmup=4, layers=40, B=32, H=10, Hq=40,
+                 T0=16384, cap=17408, G=32, n_it=3, pool=128, bits=2, kv_kw=None, variants=True, tag="decode"):
+    """The configured decode run: `run_steps` steps of append + attention on every layer,
+    from T0 prior tokens. windows == 0 times every step of the run. windows > 0 times
+    `windows` windows of `win_steps` steps spread evenly over the run; the steps between
+    them only append, so each window sees the cache the full run would have at that point.
+    Decode K, V and Q come from a pool of `pool` pre-generated steps, cycled (the bytes
+    moved do not depend on the values)."""
+    assert T0 + run_steps <= cap, "the decode run does not fit the cache capacity"
     g = K.geom(B, H, cap, G, n_it, bits=bits)
     sig = synth.sign_vector(0)
     kv_kw = kv_kw or {}
-    log(f"decode workload: {layers} layers x B={B} x Hkv={H} x Hq={Hq}, {T0} prior tokens, {steps} timed steps")
-    k0, v0 = synth.kv_device(synth.sub_seed(4, 0, 0), B, T0, H, **kv_kw)
-    caches = []
-    for l in range(layers):
-        c = K.alloc_cache(g, sig)
-        K.kvarn_quantize_prefill(g, c, k0, v0, T0)
-        caches.append(c)
-    del k0, v0
+    log(f"{tag} workload: {layers} layers x B={B} x Hkv={H} x Hq={Hq}, {T0} -> {T0 + run_steps} tokens, "
+        + (f"{windows} windows x {win_steps} steps" if windows else "every step timed"))
+    k0, v0 = synth.kv_device(synth.sub_seed(4 if B == 32 else 5, 0, 0), B, T0, H, **kv_kw)
+    caches = [K.alloc_cache(g, sig) for _ in range(layers)]
+
+    def reset():  # every layer back to the T0 prior tokens
+        for c in caches:
+            K.kvarn_quantize_prefill(g, c, k0, v0, T0)
+        torch.cuda.synchronize()
+
     kp, vp = synth.kv_device(synth.sub_seed(4, 0, 1), B, pool, H, **kv_kw)  # [B][pool][H][D]
     kp = kp.transpose(0, 1).contiguous()                              # [pool][B][H][D]
     vp = vp.transpose(0, 1).contiguous()
@@ -118,111 +147,120 @@ def bench_decode(K, synth, torch, steps, warmup=4, layers=40, B=32, H=10, Hq=40,
     ws, nws = K.alloc_workspace(g, Hq)
     out = torch.empty(B, Hq, 128, device="cuda")
     stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
 
-    def step(s, ev=None):
+    def step(s, fused=False, ev=None):
+        kk, vv, qq = kp[s % pool], vp[s % pool], qp[s % pool]
         for l in range(layers):
-            K.kvarn_append_decode(g, caches[l], kp[s % pool], vp[s % pool], stream)
-            if ev is not None:
+            if fused:
+                K.kvarn_append_attn_decode(g, caches[l], kk, vv, qq, Hq, 0.0, 0, ws, nws, out, stream)
+                continue
+            K.kvarn_append_decode(g, caches[l], kk, vv, stream)
+            if ev is not None and l == layers - 1:
                 ev[0].record(stream)
-            K.kvarn_attn_decode(g, caches[l], qp[s % pool], Hq, 0.0, 0, ws, nws, out, stream)
-            if ev is not None:
+            K.kvarn_attn_decode(g, caches[l], qq, Hq, 0.0, 0, ws, nws, out, stream)
+            if ev is not None and l == layers - 1:
                 ev[1].record(stream)
 
-    sc = 0  # decode steps issued so far (every step appends one token to every sequence)
-    for _ in range(warmup):
-        step(sc)
-        sc += 1
-    torch.cuda.synchronize()
-    ctx_start = T0 + sc
-    t0 = time.perf_counter()
-    for _ in range(steps):  # the timed steps: nothing but the library calls
-        step(sc)
-        sc += 1
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # the attention call of the last layer of each of 8 further steps, bracketed by events
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
-    ctx_attn = T0 + sc + 4  # context of the middle one
-    for i in range(8):
-        step(sc, evs[i])
-        sc += 1
-    torch.cuda.synchronize()
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    # one append launch per layer-step, timed the same way
-    ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
-    for e0, e1 in ea:
-        e0.record(stream)
-        K.kvarn_append_decode(g, caches[0], kp[sc % pool], vp[sc % pool], stream)
-        e1.record(stream)
-        for l in range(1, layers):
-            K.kvarn_append_decode(g, caches[l], kp[sc % pool], vp[sc % pool], stream)
+    def advance(s):  # append-only step: the cache moves on as in the full run
         for l in range(layers):
-            K.kvarn_attn_decode(g, caches[l], qp[sc % pool], Hq, 0.0, 0, ws, nws, out, stream)
-        sc += 1
-    torch.cuda.synchronize()
-    append_ms = [a.elapsed_time(b) for a, b in ea]
-    # the same step as one HIP graph: 40 x (append + attention) replayed, the step's inputs
-    # copied into the captured buffers first (inside the timed region)
-    k_in, v_in, q_in = torch.empty_like(kp[0]), torch.empty_like(vp[0]), torch.empty_like(qp[0])
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for l in range(layers):
-            K.kvarn_append_decode(g, caches[l], k_in, v_in)
-            K.kvarn_attn_decode(g, caches[l], q_in, Hq, 0.0, 0, ws, nws, out)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        k_in.copy_(kp[sc % pool])
-        v_in.copy_(vp[sc % pool])
-        q_in.copy_(qp[sc % pool])
-        graph.replay()
-        sc += 1
-    torch.cuda.synchronize()
-    graph_wall = time.perf_counter() - t0
-    del graph
-    # the fused step (kvarn_append_attn_decode: the append runs in the merge launch), eager
-    # and as a graph, over the same shapes
-    def fstep(s, kk, vv, qq):
-        for l in range(layers):
-            K.kvarn_append_attn_decode(g, caches[l], kk, vv, qq, Hq, 0.0, 0, ws, nws, out, stream)
+            K.kvarn_append_decode(g, caches[l], kp[s % pool], vp[s % pool], stream)
 
-    for _ in range(2):
-        fstep(sc, kp[sc % pool], vp[sc % pool], qp[sc % pool])
-        sc += 1
+    def run(fused=False):
+        """The configured run (or its windows); returns (timed steps, wall s, event ms, mean context)."""
+        reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if not windows:
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for s in range(run_steps):
+                step(s, fused)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return run_steps, time.perf_counter() - t0, e0.elapsed_time(e1), T0 + (run_steps - 1) / 2
+        starts = [i * run_steps // windows for i in range(windows)]
+        done, wall, ev_ms, ctx = 0, 0.0, 0.0, []
+        s = 0
+        for st in starts:
+            while s < st:
+                advance(s)
+                s += 1
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(win_steps):
+                step(s, fused)
+                ctx.append(T0 + s)
+                s += 1
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+            ev_ms += e0.elapsed_time(e1)
+            done += win_steps
+        return done, wall, ev_ms, sum(ctx) / len(ctx)
+
+    # warm-up on the prefilled caches, then every run starts from T0 again
+    reset()
+    for s in range(warmup):
+        step(s)
+        step(s, fused=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fstep(sc, kp[sc % pool], vp[sc % pool], qp[sc % pool])
-        sc += 1
+    res = {}
+    n, wall, ev_ms, ctx = run()
+    res["eager"] = dict(steps=n, wall=wall, event_ms=ev_ms, ctx=ctx)
+    if variants:
+        n, wall, ev_ms, ctx = run(fused=True)
+        res["fused"] = dict(steps=n, wall=wall, event_ms=ev_ms, ctx=ctx)
+        # the fused step as one HIP graph, replayed once per step with the step's inputs
+        # copied into the captured buffers first (inside the timed region)
+        reset()
+        k_in, v_in, q_in = torch.empty_like(kp[0]), torch.empty_like(vp[0]), torch.empty_like(qp[0])
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for l in range(layers):
+                K.kvarn_append_attn_decode(g, caches[l], k_in, v_in, q_in, Hq, 0.0, 0, ws, nws, out)
+        reset()  # the capture itself launched nothing, but start clean
+        steps_g = run_steps if not windows else 0
+        if steps_g:
+            t0 = time.perf_counter()
+            for s in range(steps_g):
+                k_in.copy_(kp[s % pool])
+                v_in.copy_(vp[s % pool])
+                q_in.copy_(qp[s % pool])
+                gr.replay()
+            torch.cuda.synchronize()
+            res["fused_graph"] = dict(steps=steps_g, wall=time.perf_counter() - t0)
+        del gr
+    # kernel timing at the middle of the run: the last layer's attention of 8 steps and
+    # the first layer's append of 4 steps, each bracketed by events
+    reset()
+    mid = run_steps // 2
+    for s in range(mid):
+        advance(s)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
+    for i in range(8):
+        step(mid + i, ev=evs[i])
+    ctx_attn = T0 + mid + 4
+    ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+    for i, (a0, a1) in enumerate(ea):
+        s = mid + 8 + i
+        a0.record(stream)
+        K.kvarn_append_decode(g, caches[0], kp[s % pool], vp[s % pool], stream)
+        a1.record(stream)
+        for l in range(1, layers):
+            K.kvarn_append_decode(g, caches[l], kp[s % pool], vp[s % pool], stream)
     torch.cuda.synchronize()
-    fused_wall = time.perf_counter() - t0
-    fgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(fgraph):
-        for l in range(layers):
-            K.kvarn_append_attn_decode(g, caches[l], k_in, v_in, q_in, Hq, 0.0, 0, ws, nws, out)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        k_in.copy_(kp[sc % pool])
-        v_in.copy_(vp[sc % pool])
-        q_in.copy_(qp[sc % pool])
-        fgraph.replay()
-        sc += 1
-    torch.cuda.synchronize()
-    fused_graph_wall = time.perf_counter() - t0
-    del fgraph
-    assert T0 + sc <= cap, "the decode workload outgrew its capacity"
+    attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    append_ms = sorted(a.elapsed_time(b) for a, b in ea)
     flags = K.kvarn_cache_flags(caches[0])
     # attention bytes per call at the event-timed context: K and V records of the full
     # tiles + tail rows + q + out
     nfull = ctx_attn // G
     attn_bytes = B * H * (2 * nfull * record_bytes(G, bits) + 2 * (ctx_attn % G) * 256) + B * Hq * (256 + 512)
-    del caches
+    del caches, k0, v0
     torch.cuda.empty_cache()
-    return dict(wall=wall, steps=steps, B=B, layers=layers, attn_ms=attn_ms, attn_bytes=attn_bytes, flags=flags,
-                ctx_start=ctx_start, H=H, Hq=Hq, graph_wall=graph_wall, append_ms=append_ms, fused_wall=fused_wall,
-                fused_graph_wall=fused_graph_wall)
+    return dict(res=res, B=B, layers=layers, H=H, Hq=Hq, T0=T0, run_steps=run_steps, windows=windows,
+                win_steps=win_steps, attn_ms=attn_ms, append_ms=append_ms, attn_bytes=attn_bytes, ctx_attn=ctx_attn,
+                flags=flags)
 
 
 def bench_roundtrip(K, synth, torch, steps, warmup=2, layers=36, B=8, T=16384, H=8, G=64, n_it=2, bits=2,
@@ -342,53 +380,128 @@ def copy_ceiling(torch, gib=4):
     return dict(bytes=2 * n, ms=round(ms, 3), GBps=round(2 * n / (ms * 1e-3) / 1e9, 1))
 
 
-def cpu_baseline(synth, tokens, layers):
-    """The oracle's prefill on the first `layers` layers of the prefill workload (host cores)."""
+def mix_ceiling(torch, bytes_in, bytes_out, layers=32, steps=10, grids=(1024, 2048, 4096, 8192)):
+    """The practical ceiling of a kernel with the prefill's mix of reads and writes: a plain
+    streaming kernel (libkvarn_bench.so) that reads `bytes_in` and writes `bytes_out` per
+    launch, over `layers` distinct buffer pairs per step like the prefill step; the best grid
+    of a small sweep, timed with events over `steps` steps."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_cache_bit_amd",
+                                   "libkvarn_bench.so"))
+    f = lib.kvarn_bench_stream_mix
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    ins = [torch.ones(bytes_in, dtype=torch.uint8, device="cuda") for _ in range(layers)]
+    outs = [torch.empty(bytes_out, dtype=torch.uint8, device="cuda") for _ in range(layers)]
+    st = torch.cuda.current_stream()
+    best = None
+    for grid in grids:
+        def step():
+            for l in range(layers):
+                assert f(ins[l].data_ptr(), bytes_in, outs[l].data_ptr(), bytes_out, grid, st.cuda_stream) == 0
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            step()
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
+        gbs = (bytes_in + bytes_out) / (us * 1e-6) / 1e9
+        if best is None or gbs > best["GBps"]:
+            best = dict(GBps=round(gbs, 1), launch_us=round(us, 2), grid=grid)
+    del ins, outs
+    torch.cuda.empty_cache()
+    return dict(best, bytes_read=bytes_in, bytes_written=bytes_out,
+                read_share=round(bytes_in / (bytes_in + bytes_out), 4))
+
+
+def _oracle_prefill_layer(job):
+    """One layer of the prefill workload through the oracle, in a worker process with one
+    BLAS thread; returns the oracle's seconds."""
+    tokens, layer = job
+    from threadpoolctl import threadpool_limits
+
+    from kv_cache_bit_amd import synth
     from oracle import kvarn_ref as R
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
-    H, G = 8, 32
-    dt = 0.0
-    for l in range(layers):
-        k, v = synth.kv_host(synth.sub_seed(2, l, 0), 1, tokens, H)
+    with threadpool_limits(1):
+        H, G = 8, 32
+        k, v = synth.kv_host(synth.sub_seed(2, layer, 0), 1, tokens, H)
         c = R.Cache(R.Geom(1, H, 128, tokens, G, 3, 2), synth.sign_vector(0))
         t0 = time.perf_counter()
         R.quantize_prefill(c, k, v, tokens)
-        dt += time.perf_counter() - t0
-    gbs = layers * 2 * 2 * tokens * H * 128 / dt / 1e9
-    return dict(value=round(gbs, 5), unit="GB/s", cores=int(blas), kind="oracle",
-                sample=f"layers 0..{layers - 1} of the prefill workload, {tokens} tokens x 8 KV heads x K and V "
-                       f"each ({layers * 2 * H * tokens // G} tiles), {dt:.1f} s of oracle time; NumPy fp64, "
-                       "BLAS threads = cores")
+        return time.perf_counter() - t0
 
 
-def cpu_baseline_decode(synth, T=16384, H=10, Hq=40, layers=40):
-    """The oracle's decode step (append + attention, by definition over the dequantized
-    cache) on one batch row of the Phi-4-shaped decode, extrapolated to the full step."""
+def _oracle_decode_row(job):
+    """One batch row of the Phi-4-shaped decode through the oracle (one BLAS thread): set-up
+    (untimed), then one append + attention step; returns the step's seconds."""
+    T, H, Hq, row = job
+    from threadpoolctl import threadpool_limits
+
+    from kv_cache_bit_amd import synth
     from oracle import kvarn_ref as R
+    with threadpool_limits(1):
+        G = 32
+        c = R.Cache(R.Geom(1, H, 128, T + 2 * G, G, 3, 2), synth.sign_vector(0))
+        k, v = synth.kv_host(synth.sub_seed(4, row, 0), 1, T, H)
+        R.quantize_prefill(c, k, v, T)
+        kn, vn = synth.kv_host(synth.sub_seed(4, row, 1), 1, 1, H)
+        q = synth.q_host(synth.sub_seed(4, row, 2), 1, Hq)
+        t0 = time.perf_counter()
+        R.append_decode(c, kn[:, 0], vn[:, 0])
+        R.attn_decode(c, q, Hq)
+        return time.perf_counter() - t0
+
+
+def _pool_map(fn, jobs, workers):
+    """Run jobs in `workers` fresh processes (spawned: they never touch the GPU); every
+    worker has exited when this returns. Returns (results, wall seconds)."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    pool = ctx.Pool(workers)
     try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
-    G = 32
-    c = R.Cache(R.Geom(1, H, 128, T + 2 * G, G, 3, 2), synth.sign_vector(0))
-    k, v = synth.kv_host(synth.sub_seed(4, 0, 0), 1, T, H)
-    R.quantize_prefill(c, k, v, T)                      # set-up, not timed
-    kn, vn = synth.kv_host(synth.sub_seed(4, 0, 1), 1, 1, H)
-    q = synth.q_host(synth.sub_seed(4, 0, 2), 1, Hq)
-    t0 = time.perf_counter()
-    R.append_decode(c, kn[:, 0], vn[:, 0])
-    R.attn_decode(c, q, Hq)
-    dt = time.perf_counter() - t0
-    # a step of B rows costs B times one row per layer and yields B tokens
-    return dict(value=round(1.0 / (dt * layers), 6), unit="tokens/s", cores=int(blas), kind="oracle",
-                sample=f"one batch row of the decode workload ({H} KV heads x {Hq} query heads, {T}-token "
-                       f"context): one append + attention step, {dt:.1f} s of oracle time, extrapolated "
-                       f"to {layers} layers; NumPy fp64, BLAS threads = cores")
+        t0 = time.perf_counter()
+        out = pool.map(fn, jobs, chunksize=1)
+        wall = time.perf_counter() - t0
+    finally:
+        pool.close()
+        pool.join()
+    return out, wall
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(tokens, layers, workers):
+    """The oracle's prefill on layers 0..layers-1 of the prefill workload, one layer per
+    worker process (one thread each), all workers at once: GB/s of bf16 input."""
+    dts, wall = _pool_map(_oracle_prefill_layer, [(tokens, l) for l in range(layers)], workers)
+    gb = layers * 2 * 2 * tokens * 8 * 128 / 1e9
+    return dict(value=round(gb / wall, 5), unit="GB/s", cores=workers, kind="oracle",
+                single_thread_value=round(gb / sum(dts), 5), host_cores=host_cores(),
+                sample=f"layers 0..{layers - 1} of the prefill workload ({tokens} tokens x 8 KV heads x K and V "
+                       f"each, {layers * 2 * 8 * tokens // 32} tiles), one layer per process on {workers} "
+                       f"processes with one thread each: {sum(dts):.1f} s of oracle time in {wall:.1f} s; "
+                       "NumPy fp64")
+
+
+def cpu_baseline_decode(workers, T=16384, H=10, Hq=40, layers=40):
+    """The oracle's decode step (append + attention by definition over the dequantized cache)
+    on `workers` batch rows of the Phi-4-shaped decode at once, one row per process, scaled
+    to the 40-layer step: tokens/s."""
+    dts, _ = _pool_map(_oracle_decode_row, [(T, H, Hq, r) for r in range(workers)], workers)
+    step = max(dts) * layers  # the rows run side by side; one step of every row and layer
+    return dict(value=round(workers / step, 6), unit="tokens/s", cores=workers, kind="oracle",
+                host_cores=host_cores(),
+                sample=f"{workers} batch rows of the decode workload ({H} KV heads x {Hq} query heads, {T}-token "
+                       f"context), one per process with one thread each: one append + attention step, "
+                       f"{max(dts):.1f} s per row-layer, scaled to {layers} layers; NumPy fp64")
 
 
 # HBM traffic of a kernel from committed rocprofv3 counter summaries: FETCH_SIZE and
@@ -434,15 +547,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=32)
+    ap.add_argument("--decode-steps", type=int, default=1024,
+                    help="decode steps of the Phi-4-shaped run (16384 -> 17408 tokens), every step timed")
+    ap.add_argument("--long-steps", type=int, default=4096,
+                    help="decode steps of the long-reasoning run (32768 -> 36864 tokens)")
+    ap.add_argument("--long-windows", type=int, default=16, help="timed windows of 8 steps over the long run")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true",
-                    help="skip the long-reasoning decode (64 x 32768-token contexts, Llama-3.1-8B KV geometry)")
+                    help="skip the long-reasoning prefill and decode (64 x 32768-token contexts, Llama-3.1-8B KV geometry)")
     ap.add_argument("--no-roundtrip", action="store_true",
                     help="skip the Qwen3-4B-shaped prefill + dequantize round trip")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
-    ap.add_argument("--cpu-layers", type=int, default=5, help="layers of the prefill workload the oracle runs")
+    ap.add_argument("--cpu-workers", type=int, default=8,
+                    help="oracle processes (one thread each) of the CPU baseline, at most the host's cores")
     ap.add_argument("--no-copy", action="store_true", help="skip the 4 GiB device copy ceiling")
     ap.add_argument("--no-bf16", action="store_true", help="skip the plain bf16 decode-attention baseline")
     ap.add_argument("--bits", type=int, default=2, choices=(2, 3, 4),
@@ -467,12 +585,14 @@ def main():
     ms_step = pf["wall"] * 1e3 / args.steps
     value = pf["layers"] * pf["bytes_in"] / (ms_step * 1e-3) / 1e9
     total_gbs = pf["layers"] * (pf["bytes_in"] + pf["bytes_out"]) / (ms_step * 1e-3) / 1e9
-    lm = sorted(pf["launch_ms"])
-    avg_launch = sum(lm) / len(lm)
-    achieved = (pf["bytes_in"] + pf["bytes_out"]) / (avg_launch * 1e-3) / 1e9
+    bpl = pf["bytes_in"] + pf["bytes_out"]
+    launch_us = pf["region_ms"] * 1e3 / pf["launches"]   # events over the timed region, per launch
+    achieved = bpl / (launch_us * 1e-6) / 1e9
+    iso = pf["isolated_ms"]
     graph_ms = pf["graph_wall"] * 1e3 / args.steps
     log(f"prefill: {ms_step:.3f} ms/step ({graph_ms:.3f} as a graph), {value:.1f} GB/s bf16-in, "
-        f"{total_gbs:.1f} GB/s total; kernel avg {avg_launch * 1e3:.1f} us -> {achieved:.1f} GB/s")
+        f"{total_gbs:.1f} GB/s total; {launch_us:.2f} us per launch -> {achieved:.1f} GB/s")
+    kname = "prefill_kernel<1, false, false, 1>" if args.bits == 2 else "prefill_kernel<1, false, true, 1>"
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -488,69 +608,58 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES)
                                  if args.bits == 2 else None),
-                     "traffic_unit": "bytes/launch",
-                     "kernel": "prefill_kernel<1,false,false,1>" if args.bits == 2 else "prefill_kernel<1,false,true,1>", "bytes_per_launch": pf["bytes_in"] + pf["bytes_out"],
-                     "avg_launch_us": round(avg_launch * 1e3, 2), "median_launch_us": round(lm[len(lm) // 2] * 1e3, 2)},
+                     "traffic_unit": "bytes/launch", "kernel": kname, "bytes_per_launch": bpl,
+                     "avg_launch_us": round(launch_us, 2), "launches_timed": pf["launches"],
+                     "timing": "HIP events on the launch stream around the timed step loop, / launches",
+                     "isolated_launch_us_median": round(iso[len(iso) // 2] * 1e3, 2),
+                     "source_digest": source_digest(PREFILL_SOURCES + KERNEL_SOURCES)},
         "flags": pf["flags"],
     }
     if not args.no_copy:
         res["copy_ceiling"] = copy_ceiling(torch)
         log(f"copy ceiling: {res['copy_ceiling']}")
+        mc = mix_ceiling(torch, pf["bytes_in"], pf["bytes_out"])
+        res["mix_ceiling"] = mc
+        res["roofline"]["frac_of_mix_ceiling"] = round(achieved / mc["GBps"], 4)
+        log(f"streaming ceiling at the prefill's read/write mix: {mc}")
+    if not args.no_long:
+        lp = bench_prefill(K, synth, torch, 1, 1, layers=32, B=64, distinct=False, graph=False, bits=args.bits,
+                           law=dict(law="student_t", nu=3.0, n_outlier_ch=8, ch_mult=30.0), tag="long prefill")
+        lus = lp["region_ms"] * 1e3 / lp["launches"]
+        lb = lp["bytes_in"] + lp["bytes_out"]
+        res["long_prefill"] = {
+            "workload": "long-reasoning prefill quantize: llama3.1-8b KV geometry, 64 x 32768 tokens per layer",
+            "layers": lp["layers"], "batch": lp["B"], "tokens": lp["T"], "kv_heads": lp["H"],
+            "input": "bf16, Student-t (nu 3) token norms, 8 outlier channels x30",
+            "ms_per_step": round(lp["wall"] * 1e3, 3),
+            "value": round(lp["layers"] * lp["bytes_in"] / lp["wall"] / 1e9, 1), "unit": "GB/s bf16-in",
+            "avg_launch_us": round(lus, 2), "bytes_per_launch": lb,
+            "achieved": round(lb / (lus * 1e-6) / 1e9, 1), "frac": round(lb / (lus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "flags": lp["flags"], "note": "one input buffer and cache reused by the 32 launches (8.6 GB each)"}
+        log(f"long prefill: {res['long_prefill']}")
     if not args.no_decode:
         dc = bench_decode(K, synth, torch, args.decode_steps, bits=args.bits)
-        tok_s = dc["B"] * dc["steps"] / dc["wall"]
-        am = sorted(dc["attn_ms"])
-        a_avg = sum(am) / len(am)
-        res["decode"] = {
-            "workload": "phi-4-14b-shaped decode: append + attn_decode", "tokens_per_s": round(tok_s, 1),
-            "ms_per_step": round(dc["wall"] * 1e3 / dc["steps"], 3), "steps_timed": dc["steps"],
-            "layers": dc["layers"], "batch": dc["B"], "kv_heads": dc["H"], "q_heads": dc["Hq"],
-            "context_at_start": dc["ctx_start"], "attn_avg_us": round(a_avg * 1e3, 2),
-            "attn_GBps": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9, 1),
-            "attn_frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "flags": dc["flags"],
-            "roofline": {"bound": "hbm", "kernel": f"attn_kernel<32, {args.bits}> + merge_kernel",
-                         "achieved": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(dc["attn_bytes"] / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "bytes_per_launch": dc["attn_bytes"],
-                         "traffic": (counted_traffic("attn_kernel_phi4_decode_pmc.txt", ATTN_SOURCES)
-                                     if args.bits == 2 else None),
-                         "traffic_unit": "bytes/launch (tile pass)"}}
-        ap = sorted(dc["append_ms"])
-        res["decode"]["graph_tokens_per_s"] = round(dc["B"] * dc["steps"] / dc["graph_wall"], 1)
-        res["decode"]["graph_ms_per_step"] = round(dc["graph_wall"] * 1e3 / dc["steps"], 3)
-        res["decode"]["append_us"] = round(ap[len(ap) // 2] * 1e3, 2)
-        res["decode"]["fused_tokens_per_s"] = round(dc["B"] * dc["steps"] / dc["fused_wall"], 1)
-        res["decode"]["fused_graph_tokens_per_s"] = round(dc["B"] * dc["steps"] / dc["fused_graph_wall"], 1)
-        res["decode"]["append_share"] = round(ap[len(ap) // 2] / (ap[len(ap) // 2] + a_avg), 4)
-        log(f"decode: {tok_s:.1f} tok/s eager, {res['decode']['graph_tokens_per_s']} tok/s as a graph; "
-            f"attn {a_avg * 1e3:.1f} us, append {res['decode']['append_us']} us per layer-step")
-        log(f"fused step: {res['decode']['fused_tokens_per_s']} tok/s eager, "
-            f"{res['decode']['fused_graph_tokens_per_s']} tok/s as a graph")
+        res["decode"] = decode_report(dc, args.bits, "phi-4-14b-shaped decode: append + attn_decode")
+        ah = res["decode"]
+        ah["roofline"]["traffic"] = (counted_traffic("attn_kernel_phi4_decode_pmc.txt", ATTN_SOURCES)
+                                     if args.bits == 2 else None)
+        ah["roofline"]["traffic_unit"] = "bytes/launch (tile pass)"
+        log(f"decode: {ah}")
         if not args.no_bf16:
             bf = bench_bf16_decode(torch)
-            res["decode"]["bf16_baseline"] = dict(bf, kind="plain bf16 KV cache, torch batched products, same shapes")
-            best = max(res["decode"]["graph_tokens_per_s"], res["decode"]["fused_graph_tokens_per_s"])
-            res["decode"]["speedup_vs_bf16"] = round(best / bf["tokens_per_s"], 2)
+            ah["bf16_baseline"] = dict(bf, kind="plain bf16 KV cache, torch batched products, same shapes")
+            best = max(v for k, v in ah.items() if k.endswith("tokens_per_s"))
+            ah["speedup_vs_bf16"] = round(best / bf["tokens_per_s"], 2)
             log(f"bf16 baseline: {bf}")
     if not args.no_long:
         torch.cuda.empty_cache()
-        lg = bench_decode(K, synth, torch, 8, warmup=2, layers=32, B=64, H=8, Hq=32, T0=32768, cap=36864,
-                          bits=args.bits, kv_kw=dict(law="student_t", nu=3.0, n_outlier_ch=8, ch_mult=30.0))
-        lam = sorted(lg["attn_ms"])
-        la_avg = sum(lam) / len(lam)
-        res["long_decode"] = {
-            "workload": "long-reasoning stress decode: llama3.1-8b KV geometry, 64 x 32768-token contexts",
-            "layers": lg["layers"], "batch": lg["B"], "kv_heads": lg["H"], "q_heads": lg["Hq"],
-            "context_at_start": lg["ctx_start"], "input": "bf16, Student-t (nu 3) token norms, 8 outlier channels x30",
-            "tokens_per_s": round(lg["B"] * lg["steps"] / lg["wall"], 1),
-            "ms_per_step": round(lg["wall"] * 1e3 / lg["steps"], 3), "steps_timed": lg["steps"],
-            "fused_tokens_per_s": round(lg["B"] * lg["steps"] / lg["fused_wall"], 1),
-            "attn_avg_us": round(la_avg * 1e3, 2),
-            "attn_GBps": round(lg["attn_bytes"] / (la_avg * 1e-3) / 1e9, 1),
-            "attn_frac": round(lg["attn_bytes"] / (la_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "flags": lg["flags"]}
-        log(f"long decode: {res['long_decode']['tokens_per_s']} tok/s eager, "
-            f"{res['long_decode']['fused_tokens_per_s']} fused; attn {res['long_decode']['attn_avg_us']} us "
-            f"({res['long_decode']['attn_GBps']} GB/s) per layer-step")
+        lg = bench_decode(K, synth, torch, args.long_steps, windows=args.long_windows, win_steps=8, warmup=2,
+                          layers=32, B=64, H=8, Hq=32, T0=32768, cap=36864, bits=args.bits,
+                          kv_kw=dict(law="student_t", nu=3.0, n_outlier_ch=8, ch_mult=30.0), tag="long decode")
+        res["long_decode"] = decode_report(lg, args.bits,
+                                           "long-reasoning stress decode: llama3.1-8b KV geometry, 64 sequences")
+        res["long_decode"]["input"] = "bf16, Student-t (nu 3) token norms, 8 outlier channels x30"
+        log(f"long decode: {res['long_decode']}")
     if not args.no_roundtrip:
         rt = bench_roundtrip(K, synth, torch, max(1, args.steps // 3), bits=args.bits)
         res["roundtrip"] = rt
@@ -558,12 +667,44 @@ def main():
             f"({rt['prefill']['achieved']} GB/s), dequantize {rt['dequantize']['avg_launch_us']} us "
             f"({rt['dequantize']['achieved']} GB/s) per layer")
     if not args.no_cpu:
-        log("cpu baseline (oracle) ...")
-        res["cpu_baseline"] = cpu_baseline(synth, args.cpu_tokens, args.cpu_layers)
+        workers = max(1, min(args.cpu_workers, host_cores()))
+        log(f"cpu baseline (oracle) on {workers} processes ...")
+        res["cpu_baseline"] = cpu_baseline(args.cpu_tokens, workers, workers)
         if "decode" in res:
             log("cpu baseline, decode step (oracle) ...")
-            res["decode"]["cpu_baseline"] = cpu_baseline_decode(synth)
+            res["decode"]["cpu_baseline"] = cpu_baseline_decode(workers)
     print(json.dumps(res), flush=True)
+
+
+def decode_report(dc, bits, workload):
+    r = dc["res"]
+    B = dc["B"]
+    e = r["eager"]
+    rep = {"workload": workload, "layers": dc["layers"], "batch": B, "kv_heads": dc["H"], "q_heads": dc["Hq"],
+           "context_start": dc["T0"], "context_end": dc["T0"] + dc["run_steps"], "run_steps": dc["run_steps"],
+           "timed": ("every step of the run" if not dc["windows"] else
+                     f"{dc['windows']} windows x {dc['win_steps']} steps spread evenly over the run (the steps "
+                     "between windows append only)"),
+           "steps_timed": e["steps"], "mean_context_timed": round(e["ctx"], 1),
+           "tokens_per_s": round(B * e["steps"] / e["wall"], 1), "ms_per_step": round(e["wall"] * 1e3 / e["steps"], 3),
+           "tokens_per_s_events": round(B * e["steps"] / (e["event_ms"] * 1e-3), 1), "flags": dc["flags"]}
+    if "fused" in r:
+        rep["fused_tokens_per_s"] = round(B * r["fused"]["steps"] / r["fused"]["wall"], 1)
+    if "fused_graph" in r:
+        rep["fused_graph_tokens_per_s"] = round(B * r["fused_graph"]["steps"] / r["fused_graph"]["wall"], 1)
+    am, apm = dc["attn_ms"], dc["append_ms"]
+    a_avg = sum(am) / len(am)
+    gbs = dc["attn_bytes"] / (a_avg * 1e-3) / 1e9
+    rep["attn_avg_us"] = round(a_avg * 1e3, 2)
+    rep["append_us"] = round(apm[len(apm) // 2] * 1e3, 2)
+    rep["append_share"] = round(apm[len(apm) // 2] / (apm[len(apm) // 2] + a_avg), 4)
+    rep["roofline"] = {"bound": "hbm", "kernel": f"attn_kernel<32, {bits}> + merge_kernel", "achieved": round(gbs, 1),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "bytes_per_launch": dc["attn_bytes"], "context": dc["ctx_attn"],
+                       "timing": "events around the last layer's attention call of 8 steps at mid-run"}
+    # at 100% of HBM the step would move every layer's attention bytes once
+    rep["tokens_per_s_at_hbm_peak"] = round(B / (dc["layers"] * dc["attn_bytes"] / (HBM_PEAK_GBS * 1e9)), 1)
+    return rep
 
 
 if __name__ == "__main__":

@@ -12,6 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "quantize.hip", "dequant.hip", "attn.hip"]
 LIB = os.path.join(HERE, "libkvarn.so")
+# a measurement kernel of the benchmark (streaming reads and writes), kept out of libkvarn
+BENCH_SOURCES = ["stream_mix.hip"]
+BENCH_LIB = os.path.join(HERE, "libkvarn_bench.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -28,10 +31,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into kv_cache_bit_amd/libkvarn.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,7 +43,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into kv_cache_bit_amd/libkvarn.so (and the benchmark's
+    measurement kernel into libkvarn_bench.so); returns the library's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
     return LIB
 
 

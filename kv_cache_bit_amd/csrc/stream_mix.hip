@@ -1,0 +1,41 @@
+// A measurement kernel for the benchmark, not part of the libkvarn boundary: it streams
+// `in_bytes` of reads and `out_bytes` of writes through HBM in one launch, with no other
+// work, so the benchmark can quote the practical ceiling of a kernel with the same mix of
+// reads and writes as the prefill quantizer (about 81.5% read, 18.5% written).
+//
+// Output word o (16 B) is the XOR of input words o, o + n_out, o + 2 n_out, ...: consecutive
+// lanes read and write consecutive 16-byte words, and every input byte is read once.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+__global__ __launch_bounds__(256) void stream_mix_kernel(const uint4* __restrict__ in, long long n_in,
+                                                           uint4* __restrict__ out, long long n_out) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x; o < n_out; o += stride) {
+    uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+    for (long long i = o; i < n_in; i += n_out) {
+      const uint4 v = in[i];
+      acc.x ^= v.x;
+      acc.y ^= v.y;
+      acc.z ^= v.z;
+      acc.w ^= v.w;
+    }
+    out[o] = acc;
+  }
+}
+
+}  // namespace
+
+extern "C" __attribute__((visibility("default"))) int kvarn_bench_stream_mix(const void* in, size_t in_bytes,
+                                                                           void* out, size_t out_bytes,
+                                                                           int grid, void* stream) {
+  if (!in || !out || out_bytes < 16 || in_bytes < out_bytes || (in_bytes | out_bytes) & 15 || grid <= 0) return 1;
+  if (((uintptr_t)in | (uintptr_t)out) & 15) return 2;
+  hipLaunchKernelGGL(stream_mix_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(in), (long long)(in_bytes / 16), static_cast<uint4*>(out),
+                     (long long)(out_bytes / 16));
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}

@@ -32,3 +32,15 @@ def test_no_gpu_no_fallback():
     r = run("--steps", "1", "--warmup", "0", "--no-decode", "--no-cpu")
     assert r.returncode == 1
     assert "needs a GPU" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_reports_the_processes_it_used():
+    """The oracle baseline runs one single-threaded process per worker and reports that
+    count as its cores; every worker has exited when it returns."""
+    import multiprocessing as mp
+    sys.path.insert(0, ROOT)
+    import bench
+    r = bench.cpu_baseline(64, 2, 2)
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    assert r["host_cores"] >= 1
+    assert mp.active_children() == []
