@@ -30,10 +30,26 @@
 // the attention merge launch reuses the append job for the fused decode step.
 #pragma once
 
+#include <type_traits>
+
 #include "kvarn_common.h"
 #include "kvarn_launch.h"
 
 namespace kvarn {
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{}): a loop
+// whose index is a constant expression (instruction immediates such as a byte select)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_from<0, N>(f);
+}
 
 struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
 struct OpMin { __device__ float operator()(float a, float b) const { return vmin(a, b); } };
@@ -194,23 +210,22 @@ template <bool CHECK>
 __device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m, uint32_t* flags = nullptr) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
+  bool nan = false, sat = false;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     float v[2] = {__int_as_float((int)((ws[d] + m.m[d]) << 16)), __int_as_float((int)((ws[d] ^ m.m[d]) & 0xFFFF0000u))};
     if constexpr (CHECK) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        if (!(v[e] == v[e])) {
-          *flags |= KVARN_FLAG_NAN;
-          v[e] = 0.0f;
-        } else if (fabsf(v[e]) > kFp16Max) {
-          *flags |= KVARN_FLAG_SATURATED;
-          v[e] = __builtin_amdgcn_fmed3f(v[e], -kFp16Max, kFp16Max);
-        }
+        const bool bad = !(v[e] == v[e]);
+        nan |= bad;
+        sat |= fabsf(v[e]) > kFp16Max;  // false for a NaN
+        v[e] = bad ? 0.0f : fminf(fmaxf(v[e], -kFp16Max), kFp16Max);
       }
     }
     o[d] = pack_f16x2(v[0], v[1]);
   }
+  if constexpr (CHECK) *flags |= (nan ? (uint32_t)KVARN_FLAG_NAN : 0u) | (sat ? (uint32_t)KVARN_FLAG_SATURATED : 0u);
   return __builtin_bit_cast(h8v, make_uint4(o[0], o[1], o[2], o[3]));
 }
 __device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp16 input
@@ -574,6 +589,74 @@ __device__ __forceinline__ void emit_bit_plane(const f4v (&acc)[2][8], F bit, in
   }
 }
 
+// 2-bit codes through the packed fp4 conversion. v_cvt_scalef32_pk_fp4_f32 rounds two fp32
+// values, divided by the power of two of its scale, to e2m1 with round-half-to-even and
+// writes them as the two nibbles of a chosen byte. On [0, 1.5] e2m1 is the grid
+// {0, 0.5, 1, 1.5}, so the nibble of t / 2 is RNE(t) for t in [0, 3.5): the 2-bit code in
+// bits 0..1 of a nibble. Inputs arrive as t / 4 (al4, ga4 = al / 4, ga / 4, exact), clamped to
+// [0, 1] by the multiply-add itself, which also keeps the sign bit of the nibble clear; with
+// CLAMP (some u may leave (-0.5, 3.5)) the top is cut at 3/4 as well. Two nibble words whose
+// nibble k holds codes A and B give A | B << 2: nibble k of the result holds both codes.
+//   K: word w of token t, byte k: nibble 0 = lane 2w's codes of channel blocks (2k, 2k + 1),
+//      nibble 1 = lane 2w + 1's. A lane converts its tokens t0 = 4g + i and t1 = 16 + 4g + i
+//      together (t0 into the low nibble of each byte, t1 into the high one), swaps the
+//      result with its partner lane, and each of the two keeps one token's word: the even
+//      lane t0's, the odd lane t1's.
+//   V: byte of tokens 4g .. 4g + 3 (+ 16 mb) of channel 16 nb + c: codes i = 0 | 1 << 2 |
+//      2 << 4 | 3 << 6; the low nibbles take i = 0, 1 and the high ones i = 2, 3.
+template <int NW, bool CLAMP>
+__device__ __forceinline__ void emit_codes2(const f4v (&acc)[2][8], const float (&al4)[8], const float (&ga4)[8],
+                                            int stream, int sub, int g, int c, uint8_t* base) {
+  constexpr int G = 32 * NW;
+  const int ttile0 = sub * 32 + 4 * g;
+  auto q4 = [&](float y, int nb) -> float {
+    float t;
+    asm("v_fma_f32 %0, %1, %2, %3 clamp" : "=v"(t) : "v"(y), "v"(al4[nb]), "v"(ga4[nb]));
+    if constexpr (CLAMP) t = vmin(t, 0.75f);
+    return t;
+  };
+  if (stream == 0) {
+    const bool odd = c & 1;
+    const uint32_t keep = odd ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+    const uint32_t rot = odd ? 4u : 28u;
+    uint8_t* row = base + 2 * (c & ~1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // every byte is written below, so the words start undefined (no initializing move)
+      uint32_t xa = __builtin_nondeterministic_value(0u), xb = __builtin_nondeterministic_value(0u);
+      static_for<4>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        xa = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(xa, q4(acc[0][2 * k][i], 2 * k), q4(acc[1][2 * k][i], 2 * k),
+                                                      0.5f, k);
+        xb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(xb, q4(acc[0][2 * k + 1][i], 2 * k + 1),
+                                                      q4(acc[1][2 * k + 1][i], 2 * k + 1), 0.5f, k);
+      });
+      const uint32_t z = xa | (xb << 2);
+      const uint32_t zp = (uint32_t)__builtin_amdgcn_mov_dpp((int)z, kQx1, 0xF, 0xF, true);
+      const uint32_t p = __builtin_amdgcn_alignbit(zp, zp, rot);  // even: zp << 4, odd: zp >> 4
+      const uint32_t word = (z & keep) | (p & ~keep);
+      *reinterpret_cast<uint32_t*>(row + (ttile0 + i + (odd ? 16 : 0)) * 32) = word;
+    }
+  } else {
+#pragma unroll
+    for (int n2 = 0; n2 < 4; ++n2) {  // channel blocks 2 n2 and 2 n2 + 1, both token blocks
+      uint32_t x0 = __builtin_nondeterministic_value(0u), x1 = __builtin_nondeterministic_value(0u);
+      static_for<4>([&](auto BB) {
+        constexpr int bb = decltype(BB)::value;
+        const int nb = 2 * n2 + (bb >> 1), mb = bb & 1;
+        x0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x0, q4(acc[mb][nb][0], nb), q4(acc[mb][nb][2], nb), 0.5f, bb);
+        x1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x1, q4(acc[mb][nb][1], nb), q4(acc[mb][nb][3], nb), 0.5f, bb);
+      });
+      const uint32_t z = x0 | (x1 << 2);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int nb = 2 * n2 + (bb >> 1), mb = bb & 1;
+        base[(16 * nb + c) * (G / 4) + (ttile0 + 16 * mb) / 4] = (uint8_t)(z >> (8 * bb));
+      }
+    }
+  }
+}
+
 // Writes the codes of this wave's block into the record in LDS: 2-bit codes in the layout
 // of emit_plane2; 3- and 4-bit codes as plane A (bits 0..1, that layout) followed by
 // plane B (4-bit: bits 2..3 in the same layout; 3-bit: bit 2, emit_bit_plane).
@@ -588,8 +671,8 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
     if constexpr (CLAMP) t = __builtin_amdgcn_fmed3f(t, 0.0f, top);
     return (uint32_t)__float_as_int(t + 12582912.0f);  // 1.5 * 2^23
   };
-  if (bits == 2) {
-    emit_plane2<NW>(acc, code, stream, ttile0, c, sh.rec);
+  if (bits == 2) {  // al, ga arrive divided by 4 (emit_codes2)
+    emit_codes2<NW, CLAMP>(acc, al, ga, stream, sub, g, c, sh.rec);
     return;
   }
   uint8_t* pb = sh.rec + G * kD / 4;
@@ -773,8 +856,9 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
     s16_own[q] = round_f16(sc);
     z16_own[q] = round_f16(zc);
     const float is = s16_own[q] > 0.0f ? __builtin_amdgcn_rcpf(s16_own[q]) : 0.0f;
-    al_own[q] = ic_own[q] * is;  // u = (Y - z)/s = Y' (ic/s) - z/s
-    ga_own[q] = -z16_own[q] * is;
+    const float k4 = bits == 2 ? 0.25f : 1.0f;  // the 2-bit emitter takes u / 4
+    al_own[q] = ic_own[q] * is * k4;  // u = (Y - z)/s = Y' (ic/s) - z/s
+    ga_own[q] = -z16_own[q] * is * k4;
   }
   float al[8], ga[8];
   col_gather8(al_own, al, sh.gcol[sub], g, c);
