@@ -225,6 +225,19 @@ KVARN_API kvarn_status kvarn_attn_decode(const kvarn_geom* g, const void* cache,
                                int32_t num_q_heads, float softmax_scale, uint32_t flags,
                                void* workspace, size_t workspace_bytes, float* out, void* stream);
 
+/* kvarn_attn_decode without a caller-supplied workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The span partials go to a workspace the library keeps as a file-scope device
+ * array of 32 MiB on every GPU it runs on, held until the process ends; a geometry whose
+ * kvarn_attn_workspace_bytes exceeds 32 MiB is refused with KVARN_ERR_RANGE before any HIP
+ * call. The call allocates and frees nothing; its first call on a device looks up that
+ * device's array address (the current device must be the stream's). Every call on one GPU
+ * shares the array: two calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it, so the caller must order them. Results equal kvarn_attn_decode's. */
+KVARN_API kvarn_status kvarn_attn_decode_noalloc(const kvarn_geom* g, const void* cache, const void* q_bf16,
+                                       int32_t num_q_heads, float softmax_scale, uint32_t flags, float* out,
+                                       void* stream);
+
 /* One decode step of a layer: append k, v (as kvarn_append_decode) and attend with q
  * over the cache including the new token (as kvarn_attn_decode), in the two launches of
  * the attention: the append runs inside the merge launch. Same arguments and layouts as

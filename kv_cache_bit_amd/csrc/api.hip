@@ -308,6 +308,24 @@ kvarn_status kvarn_append_attn_decode(const kvarn_geom* g, void* cache, const vo
                    v_bf16, stream);
 }
 
+kvarn_status kvarn_attn_decode_noalloc(const kvarn_geom* gin, const void* cache, const void* q_bf16,
+                                       int32_t num_q_heads, float softmax_scale, uint32_t flags, float* out,
+                                       void* stream) {
+  RESOLVE(gin, g);
+  size_t need = 0;
+  kvarn_status st = ws_need(g, num_q_heads, &need);
+  if (st != KVARN_OK) return st;
+  if (need > kAttnScratchBytes) return KVARN_ERR_RANGE;
+  if (!cache || !q_bf16 || !out) return KVARN_ERR_NULL;
+  if (!aligned16(cache) || !aligned16(q_bf16) || !aligned16(out)) return KVARN_ERR_ALIGN;
+  if ((flags & ~(uint32_t)KVARN_Q_PREROTATED) != 0) return KVARN_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVARN_ERR_RANGE;
+  void* ws = nullptr;
+  if (attn_scratch(&ws) != hipSuccess) return KVARN_ERR_DEVICE;
+  return attn_impl(gin, cache, q_bf16, num_q_heads, softmax_scale, flags, ws, kAttnScratchBytes, out, nullptr,
+                   nullptr, nullptr, stream);
+}
+
 kvarn_status kvarn_cache_flags(const void* cache, void* stream, uint32_t* flags_host) {
   if (!cache || !flags_host) return KVARN_ERR_NULL;
   if (!aligned16(cache)) return KVARN_ERR_ALIGN;

@@ -34,6 +34,8 @@
 // quantization, len update) as extra work-groups. Its rows take the call's new token
 // from the input, read only tail slots below the recorded length, and never read len
 // or tile records, so they do not race with the append jobs of the same launch.
+#include <atomic>
+
 #include "kvarn_common.h"
 #include "kvarn_launch.h"
 #include "quantize_dev.h"
@@ -737,6 +739,35 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (fr[e] * (a.idr ? 1.0f : kInvSqrtD * sg[e]) + fo[e]) * inv;
   if (gi == 0) store8f(a.out + (long long)rr * kD + 8 * cg, o);
+}
+
+// ----------------------------------------------------------------------------- static workspace
+// The span partials of kvarn_attn_decode_noalloc live in a file-scope device array instead
+// of a caller's workspace; every GPU the library runs on holds its own copy until the
+// process ends. Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in): the device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t attn_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(p, std::memory_order_release);  // the same value from every caller
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {

@@ -94,4 +94,9 @@ hipError_t launch_set_pages(const SetPagesArgs& a, hipStream_t st);
 hipError_t launch_tokens(const TokensArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
+// Size of the file-scope workspace of kvarn_attn_decode_noalloc, and its device address on
+// the current device (looked up once per device).
+constexpr size_t kAttnScratchBytes = (size_t)32 << 20;
+hipError_t attn_scratch(void** ptr);
+
 }  // namespace kvarn

@@ -23,7 +23,7 @@ KVARN_VARIANT_CENTERED = 8
 EXPORTS = ("kvarn_format_version", "kvarn_cache_bytes", "kvarn_cache_init", "kvarn_quantize_prefill",
            "kvarn_append_decode", "kvarn_dequantize", "kvarn_attn_workspace_bytes", "kvarn_attn_decode",
            "kvarn_cache_flags", "kvarn_status_str", "kvarn_debug_prefill", "kvarn_append_attn_decode",
-           "kvarn_append_tokens", "kvarn_cache_set_pages")
+           "kvarn_append_tokens", "kvarn_cache_set_pages", "kvarn_attn_decode_noalloc")
 
 
 class KvarnError(RuntimeError):
@@ -93,6 +93,7 @@ def _load():
         "kvarn_attn_workspace_bytes": ([G, I32, S], ctypes.c_int),
         "kvarn_attn_decode": ([G, P, P, I32, F32, U32, P, ctypes.c_size_t, P, P], ctypes.c_int),
         "kvarn_append_attn_decode": ([G, P, P, P, P, I32, F32, U32, P, ctypes.c_size_t, P, P], ctypes.c_int),
+        "kvarn_attn_decode_noalloc": ([G, P, P, I32, F32, U32, P, P], ctypes.c_int),
         "kvarn_append_tokens": ([G, P, P, P, I32, P, P], ctypes.c_int),
         "kvarn_cache_set_pages": ([G, P, P, I32, I32, P], ctypes.c_int),
         "kvarn_cache_flags": ([P, P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
@@ -191,6 +192,12 @@ def kvarn_attn_decode(g: kvarn_geom, cache, q, num_q_heads: int, softmax_scale: 
                       workspace_bytes: int, out, stream=None) -> None:
     _check(lib.kvarn_attn_decode(_g(g), _ptr(cache), _ptr(q), num_q_heads, softmax_scale, flags,
                                  _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "kvarn_attn_decode")
+
+
+def kvarn_attn_decode_noalloc(g: kvarn_geom, cache, q, num_q_heads: int, softmax_scale: float, flags: int, out,
+                              stream=None) -> None:
+    _check(lib.kvarn_attn_decode_noalloc(_g(g), _ptr(cache), _ptr(q), num_q_heads, softmax_scale, flags, _ptr(out),
+                                         _stream(stream)), "kvarn_attn_decode_noalloc")
 
 
 def kvarn_append_attn_decode(g: kvarn_geom, cache, k, v, q, num_q_heads: int, softmax_scale: float, flags: int,

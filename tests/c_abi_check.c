@@ -13,7 +13,7 @@ static const entry_fn every_entry_point[] = {
     (entry_fn)kvarn_quantize_prefill, (entry_fn)kvarn_append_decode,      (entry_fn)kvarn_append_tokens,
     (entry_fn)kvarn_cache_set_pages,  (entry_fn)kvarn_dequantize,         (entry_fn)kvarn_attn_workspace_bytes,
     (entry_fn)kvarn_attn_decode,      (entry_fn)kvarn_append_attn_decode, (entry_fn)kvarn_cache_flags,
-    (entry_fn)kvarn_status_str,       (entry_fn)kvarn_debug_prefill,
+    (entry_fn)kvarn_status_str,       (entry_fn)kvarn_debug_prefill,      (entry_fn)kvarn_attn_decode_noalloc,
 };
 
 /* A seven-field geometry followed in memory by values that would select an ablation

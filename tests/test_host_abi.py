@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(K.lib, n), n
     assert sorted(K.EXPORTS) == names
@@ -184,6 +184,14 @@ def test_argument_errors_return_before_any_launch():
     assert _code(K.kvarn_append_attn_decode, g, 0, A2, A2, A2, 4, 0.0, 0, A, ws, A2, 0) == K.KVARN_ERR_NULL
     assert _code(K.kvarn_append_attn_decode, g, A, A2, A2, A2, 4, 0.0, 2, A, ws, A2, 0) == K.KVARN_ERR_UNSUPPORTED
     assert _code(K.kvarn_cache_flags, 0, 0) == K.KVARN_ERR_NULL
+    # the no-allocation attention: its own size limit, then the attention's checks, all on the host
+    big = K.geom(64, 8, 1 << 17, 32, 3)
+    assert K.kvarn_attn_workspace_bytes(big, 64) > 32 << 20
+    assert _code(K.kvarn_attn_decode_noalloc, big, A, A2, 64, 0.0, 0, A2, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_attn_decode_noalloc, g, 0, A2, 4, 0.0, 0, A2, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_attn_decode_noalloc, g, A, MIS, 4, 0.0, 0, A2, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_attn_decode_noalloc, g, A, A2, 3, 0.0, 0, A2, 0) == K.KVARN_ERR_GEOM
+    assert _code(K.kvarn_attn_decode_noalloc, g, A, A2, 4, 0.0, 4, A2, 0) == K.KVARN_ERR_UNSUPPORTED
     bad = K.geom(1, 2, 100, 32, 3)
     assert _code(K.kvarn_quantize_prefill, bad, A, A, A2, 10, 0) == K.KVARN_ERR_GEOM
     assert _code(K.kvarn_cache_init, None if False else K.geom(1, 2, 128, 32, 3, head_dim=96), A, signs, 0) \
