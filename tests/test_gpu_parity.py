@@ -443,3 +443,23 @@ def test_full_size_long_reasoning_quantize_and_decode():
         for g in range(h * grp, (h + 1) * grp):
             m = np.abs(ref[b, g]).max()
             assert np.abs(out[b, g] - ref[b, g]).max() <= 2e-3 * m, (b, g)
+
+
+@pytest.mark.parametrize("B,H,T,G,n_it,law", [(1, 1, 256, 32, 3, "lognormal"), (2, 3, 1000, 32, 3, "lognormal"),
+                                              (3, 8, 4133, 32, 3, "student_t"), (2, 2, 532, 64, 2, "spike"),
+                                              (1, 8, 9000, 64, 2, "lognormal"), (1, 1, 31, 32, 3, "lognormal")])
+def test_prefill_entry_points_agree(B, H, T, G, n_it, law):
+    """kvarn_quantize_prefill (resident work-groups looping over tiles, inputs prefetched into
+    LDS) and the test hook kvarn_debug_prefill (one tile per work-group, the path the parity
+    chain above checks) write bit-identical caches, flags included."""
+    say("prefill entry points", B, H, T, G, law)
+    kw = dict(nu=3.0) if law == "student_t" else {}
+    k, v = outlier_kv(23, B, T, H, law=law, **kw)
+    cap = (T // G + 1) * G
+    a, b = GpuCache(B, H, cap, G, n_it), GpuCache(B, H, cap, G, n_it)
+    gpu_prefill(a, k, v, T)
+    gpu_prefill(b, k, v, T, debug=True)
+    ha, hb = a.host_cache(), b.host_cache()
+    m = ha.defined_mask()
+    assert np.array_equal(ha.buf[m], hb.buf[m])
+    assert K.kvarn_cache_flags(a.buf) == K.kvarn_cache_flags(b.buf)
