@@ -46,6 +46,36 @@ def _compile(sources, lib, verbose):
     os.replace(tmp, lib)
 
 
+SANITIZE = [  # host code only; the GPU code is built as usual
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-shared-libasan", "-g", "-O1",
+]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime a process must preload to load a sanitized build."""
+    import glob
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    hits = sorted(glob.glob(os.path.join(rocm, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return hits[-1]
+
+
+def build_sanitized(out: str, verbose: bool = False) -> str:
+    """libkvarn with AddressSanitizer and UndefinedBehaviorSanitizer on its host code (argument
+    validation, layout and workspace arithmetic), for the CPU tests of the host path."""
+    cmd = [hipcc(), *[f for f in FLAGS if f != "-O3"], *SANITIZE, *[os.path.join(CSRC, s) for s in SOURCES],
+           "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc (sanitized) failed ({res.returncode}):\n{res.stderr}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into kv_cache_bit_amd/libkvarn.so (and the benchmark's
     measurement kernel into libkvarn_bench.so); returns the library's path."""

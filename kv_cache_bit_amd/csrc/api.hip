@@ -87,7 +87,11 @@ extern "C" {
 int kvarn_format_version(void) { return kVersion; }
 
 const char* kvarn_status_str(kvarn_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the argument's bits, not an enum value C++ may assume
+  // to lie in the enumeration's range
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case KVARN_OK: return "ok";
     case KVARN_ERR_NULL: return "null pointer";
     case KVARN_ERR_ALIGN: return "device pointer not 16-byte aligned";

@@ -10,7 +10,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvarn.so")
+# KVARN_LIB selects another build of the same library (the sanitized host build of the tests)
+LIB_PATH = os.environ.get("KVARN_LIB") or os.path.join(HERE, "libkvarn.so")
 
 KVARN_OK, KVARN_ERR_NULL, KVARN_ERR_ALIGN, KVARN_ERR_GEOM = 0, 1, 2, 3
 KVARN_ERR_UNSUPPORTED, KVARN_ERR_RANGE, KVARN_ERR_DEVICE = 4, 5, 6

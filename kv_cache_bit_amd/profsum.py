@@ -36,7 +36,7 @@ def source_digest(files=SOURCES) -> str:
 
 def short_name(name: str) -> str:
     n = name
-    for p in ("void ", "kvarn::"):
+    for p in ("void ", "(anonymous namespace)::", "kvarn::"):
         if n.startswith(p):
             n = n[len(p):]
     return n.split("(")[0].strip()
