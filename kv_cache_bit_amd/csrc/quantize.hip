@@ -57,6 +57,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
   const uint16_t* rows = src + (((long long)b * a.T + t0 + c) * L.Hkv + h) * kD + 8 * g;
   const long long row16 = 16LL * L.Hkv * kD;  // 16 tokens further
   float p[2][8][4];
+  f4v w4[2][8];
   float st;
   h8v av[2][4];
   {
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) av[mb][ks] = canon_a<false>(raw[mb][ks], m[ks]);
   }
-  st = rotate_squares_v<ABL>(idr, av, hf, p, c);
+  st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
   if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion) or NaN: redo checked
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
       for (int mb = 0; mb < 2; ++mb)
         av[mb][ks] = canon_a<true>(*reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks), m, &flags);
     }
-    st = rotate_squares_v<ABL>(idr, av, hf, p, c);
+    st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
   }
 
   float* dw = nullptr;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
     dw = (valid && pw) ? pw + doff : nullptr;
     dy = (valid && py) ? py + doff : nullptr;
   }
-  tile_finish<NW, DBG, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, dw, dy, dstride);
+  tile_finish<NW, DBG, ABL>(av, hf, w4, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, dw, dy, dstride);
   if (valid) {
     const long long ro = record_at(a.cache, L, b, h, tile, s);
     if (ro >= 0)
@@ -184,8 +185,10 @@ __global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
     }
   }
   float p[2][8][4];
-  const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
-  tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr, nullptr, 0);
+  f4v w4[2][8];
+  const float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+  tile_finish<NW, false, ABL>(av, hf, w4, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr, nullptr,
+                              0);
   if (valid) {
     const long long ro = record_at(a.cache, L, b, h, tile, s);
     if (ro >= 0)

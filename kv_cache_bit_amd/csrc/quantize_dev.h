@@ -305,10 +305,18 @@ __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& 
 // 8 g + 7 of the K step). Lane (g, c) of the Gram block holds rows 4 g + i at column c:
 // the diagonal sits in lanes c = 4 g + j at element j, and the owner lane fetches it.
 template <bool ID>
-__device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, float (&p)[2][8][4],
-                                                int c) {
+__device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
+                                                float (&p)[2][8][4], int c) {
+  float d[2];  // this lane's diagonal candidate of each token block (element c % 4)
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
+    // the Gram block first: a token block's inputs are dead once its rotation is done
+    f4v gm = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) gm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], a[mb][ks], gm, 0, 0, 0);
+    asm volatile("" : "+v"(gm) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]));
+    const float lo = (c & 1) ? gm[1] : gm[0], hi = (c & 1) ? gm[3] : gm[2];
+    d[mb] = (c & 2) ? hi : lo;
     if constexpr (ID) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
@@ -316,6 +324,7 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
         asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
                      "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
+        w4[mb][nb] = s;
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[mb][nb][i] = s[i] * s[i];
       }
@@ -326,21 +335,13 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
         h32_steps(a[mb], hf, h, y);
         h4_combine(y, w);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q) {
+          w4[mb][2 * q + h] = w[q];
 #pragma unroll
           for (int i = 0; i < 4; ++i) p[mb][2 * q + h][i] = w[q][i] * w[q][i];
+        }
       }
     }
-  }
-  float d[2];  // this lane's diagonal candidate of each token block (element c % 4)
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    f4v gm = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) gm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], a[mb][ks], gm, 0, 0, 0);
-    asm volatile("" : "+v"(gm) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]));
-    const float lo = (c & 1) ? gm[1] : gm[0], hi = (c & 1) ? gm[3] : gm[2];
-    d[mb] = (c & 2) ? hi : lo;
   }
   const int g = (int)(threadIdx.x & 63) >> 4;
   const int src = 4 * (20 * g + ((c >> 1) & 3));  // byte address of lane 16 g + 4 g + (c/2) % 4
@@ -352,12 +353,12 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
 // Dispatch for the ablation build (ABL): the identity rotation is a runtime choice there;
 // the standard build compiles the Hadamard path only.
 template <bool ABL>
-__device__ __forceinline__ float rotate_squares_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
+__device__ __forceinline__ float rotate_squares_v(bool idr, const h8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
                                                   float (&p)[2][8][4], int c) {
   if constexpr (ABL) {
-    if (idr) return rotate_squares<true>(a, hf, p, c);
+    if (idr) return rotate_squares<true>(a, hf, w4, p, c);
   }
-  return rotate_squares<false>(a, hf, p, c);
+  return rotate_squares<false>(a, hf, w4, p, c);
 }
 template <bool ABL>
 __device__ __forceinline__ void rotate_block_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
@@ -706,7 +707,8 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
 // its scale at 1 (the other pass then repeats the same sums every iteration). The
 // centered reading of "variance" runs its own loop (centered_varn).
 template <int NW, bool DBG, bool ABL>
-__device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2][8][4], float st_own, int lane,
+__device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, f4v (&acc)[2][8], float (&p)[2][8][4],
+                            float st_own, int lane,
                             int sub, int stream, int n_it, int var, int bits_in, TileLds<NW>& sh, uint32_t& flags,
                             float* dbg_w, float* dbg_y, long long dstride) {
   constexpr int G = 32 * NW;
@@ -786,19 +788,6 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, float (&p)[2
     c16_own[q] = round_f16(x);
     ic_own[q] = __builtin_amdgcn_rcpf(c16_own[q]);
   }
-  // W' again, from the kept fp16 inputs: the matrix cores redo the exact rotation so the
-  // 64 fp32 values need not stay in registers through VarN (the asm ties the inputs to
-  // the last VarN sums, so the recomputation is not hoisted back into VarN)
-  h8v av2[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      av2[mb][ks] = av[mb][ks];
-      asm volatile("" : "+v"(av2[mb][ks]) : "v"(s_tok), "v"(s_ch[0]), "v"(s_ch[1]));
-    }
-  f4v acc[2][8];
-  rotate_block_v<ABL>(idr, av2, hf, acc);
   if constexpr (DBG) {
     float ic[8];
     col_gather8(ic_own, ic, sh.gcol[sub], g, c);
@@ -981,8 +970,10 @@ __device__ void append_job(const AppendArgs& a, int job, int sub, int lane, Tile
       }
     }
     float p[2][8][4];
-    const float st = rotate_squares_v<ABL>(idr, av, hf, p, c);
-    tile_finish<NW, false, ABL>(av, hf, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr, nullptr, 0);
+    f4v w4[2][8];
+    const float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+    tile_finish<NW, false, ABL>(av, hf, w4, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr,
+                                nullptr, 0);
     const long long ro = record_at(a.cache, L, b, h, (pos + 1) / G - 1, s);
     if (ro >= 0)
       copy_record<NW>(sh, a.cache + ro, lane, sub, L.tr);
