@@ -61,24 +61,30 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
   float st;
   h8v av[2][4];
   {
+    // the sign masks (header, cached) first: loads complete in issue order
+    SigMask m[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) m[ks] = masks_v<ABL>(idr, hdr, 4 * ks + g);
+    __builtin_amdgcn_sched_barrier(0);
     uint4 raw[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) raw[mb][ks] = *reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks);
-    SigMask m[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) m[ks] = masks_v<ABL>(idr, hdr, 4 * ks + g);
-    // every input load is issued before any of them is used: one memory round trip per
-    // tile (left to itself the scheduler issues the second token block's loads only after
-    // the first block's rotation has started)
+    // every input load is issued before any of them is used (one memory round trip per
+    // tile), and the first token block is converted and rotated while the second one's
+    // loads are still in flight
     __builtin_amdgcn_sched_barrier(0);
+    float d[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) av[mb][ks] = canon_a<false>(raw[mb][ks], m[ks]);
+      for (int ks = 0; ks < 4; ++ks) av[mb][ks] = canon_a<false>(raw[mb][ks], m[ks]);
+      d[mb] = rotate_squares_mb_v<ABL>(idr, av[mb], hf, w4[mb], p[mb], c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st = gram_own_v<ABL>(idr, d[0], d[1], c);
   }
-  st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
   if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion) or NaN: redo checked
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {

@@ -305,49 +305,57 @@ __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& 
 // 8 g + 7 of the K step). Lane (g, c) of the Gram block holds rows 4 g + i at column c:
 // the diagonal sits in lanes c = 4 g + j at element j, and the owner lane fetches it.
 template <bool ID>
-__device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
-                                                float (&p)[2][8][4], int c) {
-  float d[2];  // this lane's diagonal candidate of each token block (element c % 4)
+__device__ __forceinline__ float rotate_squares_mb(const h8v (&a)[4], const Frags& hf, f4v (&w4)[8], float (&p)[8][4],
+                                                   int c) {
+  // the Gram block first: the token block's inputs are dead once its rotation is done
+  f4v gm = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    // the Gram block first: a token block's inputs are dead once its rotation is done
-    f4v gm = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int ks = 0; ks < 4; ++ks) gm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], a[ks], gm, 0, 0, 0);
+  asm volatile("" : "+v"(gm) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+  if constexpr (ID) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) gm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][ks], a[mb][ks], gm, 0, 0, 0);
-    asm volatile("" : "+v"(gm) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]));
-    const float lo = (c & 1) ? gm[1] : gm[0], hi = (c & 1) ? gm[3] : gm[2];
-    d[mb] = (c & 2) ? hi : lo;
-    if constexpr (ID) {
+    for (int nb = 0; nb < 8; ++nb) {
+      f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
+      asm volatile("" : "+v"(s) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(hf.v[0]), "v"(hf.v[1]),
+                   "v"(hf.v[2]), "v"(hf.v[3]));
+      w4[nb] = s;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
-        asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
-                     "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
-        w4[mb][nb] = s;
+      for (int i = 0; i < 4; ++i) p[nb][i] = s[i] * s[i];
+    }
+  } else {  // H_4 (x) H_32, as in rotate_block; each block is squared once combined
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[mb][nb][i] = s[i] * s[i];
-      }
-    } else {  // H_4 (x) H_32, as in rotate_block; each block is squared once combined
+    for (int h = 0; h < 2; ++h) {
+      f4v y[4], w[4];
+      h32_steps(a, hf, h, y);
+      h4_combine(y, w);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f4v y[4], w[4];
-        h32_steps(a[mb], hf, h, y);
-        h4_combine(y, w);
+      for (int q = 0; q < 4; ++q) {
+        w4[2 * q + h] = w[q];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          w4[mb][2 * q + h] = w[q];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[mb][2 * q + h][i] = w[q][i] * w[q][i];
-        }
+        for (int i = 0; i < 4; ++i) p[2 * q + h][i] = w[q][i] * w[q][i];
       }
     }
   }
+  // this lane's diagonal candidate (element c % 4)
+  const float lo = (c & 1) ? gm[1] : gm[0], hi = (c & 1) ? gm[3] : gm[2];
+  return (c & 2) ? hi : lo;
+}
+// The owner lane's diagonal element from the candidates of the two token blocks
+template <bool ID>
+__device__ __forceinline__ float gram_own(float d0, float d1, int c) {
   const int g = (int)(threadIdx.x & 63) >> 4;
   const int src = 4 * (20 * g + ((c >> 1) & 3));  // byte address of lane 16 g + 4 g + (c/2) % 4
-  const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(d[0])));
-  const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(d[1])));
+  const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(d0)));
+  const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(d1)));
   return ((c >> 3) ? x1 : x0) * (ID ? 1.0f : (float)kD);
+}
+template <bool ID>
+__device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
+                                                float (&p)[2][8][4], int c) {
+  const float d0 = rotate_squares_mb<ID>(a[0], hf, w4[0], p[0], c);
+  const float d1 = rotate_squares_mb<ID>(a[1], hf, w4[1], p[1], c);
+  return gram_own<ID>(d0, d1, c);
 }
 
 // Dispatch for the ablation build (ABL): the identity rotation is a runtime choice there;
@@ -359,6 +367,21 @@ __device__ __forceinline__ float rotate_squares_v(bool idr, const h8v (&a)[2][4]
     if (idr) return rotate_squares<true>(a, hf, w4, p, c);
   }
   return rotate_squares<false>(a, hf, w4, p, c);
+}
+template <bool ABL>
+__device__ __forceinline__ float rotate_squares_mb_v(bool idr, const h8v (&a)[4], const Frags& hf, f4v (&w4)[8],
+                                                     float (&p)[8][4], int c) {
+  if constexpr (ABL) {
+    if (idr) return rotate_squares_mb<true>(a, hf, w4, p, c);
+  }
+  return rotate_squares_mb<false>(a, hf, w4, p, c);
+}
+template <bool ABL>
+__device__ __forceinline__ float gram_own_v(bool idr, float d0, float d1, int c) {
+  if constexpr (ABL) {
+    if (idr) return gram_own<true>(d0, d1, c);
+  }
+  return gram_own<false>(d0, d1, c);
 }
 template <bool ABL>
 __device__ __forceinline__ void rotate_block_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
