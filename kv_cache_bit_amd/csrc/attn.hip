@@ -82,18 +82,6 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
 }
 
-// Exact product of two fp16 values taken from the same half (low: HI = 0, high: HI = 1)
-// of two packed registers, one v_fma_mix_f32 (an fp16 x fp16 product fits fp32 exactly).
-template <int HI>
-__device__ __forceinline__ float mul_f16(uint32_t a, uint32_t b) {
-  float r;
-  if constexpr (HI)
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
 // x - m * (fp16 half HI of h), one v_fma_mix_f32: the residual of an fp16 rounding
 // (exact, as x and the rounded value are within a factor of two of each other)
 template <int HI>

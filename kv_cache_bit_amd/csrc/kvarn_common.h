@@ -210,6 +210,18 @@ __device__ __forceinline__ uint32_t f16bits(float x) {  // RNE, x assumed within
 }
 __device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x; }
 
+// Exact product of two fp16 values taken from the same half (low: HI = 0, high: HI = 1)
+// of two packed registers, one v_fma_mix_f32 (an fp16 x fp16 product fits fp32 exactly).
+template <int HI>
+__device__ __forceinline__ float mul_f16(uint32_t a, uint32_t b) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // ----------------------------------------------------------------------------- Hadamard
 __device__ __forceinline__ void fwht8(float (&a)[8]) {
 #pragma unroll
