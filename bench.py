@@ -319,9 +319,10 @@ def bench_roundtrip(K, synth, torch, steps, warmup=2, layers=36, B=8, T=16384, H
         "prefill": {"kernel": f"prefill_kernel<2,false,{'false' if bits == 2 else 'true'},1>",
                     "avg_launch_us": round(pf_avg * 1e3, 2), "bytes_per_launch": bytes_in + bytes_rec,
                     "achieved": round(pf_gbs, 1), "frac": round(pf_gbs / HBM_PEAK_GBS, 4), "unit": "GB/s"},
-        "dequantize": {"kernel": "dequant_kernel (bf16 out)", "avg_launch_us": round(dq_avg * 1e3, 2),
-                       "bytes_per_launch": bytes_rec + bytes_in, "achieved": round(dq_gbs, 1),
-                       "frac": round(dq_gbs / HBM_PEAK_GBS, 4), "unit": "GB/s"},
+        "dequantize": {"kernel": f"dequant_kernel<{'true' if bits == 2 else 'false'}> (bf16 out)",
+                       "avg_launch_us": round(dq_avg * 1e3, 2),
+                       "bytes_per_launch": bytes_rec + bytes_in, "bytes_read": bytes_rec, "bytes_written": bytes_in,
+                       "achieved": round(dq_gbs, 1), "frac": round(dq_gbs / HBM_PEAK_GBS, 4), "unit": "GB/s"},
         "flags": flags,
     }
 
@@ -381,10 +382,10 @@ def copy_ceiling(torch, gib=4):
 
 
 def mix_ceiling(torch, bytes_in, bytes_out, layers=32, steps=10, grids=(1024, 2048, 4096, 8192)):
-    """The practical ceiling of a kernel with the prefill's mix of reads and writes: a plain
-    streaming kernel (libkvarn_bench.so) that reads `bytes_in` and writes `bytes_out` per
-    launch, over `layers` distinct buffer pairs per step like the prefill step; the best grid
-    of a small sweep, timed with events over `steps` steps."""
+    """The practical ceiling of a kernel with a given mix of reads and writes (the prefill's
+    or the dequantizer's): a plain streaming kernel (libkvarn_bench.so) that reads `bytes_in`
+    and writes `bytes_out` per launch, over `layers` distinct buffer pairs per step like the
+    benchmarked step; the best grid of a small sweep, timed with events over `steps` steps."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_cache_bit_amd",
                                    "libkvarn_bench.so"))
@@ -511,6 +512,7 @@ def cpu_baseline_decode(workers, T=16384, H=10, Hq=40, layers=40):
 KERNEL_SOURCES = ["kv_cache_bit_amd/csrc/kvarn_common.h", "kv_cache_bit_amd/csrc/kvarn_launch.h"]
 PREFILL_SOURCES = ["kv_cache_bit_amd/csrc/quantize.hip", "kv_cache_bit_amd/csrc/quantize_dev.h"]
 ATTN_SOURCES = ["kv_cache_bit_amd/csrc/attn.hip", "kv_cache_bit_amd/csrc/quantize_dev.h"]
+DEQUANT_SOURCES = ["kv_cache_bit_amd/csrc/dequant.hip"]
 
 
 def source_digest(files):
@@ -662,6 +664,15 @@ def main():
         log(f"long decode: {res['long_decode']}")
     if not args.no_roundtrip:
         rt = bench_roundtrip(K, synth, torch, max(1, args.steps // 3), bits=args.bits)
+        dq = rt["dequantize"]
+        if args.bits == 2:
+            dq["traffic"] = counted_traffic("dequant_kernel_qwen3_pmc.txt", DEQUANT_SOURCES)
+            dq["source_digest"] = source_digest(DEQUANT_SOURCES + KERNEL_SOURCES)
+        if not args.no_copy:  # the streaming ceiling at the dequantizer's mix (15% read, 85% written)
+            mc = mix_ceiling(torch, dq["bytes_read"], dq["bytes_written"], layers=8,
+                             grids=(1024, 2048, 4096, 8192, 16384))
+            dq["mix_ceiling"] = mc
+            dq["frac_of_mix_ceiling"] = round(dq["achieved"] / mc["GBps"], 4)
         res["roundtrip"] = rt
         log(f"round trip: {rt['ms_per_step']} ms/step; prefill {rt['prefill']['avg_launch_us']} us "
             f"({rt['prefill']['achieved']} GB/s), dequantize {rt['dequantize']['avg_launch_us']} us "

@@ -644,10 +644,11 @@ __device__ __forceinline__ void emit_codes2(const f4v (&acc)[2][8], const float 
     const uint32_t keep = odd ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
     const uint32_t rot = odd ? 4u : 28u;
     uint8_t* row = base + 2 * (c & ~1);
+    // every byte of xa, xb is rewritten in each iteration, so they start undefined and
+    // carry the last iteration's (dead) words: no initializing moves
+    uint32_t xa = __builtin_nondeterministic_value(0u), xb = __builtin_nondeterministic_value(0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // every byte is written below, so the words start undefined (no initializing move)
-      uint32_t xa = __builtin_nondeterministic_value(0u), xb = __builtin_nondeterministic_value(0u);
       static_for<4>([&](auto K) {
         constexpr int k = decltype(K)::value;
         xa = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(xa, q4(acc[0][2 * k][i], 2 * k), q4(acc[1][2 * k][i], 2 * k),
@@ -662,9 +663,9 @@ __device__ __forceinline__ void emit_codes2(const f4v (&acc)[2][8], const float 
       *reinterpret_cast<uint32_t*>(row + (ttile0 + i + (odd ? 16 : 0)) * 32) = word;
     }
   } else {
+    uint32_t x0 = __builtin_nondeterministic_value(0u), x1 = __builtin_nondeterministic_value(0u);
 #pragma unroll
     for (int n2 = 0; n2 < 4; ++n2) {  // channel blocks 2 n2 and 2 n2 + 1, both token blocks
-      uint32_t x0 = __builtin_nondeterministic_value(0u), x1 = __builtin_nondeterministic_value(0u);
       static_for<4>([&](auto BB) {
         constexpr int bb = decltype(BB)::value;
         const int nb = 2 * n2 + (bb >> 1), mb = bb & 1;
