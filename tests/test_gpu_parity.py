@@ -449,9 +449,9 @@ def test_full_size_long_reasoning_quantize_and_decode():
                                               (3, 8, 4133, 32, 3, "student_t"), (2, 2, 532, 64, 2, "spike"),
                                               (1, 8, 9000, 64, 2, "lognormal"), (1, 1, 31, 32, 3, "lognormal")])
 def test_prefill_entry_points_agree(B, H, T, G, n_it, law):
-    """kvarn_quantize_prefill (resident work-groups looping over tiles, inputs prefetched into
-    LDS) and the test hook kvarn_debug_prefill (one tile per work-group, the path the parity
-    chain above checks) write bit-identical caches, flags included."""
+    """kvarn_quantize_prefill and the test hook kvarn_debug_prefill (the same kernel built with
+    the debug outputs that the parity chain above reads) write bit-identical caches, flags
+    included, across group sizes, data laws and ragged tails."""
     say("prefill entry points", B, H, T, G, law)
     kw = dict(nu=3.0) if law == "student_t" else {}
     k, v = outlier_kv(23, B, T, H, law=law, **kw)

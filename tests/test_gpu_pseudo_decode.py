@@ -1,7 +1,11 @@
-"""The synthetic pseudo-decode harness on a small random decoder: while every token is
-still in the fp16 tail the quantized runs match the exact one; once groups are
-quantized the full method's output distribution stays closer to the exact one than
-Hadamard-only's, in both the pseudo-decode and the parallel evaluation.
+"""The synthetic pseudo-decode harness on a small random decoder, through the library's
+kernels. Asserted: every statistic is finite; while every token is still in the fp16 tail
+(steps 0..30) the quantized runs match the exact one (KL below 1e-6, attention output
+within 1e-4, the same top-1 token); at step 31, where the first group is quantized, the
+attention output moves by more than 1e-3. The mean KL of the full method and of
+Hadamard-only after step 64 is printed, not asserted: on this small random decoder the
+full method is not reliably the closer one. The pairwise test asserts how VarN changes the
+error of an outlier token (its docstring).
 """
 import numpy as np
 import pytest
