@@ -47,6 +47,16 @@ def record_bytes(g: int, bits: int = 2) -> int:
     return g * 128 * bits // 8 + 2 * g + 6 * 128
 
 
+def settle(torch, step, seconds=0.25):
+    """Untimed steps until the GPU has been busy for `seconds`, before the warm-up steps:
+    clocks rise over the first tens of milliseconds under load (a one-layer launch measured
+    45.7 us after 3 warm-up steps, 43.4 us after 30 and 43.0 us after 200 on one box)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
+
+
 def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32, n_it=3, bits=2, B=1,
                   distinct=True, graph=True, law=None, tag="prefill"):
     """`steps` steps of `layers` prefill launches, issued eagerly with nothing between them.
@@ -71,6 +81,7 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
             i = l if distinct else 0
             K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T, stream)
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -290,6 +301,7 @@ def bench_roundtrip(K, synth, torch, steps, warmup=2, layers=36, B=8, T=16384, H
             if ev is not None:
                 ev[l][2].record(stream)
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -547,8 +559,8 @@ def counted_traffic(profile, sources):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1024,
                     help="decode steps of the Phi-4-shaped run (16384 -> 17408 tokens), every step timed")
     ap.add_argument("--long-steps", type=int, default=4096,
@@ -669,8 +681,10 @@ def main():
             dq["traffic"] = counted_traffic("dequant_kernel_qwen3_pmc.txt", DEQUANT_SOURCES)
             dq["source_digest"] = source_digest(DEQUANT_SOURCES + KERNEL_SOURCES)
         if not args.no_copy:  # the streaming ceiling at the dequantizer's mix (15% read, 85% written)
+            # (grids other than the prefill mix's, so a counter summary keyed by kernel and
+            # grid keeps the two mixes apart)
             mc = mix_ceiling(torch, dq["bytes_read"], dq["bytes_written"], layers=8,
-                             grids=(1024, 2048, 4096, 8192, 16384))
+                             grids=(1536, 3072, 6144, 12288))
             dq["mix_ceiling"] = mc
             dq["frac_of_mix_ceiling"] = round(dq["achieved"] / mc["GBps"], 4)
         res["roundtrip"] = rt
