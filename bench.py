@@ -4,8 +4,10 @@
 Headline (`value`): prefill quantization throughput in GB/s of bf16 input on the
 Llama-3.1-8B-shaped KV workload -- 32 layers x 8 KV heads x head_dim 128, 32768
 tokens, batch 1, group 32, 3 VarN iterations, 2 bits -- one step = the 32 layer
-caches quantized from 32 distinct input buffers resident in HBM, issued eagerly (the
-same step replayed as one HIP graph is reported beside it). Beside it:
+caches quantized from 32 distinct input buffers resident in HBM by one
+kvarn_quantize_prefill_layers call (one launch), issued eagerly (the same step replayed
+as one HIP graph is reported beside it, and so is the step as 32 kvarn_quantize_prefill
+calls, `per_layer_calls`). Beside it:
   * roofline of the quantize kernel: algorithmic bytes per launch (bf16 in + tile
     records out) over the launch time, measured with HIP events on the launch stream
     around the whole timed step loop and divided by the number of launches, against the
@@ -58,10 +60,12 @@ def settle(torch, step, seconds=0.25):
 
 
 def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32, n_it=3, bits=2, B=1,
-                  distinct=True, graph=True, law=None, tag="prefill"):
-    """`steps` steps of `layers` prefill launches, issued eagerly with nothing between them.
-    The timed region is bracketed by HIP events on the launch stream (so the per-launch
-    average is the kernel time of the step, gaps included) and by the wall clock."""
+                  distinct=True, graph=True, law=None, tag="prefill", batched=False):
+    """`steps` steps of the `layers`-layer prefill, issued eagerly with nothing between them:
+    one kvarn_quantize_prefill_layers call per step (batched; one launch per 64 layers), or
+    one kvarn_quantize_prefill call per layer. The timed region is bracketed by HIP events
+    on the launch stream (so the per-launch average is the kernel time of the step, gaps
+    included) and by the wall clock."""
     g = K.geom(B, H, T, G, n_it, bits=bits)
     sig = synth.sign_vector(0)
     law = law or {}
@@ -76,11 +80,18 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step():
+    if batched:
+        assert distinct, "the multi-layer call needs distinct caches"
+
+    def step(st=stream):
+        if batched:
+            K.kvarn_quantize_prefill_layers(g, caches, ks, vs, T, st)
+            return
         for l in range(layers):
             i = l if distinct else 0
-            K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T, stream)
+            K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T, st)
 
+    launches_per_step = (layers + 63) // 64 if batched else layers
     settle(torch, step)
     for _ in range(warmup):
         step()
@@ -94,22 +105,27 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_ms = e0.elapsed_time(e1)
-    # diagnostic only: every launch bracketed by its own event pair (adds a dispatch per launch)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
-    for l in range(layers):
-        i = l if distinct else 0
-        ev[l][0].record(stream)
-        K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T, stream)
-        ev[l][1].record(stream)
+    # diagnostic only: every call bracketed by its own event pair (adds a dispatch per call)
+    if batched:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+        for a0, a1 in ev:
+            a0.record(stream)
+            step()
+            a1.record(stream)
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+        for l in range(layers):
+            i = l if distinct else 0
+            ev[l][0].record(stream)
+            K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T, stream)
+            ev[l][1].record(stream)
     torch.cuda.synchronize()
     isolated_ms = sorted(a.elapsed_time(b) for a, b in ev)
     graph_wall = None
-    if graph:  # the same step as one HIP graph of its layer launches, replayed
+    if graph:  # the same step as one HIP graph of its launches, replayed
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
-            for l in range(layers):
-                i = l if distinct else 0
-                K.kvarn_quantize_prefill(g, caches[i], ks[i], vs[i], T)
+            step(None)
         torch.cuda.synchronize()
         gr.replay()
         torch.cuda.synchronize()
@@ -124,7 +140,8 @@ def bench_prefill(K, synth, torch, steps, warmup, layers=32, T=32768, H=8, G=32,
     flags = K.kvarn_cache_flags(caches[0])
     del ks, vs, caches
     torch.cuda.empty_cache()
-    return dict(wall=wall, graph_wall=graph_wall, region_ms=region_ms, launches=steps * layers,
+    return dict(wall=wall, graph_wall=graph_wall, region_ms=region_ms, launches=steps * launches_per_step,
+                layers_per_launch=layers // launches_per_step,
                 isolated_ms=isolated_ms, bytes_in=bytes_in, bytes_out=bytes_out, layers=layers, T=T, H=H, G=G,
                 n_it=n_it, B=B, flags=flags)
 
@@ -595,18 +612,31 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     log("device", torch.cuda.get_device_name(0))
-    pf = bench_prefill(K, synth, torch, args.steps, args.warmup, bits=args.bits)
-    ms_step = pf["wall"] * 1e3 / args.steps
-    value = pf["layers"] * pf["bytes_in"] / (ms_step * 1e-3) / 1e9
-    total_gbs = pf["layers"] * (pf["bytes_in"] + pf["bytes_out"]) / (ms_step * 1e-3) / 1e9
-    bpl = pf["bytes_in"] + pf["bytes_out"]
-    launch_us = pf["region_ms"] * 1e3 / pf["launches"]   # events over the timed region, per launch
-    achieved = bpl / (launch_us * 1e-6) / 1e9
-    iso = pf["isolated_ms"]
-    graph_ms = pf["graph_wall"] * 1e3 / args.steps
-    log(f"prefill: {ms_step:.3f} ms/step ({graph_ms:.3f} as a graph), {value:.1f} GB/s bf16-in, "
-        f"{total_gbs:.1f} GB/s total; {launch_us:.2f} us per launch -> {achieved:.1f} GB/s")
-    kname = "prefill_kernel<1, false, false, 1>" if args.bits == 2 else "prefill_kernel<1, false, true, 1>"
+    # the headline: the 32-layer prefill as one kvarn_quantize_prefill_layers call per step
+    # (one launch); beside it the same step as 32 kvarn_quantize_prefill calls
+    pf = bench_prefill(K, synth, torch, args.steps, args.warmup, bits=args.bits, batched=True)
+    pl = bench_prefill(K, synth, torch, args.steps, args.warmup, bits=args.bits, graph=True, tag="prefill per layer")
+
+    def prefill_figures(r):
+        ms = r["wall"] * 1e3 / args.steps
+        bpl = r["layers_per_launch"] * (r["bytes_in"] + r["bytes_out"])
+        us = r["region_ms"] * 1e3 / r["launches"]  # events over the timed region, per launch
+        iso = r["isolated_ms"]
+        return dict(ms_step=ms, value=r["layers"] * r["bytes_in"] / (ms * 1e-3) / 1e9,
+                    total_gbs=r["layers"] * (r["bytes_in"] + r["bytes_out"]) / (ms * 1e-3) / 1e9,
+                    bpl=bpl, launch_us=us, achieved=bpl / (us * 1e-6) / 1e9,
+                    graph_ms=r["graph_wall"] * 1e3 / args.steps, iso_us=iso[len(iso) // 2] * 1e3)
+
+    f, fl = prefill_figures(pf), prefill_figures(pl)
+    ms_step, value, achieved, launch_us = f["ms_step"], f["value"], f["achieved"], f["launch_us"]
+    log(f"prefill (one call): {ms_step:.3f} ms/step ({f['graph_ms']:.3f} as a graph), {value:.1f} GB/s bf16-in; "
+        f"{launch_us:.2f} us per launch of {pf['layers_per_launch']} layers -> {achieved:.1f} GB/s")
+    log(f"prefill (a call per layer): {fl['ms_step']:.3f} ms/step, {fl['value']:.1f} GB/s bf16-in; "
+        f"{fl['launch_us']:.2f} us per launch -> {fl['achieved']:.1f} GB/s")
+    abl = "true" if args.bits != 2 else "false"
+    kname = f"prefill_layers_kernel<1, {abl}, 1>"
+    per_layer_bytes = pf["bytes_in"] + pf["bytes_out"]
+    traffic_layer = counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES) if args.bits == 2 else None
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -614,19 +644,28 @@ def main():
         "config": {"workload": "llama3.1-8b-shaped KV prefill quantize", "layers": pf["layers"], "batch": 1,
                    "tokens": pf["T"], "kv_heads": pf["H"], "head_dim": 128, "group": pf["G"],
                    "varn_iters": pf["n_it"], "bits": args.bits,
-                   "input": "bf16, outlier channels x20, 5% lognormal tokens"},
-        "hbm_frac_step": round(total_gbs / HBM_PEAK_GBS, 4),
-        "step_as_graph": {"ms_per_step": round(graph_ms, 4),
-                          "value": round(pf["layers"] * pf["bytes_in"] / (graph_ms * 1e-3) / 1e9, 2)},
+                   "input": "bf16, outlier channels x20, 5% lognormal tokens",
+                   "call": "kvarn_quantize_prefill_layers: the 32 layers' caches in one call (one launch)"},
+        "hbm_frac_step": round(f["total_gbs"] / HBM_PEAK_GBS, 4),
+        "step_as_graph": {"ms_per_step": round(f["graph_ms"], 4),
+                          "value": round(pf["layers"] * pf["bytes_in"] / (f["graph_ms"] * 1e-3) / 1e9, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES)
-                                 if args.bits == 2 else None),
-                     "traffic_unit": "bytes/launch", "kernel": kname, "bytes_per_launch": bpl,
+                     "traffic": (round(traffic_layer * pf["layers_per_launch"]) if traffic_layer else None),
+                     "traffic_unit": "bytes/launch (the one-layer kernel's counted traffic x layers per launch)",
+                     "kernel": kname, "layers_per_launch": pf["layers_per_launch"], "bytes_per_launch": f["bpl"],
                      "avg_launch_us": round(launch_us, 2), "launches_timed": pf["launches"],
                      "timing": "HIP events on the launch stream around the timed step loop, / launches",
-                     "isolated_launch_us_median": round(iso[len(iso) // 2] * 1e3, 2),
+                     "isolated_launch_us_median": round(f["iso_us"], 2),
                      "source_digest": source_digest(PREFILL_SOURCES + KERNEL_SOURCES)},
+        "per_layer_calls": {
+            "call": "kvarn_quantize_prefill once per layer (32 launches per step)",
+            "value": round(fl["value"], 2), "unit": "GB/s bf16-in", "ms_per_step": round(fl["ms_step"], 4),
+            "step_as_graph_ms": round(fl["graph_ms"], 4),
+            "roofline": {"kernel": "prefill_kernel<1, %s, %s, 1>" % ("false", abl), "bytes_per_launch": per_layer_bytes,
+                         "avg_launch_us": round(fl["launch_us"], 2), "achieved": round(fl["achieved"], 1),
+                         "frac": round(fl["achieved"] / HBM_PEAK_GBS, 4), "traffic": traffic_layer,
+                         "isolated_launch_us_median": round(fl["iso_us"], 2)}},
         "flags": pf["flags"],
     }
     if not args.no_copy:
@@ -635,6 +674,7 @@ def main():
         mc = mix_ceiling(torch, pf["bytes_in"], pf["bytes_out"])
         res["mix_ceiling"] = mc
         res["roofline"]["frac_of_mix_ceiling"] = round(achieved / mc["GBps"], 4)
+        res["per_layer_calls"]["roofline"]["frac_of_mix_ceiling"] = round(fl["achieved"] / mc["GBps"], 4)
         log(f"streaming ceiling at the prefill's read/write mix: {mc}")
     if not args.no_long:
         lp = bench_prefill(K, synth, torch, 1, 1, layers=32, B=64, distinct=False, graph=False, bits=args.bits,

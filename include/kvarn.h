@@ -168,6 +168,20 @@ KVARN_API kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const 
 KVARN_API kvarn_status kvarn_quantize_prefill(const kvarn_geom* g, void* cache, const void* k_bf16,
                                     const void* v_bf16, int32_t num_tokens, void* stream);
 
+/* kvarn_quantize_prefill for n_layers caches of one geometry and token count at once,
+ * e.g. every layer of a model after its prefill forward pass: caches[i], k_bf16[i] and
+ * v_bf16[i] are layer i's cache and inputs, with the layouts and the result of
+ * kvarn_quantize_prefill(g, caches[i], k_bf16[i], v_bf16[i], num_tokens, stream) for each
+ * i (bit-identical, flags included); each cache keeps its own sigma. The three pointer
+ * arrays are host memory, read during the call; the caches must be distinct (two entries
+ * naming one cache: KVARN_ERR_GEOM). 1 <= n_layers <= KVARN_MAX_PREFILL_LAYERS. The layers
+ * run in one launch per 64, so the launch's ramp and tail are paid once for all of them.
+ * (ai-paper-analysis page, sections 3.1-3.2.) */
+#define KVARN_MAX_PREFILL_LAYERS 1024
+KVARN_API kvarn_status kvarn_quantize_prefill_layers(const kvarn_geom* g, int32_t n_layers, void* const* caches,
+                                           const void* const* k_bf16, const void* const* v_bf16,
+                                           int32_t num_tokens, void* stream);
+
 /* Append one token to every (batch, kv head): k_bf16, v_bf16 device bf16 [B][Hkv][D].
  * The token enters the fp16 tail; when the group of G fills it is quantized into
  * the next tile record (ai-paper-analysis page, section 3.2: the current group's

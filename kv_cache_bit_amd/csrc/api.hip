@@ -2,6 +2,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "kvarn_common.h"
 #include "kvarn_launch.h"
 
@@ -56,6 +58,26 @@ kvarn_status check_prefill(const Geo* g, void* cache, const void* k, const void*
   return KVARN_OK;
 }
 
+// Work-groups of one layer's prefill launch (tile work-groups + tail work-groups), and the
+// waves per work-group; a launch's work-items (all layers) must stay below 2^32.
+long long prefill_blocks(const Geo* g, int32_t T) {
+  const long long nw = g->group / 32;
+  return (long long)g->batch * g->num_kv_heads * (T / g->group) * 2 + (2LL * g->batch * g->num_kv_heads + nw - 1) / nw;
+}
+constexpr long long kMaxWorkItems = (1LL << 32) - 1;
+
+// The fields of a prefill launch shared by every layer of one geometry and token count
+PrefillArgs prefill_args(const Geo* g, int32_t T) {
+  PrefillArgs a{};
+  a.L = make_layout(*g);
+  a.T = T;
+  a.nfull = T / g->group;
+  a.jobs = g->batch * g->num_kv_heads * a.nfull * 2;
+  a.dhkv = make_fastdiv((uint32_t)g->num_kv_heads);
+  a.dnfull = make_fastdiv((uint32_t)a.nfull);
+  return a;
+}
+
 kvarn_status prefill_impl(const kvarn_geom* gin, void* cache, const void* k, const void* v, int32_t T,
                           float* wk, float* wv, float* yk, float* yv, void* stream) {
   RESOLVE(gin, g);
@@ -63,16 +85,11 @@ kvarn_status prefill_impl(const kvarn_geom* gin, void* cache, const void* k, con
   if (st != KVARN_OK) return st;
   for (const float* p : {wk, wv, yk, yv})
     if (p && !aligned16(p)) return KVARN_ERR_ALIGN;
-  PrefillArgs a{};
-  a.L = make_layout(*g);
+  if (prefill_blocks(g, T) * 64 * (g->group / 32) > kMaxWorkItems) return KVARN_ERR_RANGE;
+  PrefillArgs a = prefill_args(g, T);
   a.cache = static_cast<uint8_t*>(cache);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
-  a.T = T;
-  a.nfull = T / g->group;
-  a.jobs = g->batch * g->num_kv_heads * a.nfull * 2;
-  a.dhkv = make_fastdiv((uint32_t)g->num_kv_heads);
-  a.dnfull = make_fastdiv((uint32_t)a.nfull);
   a.wk = wk;
   a.wv = wv;
   a.yk = yk;
@@ -142,6 +159,43 @@ kvarn_status kvarn_cache_init(const kvarn_geom* gin, void* cache, const int8_t* 
 kvarn_status kvarn_quantize_prefill(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
                                     int32_t num_tokens, void* stream) {
   return prefill_impl(g, cache, k_bf16, v_bf16, num_tokens, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+kvarn_status kvarn_quantize_prefill_layers(const kvarn_geom* gin, int32_t n_layers, void* const* caches,
+                                           const void* const* k_bf16, const void* const* v_bf16,
+                                           int32_t num_tokens, void* stream) {
+  RESOLVE(gin, g);
+  if (!caches || !k_bf16 || !v_bf16) return KVARN_ERR_NULL;
+  if (n_layers < 1 || n_layers > KVARN_MAX_PREFILL_LAYERS) return KVARN_ERR_RANGE;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const kvarn_status st = check_prefill(g, caches[i], k_bf16[i], v_bf16[i], num_tokens);
+    if (st != KVARN_OK) return st;
+  }
+  {  // distinct caches: two entries writing one cache would race
+    uintptr_t sorted[KVARN_MAX_PREFILL_LAYERS];
+    for (int32_t i = 0; i < n_layers; ++i) sorted[i] = (uintptr_t)caches[i];
+    std::sort(sorted, sorted + n_layers);
+    for (int32_t i = 1; i < n_layers; ++i)
+      if (sorted[i] == sorted[i - 1]) return KVARN_ERR_GEOM;
+  }
+  // layers per launch: at most kMaxLayersPerLaunch, and fewer work-items than 2^32
+  const long long per_layer = prefill_blocks(g, num_tokens) * 64 * (g->group / 32);
+  const long long fit = kMaxWorkItems / per_layer;
+  if (fit < 1) return KVARN_ERR_RANGE;
+  const int32_t step = fit < kMaxLayersPerLaunch ? (int32_t)fit : kMaxLayersPerLaunch;
+  const PrefillArgs a = prefill_args(g, num_tokens);
+  for (int32_t l0 = 0; l0 < n_layers; l0 += step) {
+    const int n = n_layers - l0 < step ? n_layers - l0 : step;
+    PrefillLayers ly{};
+    for (int i = 0; i < n; ++i) {
+      ly.cache[i] = static_cast<uint8_t*>(caches[l0 + i]);
+      ly.k[i] = static_cast<const uint16_t*>(k_bf16[l0 + i]);
+      ly.v[i] = static_cast<const uint16_t*>(v_bf16[l0 + i]);
+    }
+    const kvarn_status st = dev(launch_prefill_layers(a, ly, n, static_cast<hipStream_t>(stream)));
+    if (st != KVARN_OK) return st;
+  }
+  return KVARN_OK;
 }
 
 kvarn_status kvarn_debug_prefill(const kvarn_geom* g, void* cache, const void* k_bf16, const void* v_bf16,
@@ -220,6 +274,7 @@ kvarn_status kvarn_dequantize(const kvarn_geom* gin, const void* cache, void* k_
   a.nblk = (max_tokens + 31) / 32;
   const long long jobs = (long long)g->batch * g->num_kv_heads * 2 * a.nblk;
   if (jobs >= (1LL << 31)) return KVARN_ERR_RANGE;  // defensive: check_geom's bound keeps it below 2^29
+  if (((jobs + 3) / 4) * 256 > kMaxWorkItems) return KVARN_ERR_RANGE;  // work-items of the launch
   a.jobs = (int)jobs;
   a.dhkv = make_fastdiv((uint32_t)g->num_kv_heads);
   a.dnblk = make_fastdiv((uint32_t)a.nblk);

@@ -49,6 +49,17 @@ struct PrefillArgs {
   float *wk, *wv, *yk, *yv;  // optional fp32 intermediates [B][nfull*G][Hkv][D]
 };
 
+// Per-layer pointers of a multi-layer prefill launch (kernel argument, at most
+// kMaxLayersPerLaunch layers; the host splits longer lists over several launches).
+constexpr int kMaxLayersPerLaunch = 64;
+struct PrefillLayers {
+  uint8_t* cache[kMaxLayersPerLaunch];
+  const uint16_t* k[kMaxLayersPerLaunch];
+  const uint16_t* v[kMaxLayersPerLaunch];
+  uint32_t blocks;  // work-groups per layer
+  FastDiv dblocks;  // division by blocks
+};
+
 struct AppendArgs {
   Layout L;
   uint8_t* cache;
@@ -88,6 +99,7 @@ struct AttnArgs {
 
 hipError_t launch_init(const InitArgs& a, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_layers(const PrefillArgs& a, PrefillLayers& ly, int n_layers, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);
 hipError_t launch_set_pages(const SetPagesArgs& a, hipStream_t st);

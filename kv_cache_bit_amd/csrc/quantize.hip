@@ -8,38 +8,40 @@ namespace kvarn {
 // Work-groups [0, tile_blocks) quantize full tiles, TPW tiles (NW waves each) per
 // work-group; the remaining work-groups write the fp16 tail and len[], one (b, h, s)
 // per wave.
+// Work-group `blk` of one layer's prefill, whose cache and inputs are `cache`, `kin`, `vin`
+// (the other fields of `a` are shared by every layer of a multi-layer launch).
 template <int NW, bool DBG, bool ABL, int TPW>
-__global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_block(const PrefillArgs& a, uint8_t* cache, const uint16_t* kin,
+                                              const uint16_t* vin, uint32_t blk, TileLds<NW> (&sh_all)[TPW]) {
   constexpr int WPG = NW * TPW;  // waves per work-group
-  __shared__ TileLds<NW> sh_all[TPW];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: job math on the SALU
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
   const Layout& L = a.L;
-  uint8_t* hdr = a.cache;
+  uint8_t* hdr = cache;
   uint32_t flags = 0;
   const uint32_t tile_blocks = ((uint32_t)a.jobs + TPW - 1) / TPW;
 
-  if (blockIdx.x >= tile_blocks) {
-    const uint32_t sj = (blockIdx.x - tile_blocks) * WPG + wave;  // (b, h, s)
+  if (blk >= tile_blocks) {
+    const uint32_t sj = (blk - tile_blocks) * WPG + wave;  // (b, h, s)
     if (sj >= 2u * L.B * L.Hkv) return;
     const uint32_t q = fdiv(sj >> 1, a.dhkv);
     const int s = (int)(sj & 1u), h = (int)((sj >> 1) - q * (uint32_t)L.Hkv), b = (int)q;
-    const uint16_t* src = s ? a.v : a.k;
+    const uint16_t* src = s ? vin : kin;
     for (int t = a.nfull * L.G + g; t < a.T; t += 4) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + (((long long)b * a.T + t) * L.Hkv + h) * kD + 8 * c);
       float x[8];
       canon8_bf16(w, x, flags);
-      *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = pack8_f16(x);
+      *reinterpret_cast<uint4*>(cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = pack8_f16(x);
     }
-    if (lane == 0) *reinterpret_cast<int32_t*>(a.cache + L.len_off(b, h, s)) = a.T;
+    if (lane == 0) *reinterpret_cast<int32_t*>(cache + L.len_off(b, h, s)) = a.T;
     raise_flags(hdr, flags);
     return;
   }
 
   const int tw = wave / NW, sub = wave % NW;
   TileLds<NW>& sh = sh_all[tw];
-  uint32_t job = blockIdx.x * TPW + tw;
+  uint32_t job = blk * TPW + tw;
   const bool valid = job < (uint32_t)a.jobs;
   if (!valid) job = 0;  // keep the barrier sequence uniform; results are discarded
   // job = ((b * nfull + tile) * 2 + s) * Hkv + h : neighbouring waves read neighbouring heads
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
   const int s = (int)(q1 & 1u);
   const int tile = (int)(q2 - q3 * (uint32_t)a.nfull);
   const int b = (int)q3;
-  const uint16_t* src = s ? a.v : a.k;
+  const uint16_t* src = s ? vin : kin;
   const int t0 = tile * L.G + sub * 32;  // first token of this wave's block
   const bool idr = ABL && (L.variant & KVARN_VARIANT_NO_ROTATION);
   const Frags hf = frags_v<ABL>(idr, lane);
@@ -110,13 +112,29 @@ __global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
   }
   tile_finish<NW, DBG, ABL>(av, hf, w4, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, dw, dy, dstride);
   if (valid) {
-    const long long ro = record_at(a.cache, L, b, h, tile, s);
+    const long long ro = record_at(cache, L, b, h, tile, s);
     if (ro >= 0)
-      copy_record<NW>(sh, a.cache + ro, lane, sub, L.tr);
+      copy_record<NW>(sh, cache + ro, lane, sub, L.tr);
     else
       flags |= KVARN_FLAG_UNMAPPED;
     raise_flags(hdr, flags);
   }
+}
+
+template <int NW, bool DBG, bool ABL, int TPW>
+__global__ __launch_bounds__(64 * NW * TPW) void prefill_kernel(PrefillArgs a) {
+  __shared__ TileLds<NW> sh_all[TPW];
+  prefill_block<NW, DBG, ABL, TPW>(a, a.cache, a.k, a.v, blockIdx.x, sh_all);
+}
+
+// Several layers of one geometry in one launch: work-groups [l * blocks, (l + 1) * blocks)
+// run layer l's prefill. One launch pays the ramp (every wave of the first round waiting
+// for its input) and the tail (the last partial round) once for all the layers.
+template <int NW, bool ABL, int TPW>
+__global__ __launch_bounds__(64 * NW * TPW) void prefill_layers_kernel(PrefillArgs a, PrefillLayers ly) {
+  __shared__ TileLds<NW> sh_all[TPW];
+  const uint32_t l = fdiv(blockIdx.x, ly.dblocks);
+  prefill_block<NW, false, ABL, TPW>(a, ly.cache[l], ly.k[l], ly.v[l], blockIdx.x - l * ly.blocks, sh_all);
 }
 
 // ----------------------------------------------------------------------------- append
@@ -247,6 +265,26 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     case 5: hipLaunchKernelGGL((prefill_kernel<2, false, true, TPW>), grid, block, 0, st, a); break;
     case 6: hipLaunchKernelGGL((prefill_kernel<2, true, false, TPW>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((prefill_kernel<2, true, true, TPW>), grid, block, 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+// ly.cache/k/v hold n_layers entries; blocks and dblocks are filled in here.
+hipError_t launch_prefill_layers(const PrefillArgs& a, PrefillLayers& ly, int n_layers, hipStream_t st) {
+  constexpr int TPW = 1;
+  const int nw = a.L.G / 32;
+  const long long tile_blocks = (a.jobs + TPW - 1) / TPW;
+  const long long tail_blocks = (2LL * a.L.B * a.L.Hkv + nw * TPW - 1) / (nw * TPW);
+  ly.blocks = (uint32_t)(tile_blocks + tail_blocks);
+  ly.dblocks = make_fastdiv(ly.blocks);
+  const dim3 grid((unsigned)((long long)n_layers * ly.blocks)), block((unsigned)(64 * nw * TPW));
+  const bool abl = a.L.variant != 0 || a.L.bits != 2;  // the extended build
+  const int which = (a.L.G == 32 ? 0 : 2) + (abl ? 1 : 0);
+  switch (which) {
+    case 0: hipLaunchKernelGGL((prefill_layers_kernel<1, false, TPW>), grid, block, 0, st, a, ly); break;
+    case 1: hipLaunchKernelGGL((prefill_layers_kernel<1, true, TPW>), grid, block, 0, st, a, ly); break;
+    case 2: hipLaunchKernelGGL((prefill_layers_kernel<2, false, TPW>), grid, block, 0, st, a, ly); break;
+    default: hipLaunchKernelGGL((prefill_layers_kernel<2, true, TPW>), grid, block, 0, st, a, ly); break;
   }
   return hipGetLastError();
 }

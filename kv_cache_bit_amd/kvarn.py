@@ -24,7 +24,9 @@ KVARN_VARIANT_CENTERED = 8
 EXPORTS = ("kvarn_format_version", "kvarn_cache_bytes", "kvarn_cache_init", "kvarn_quantize_prefill",
            "kvarn_append_decode", "kvarn_dequantize", "kvarn_attn_workspace_bytes", "kvarn_attn_decode",
            "kvarn_cache_flags", "kvarn_status_str", "kvarn_debug_prefill", "kvarn_append_attn_decode",
-           "kvarn_append_tokens", "kvarn_cache_set_pages", "kvarn_attn_decode_noalloc")
+           "kvarn_append_tokens", "kvarn_cache_set_pages", "kvarn_attn_decode_noalloc",
+           "kvarn_quantize_prefill_layers")
+KVARN_MAX_PREFILL_LAYERS = 1024
 
 
 class KvarnError(RuntimeError):
@@ -89,6 +91,7 @@ def _load():
         "kvarn_cache_bytes": ([G, S], ctypes.c_int),
         "kvarn_cache_init": ([G, P, P, P], ctypes.c_int),
         "kvarn_quantize_prefill": ([G, P, P, P, I32, P], ctypes.c_int),
+        "kvarn_quantize_prefill_layers": ([G, I32, P, P, P, I32, P], ctypes.c_int),
         "kvarn_append_decode": ([G, P, P, P, P], ctypes.c_int),
         "kvarn_dequantize": ([G, P, P, P, I32, I32, P], ctypes.c_int),
         "kvarn_attn_workspace_bytes": ([G, I32, S], ctypes.c_int),
@@ -163,6 +166,25 @@ def kvarn_cache_init(g: kvarn_geom, cache, signs, stream=None) -> None:
 def kvarn_quantize_prefill(g: kvarn_geom, cache, k, v, num_tokens: int, stream=None) -> None:
     _check(lib.kvarn_quantize_prefill(_g(g), _ptr(cache), _ptr(k), _ptr(v), num_tokens, _stream(stream)),
            "kvarn_quantize_prefill")
+
+
+def _ptr_array(items):
+    """A host array of device pointers (void* const*), or None for None."""
+    if items is None:
+        return None
+    return (ctypes.c_void_p * max(1, len(items)))(*[_ptr(t) for t in items])
+
+
+def kvarn_quantize_prefill_layers(g: kvarn_geom, caches, ks, vs, num_tokens: int, stream=None,
+                                  n_layers: int | None = None) -> None:
+    """caches, ks, vs: sequences of device tensors (or addresses), one per layer; n_layers
+    defaults to len(caches)."""
+    if n_layers is None:
+        n_layers = len(caches) if caches is not None else len(ks or vs or ())
+    n = n_layers
+    ca, ka, va = _ptr_array(caches), _ptr_array(ks), _ptr_array(vs)
+    _check(lib.kvarn_quantize_prefill_layers(_g(g), n, ca, ka, va, num_tokens, _stream(stream)),
+           "kvarn_quantize_prefill_layers")
 
 
 def kvarn_debug_prefill(g: kvarn_geom, cache, k, v, num_tokens: int, w_k=None, w_v=None, y_k=None, y_v=None,

@@ -14,6 +14,7 @@ static const entry_fn every_entry_point[] = {
     (entry_fn)kvarn_cache_set_pages,  (entry_fn)kvarn_dequantize,         (entry_fn)kvarn_attn_workspace_bytes,
     (entry_fn)kvarn_attn_decode,      (entry_fn)kvarn_append_attn_decode, (entry_fn)kvarn_cache_flags,
     (entry_fn)kvarn_status_str,       (entry_fn)kvarn_debug_prefill,      (entry_fn)kvarn_attn_decode_noalloc,
+    (entry_fn)kvarn_quantize_prefill_layers,
 };
 
 /* A seven-field geometry followed in memory by values that would select an ablation
@@ -53,6 +54,18 @@ int main(void) {
     printf("gqa_not_multiple_status %d\n", (int)kvarn_attn_workspace_bytes(&g, 15, &ws));
     /* a device call with a NULL cache is refused on the host, before any HIP call */
     printf("prefill_null_cache_status %d\n", (int)kvarn_quantize_prefill(&g, NULL, NULL, NULL, 0, NULL));
+    {
+        /* the multi-layer entry: host arrays of device pointers; two entries naming one cache */
+        void* caches[2];
+        const void* ins[2];
+        caches[0] = (void*)(size_t)0x10000;
+        caches[1] = (void*)(size_t)0x10000;
+        ins[0] = (const void*)(size_t)0x20000;
+        ins[1] = (const void*)(size_t)0x20000;
+        printf("layers_null_status %d\n", (int)kvarn_quantize_prefill_layers(&g, 2, NULL, ins, ins, 0, NULL));
+        printf("layers_duplicate_status %d\n", (int)kvarn_quantize_prefill_layers(&g, 2, caches, ins, ins, 0, NULL));
+        printf("layers_count_status %d\n", (int)kvarn_quantize_prefill_layers(&g, 0, caches, ins, ins, 0, NULL));
+    }
     printf("sizeof_geom %d\nsizeof_geom_ext %d\n", (int)sizeof(kvarn_geom), (int)sizeof(kvarn_geom_ext));
     bx.g = g;
     bx.after[0] = 40; bx.after[1] = 8; bx.after[2] = 100; bx.after[3] = -1;

@@ -66,5 +66,8 @@ def test_c_caller_gets_host_side_errors(c_results):
     assert int(c_results["null_out_status"]) == K.KVARN_ERR_NULL
     assert int(c_results["gqa_not_multiple_status"]) == K.KVARN_ERR_GEOM
     assert int(c_results["prefill_null_cache_status"]) == K.KVARN_ERR_NULL
+    assert int(c_results["layers_null_status"]) == K.KVARN_ERR_NULL
+    assert int(c_results["layers_duplicate_status"]) == K.KVARN_ERR_GEOM
+    assert int(c_results["layers_count_status"]) == K.KVARN_ERR_RANGE
     assert c_results["status_str_ok"] == K.status_str(K.KVARN_OK)
     assert c_results["status_str_geom"] == K.status_str(K.KVARN_ERR_GEOM)

@@ -463,3 +463,61 @@ def test_prefill_entry_points_agree(B, H, T, G, n_it, law):
     m = ha.defined_mask()
     assert np.array_equal(ha.buf[m], hb.buf[m])
     assert K.kvarn_cache_flags(a.buf) == K.kvarn_cache_flags(b.buf)
+
+
+@pytest.mark.parametrize("n,B,H,T,G,n_it,variant,law", [
+    (3, 1, 2, 250, 32, 3, 0, "lognormal"),
+    (2, 2, 3, 532, 64, 2, 0, "spike"),
+    (70, 1, 1, 100, 32, 3, 0, "lognormal"),      # two launches (at most 64 layers each)
+    (2, 1, 2, 96, 32, 2, K.KVARN_VARIANT_NO_TOKEN_PASS, "lognormal"),  # the extended build
+    (3, 2, 2, 150, 32, 3, 0, "student_t"),        # paged caches, each with its own page map
+])
+def test_prefill_layers_equals_per_layer_calls(n, B, H, T, G, n_it, variant, law):
+    """kvarn_quantize_prefill_layers over n caches of one geometry (each with its own sigma and
+    inputs) writes the same bytes and flags as n calls of kvarn_quantize_prefill; the first
+    layer also goes through the parity chain against the oracle."""
+    say("prefill layers", n, B, H, T, G, variant, law)
+    cap = (T // G + 1) * G
+    paged = law == "student_t"
+    kw = dict(nu=3.0) if law == "student_t" else {}
+    ins = [outlier_kv(40 + i, B, T, H, law=law, **kw) for i in range(n)]
+    if paged:
+        tiles = cap // G
+        geo = K.geom(B, H, cap, G, n_it, num_pages=B * tiles + 3)
+        rng = np.random.default_rng(7)
+
+        def make(i):
+            c = GpuCache(B, H, cap, G, n_it, seed_sigma=i)
+            c.g = geo
+            c.og = R.Geom(B, H, 128, cap, G, n_it, 2, 0, B * tiles + 3)
+            c.buf = K.alloc_cache(geo, c.sigma)
+            pages = rng.permutation(B * tiles + 3)[:B * tiles].reshape(B, tiles).astype(np.int32)
+            p = torch.from_numpy(pages).cuda()
+            K.kvarn_cache_set_pages(geo, c.buf, p, 0, tiles)
+            return c, pages
+        pairs = [make(i) for i in range(n)]
+        a = [p[0] for p in pairs]
+        bl = []
+        for i in range(n):  # the same page maps in the second set
+            c = GpuCache(B, H, cap, G, n_it, seed_sigma=i)
+            c.g, c.og = geo, a[i].og
+            c.buf = K.alloc_cache(geo, c.sigma)
+            K.kvarn_cache_set_pages(geo, c.buf, torch.from_numpy(pairs[i][1]).cuda(), 0, tiles)
+            bl.append(c)
+        b = bl
+    else:
+        a = [GpuCache(B, H, cap, G, n_it, seed_sigma=i, variant=variant) for i in range(n)]
+        b = [GpuCache(B, H, cap, G, n_it, seed_sigma=i, variant=variant) for i in range(n)]
+    for i in range(n):
+        gpu_prefill(a[i], ins[i][0], ins[i][1], T)
+    kd = [from_u16(k[:, :T]) for k, _ in ins]
+    vd = [from_u16(v[:, :T]) for _, v in ins]
+    K.kvarn_quantize_prefill_layers(b[0].g, [c.buf for c in b], kd, vd, T)
+    torch.cuda.synchronize()
+    for i in range(n):
+        ha, hb = a[i].host_cache(), b[i].host_cache()
+        m = ha.defined_mask()
+        assert np.array_equal(ha.buf[m], hb.buf[m]), i
+        assert K.kvarn_cache_flags(a[i].buf) == K.kvarn_cache_flags(b[i].buf), i
+    if variant == 0:
+        check_prefill(b[0], ins[0][0], ins[0][1], T)

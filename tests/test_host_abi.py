@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(K.lib, n), n
     assert sorted(K.EXPORTS) == names
@@ -194,6 +194,22 @@ def test_argument_errors_return_before_any_launch():
     assert _code(K.kvarn_attn_decode_noalloc, g, A, A2, 4, 0.0, 4, A2, 0) == K.KVARN_ERR_UNSUPPORTED
     bad = K.geom(1, 2, 100, 32, 3)
     assert _code(K.kvarn_quantize_prefill, bad, A, A, A2, 10, 0) == K.KVARN_ERR_GEOM
+    # a launch of 2^32 or more work-items is refused (B * Hkv * T/G * 2 = 2^27 tiles)
+    wide = K.geom(1024, 8, 1 << 18, 32, 3)
+    assert _code(K.kvarn_quantize_prefill, wide, A, A, A2, 1 << 18, 0) == K.KVARN_ERR_RANGE
+    # several layers in one call: the per-layer checks, the pointer arrays, distinct caches
+    L3 = [A, A + 1024, A + 2048]
+    assert _code(K.kvarn_quantize_prefill_layers, g, L3, [A2] * 3, [A2] * 3, 10, 0, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_quantize_prefill_layers, g, L3, [A2] * 3, [A2] * 3, 10, 0, 1025) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_quantize_prefill_layers, g, None, [A2] * 3, [A2] * 3, 10, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_quantize_prefill_layers, g, L3, None, [A2] * 3, 10, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_quantize_prefill_layers, g, [A, 0, A + 64], [A2] * 3, [A2] * 3, 10, 0) == K.KVARN_ERR_NULL
+    assert _code(K.kvarn_quantize_prefill_layers, g, L3, [A2, MIS, A2], [A2] * 3, 10, 0) == K.KVARN_ERR_ALIGN
+    assert _code(K.kvarn_quantize_prefill_layers, g, L3, [A2] * 3, [A2] * 3, 129, 0) == K.KVARN_ERR_RANGE
+    assert _code(K.kvarn_quantize_prefill_layers, g, [A, A + 1024, A], [A2] * 3, [A2] * 3, 10, 0) \
+        == K.KVARN_ERR_GEOM
+    assert _code(K.kvarn_quantize_prefill_layers, bad, L3, [A2] * 3, [A2] * 3, 10, 0) == K.KVARN_ERR_GEOM
+    assert _code(K.kvarn_quantize_prefill_layers, wide, L3, [A2] * 3, [A2] * 3, 1 << 18, 0) == K.KVARN_ERR_RANGE
     assert _code(K.kvarn_cache_init, None if False else K.geom(1, 2, 128, 32, 3, head_dim=96), A, signs, 0) \
         == K.KVARN_ERR_UNSUPPORTED
 
