@@ -5,9 +5,9 @@ Headline (`value`): prefill quantization throughput in GB/s of bf16 input on the
 Llama-3.1-8B-shaped KV workload -- 32 layers x 8 KV heads x head_dim 128, 32768
 tokens, batch 1, group 32, 3 VarN iterations, 2 bits -- one step = the 32 layer
 caches quantized from 32 distinct input buffers resident in HBM by one
-kvarn_quantize_prefill_layers call (one launch), issued eagerly (the same step replayed
-as one HIP graph is reported beside it, and so is the step as 32 kvarn_quantize_prefill
-calls, `per_layer_calls`). Beside it:
+kvarn_quantize_prefill_layers call (one launch), issued eagerly. The step as 32
+kvarn_quantize_prefill calls is reported beside it (`per_layer_calls`, also replayed as one
+HIP graph). Beside it:
   * roofline of the quantize kernel: algorithmic bytes per launch (bf16 in + tile
     records out) over the launch time, measured with HIP events on the launch stream
     around the whole timed step loop and divided by the number of launches, against the
@@ -614,7 +614,9 @@ def main():
     log("device", torch.cuda.get_device_name(0))
     # the headline: the 32-layer prefill as one kvarn_quantize_prefill_layers call per step
     # (one launch); beside it the same step as 32 kvarn_quantize_prefill calls
-    pf = bench_prefill(K, synth, torch, args.steps, args.warmup, bits=args.bits, batched=True)
+    # (no graph replay of the one-launch step: a graph of one launch adds nothing, and its
+    # replays would mix into the kernel's trace average)
+    pf = bench_prefill(K, synth, torch, args.steps, args.warmup, bits=args.bits, batched=True, graph=False)
     pl = bench_prefill(K, synth, torch, args.steps, args.warmup, bits=args.bits, graph=True, tag="prefill per layer")
 
     def prefill_figures(r):
@@ -625,11 +627,12 @@ def main():
         return dict(ms_step=ms, value=r["layers"] * r["bytes_in"] / (ms * 1e-3) / 1e9,
                     total_gbs=r["layers"] * (r["bytes_in"] + r["bytes_out"]) / (ms * 1e-3) / 1e9,
                     bpl=bpl, launch_us=us, achieved=bpl / (us * 1e-6) / 1e9,
-                    graph_ms=r["graph_wall"] * 1e3 / args.steps, iso_us=iso[len(iso) // 2] * 1e3)
+                    graph_ms=(r["graph_wall"] * 1e3 / args.steps if r["graph_wall"] else None),
+                    iso_us=iso[len(iso) // 2] * 1e3)
 
     f, fl = prefill_figures(pf), prefill_figures(pl)
     ms_step, value, achieved, launch_us = f["ms_step"], f["value"], f["achieved"], f["launch_us"]
-    log(f"prefill (one call): {ms_step:.3f} ms/step ({f['graph_ms']:.3f} as a graph), {value:.1f} GB/s bf16-in; "
+    log(f"prefill (one call): {ms_step:.3f} ms/step, {value:.1f} GB/s bf16-in; "
         f"{launch_us:.2f} us per launch of {pf['layers_per_launch']} layers -> {achieved:.1f} GB/s")
     log(f"prefill (a call per layer): {fl['ms_step']:.3f} ms/step, {fl['value']:.1f} GB/s bf16-in; "
         f"{fl['launch_us']:.2f} us per launch -> {fl['achieved']:.1f} GB/s")
@@ -637,6 +640,9 @@ def main():
     kname = f"prefill_layers_kernel<1, {abl}, 1>"
     per_layer_bytes = pf["bytes_in"] + pf["bytes_out"]
     traffic_layer = counted_traffic("prefill_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES) if args.bits == 2 else None
+    # the multi-layer launch's own counters hold for a launch of 32 layers
+    traffic_launch = (counted_traffic("prefill_layers_kernel_llama8b_32k_pmc.txt", PREFILL_SOURCES)
+                      if args.bits == 2 and pf["layers_per_launch"] == 32 else None)
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -647,12 +653,11 @@ def main():
                    "input": "bf16, outlier channels x20, 5% lognormal tokens",
                    "call": "kvarn_quantize_prefill_layers: the 32 layers' caches in one call (one launch)"},
         "hbm_frac_step": round(f["total_gbs"] / HBM_PEAK_GBS, 4),
-        "step_as_graph": {"ms_per_step": round(f["graph_ms"], 4),
-                          "value": round(pf["layers"] * pf["bytes_in"] / (f["graph_ms"] * 1e-3) / 1e9, 2)},
+
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (round(traffic_layer * pf["layers_per_launch"]) if traffic_layer else None),
-                     "traffic_unit": "bytes/launch (the one-layer kernel's counted traffic x layers per launch)",
+                     "traffic": traffic_launch, "traffic_unit": "bytes/launch",
+                     "traffic_over_bytes": (round(traffic_launch / f["bpl"], 4) if traffic_launch else None),
                      "kernel": kname, "layers_per_launch": pf["layers_per_launch"], "bytes_per_launch": f["bpl"],
                      "avg_launch_us": round(launch_us, 2), "launches_timed": pf["launches"],
                      "timing": "HIP events on the launch stream around the timed step loop, / launches",
@@ -661,7 +666,8 @@ def main():
         "per_layer_calls": {
             "call": "kvarn_quantize_prefill once per layer (32 launches per step)",
             "value": round(fl["value"], 2), "unit": "GB/s bf16-in", "ms_per_step": round(fl["ms_step"], 4),
-            "step_as_graph_ms": round(fl["graph_ms"], 4),
+            "step_as_graph": {"ms_per_step": round(fl["graph_ms"], 4),
+                              "value": round(pl["layers"] * pl["bytes_in"] / (fl["graph_ms"] * 1e-3) / 1e9, 2)},
             "roofline": {"kernel": "prefill_kernel<1, %s, %s, 1>" % ("false", abl), "bytes_per_launch": per_layer_bytes,
                          "avg_launch_us": round(fl["launch_us"], 2), "achieved": round(fl["achieved"], 1),
                          "frac": round(fl["achieved"] / HBM_PEAK_GBS, 4), "traffic": traffic_layer,
