@@ -282,25 +282,25 @@ kvarn_status kvarn_dequantize(const kvarn_geom* gin, const void* cache, void* k_
 }
 
 // Work split of attn_decode: a work-group of 4 waves per (batch, kv head, group of up to
-// 4 query heads, span of 4 * tpw tiles). tpw is chosen for about 2048 work-groups over
-// the cache capacity, between 2 and 16 tiles per wave. Depends only on the geometry, so
-// the workspace size is static.
-static void attn_split(const Geo* g, int grp, int* tpw, int* nspan) {
-  const int tiles = g->capacity / g->group;
+// 4 query heads, span), the full tiles of a sequence cut into nspan equal spans. nspan is
+// chosen for about KVARN_ATTN_WG_TARGET work-groups, with at most 16 and at least 2 tiles
+// per wave at the capacity. Depends only on the geometry, so the workspace size is static.
+#ifndef KVARN_ATTN_WG_TARGET
+#define KVARN_ATTN_WG_TARGET 2048
+#endif
+static int attn_split(const Geo* g, int grp) {
+  const long long tiles = g->capacity / g->group;
   const long long units = (long long)g->batch * g->num_kv_heads * ((grp + 3) / 4);
-  const long long want = (2048 + units - 1) / units;  // spans wanted per sequence
-  long long t = (tiles + 4 * want - 1) / (4 * want);
-  if (t < 2) t = 2;
-  if (t > 16) t = 16;
-  *tpw = (int)t;
-  *nspan = (int)((tiles + 4 * t - 1) / (4 * t));
+  long long ns = (KVARN_ATTN_WG_TARGET + units - 1) / units;
+  ns = std::max(ns, (tiles + 63) / 64);
+  ns = std::min(ns, std::max(1LL, tiles / 8));
+  return (int)ns;
 }
 
 // Workspace: the span partials [B][Hq][nspan][4 + D] f32, then len [B][Hkv] i32 as the
 // tile pass saw it.
 static size_t attn_partial_bytes(const Geo* g, int32_t num_q_heads) {
-  int tpw, nspan;
-  attn_split(g, num_q_heads / g->num_kv_heads, &tpw, &nspan);
+  const int nspan = attn_split(g, num_q_heads / g->num_kv_heads);
   return (size_t)g->batch * num_q_heads * nspan * (4 + kD) * sizeof(float);
 }
 
@@ -341,7 +341,7 @@ static kvarn_status attn_impl(const kvarn_geom* gin, const void* cache, const vo
   a.Hq = num_q_heads;
   a.grp = num_q_heads / g->num_kv_heads;
   a.nqg = (a.grp + 3) / 4;
-  attn_split(g, a.grp, &a.tpw, &a.nspan);
+  a.nspan = attn_split(g, a.grp);
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)kD);
   a.flags = flags;
   a.idr = (g->variant & KVARN_VARIANT_NO_ROTATION) != 0;

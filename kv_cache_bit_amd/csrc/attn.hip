@@ -23,7 +23,9 @@
 // consecutive tokens of a channel per 16-bit load.
 //
 // Work split: a work-group of 4 waves per (batch, kv head, group of up to 4 query heads,
-// span of 4 x tpw tiles); wave w takes tiles w, w + 4, ... of the span with its own
+// span); the full tiles of a sequence are cut into min(nspan, tiles) spans of equal size,
+// so every work-group of a call has the same work. Wave w takes tiles w, w + 4, ... of its
+// span with its own
 // online softmax, the 4 wave states are merged in LDS and one partial (m, l, o_rot) per
 // query head and span goes to the workspace. The merge kernel combines the spans in
 // index order (log-sum-exp), adds the fp16 tail tokens (unrotated, scored in original
@@ -187,10 +189,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int h = bid % L.Hkv, b = bid / L.Hkv;
   const int n = *reinterpret_cast<const int32_t*>(a.cache + L.len_off(b, h, 0));
   if (span == 0 && qg == 0 && threadIdx.x == 0) a.lens_ws[b * L.Hkv + h] = n;  // for the merge
-  const int nfull = n / G;
-  const int t0 = span * 4 * a.tpw;
-  if (t0 >= nfull) return;  // uniform over the work-group
-  const int t1 = min(t0 + 4 * a.tpw, nfull);
+  // the full tiles split into nsp spans of equal size (within one tile) whatever the length
+  const int nfull = n / G, nsp = min(a.nspan, nfull);
+  if (span >= nsp) return;  // uniform over the work-group
+  const int t0 = (int)((long long)span * nfull / nsp), t1 = (int)((long long)(span + 1) * nfull / nsp);
   const int q0 = qg * 4;
   const float qscale = kLog2e * a.scale;
 
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int nfull = n / G, nt_old = n - nfull * G;
   // the call's own token (fused, unless the sequence is full) follows the tail
   const int nt = nt_old + ((FUSED && n < a.L.cap) ? 1 : 0);
-  const int nsp = (nfull + 4 * a.tpw - 1) / (4 * a.tpw);
+  const int nsp = min(a.nspan, nfull);  // the tile pass's non-empty spans
   const float* w = a.ws + (long long)rr * a.nspan * kPart;
 
   // tail tokens gi + 16k (k < kt), loaded up front; slots past the tail read the last

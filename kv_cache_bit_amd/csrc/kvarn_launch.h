@@ -85,7 +85,7 @@ struct AttnArgs {
   float* out;         // [B][Hq][D]
   int Hq, grp;        // query heads; query heads per kv head
   int nqg;            // groups of up to 4 query heads per kv head
-  int nspan, tpw;     // spans of 4 * tpw tiles per sequence; tiles per wave
+  int nspan;         // spans per sequence: min(nspan, full tiles) equal spans of the length
   float scale;
   uint32_t flags;
   int idr;            // identity in place of H_D (KVARN_VARIANT_NO_ROTATION)

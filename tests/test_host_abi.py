@@ -62,8 +62,9 @@ def test_variants_accepted():
 def test_workspace_bytes():
     g = K.geom(32, 10, 17408, 32, 3)
     n = K.kvarn_attn_workspace_bytes(g, 40)
-    # one partial (m, l, 2 pad, o[128]) per (b, q head, span); at this geometry a span is
-    # 4 waves x 16 tiles, so 544 tiles give 9 spans; then len per (b, kv head), 16-B padded
+    # one partial (m, l, 2 pad, o[128]) per (b, q head, span); at this geometry a span holds
+    # at most 4 waves x 16 tiles of the capacity, so 544 tiles give 9 spans; then len per
+    # (b, kv head), 16-B padded
     assert n == 32 * 40 * 9 * (4 + 128) * 4 + 32 * 10 * 4
     with pytest.raises(K.KvarnError) as e:
         K.kvarn_attn_workspace_bytes(g, 41)
