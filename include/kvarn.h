@@ -17,8 +17,8 @@
  *
  * Conventions fixed by this library where the pages are silent:
  *   H_D = diag(sigma) H_syl / sqrt(D), H_syl[i][j] = (-1)^popcount(i & j), sigma in {+1,-1}^D;
- *   inputs are canonicalized bf16 -> fp16 (round-half-to-even, saturating at +-65504;
- *   a NaN input becomes 0 and raises KVARN_FLAG_NAN);
+ *   inputs are taken as given (bf16) and kept so in the tail; a value beyond +-2^16
+ *   saturates at +-2^16 (KVARN_FLAG_SATURATED), a NaN becomes +0 (KVARN_FLAG_NAN);
  *   "variance" is the mean square; a tile is G consecutive tokens x D channels of
  *   one (batch, kv head, stream); r (per token) and c (per channel) are stored as
  *   fp16 clamped to [2^-14, 65504]; the 2-bit grid is per channel over the tile's
@@ -26,9 +26,9 @@
  *   codes round half to even and clamp to [0, 3] (3- and 4-bit codes: 2^bits levels,
  *   s = (max - min)/(2^bits - 1), clamp to [0, 2^bits - 1]).
  *
- * Cache buffer, format v2 (one caller-owned buffer per layer, 256-B aligned regions):
+ * Cache buffer, format v3 (one caller-owned buffer per layer, 256-B aligned regions):
  *   header  align256(512 + 8*B*Hkv) bytes:
- *           u32 magic 0x4E52564B, u32 version 2, i32 geom[7] (batch, num_kv_heads,
+ *           u32 magic 0x4E52564B, u32 version 3, i32 geom[7] (batch, num_kv_heads,
  *           head_dim, capacity, group, varn_iters, bits), u32 flags (sticky) at byte 36,
  *           u32 variant at byte 40, i32 num_pages at byte 44, i8 sigma[D] at byte 64,
  *           u32 sign words[D/2] at byte 192 (word d: bit 15 set iff sigma[2d] = -1,
@@ -43,7 +43,7 @@
  *           4*B*capacity/G). A tile whose map entry is not a valid page is dropped by
  *           writers (KVARN_FLAG_UNMAPPED) and skipped by readers (attention leaves its
  *           tokens out, dequantization writes zeros).
- *   tail    [B][Hkv][2][G][D] fp16, unrotated tokens of the group being filled,
+ *   tail    [B][Hkv][2][G][D] bf16, unrotated tokens of the group being filled,
  *           slot = token index mod G.
  *   Tile record TR = G*D*bits/8 + 2G + 6D bytes (2 bits: 1856 at G=32, 2944 at G=64):
  *     codes  G*D*bits/8 B. 2-bit codes: four per byte, slot k of a byte at bits 2k..2k+1:
@@ -64,7 +64,8 @@
  *   A tile token dequantizes as x_hat = (r_t c_j (z_j + s_j q_tj))_j H_D^T.
  *   Format history: v1 stored K and V codes alike (channel order, four per byte) and had
  *   no sign words, variant, num_pages or page map; v2 is the layout above (K channel-pair
- *   slots, V tokens fastest, sign words at 192, variant at 40, num_pages at 44, page map).
+ *   slots, V tokens fastest, sign words at 192, variant at 40, num_pages at 44, page map)
+ *   with the tail in fp16 (inputs rounded to fp16); v3 keeps the tail in bf16.
  *
  * Errors: every argument check runs on the host before any HIP call; on error
  * nothing is enqueued and the cache is untouched. A failed launch returns
@@ -142,12 +143,12 @@ enum { KVARN_VARIANT_NO_ROTATION = 1u,      /* H_D = I: "VarN only"             
 enum { KVARN_OUT_F32 = 0, KVARN_OUT_BF16 = 1 };            /* dequantize output dtype     */
 enum { KVARN_Q_PREROTATED = 1u };                          /* attention: q is already q H_D */
 enum { KVARN_FLAG_CAPACITY = 1u,      /* an append found a full sequence; token dropped      */
-       KVARN_FLAG_SATURATED = 2u,     /* an input had |x| > 65504 and was saturated          */
+       KVARN_FLAG_SATURATED = 2u,     /* an input had |x| > 2^16 and was saturated           */
        KVARN_FLAG_SCALE_CLAMPED = 4u, /* r or c hit [2^-14, 65504], or s/z saturated        */
        KVARN_FLAG_UNMAPPED = 8u,      /* a paged cache had no page for a tile being written  */
        KVARN_FLAG_NAN = 16u           /* an input was NaN; it was stored as 0                */ };
 
-/* Format version of the cache buffer (2). */
+/* Format version of the cache buffer (3). */
 KVARN_API int kvarn_format_version(void);
 
 /* Size in bytes of a cache buffer for geometry *g. Host only. */
@@ -164,7 +165,7 @@ KVARN_API kvarn_status kvarn_cache_init(const kvarn_geom* g, void* cache, const 
  * k_bf16, v_bf16: device bf16 [B][num_tokens][Hkv][D], contiguous.
  * Full groups of G tokens are rotated, VarN-normalized and quantized into tile
  * records (ai-paper-analysis page, sections 3.1-3.2); the last num_tokens mod G
- * tokens go to the fp16 tail. Sets len = num_tokens. 0 <= num_tokens <= capacity. */
+ * tokens go to the bf16 tail. Sets len = num_tokens. 0 <= num_tokens <= capacity. */
 KVARN_API kvarn_status kvarn_quantize_prefill(const kvarn_geom* g, void* cache, const void* k_bf16,
                                     const void* v_bf16, int32_t num_tokens, void* stream);
 
@@ -183,7 +184,7 @@ KVARN_API kvarn_status kvarn_quantize_prefill_layers(const kvarn_geom* g, int32_
                                            int32_t num_tokens, void* stream);
 
 /* Append one token to every (batch, kv head): k_bf16, v_bf16 device bf16 [B][Hkv][D].
- * The token enters the fp16 tail; when the group of G fills it is quantized into
+ * The token enters the bf16 tail; when the group of G fills it is quantized into
  * the next tile record (ai-paper-analysis page, section 3.2: the current group's
  * statistics are computed as tokens are written). A full sequence drops the token
  * and sets KVARN_FLAG_CAPACITY. */
@@ -257,7 +258,7 @@ KVARN_API kvarn_status kvarn_attn_decode_noalloc(const kvarn_geom* g, const void
  * the attention: the append runs inside the merge launch. Same arguments and layouts as
  * those two calls. The result equals kvarn_append_decode followed by kvarn_attn_decode,
  * except on a step whose token completes a group of G: the attention then reads that
- * group as the fp16 values it is quantized from (the tile is written for later steps).
+ * group as the bf16 values it is quantized from (the tile is written for later steps).
  * A full sequence drops the token (KVARN_FLAG_CAPACITY) and attends without it.
  * (ai-paper-analysis page, section 3.2: the group being filled is kept until complete;
  * section 3.1: the query is rotated like the keys.) */

@@ -28,7 +28,7 @@
 // span with its own
 // online softmax, the 4 wave states are merged in LDS and one partial (m, l, o_rot) per
 // query head and span goes to the workspace. The merge kernel combines the spans in
-// index order (log-sum-exp), adds the fp16 tail tokens (unrotated, scored in original
+// index order (log-sum-exp), adds the bf16 tail tokens (unrotated, scored in original
 // space), rotates the V part back by H_D^T and normalizes. Scores live in log2 units.
 //
 // Fused decode step (append + attention): the tile pass records each sequence's length
@@ -615,14 +615,11 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     for (int k = 0; k < KT; ++k) {
       if (k >= kt) break;
       const int t = min(gi + 16 * k, nt - 1);
-      if (FUSED && t == nt_old) {  // the new token, canonicalized as the append stores it
+      if (FUSED && t == nt_old) {  // the new token, canonical as the append stores it
         const long long src = ((long long)b * a.L.Hkv + h) * kD + 8 * cg;
-        float xk[8], xv[8];
         uint32_t seen = 0;  // the append job of this launch raises the token's flags
-        canon8_bf16(*reinterpret_cast<const uint4*>(a.kn + src), xk, seen);
-        canon8_bf16(*reinterpret_cast<const uint4*>(a.vn + src), xv, seen);
-        kw[k] = pack8_f16(xk);
-        vw[k] = pack8_f16(xv);
+        kw[k] = canon8(*reinterpret_cast<const uint4*>(a.kn + src), seen);
+        vw[k] = canon8(*reinterpret_cast<const uint4*>(a.vn + src), seen);
       } else {
         kw[k] = *reinterpret_cast<const uint4*>(tk + t * 2 * kD + 16 * cg);
         vw[k] = *reinterpret_cast<const uint4*>(tv + t * 2 * kD + 16 * cg);
@@ -666,7 +663,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       const uint32_t kk[4] = {kw[k].x, kw[k].y, kw[k].z, kw[k].w};
       float d = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d = fmaf(qv[2 * e], f16lo(kk[e]), fmaf(qv[2 * e + 1], f16hi(kk[e]), d));
+      for (int e = 0; e < 4; ++e) d = fmaf(qv[2 * e], bf16lo(kk[e]), fmaf(qv[2 * e + 1], bf16hi(kk[e]), d));
       d = row16_sum(d);
       lt[k] = gi + 16 * k < nt ? d * qs : -INFINITY;
     }
@@ -688,8 +685,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       const uint32_t vv[4] = {vw[k].x, vw[k].y, vw[k].z, vw[k].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        oorig[2 * e] = fmaf(pw, f16lo(vv[e]), oorig[2 * e]);
-        oorig[2 * e + 1] = fmaf(pw, f16hi(vv[e]), oorig[2 * e + 1]);
+        oorig[2 * e] = fmaf(pw, bf16lo(vv[e]), oorig[2 * e]);
+        oorig[2 * e + 1] = fmaf(pw, bf16hi(vv[e]), oorig[2 * e + 1]);
       }
     }
     m = mn;

@@ -23,6 +23,14 @@ __device__ __forceinline__ void widen8_f16(const uint4 w, float (&x)[8]) {
     x[2 * k + 1] = f16hi(ws[k]);
   }
 }
+__device__ __forceinline__ void widen8_bf16(const uint4 w, float (&x)[8]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = bf16lo(ws[k]);
+    x[2 * k + 1] = bf16hi(ws[k]);
+  }
+}
 
 // ----------------------------------------------------------------------------- 2-bit helpers
 constexpr uint32_t kNib2 = 0x33333333u;  // bits 0..1 of every nibble
@@ -456,7 +464,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       const int t = t0 + i;
       float y[8];
       if (t < n) {
-        widen8_f16(*reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * cg), y);
+        widen8_bf16(*reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * cg), y);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = 0.0f;

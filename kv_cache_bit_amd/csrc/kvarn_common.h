@@ -11,7 +11,7 @@ namespace kvarn {
 
 constexpr int kD = 128;                     // the one head_dim the kernels support
 constexpr uint32_t kMagic = 0x4E52564Bu;    // 'K' 'V' 'R' 'N'
-constexpr int kVersion = 2;
+constexpr int kVersion = 3;
 constexpr int kHdrFixed = 512;              // len[] offset
 constexpr int kSigmaOff = 64;
 constexpr int kSignOff = 192;               // sign words [64]: bit 15 / bit 31 of word d set
@@ -20,6 +20,7 @@ constexpr int kFlagsOff = 36;
 constexpr int kVariantOff = 40;
 constexpr int kNumPagesOff = 44;
 constexpr float kFp16Max = 65504.0f;
+constexpr float kInMax = 65536.0f;                      // inputs saturate at +-2^16
 constexpr float kScaleMin = 6.103515625e-05f;          // 2^-14
 constexpr float kInvSqrtD = 0.08838834764831845f;      // 1/sqrt(128), fp32-rounded
 
@@ -112,6 +113,7 @@ __device__ __forceinline__ long long record_at(const uint8_t* cache, const Layou
 }
 
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef __bf16 b8v __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));

@@ -6,7 +6,7 @@ namespace kvarn {
 
 // ----------------------------------------------------------------------------- prefill
 // Work-groups [0, tile_blocks) quantize full tiles, TPW tiles (NW waves each) per
-// work-group; the remaining work-groups write the fp16 tail and len[], one (b, h, s)
+// work-group; the remaining work-groups write the bf16 tail and len[], one (b, h, s)
 // per wave.
 // Work-group `blk` of one layer's prefill, whose cache and inputs are `cache`, `kin`, `vin`
 // (the other fields of `a` are shared by every layer of a multi-layer launch).
@@ -30,9 +30,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, uint8_t* cac
     const uint16_t* src = s ? vin : kin;
     for (int t = a.nfull * L.G + g; t < a.T; t += 4) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + (((long long)b * a.T + t) * L.Hkv + h) * kD + 8 * c);
-      float x[8];
-      canon8_bf16(w, x, flags);
-      *reinterpret_cast<uint4*>(cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = pack8_f16(x);
+      *reinterpret_cast<uint4*>(cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = canon8(w, flags);
     }
     if (lane == 0) *reinterpret_cast<int32_t*>(cache + L.len_off(b, h, s)) = a.T;
     raise_flags(hdr, flags);
@@ -61,7 +59,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, uint8_t* cac
   float p[2][8][4];
   f4v w4[2][8];
   float st;
-  h8v av[2][4];
+  b8v av[2][4];
   {
     // the sign masks (header, cached) first: loads complete in issue order
     SigMask m[4];
@@ -81,22 +79,24 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, uint8_t* cac
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) av[mb][ks] = canon_a<false>(raw[mb][ks], m[ks]);
+      for (int ks = 0; ks < 4; ++ks) av[mb][ks] = sign8(raw[mb][ks], m[ks]);
       d[mb] = rotate_squares_mb_v<ABL>(idr, av[mb], hf, w4[mb], p[mb], c);
       __builtin_amdgcn_sched_barrier(0);
     }
     st = gram_own_v<ABL>(idr, d[0], d[1], c);
   }
-  if (__any(!(st <= 3.0e38f))) {  // an input beyond fp16 (inf after conversion) or NaN: redo checked
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        av[mb][ks] = canon_a<true>(*reinterpret_cast<const uint4*>(rows + mb * row16 + 32 * ks), m, &flags);
-    }
-    st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
-  }
+  // a value beyond 2^16, a NaN, or a token too small for fp32 squares: the checked rotation
+  int sx_own = 0;
+  if (__any(!rotation_stands(idr, st)))
+    st = rotate_checked<ABL>(
+        idr,
+        [&](int mb, int ks) {
+          // a fresh read each time: the compiler must not keep the first pass's registers for it
+          const uint16_t* r = rows;
+          asm volatile("" : "+v"(r));
+          return *reinterpret_cast<const uint4*>(r + mb * row16 + 32 * ks);
+        },
+        hdr, hf, av, w4, p, g, c, flags, sx_own);
 
   float* dw = nullptr;
   float* dy = nullptr;
@@ -110,7 +110,8 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, uint8_t* cac
     dw = (valid && pw) ? pw + doff : nullptr;
     dy = (valid && py) ? py + doff : nullptr;
   }
-  tile_finish<NW, DBG, ABL>(av, hf, w4, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, dw, dy, dstride);
+  tile_finish<NW, DBG, ABL>(av, hf, w4, p, st, sx_own, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, dw, dy,
+                            dstride);
   if (valid) {
     const long long ro = record_at(cache, L, b, h, tile, s);
     if (ro >= 0)
@@ -187,32 +188,31 @@ __global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
   const Frags hf = frags_v<ABL>(idr, lane);
   const uint16_t* src = (s ? a.v : a.k) + ((long long)b * a.T * L.Hkv + h) * kD;  // + row * Hkv * D
   uint32_t flags = 0;
-  h8v av[2][4];
+  // token 16 mb + c of this wave's block, channels 8 (4 ks + g) .. +7: stored in the tail,
+  // or a new token (canonical; its flags count where the job is valid)
+  auto load = [&](int mb, int ks) -> uint4 {
+    const int tt = tile * G + sub * 32 + 16 * mb + c;  // token of this A row in the sequence
+    if (tt < l0) return *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, tt % G) + 16 * (4 * ks + g));
+    const int row = min(tt - l0, a.T - 1);
+    uint32_t f = 0;
+    const uint4 w = canon8(*reinterpret_cast<const uint4*>(src + (long long)row * L.Hkv * kD + 8 * (4 * ks + g)), f);
+    if (valid) flags |= f;
+    return w;
+  };
+  b8v av[2][4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int tt = tile * G + sub * 32 + 16 * mb + c;  // token of this A row in the sequence
-      uint4 w;
-      if (tt < l0) {  // stored in the tail
-        w = *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, tt % G) + 16 * (4 * ks + g));
-      } else {        // a new token
-        const int row = min(tt - l0, a.T - 1);
-        float x[8];
-        uint32_t f = 0;
-        canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)row * L.Hkv * kD + 8 * (4 * ks + g)), x, f);
-        if (valid) flags |= f;
-        w = pack8_f16(x);
-      }
-      av[mb][ks] = sign_a(w, m);
-    }
+    for (int mb = 0; mb < 2; ++mb) av[mb][ks] = sign8(load(mb, ks), m);
   }
   float p[2][8][4];
   f4v w4[2][8];
-  const float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
-  tile_finish<NW, false, ABL>(av, hf, w4, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr, nullptr,
-                              0);
+  float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+  int sx_own = 0;
+  if (__any(!rotation_stands(idr, st))) st = rotate_checked<ABL>(idr, load, hdr, hf, av, w4, p, g, c, flags, sx_own);
+  tile_finish<NW, false, ABL>(av, hf, w4, p, st, sx_own, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr,
+                              nullptr, 0);
   if (valid) {
     const long long ro = record_at(a.cache, L, b, h, tile, s);
     if (ro >= 0)
@@ -235,11 +235,9 @@ __global__ __launch_bounds__(256) void tokens_tail_kernel(TokensArgs a) {
   tokens_range(a, b, h, s, l0, l1, dropped);
   uint32_t flags = dropped ? (uint32_t)KVARN_FLAG_CAPACITY : 0u;
   const uint16_t* src = (s ? a.v : a.k) + ((long long)b * a.T * L.Hkv + h) * kD;
-  for (int t = max(l0, l1 / L.G * L.G) + g; t < l1; t += 4) {
-    float x[8];
-    canon8_bf16(*reinterpret_cast<const uint4*>(src + (long long)(t - l0) * L.Hkv * kD + 8 * c), x, flags);
-    *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * c) = pack8_f16(x);
-  }
+  for (int t = max(l0, l1 / L.G * L.G) + g; t < l1; t += 4)
+    *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, t % L.G) + 16 * c) =
+        canon8(*reinterpret_cast<const uint4*>(src + (long long)(t - l0) * L.Hkv * kD + 8 * c), flags);
   raise_flags(a.cache, flags);
   if (lane == 0) *reinterpret_cast<int32_t*>(a.cache + L.len_off(b, h, s)) = l1;  // the wave read len first
 }

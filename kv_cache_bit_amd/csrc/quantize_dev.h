@@ -8,9 +8,9 @@
 //
 // Work mapping. A tile (G tokens x 128 channels of one batch row, kv head and
 // stream) is handled by G/32 waves, one 32-token block each.
-//   * Rotation on the matrix cores: the canonical inputs are exact in fp16 and the
-//     Sylvester matrix is +-1, so the products are exact in v_mfma_f32_16x16x32_f16
-//     with fp32 accumulation. H_syl of order 128 is H_4 (x) H_32: each 32-channel K step
+//   * Rotation on the matrix cores: the inputs are bf16 values and the Sylvester
+//     matrix is +-1, so the products are exact in v_mfma_f32_16x16x32_bf16 with fp32
+//     accumulation, and the sign flips of sigma are one XOR per pair of inputs. H_syl of order 128 is H_4 (x) H_32: each 32-channel K step
 //     goes through H_32 on the matrix cores (its two 32x16 halves are the register
 //     fragments F and G, so no matrix leaves registers), and the four K steps are
 //     combined by the 4-point transform H_4 in registers (16 MFMAs and 128 adds per
@@ -131,9 +131,9 @@ __device__ __forceinline__ void col_gather8(const float (&own)[2], float (&v)[8]
 // and G (the two halves of H_32) and applies H_4 after the products; the identity
 // ablation fills the four slots with its own one-hot fragments.
 struct Frags {
-  h8v v[4];  // F, -F, G, -G
+  b8v v[4];  // F, -F, G, -G
 };
-// The four fragments of every lane as fp16 bit patterns, computed at compile time:
+// The four fragments of every lane as bf16 bit patterns, computed at compile time:
 // word [lane][4 f + d] holds elements 2d, 2d+1 of fragment f.
 struct FragTable {
   uint32_t w[64][16];
@@ -145,7 +145,7 @@ constexpr FragTable make_frag_table() {
     for (int e = 0; e < 8; ++e) {
       int pc = (g & 1) & (c >> 3);
       for (int b = 0; b < 3; ++b) pc += (e >> b) & (c >> b) & 1;
-      const uint32_t f = (pc & 1) ? 0xBC00u : 0x3C00u;  // -1 / +1
+      const uint32_t f = (pc & 1) ? 0xBF80u : 0x3F80u;  // -1 / +1
       const uint32_t gg = (g >> 1) ? f ^ 0x8000u : f;
       const uint32_t vals[4] = {f, f ^ 0x8000u, gg, gg ^ 0x8000u};
       for (int q = 0; q < 4; ++q) t.w[lane][4 * q + e / 2] |= vals[q] << (16 * (e & 1));
@@ -158,7 +158,7 @@ __device__ __forceinline__ Frags hadamard_frags(int lane) {
   const uint4* p = reinterpret_cast<const uint4*>(kFrags.w[lane]);
   Frags h;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) h.v[q] = __builtin_bit_cast(h8v, p[q]);
+  for (int q = 0; q < 4; ++q) h.v[q] = __builtin_bit_cast(b8v, p[q]);
   return h;
 }
 // Identity in place of H_syl (the "VarN only" ablation): block nb takes the single K-step
@@ -172,8 +172,8 @@ __device__ __forceinline__ Frags identity_frags(int lane) {
     uint32_t w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
-      w[d] = (g == 2 * P + (c >> 3) && d == ((c & 7) >> 1)) ? 0x3C00u << (16 * (c & 1)) : 0u;
-    h.v[P] = __builtin_bit_cast(h8v, make_uint4(w[0], w[1], w[2], w[3]));
+      w[d] = (g == 2 * P + (c >> 3) && d == ((c & 7) >> 1)) ? 0x3F80u << (16 * (c & 1)) : 0u;
+    h.v[P] = __builtin_bit_cast(b8v, make_uint4(w[0], w[1], w[2], w[3]));
   }
   h.v[2] = h.v[0];
   h.v[3] = h.v[1];
@@ -200,36 +200,53 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, h2v));
 }
 
-// 8 bf16 -> 8 canonical fp16 (round half to even), times sigma: the sign flip rides on
-// the bf16 -> fp32 unpack. (w + m) << 16 flips bit 15 of the low bf16 before it moves up
-// (the carry out of bit 15 and bit 31 of m are shifted out), and (w ^ m) & 0xFFFF0000
-// flips the high one. Without CHECK a value beyond fp16 becomes inf and a NaN stays NaN,
-// which the caller detects and then redoes with CHECK: saturation at +-65504
-// (KVARN_FLAG_SATURATED), a NaN as 0 (KVARN_FLAG_NAN).
-template <bool CHECK>
-__device__ __forceinline__ h8v canon_a(const uint4 w, const SigMask& m, uint32_t* flags = nullptr) {
+// 8 bf16 values times sigma: the sign bits of the pairs flip where the mask words are set
+__device__ __forceinline__ b8v sign8(const uint4 w, const SigMask& m) {
+  return __builtin_bit_cast(b8v, make_uint4(w.x ^ m.m[0], w.y ^ m.m[1], w.z ^ m.m[2], w.w ^ m.m[3]));
+}
+// 8 bf16 inputs -> their canonical values (bf16 bits): a NaN becomes +0 (KVARN_FLAG_NAN)
+// and a magnitude beyond 2^16 (bf16 0x4780), infinities included, becomes +-2^16
+// (KVARN_FLAG_SATURATED); every other value is kept as it is. Integer arithmetic on both
+// halves of a word at once, with no per-value compares: for a magnitude m <= 0x7FFF, bit 15
+// of m + 0x7F is set iff m > 0x7F80 (NaN) and bit 15 of m + 0x387F iff m > 0x4780.
+__device__ __forceinline__ uint32_t canon2(uint32_t w, uint32_t& nan_acc, uint32_t& sat_acc) {
+  const uint32_t m = w & 0x7FFF7FFFu;
+  const uint32_t nan = (m + 0x007F007Fu) & 0x80008000u;         // no carry leaves a half
+  const uint32_t big = (m + 0x387F387Fu) & 0x80008000u & ~nan;
+  nan_acc |= nan;
+  sat_acc |= big;
+  const uint32_t nan_all = nan | (nan - (nan >> 15));            // 0xFFFF in NaN halves
+  const uint32_t big_all = big | (big - (big >> 15));            // 0xFFFF in saturated halves
+  const uint32_t v = (w & ~big_all) | (big_all & ((w & 0x80008000u) | 0x47804780u));
+  return v & ~nan_all;
+}
+__device__ __forceinline__ uint4 canon8(const uint4 w, uint32_t& flags) {
+  uint32_t nan = 0, sat = 0;
+  const uint4 o = make_uint4(canon2(w.x, nan, sat), canon2(w.y, nan, sat), canon2(w.z, nan, sat),
+                             canon2(w.w, nan, sat));
+  flags |= (nan ? (uint32_t)KVARN_FLAG_NAN : 0u) | (sat ? (uint32_t)KVARN_FLAG_SATURATED : 0u);
+  return o;
+}
+// the largest magnitude of 8 bf16 values
+__device__ __forceinline__ float maxabs8(const uint4 w) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) m = fmaxf(m, fmaxf(fabsf(bf16lo(ws[d])), fabsf(bf16hi(ws[d]))));
+  return m;
+}
+// 8 bf16 values times 2^e, exactly (e only scales tokens whose values all lie below 2^-20,
+// up to magnitudes below 1, so every result is a bf16 value again)
+__device__ __forceinline__ uint4 scale8(const uint4 w, int e) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
-  bool nan = false, sat = false;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    float v[2] = {__int_as_float((int)((ws[d] + m.m[d]) << 16)), __int_as_float((int)((ws[d] ^ m.m[d]) & 0xFFFF0000u))};
-    if constexpr (CHECK) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const bool bad = !(v[e] == v[e]);
-        nan |= bad;
-        sat |= fabsf(v[e]) > kFp16Max;  // false for a NaN
-        v[e] = bad ? 0.0f : fminf(fmaxf(v[e], -kFp16Max), kFp16Max);
-      }
-    }
-    o[d] = pack_f16x2(v[0], v[1]);
+    const uint32_t lo = (uint32_t)__float_as_int(__builtin_amdgcn_ldexpf(bf16lo(ws[d]), e));
+    const uint32_t hi = (uint32_t)__float_as_int(__builtin_amdgcn_ldexpf(bf16hi(ws[d]), e));
+    o[d] = (lo >> 16) | (hi & 0xFFFF0000u);
   }
-  if constexpr (CHECK) *flags |= (nan ? (uint32_t)KVARN_FLAG_NAN : 0u) | (sat ? (uint32_t)KVARN_FLAG_SATURATED : 0u);
-  return __builtin_bit_cast(h8v, make_uint4(o[0], o[1], o[2], o[3]));
-}
-__device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp16 input
-  return __builtin_bit_cast(h8v, make_uint4(w.x ^ m.m[0], w.y ^ m.m[1], w.z ^ m.m[2], w.w ^ m.m[3]));
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // W'[token 16mb + 4g + i][channel 16nb + c] = sum_k A[mb][k] H[k][16nb + c]; with ID the
@@ -248,11 +265,11 @@ __device__ __forceinline__ h8v sign_a(const uint4 w, const SigMask& m) {  // fp1
 // result as read-write and all its A and B fragments as inputs: the data dependency
 // pins it after the MFMAs, so every source is still live when each of them issues and
 // the register allocator cannot hand a source's registers to the result.
-__device__ __forceinline__ void h32_steps(const h8v (&a)[4], const Frags& hf, int h, f4v (&y)[4]) {
+__device__ __forceinline__ void h32_steps(const b8v (&a)[4], const Frags& hf, int h, f4v (&y)[4]) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     f4v t = {0.0f, 0.0f, 0.0f, 0.0f};
-    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], hf.v[2 * h], t, 0, 0, 0);
+    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], hf.v[2 * h], t, 0, 0, 0);
     asm volatile("" : "+v"(t) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(hf.v[0]), "v"(hf.v[2]));
     y[ks] = t;
   }
@@ -270,14 +287,14 @@ __device__ __forceinline__ void h4_combine(const f4v (&y)[4], f4v (&out)[4]) {
   }
 }
 template <bool ID>
-__device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& hf, f4v (&acc)[2][8]) {
+__device__ __forceinline__ void rotate_block(const b8v (&a)[2][4], const Frags& hf, f4v (&acc)[2][8]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if constexpr (ID) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb][nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
         asm volatile("" : "+v"(s) : "v"(a[mb][0]), "v"(a[mb][1]), "v"(a[mb][2]), "v"(a[mb][3]), "v"(hf.v[0]),
                      "v"(hf.v[1]), "v"(hf.v[2]), "v"(hf.v[3]));
         acc[mb][nb] = s;
@@ -305,18 +322,18 @@ __device__ __forceinline__ void rotate_block(const h8v (&a)[2][4], const Frags& 
 // 8 g + 7 of the K step). Lane (g, c) of the Gram block holds rows 4 g + i at column c:
 // the diagonal sits in lanes c = 4 g + j at element j, and the owner lane fetches it.
 template <bool ID>
-__device__ __forceinline__ float rotate_squares_mb(const h8v (&a)[4], const Frags& hf, f4v (&w4)[8], float (&p)[8][4],
+__device__ __forceinline__ float rotate_squares_mb(const b8v (&a)[4], const Frags& hf, f4v (&w4)[8], float (&p)[8][4],
                                                    int c) {
   // the Gram block first: the token block's inputs are dead once its rotation is done
   f4v gm = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) gm = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ks], a[ks], gm, 0, 0, 0);
+  for (int ks = 0; ks < 4; ++ks) gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], a[ks], gm, 0, 0, 0);
   asm volatile("" : "+v"(gm) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
   if constexpr (ID) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       f4v s = {0.0f, 0.0f, 0.0f, 0.0f};
-      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[nb >> 1], hf.v[nb & 1], s, 0, 0, 0);
       asm volatile("" : "+v"(s) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(hf.v[0]), "v"(hf.v[1]),
                    "v"(hf.v[2]), "v"(hf.v[3]));
       w4[nb] = s;
@@ -351,7 +368,7 @@ __device__ __forceinline__ float gram_own(float d0, float d1, int c) {
   return ((c >> 3) ? x1 : x0) * (ID ? 1.0f : (float)kD);
 }
 template <bool ID>
-__device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
+__device__ __forceinline__ float rotate_squares(const b8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
                                                 float (&p)[2][8][4], int c) {
   const float d0 = rotate_squares_mb<ID>(a[0], hf, w4[0], p[0], c);
   const float d1 = rotate_squares_mb<ID>(a[1], hf, w4[1], p[1], c);
@@ -361,7 +378,7 @@ __device__ __forceinline__ float rotate_squares(const h8v (&a)[2][4], const Frag
 // Dispatch for the ablation build (ABL): the identity rotation is a runtime choice there;
 // the standard build compiles the Hadamard path only.
 template <bool ABL>
-__device__ __forceinline__ float rotate_squares_v(bool idr, const h8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
+__device__ __forceinline__ float rotate_squares_v(bool idr, const b8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
                                                   float (&p)[2][8][4], int c) {
   if constexpr (ABL) {
     if (idr) return rotate_squares<true>(a, hf, w4, p, c);
@@ -369,7 +386,7 @@ __device__ __forceinline__ float rotate_squares_v(bool idr, const h8v (&a)[2][4]
   return rotate_squares<false>(a, hf, w4, p, c);
 }
 template <bool ABL>
-__device__ __forceinline__ float rotate_squares_mb_v(bool idr, const h8v (&a)[4], const Frags& hf, f4v (&w4)[8],
+__device__ __forceinline__ float rotate_squares_mb_v(bool idr, const b8v (&a)[4], const Frags& hf, f4v (&w4)[8],
                                                      float (&p)[8][4], int c) {
   if constexpr (ABL) {
     if (idr) return rotate_squares_mb<true>(a, hf, w4, p, c);
@@ -384,7 +401,7 @@ __device__ __forceinline__ float gram_own_v(bool idr, float d0, float d1, int c)
   return gram_own<false>(d0, d1, c);
 }
 template <bool ABL>
-__device__ __forceinline__ void rotate_block_v(bool idr, const h8v (&a)[2][4], const Frags& hf,
+__device__ __forceinline__ void rotate_block_v(bool idr, const b8v (&a)[2][4], const Frags& hf,
                                                f4v (&acc)[2][8]) {
   if constexpr (ABL) {
     if (idr) {
@@ -407,6 +424,65 @@ __device__ __forceinline__ Frags frags_v(bool idr, int lane) {
     if (idr) return identity_frags(lane);
   }
   return hadamard_frags(lane);
+}
+
+// ----------------------------------------------------------------------------- checked rotation
+// The rotation runs on the bf16 inputs as given. It stands when every token's sum of
+// squares lies in [2^-100, 2^32]: then no value exceeds 2^16 in magnitude, none is NaN,
+// and the squares that carry a token's mean square do not underflow fp32. st is the
+// owner lane's first token-axis sum (D or 1 times the token's sum of squares), so a wave
+// checks its 32 tokens with one vote.
+__device__ __forceinline__ bool rotation_stands(bool idr, float st) {
+  const float k = idr ? 1.0f : (float)kD;
+  return st >= 0x1p-100f * k && st <= 0x1p32f * k;
+}
+// max over the 4 rows (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float rows_max4(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+// Otherwise the wave redoes its block from load(mb, ks), the bf16 rows the first pass read
+// (token 16 mb + c, channels 8 (4 ks + g) .. +7): the values are made canonical (canon8,
+// flags), and a token whose largest magnitude is below 2^-20 is scaled by the power of two
+// 2^sx that brings it into [0.5, 1), exactly, so that no square it needs underflows. Every
+// step of VarN is invariant under a per-token power of two except r itself and the factor
+// that maps W' to Y, which the owner lane corrects with its token's sx (sx_own).
+template <bool ABL, typename Load>
+__device__ float rotate_checked(bool idr, Load&& load, const uint8_t* hdr, const Frags& hf, b8v (&av)[2][4],
+                                f4v (&w4)[2][8], float (&p)[2][8][4], int g, int c, uint32_t& flags, int& sx_own) {
+  // two passes over the rows (the second reads them again rather than holding them):
+  // each token's largest magnitude, then the scaled, signed operands
+  float mx[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint32_t counted_below = 0;
+      mx[mb] = fmaxf(mx[mb], maxabs8(canon8(load(mb, ks), counted_below)));
+    }
+  int sx[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const float m = rows_max4(mx[mb]);  // token 16 mb + c has its channels in lanes c + 16 g'
+    sx[mb] = (m > 0.0f && m < 0x1p-20f) ? -__builtin_amdgcn_frexp_expf(m) : 0;
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint4 x = canon8(load(mb, ks), flags);
+      av[mb][ks] = sign8(sx[mb] ? scale8(x, sx[mb]) : x, m);
+    }
+  }
+  const float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+  // the owner lane of token 16 (c/8) + 4 g + (c/2) % 4 reads sx where that token is an A row
+  const int src = 4 * (20 * g + ((c >> 1) & 3));
+  const int s0 = __builtin_amdgcn_ds_bpermute(src, sx[0]), s1 = __builtin_amdgcn_ds_bpermute(src, sx[1]);
+  sx_own = (c >> 3) ? s1 : s0;
+  return st;
 }
 
 // ----------------------------------------------------------------------------- LDS
@@ -460,7 +536,7 @@ __device__ __forceinline__ void chan_reduce(const float (&v)[8], float (&own)[2]
 // rotation is recomputed here (the ablation build only). r_own, c_own: the owner
 // lane's token and channel scales, in units of W.
 template <int NW, bool ABL>
-__device__ void centered_varn(const h8v (&av)[2][4], const Frags& hf, bool idr, bool tok, bool chp, int n_it,
+__device__ void centered_varn(const b8v (&av)[2][4], const Frags& hf, bool idr, bool tok, bool chp, int n_it,
                               float inv_k, int lane, int sub, TileLds<NW>& sh, float& r_own, float (&c_own)[2]) {
   constexpr int G = 32 * NW;
   const int g = lane >> 4, c = lane & 15;
@@ -731,8 +807,8 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
 // its scale at 1 (the other pass then repeats the same sums every iteration). The
 // centered reading of "variance" runs its own loop (centered_varn).
 template <int NW, bool DBG, bool ABL>
-__device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, f4v (&acc)[2][8], float (&p)[2][8][4],
-                            float st_own, int lane,
+__device__ void tile_finish(const b8v (&av)[2][4], const Frags& hf, f4v (&acc)[2][8], float (&p)[2][8][4],
+                            float st_own, int sx_own, int lane,
                             int sub, int stream, int n_it, int var, int bits_in, TileLds<NW>& sh, uint32_t& flags,
                             float* dbg_w, float* dbg_y, long long dstride) {
   constexpr int G = 32 * NW;
@@ -798,11 +874,12 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, f4v (&acc)[2
   if constexpr (ABL) {
     if (cen) centered_varn<NW, ABL>(av, hf, idr, tok, chp, n_it, inv_k, lane, sub, sh, r_own, c_own);
   }
+  r_own = __builtin_amdgcn_ldexpf(r_own, -sx_own);  // the token's scale of the checked rotation undone
   const float rc = fminf(fmaxf(r_own, kScaleMin), kFp16Max);
   if (rc != r_own) flags |= KVARN_FLAG_SCALE_CLAMPED;
   const float r16_own = round_f16(rc);
   float at[8];  // Y = W' / (k r16 c16): per-token factor 1 / (k r16)
-  row_gather8(inv_k * __builtin_amdgcn_rcpf(r16_own), at, sh.grow[sub], g, c);
+  row_gather8(__builtin_amdgcn_ldexpf(inv_k * __builtin_amdgcn_rcpf(r16_own), -sx_own), at, sh.grow[sub], g, c);
   float c16_own[2], ic_own[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -813,8 +890,9 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, f4v (&acc)[2
     ic_own[q] = __builtin_amdgcn_rcpf(c16_own[q]);
   }
   if constexpr (DBG) {
-    float ic[8];
+    float ic[8], ex[8];
     col_gather8(ic_own, ic, sh.gcol[sub], g, c);
+    row_gather8(__builtin_amdgcn_ldexpf(1.0f, -sx_own), ex, sh.grow[sub], g, c);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -822,7 +900,7 @@ __device__ void tile_finish(const h8v (&av)[2][4], const Frags& hf, f4v (&acc)[2
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           const long long off = (16 * mb + 4 * g + i) * dstride + 16 * nb + c;
-          if (dbg_w) dbg_w[off] = acc[mb][nb][i] * inv_k;
+          if (dbg_w) dbg_w[off] = acc[mb][nb][i] * inv_k * ex[4 * mb + i];
           if (dbg_y) dbg_y[off] = (acc[mb][nb][i] * at[4 * mb + i]) * ic[nb];
         }
   }
@@ -918,34 +996,6 @@ __device__ __forceinline__ void raise_flags(uint8_t* hdr, uint32_t f) {
   if (f) atomicOr(reinterpret_cast<uint32_t*>(hdr + kFlagsOff), f);
 }
 
-__device__ __forceinline__ uint4 pack8_f16(const float (&x)[8]) {
-  uint4 o;
-  o.x = pack_f16x2(x[0], x[1]);
-  o.y = pack_f16x2(x[2], x[3]);
-  o.z = pack_f16x2(x[4], x[5]);
-  o.w = pack_f16x2(x[6], x[7]);
-  return o;
-}
-// bf16 x 8 -> canonical fp16 values: saturated at +-65504 (KVARN_FLAG_SATURATED into
-// flags), a NaN stored as 0 (KVARN_FLAG_NAN)
-__device__ __forceinline__ void canon8_bf16(const uint4 w, float (&x)[8], uint32_t& flags) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float amax = 0.0f;
-  bool nan = false;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float v[2] = {bf16lo(ws[k]), bf16hi(ws[k])};
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      nan |= !(v[e] == v[e]);
-      amax = fmaxf(amax, fabsf(v[e]));  // a NaN operand is ignored
-      x[2 * k + e] = v[e] == v[e] ? round_f16(fminf(fmaxf(v[e], -kFp16Max), kFp16Max)) : 0.0f;
-    }
-  }
-  if (amax > kFp16Max) flags |= KVARN_FLAG_SATURATED;
-  if (nan) flags |= KVARN_FLAG_NAN;
-}
-
 // ----------------------------------------------------------------------------- append
 // Decode append of one (b, h, s) = job (s fastest, then h) by the G/32 waves
 // sub = 0 .. NW-1 of a work-group; any further waves of the work-group must have exited
@@ -966,38 +1016,37 @@ __device__ void append_job(const AppendArgs& a, int job, int sub, int lane, Tile
   }
   uint32_t flags = 0;
   const uint16_t* src = (s ? a.v : a.k) + ((long long)b * L.Hkv + h) * kD;
-  if (sub == 0 && g == 0) {  // the new token into the fp16 tail (16 lanes x 8 channels)
-    float xin[8];
-    canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * c), xin, flags);
-    *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, pos % G) + 16 * c) = pack8_f16(xin);
+  if (sub == 0 && g == 0) {  // the new token into the bf16 tail (16 lanes x 8 channels)
+    *reinterpret_cast<uint4*>(a.cache + L.tail_row(b, h, s, pos % G) + 16 * c) =
+        canon8(*reinterpret_cast<const uint4*>(src + 8 * c), flags);
   }
   if ((pos + 1) % G == 0) {
     const bool idr = ABL && (L.variant & KVARN_VARIANT_NO_ROTATION);
     const Frags hf = frags_v<ABL>(idr, lane);
-    h8v av[2][4];
+    // token 16 mb + c of this wave's block, channels 8 (4 ks + g) .. +7: the stored tail
+    // tokens, and the token just written taken from the input, not from memory
+    auto load = [&](int mb, int ks) -> uint4 {
+      const int t = sub * 32 + 16 * mb + c;
+      if (t == G - 1) {
+        uint32_t seen = 0;  // flags of this token were raised with its tail write
+        return canon8(*reinterpret_cast<const uint4*>(src + 8 * (4 * ks + g)), seen);
+      }
+      return *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, t) + 16 * (4 * ks + g));
+    };
+    b8v av[2][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int t = sub * 32 + 16 * mb + c;  // token of this A row inside the tile
-        uint4 w;
-        if (t == G - 1) {  // the token just written: take it from the input, not from memory
-          float x[8];
-          uint32_t seen = 0;  // flags of this token were raised with its tail write
-          canon8_bf16(*reinterpret_cast<const uint4*>(src + 8 * (4 * ks + g)), x, seen);
-          w = pack8_f16(x);
-        } else {
-          w = *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, t) + 16 * (4 * ks + g));
-        }
-        av[mb][ks] = sign_a(w, m);
-      }
+      for (int mb = 0; mb < 2; ++mb) av[mb][ks] = sign8(load(mb, ks), m);
     }
     float p[2][8][4];
     f4v w4[2][8];
-    const float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
-    tile_finish<NW, false, ABL>(av, hf, w4, p, st, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr,
-                                nullptr, 0);
+    float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+    int sx_own = 0;
+    if (__any(!rotation_stands(idr, st))) st = rotate_checked<ABL>(idr, load, hdr, hf, av, w4, p, g, c, flags, sx_own);
+    tile_finish<NW, false, ABL>(av, hf, w4, p, st, sx_own, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags,
+                                nullptr, nullptr, 0);
     const long long ro = record_at(a.cache, L, b, h, (pos + 1) / G - 1, s);
     if (ro >= 0)
       copy_record<NW>(sh, a.cache + ro, lane, sub, L.tr);

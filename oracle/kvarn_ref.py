@@ -25,9 +25,9 @@ Method ([AP] section 3; [RP] "how KVarN does it"; [CP] abstract):
      Q K^T is unchanged ([AP] 3.1).
 
 Where the pages leave a step open, the reading taken is stated at the function
-that implements it (fp16 canonical input, second-moment "variance", Sylvester
+that implements it (bf16 inputs kept as given, second-moment "variance", Sylvester
 ordering of H, fp16 stored scales, per-channel min/max grid over a group of G
-tokens, round-half-to-even, fp16 tail of unrotated tokens, tile record layout).
+tokens, round-half-to-even, bf16 tail of unrotated tokens, tile record layout).
 
 Pinned by tests/test_oracle_*.py against closed forms, invariants, brute force
 and library routines (see each test's docstring).
@@ -39,14 +39,15 @@ import numpy as np
 # ----------------------------------------------------------------------------- format constants
 # Written out here on purpose: the oracle includes nothing from the library.
 MAGIC = 0x4E52564B          # bytes 'K','V','R','N' little-endian
-VERSION = 2
+VERSION = 3                 # 3: the tail holds bf16 (2: fp16)
 FLAG_CAPACITY = 1           # an append found the cache full (token dropped)
-FLAG_SATURATED = 2          # an input value was outside the fp16 range and was saturated
+FLAG_SATURATED = 2          # an input value was beyond +-2^16 (or infinite) and was saturated
 FLAG_SCALE_CLAMPED = 4      # a stored scale hit the fp16 clamp range
 FLAG_UNMAPPED = 8           # a paged cache had no page for a tile that was written
 FLAG_NAN = 16               # an input value was NaN (stored as 0)
 Q_PREROTATED = 1            # attention flag: the query is already rotated (q H)
 FP16_MAX = 65504.0
+IN_MAX = 65536.0            # inputs saturate at +-2^16 (a bf16 value)
 SCALE_MIN = 2.0 ** -14      # smallest normal fp16; lower clamp of r and c
 HEADER_FIXED = 512          # len[] starts here
 SIGMA_OFFSET = 64
@@ -89,16 +90,27 @@ def bf16_to_f64(bits) -> np.ndarray:
 
 
 def canonicalize(bits) -> tuple[np.ndarray, bool, bool]:
-    """Reading: every K/V input token is first brought to fp16, the dtype of the
-    decode-time tail, so a token quantizes identically whether it arrives in a
-    prefill or through the tail. bf16 -> fp16 is exact for 2^-17 <= |x| <= 65504 (a
-    bf16 value keeps 8 significant bits); smaller values round (RNE) to the fp16
-    subnormal grid, larger ones (and infinities) saturate. The pages assume finite
-    inputs; a NaN is stored as 0 and reported. Returns (values, saturated, had_nan)."""
+    """Reading: the K/V inputs are taken as given, bf16 values, and the decode-time
+    tail stores them unchanged (bf16), so a token quantizes identically whether it
+    arrives in a prefill or through the tail. The pages fix neither the dtype of the
+    tokens not yet quantized nor any conversion of the inputs (their "FP16" names the
+    16-bit cache the method is compared with); keeping the model's bf16 values stores
+    those tokens exactly. Values beyond +-2^16, infinities included, saturate at +-2^16
+    (a bf16 value), which bounds every sum the method takes; the pages assume finite
+    inputs, so a NaN is stored as 0 and reported. Returns (values, saturated, had_nan)."""
     x = bf16_to_f64(bits)
     nan = np.isnan(x)
-    v, clamped = fp16_saturate(np.where(nan, 0.0, x))
-    return v, bool(clamped.any()), bool(nan.any())
+    x = np.where(nan, 0.0, x)
+    sat = np.abs(x) > IN_MAX
+    return np.clip(x, -IN_MAX, IN_MAX), bool(sat.any()), bool(nan.any())
+
+
+def bf16_bits(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) of values that bf16 holds exactly (canonical inputs)."""
+    x = np.asarray(x, dtype=np.float64)
+    u = x.astype(np.float32).view(np.uint32)
+    assert not np.any(u & 0xFFFF) and np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    return (u >> 16).astype(np.uint16)
 
 
 def fp16_bits(x) -> np.ndarray:
@@ -527,10 +539,14 @@ class Cache:
         return None if r is None else int(r.ctypes.data - self.buf.ctypes.data)
 
     def tail(self, b, h, s) -> np.ndarray:
-        """fp16 view [G][D] of one tail."""
+        """bf16 bit patterns, a uint16 view [G][D] of one tail."""
         o = self.g.tail_slot_offset(b, h, s, 0)
         n = self.g.group * self.g.head_dim * 2
-        return self.buf[o:o + n].view(np.float16).reshape(self.g.group, self.g.head_dim)
+        return self.buf[o:o + n].view(np.uint16).reshape(self.g.group, self.g.head_dim)
+
+    def tail_values(self, b, h, s) -> np.ndarray:
+        """The values of one tail, fp64 [G][D]."""
+        return bf16_to_f64(self.tail(b, h, s))
 
     def defined_mask(self) -> np.ndarray:
         """Bytes whose content the format defines given the current lengths."""
@@ -566,7 +582,7 @@ def _quantize_stream(x, sigma, g: Geom, stream: int):
 def quantize_prefill(cache: Cache, k_bits, v_bits, num_tokens: int) -> None:
     """Reset the cache to hold tokens [0, T) of k, v (bf16 bits [B][T][Hkv][D]).
     Full groups of G tokens become tile records; the last T mod G tokens stay in
-    the fp16 tail, unrotated ([AP] 3.2: the current group is still being filled)."""
+    the bf16 tail, unrotated ([AP] 3.2: the current group is still being filled)."""
     g = cache.g
     T = int(num_tokens)
     assert 0 <= T <= g.capacity
@@ -593,12 +609,12 @@ def quantize_prefill(cache: Cache, k_bits, v_bits, num_tokens: int) -> None:
             for h in range(g.num_kv_heads):
                 tail = cache.tail(b, h, s)
                 for t in range(nfull * g.group, T):
-                    tail[t % g.group] = xt[b, h, t].astype(np.float16)
+                    tail[t % g.group] = bf16_bits(xt[b, h, t])
     cache.lens[:] = T
 
 
 def append_decode(cache: Cache, k_bits, v_bits, mask=None) -> None:
-    """Append one token per (batch, kv head) (bf16 bits [B][Hkv][D]) through the fp16 tail.
+    """Append one token per (batch, kv head) (bf16 bits [B][Hkv][D]) through the bf16 tail.
     When a group of G fills, it is rotated, normalized and quantized into the next
     tile record ([AP] 3.2: statistics of the current group are updated as tokens arrive).
     `mask` (bool [B]) restricts the append to the sequences it selects. Flags: a token
@@ -621,9 +637,9 @@ def append_decode(cache: Cache, k_bits, v_bits, mask=None) -> None:
                 if nan:
                     cache.or_flags(FLAG_NAN)
                 tail = cache.tail(b, h, s)
-                tail[pos % g.group] = x.astype(np.float16)
+                tail[pos % g.group] = bf16_bits(x)
                 if (pos + 1) % g.group == 0:
-                    tile_x = tail.astype(np.float64)[None]         # [1][G][D]
+                    tile_x = cache.tail_values(b, h, s)[None]      # [1][G][D]
                     recs, f = _quantize_stream(tile_x, cache.sigma, g, s)
                     cache.or_flags(f)
                     rec = cache.record(b, h, (pos + 1) // g.group - 1, s)
@@ -665,7 +681,7 @@ def stream_values(cache: Cache, b: int, h: int, s: int, rotated: bool = False, w
         u = unpack_record(rec, g.group, g.head_dim, s, g.bits)
         w = dequantize_tile(u["q"], u["r16"], u["c16"], u["s16"], u["z16"])
         out[tile * g.group:(tile + 1) * g.group] = w if rotated else undo_rotation(w, cache.sigma, g.variant)
-    tail = cache.tail(b, h, s).astype(np.float64)
+    tail = cache.tail_values(b, h, s)
     for t in range(nfull * g.group, n):
         out[t] = apply_rotation(tail[t % g.group], cache.sigma, g.variant) if rotated else tail[t % g.group]
     return (out, present) if with_mask else out
@@ -721,8 +737,8 @@ def attn_decode(cache: Cache, q_bits, num_q_heads: int, softmax_scale: float = 0
 def append_attn_decode(cache: Cache, k_bits, v_bits, q_bits, num_q_heads: int, softmax_scale: float = 0.0,
                        flags: int = 0) -> np.ndarray:
     """One decode step: attend with q over the stored tokens plus the new one, then append it.
-    The stored tokens are read as in attn_decode (tiles dequantized, the tail as fp16);
-    the new token is its canonical fp16 value, which is also what a group completed by
+    The stored tokens are read as in attn_decode (tiles dequantized, the tail as stored);
+    the new token is its canonical bf16 value, which is also what a group completed by
     this token holds before it is quantized ([AP] 3.2: the group being filled is kept
     until it is complete). A full sequence attends without the token, which the append
     then drops."""

@@ -129,9 +129,10 @@ def check_prefill(gc: GpuCache, k_bits: np.ndarray, v_bits: np.ndarray, T: int, 
     for s, bits in enumerate((k_bits, v_bits)):
         for b in range(og.batch):
             for h in range(og.num_kv_heads):
-                tail = hc.tail(b, h, s).astype(np.float64)
+                tail = hc.tail(b, h, s)
                 for t in range(nfull * G, T):
-                    assert np.array_equal(tail[t % G], R.canonicalize(bits[b, t, h])[0]), ("tail", s, b, h, t)
+                    want = R.bf16_bits(R.canonicalize(bits[b, t, h])[0])
+                    assert np.array_equal(tail[t % G], want), ("tail", s, b, h, t)
     if stats["n_r"]:
         assert stats["r_mis"] / (2 * stats["n_r"]) <= 1e-2
         assert stats["c_mis"] / (2 * stats["n_c"]) <= 1e-2

@@ -35,7 +35,7 @@ def c_results(tmp_path_factory):
 
 def test_c_caller_sees_every_entry_point(c_results):
     assert int(c_results["entry_points"]) == len(K.EXPORTS)
-    assert int(c_results["format_version"]) == 2
+    assert int(c_results["format_version"]) == 3
 
 
 def test_c_caller_sizes_match_oracle_and_binding(c_results):

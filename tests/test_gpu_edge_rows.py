@@ -1,8 +1,10 @@
-"""GPU parity on token rows at the edges of the input range: all-zero rows, and rows far
-below fp16's normal range (f16 subnormals after canonicalization), inside tiles of
-ordinary outlier-bearing rows. The first token-axis pass of VarN takes its sums from the
-Gram diagonal (exact products of the canonical inputs on the matrix cores); with one
-iteration those sums fix the token scale r directly. Run on an MI355X: pytest -m gpu.
+"""GPU parity on token rows at the edges of the input range, inside tiles of ordinary
+outlier-bearing rows: all-zero rows, small rows (1e-6, 2^-22), and rows whose squares
+would underflow fp32 (1e-30, and bf16 subnormals around 2^-128), which the kernels route
+through the checked rotation with a per-token power-of-two scale. The first token-axis
+pass of VarN takes its sums from the Gram diagonal (exact products of the inputs on the
+matrix cores); with one iteration those sums fix the token scale r directly. Run on an
+MI355X: pytest -m gpu.
 """
 import numpy as np
 import pytest
@@ -19,12 +21,14 @@ def edge_rows_kv(seed, B, T, H, span):
     k, v = synth.kv_host(seed, B, T, H)
     rng = np.random.Generator(np.random.PCG64(seed + 1))
     for arr in (k, v):
-        rows = rng.choice(span, size=6, replace=False)
+        rows = rng.choice(span, size=10, replace=False)
         tiny = rng.standard_normal((2, B, H, 128)).astype(np.float32)
         for j in range(2):
             arr[:, rows[j]] = 0                                                         # all zero
-            arr[:, rows[2 + j]] = synth.f32_to_bf16_bits(tiny[j] * 1e-6)                 # subnormal in fp16
-            arr[:, rows[4 + j]] = synth.f32_to_bf16_bits(tiny[j] * 2.0 ** -22)           # a few fp16 ulps
+            arr[:, rows[2 + j]] = synth.f32_to_bf16_bits(tiny[j] * 1e-6)
+            arr[:, rows[4 + j]] = synth.f32_to_bf16_bits(tiny[j] * 2.0 ** -22)
+            arr[:, rows[6 + j]] = synth.f32_to_bf16_bits(tiny[j] * 1e-30)                # squares below fp32
+            arr[:, rows[8 + j]] = synth.f32_to_bf16_bits(tiny[j] * np.float32(2.0 ** -128))  # bf16 subnormals
     return k, v
 
 
@@ -51,7 +55,7 @@ def test_prefill_zero_and_tiny_token_rows(G, n_it):
 
 @pytest.mark.parametrize("G", [32, 64])
 def test_non_finite_inputs(G):
-    """NaN inputs are stored as 0 and raise KVARN_FLAG_NAN; infinities saturate at +-65504
+    """NaN inputs are stored as 0 and raise KVARN_FLAG_NAN; infinities saturate at +-2^16
     (KVARN_FLAG_SATURATED). Checked through the parity chain (a full tile and the tail) and
     through single-token appends, which must give the same bytes and flags."""
     print("[case] non-finite inputs", G, flush=True)

@@ -1,5 +1,5 @@
 """The synthetic pseudo-decode harness on a small random decoder, through the library's
-kernels. Asserted: every statistic is finite; while every token is still in the fp16 tail
+kernels. Asserted: every statistic is finite; while every token is still in the bf16 tail
 (steps 0..30) the quantized runs match the exact one (KL below 1e-6, attention output
 within 1e-4, the same top-1 token); at step 31, where the first group is quantized, the
 attention output moves by more than 1e-3. The mean KL of the full method and of
@@ -22,7 +22,7 @@ def test_pseudo_decode_small():
     for name, st in stats.items():
         for m, x in st.items():
             assert np.all(np.isfinite(x)), (name, m)
-        # steps 0..30 read the fp16 tail only (bf16 -> fp16 is exact here); step 31
+        # steps 0..30 read the bf16 tail only (the inputs as given); step 31
         # completes the first group, which the append quantizes before the attention
         assert st["pd_kl"][:31].max() < 1e-6, (name, st["pd_kl"][:31].max())
         assert st["pd_attn"][:31].max() < 1e-4, (name, st["pd_attn"][:31].max())

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_format_version_and_status_strings():
-    assert K.kvarn_format_version() == R.VERSION == 2
+    assert K.kvarn_format_version() == R.VERSION == 3
     for s in range(7):
         assert K.status_str(s)
     assert K.status_str(99) == "unknown status"

@@ -34,7 +34,7 @@ def sdpa(q, k, v, scale):
 def test_header_fields():
     c, _, _ = make_cache(B=2, H=3, T=70)
     assert c.buf[0:4].view(np.uint32)[0] == R.MAGIC
-    assert c.buf[4:8].view(np.uint32)[0] == 2
+    assert c.buf[4:8].view(np.uint32)[0] == 3
     assert c.buf[8:36].view(np.int32).tolist() == [2, 3, 128, 128, 32, 3, 2]
     assert np.all(c.lens == 70)
     assert c.g.header == 768 and c.g.total % 256 == 0
@@ -53,10 +53,13 @@ def test_header_sign_words():
     assert words[3] == 0                     # (+1, +1)
     assert words[63] == 0x80000000           # (+1, -1): channels 126, 127
     assert np.count_nonzero(words[4:63]) == 0
-    # and XORed into a packed pair of fp16 values it flips exactly those signs
+    # and XORed into a packed pair of fp16 or bf16 values it flips exactly those signs
     pair = np.array([1.5, -2.25], dtype=np.float16).view(np.uint32)[0]
     flipped = np.array([pair ^ words[2]], dtype=np.uint32).view(np.float16)
     assert flipped.tolist() == [-1.5, 2.25]
+    pair = np.array([0xC010, 0x3FC0], dtype=np.uint16).view(np.uint32)[0]      # bf16 (-2.25, 1.5)
+    flipped = R.bf16_to_f64(np.array([pair ^ words[1]], dtype=np.uint32).view(np.uint16))
+    assert flipped.tolist() == [2.25, 1.5]
 
 
 @pytest.mark.parametrize("T", [0, 5, 31, 32, 33, 100])
@@ -85,11 +88,15 @@ def test_capacity_and_saturation_flags():
     R.append_decode(c, k[:, 32], v[:, 32])
     assert c.flags & R.FLAG_CAPACITY and np.all(c.lens == 32)
     k2 = k.copy()
-    k2[0, 3, 0, 5] = 0x4780                                          # 65536: beyond fp16
+    k2[0, 3, 0, 5] = 0x4780                                          # 65536 = 2^16: kept
     c2 = R.Cache(geom, synth.sign_vector(0))
     R.quantize_prefill(c2, k2, v, 10)
-    assert c2.flags == R.FLAG_SATURATED
-    assert c2.tail(0, 0, 0)[3, 5] == np.float16(65504)
+    assert c2.flags == 0 and c2.tail(0, 0, 0)[3, 5] == 0x4780
+    k2[0, 3, 0, 5] = 0xC781                                          # -65792: beyond 2^16
+    c3 = R.Cache(geom, synth.sign_vector(0))
+    R.quantize_prefill(c3, k2, v, 10)
+    assert c3.flags == R.FLAG_SATURATED
+    assert c3.tail(0, 0, 0)[3, 5] == 0xC780 and c3.tail_values(0, 0, 0)[3, 5] == -65536.0
 
 
 def test_dequantize_tail_exact_and_rows_past_length_zero():
@@ -215,11 +222,11 @@ def test_append_attn_step_equals_append_then_attend(T):
     assert np.array_equal(a.buf, b.buf)
 
 
-def test_append_attn_step_completing_a_group_reads_fp16():
+def test_append_attn_step_completing_a_group_reads_it_unquantized():
     """A step whose token completes a group (T = 63, G = 32): the attention reads tile 0
-    from its record and the 32 tokens of the completed group as fp16 (the 31 tail tokens,
-    then the new token); afterwards the cache equals the plain append's, and attending
-    again reads the group quantized, which differs."""
+    from its record and the 32 tokens of the completed group as given (the 31 bf16 tail
+    tokens, then the new token); afterwards the cache equals the plain append's, and
+    attending again reads the group quantized, which differs."""
     T = 63
     a, k, v = _fresh(T)
     before, _, _ = _fresh(T)
@@ -234,8 +241,8 @@ def test_append_attn_step_completing_a_group_reads_fp16():
                 rec = R.unpack_record(before.record(bb, h, 0, s), 32, 128, s)
                 tile0 = R.unrotate(R.dequantize_tile(rec["q"], rec["r16"], rec["c16"], rec["s16"], rec["z16"]),
                                    before.sigma)
-                tail = before.tail(bb, h, s)[:31].astype(np.float64)
-                new = R.fp16_round(R.bf16_to_f64(bits[bb, T, h]))
+                tail = before.tail_values(bb, h, s)[:31]
+                new = R.bf16_to_f64(bits[bb, T, h])
                 kv.append(np.vstack([tile0, tail, new[None]]))
             for gi in range(2 * h, 2 * h + 2):
                 lg = kv[0] @ qq[bb, gi] / np.sqrt(128)

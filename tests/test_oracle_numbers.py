@@ -69,20 +69,23 @@ def test_bf16_decoding_known_patterns():
 
 
 def test_canonicalize_range_edges():
-    # 65536 does not fit fp16: saturates to 65504 and raises the flag
-    v, sat, _ = R.canonicalize(np.array([0x4780], dtype=np.uint16))
-    assert v[0] == 65504.0 and sat
+    # 2^16 = 0x4780 is kept; the next bf16 value, 2^16 (1 + 2^-7) = 0x4781, saturates to 2^16
+    v, sat, _ = R.canonicalize(np.array([0x4780, 0xC780], dtype=np.uint16))
+    assert v.tolist() == [65536.0, -65536.0] and not sat
+    v, sat, _ = R.canonicalize(np.array([0x4781, 0xC7FF, 0x7F7F], dtype=np.uint16))
+    assert v.tolist() == [65536.0, -65536.0, 65536.0] and sat
     v, sat, _ = R.canonicalize(np.array([0x477F, 0x3F80], dtype=np.uint16))
     assert v.tolist() == [65280.0, 1.0] and not sat
-    # below 2^-14 the fp16 grid is 2^-24: 1.5 * 2^-24 and 2.5 * 2^-24 round to even (2 * 2^-24)
-    x = np.array([1.5 * 2.0 ** -24, 2.5 * 2.0 ** -24, 2.0 ** -20 * (1 + 2.0 ** -7)], dtype=np.float32)
-    v, sat, _ = R.canonicalize(synth.f32_to_bf16_bits(x))
-    assert v.tolist() == [2 * 2.0 ** -24, 2 * 2.0 ** -24, 2.0 ** -20] and not sat
-    # in the normal fp16 range bf16 -> fp16 is exact
+    # small values are kept as given, down to the smallest bf16 subnormal 2^-133 = 0x0001
+    b = np.array([0x33C0, 0x0001, 0x8001, 0x0080, 0x0000, 0x8000], dtype=np.uint16)
+    v, sat, nan = R.canonicalize(b)
+    assert v.tolist() == [1.5 * 2.0 ** -24, 2.0 ** -133, -2.0 ** -133, 2.0 ** -126, 0.0, 0.0] and not sat and not nan
+    assert math.copysign(1, v[5]) == -1
+    # every finite bf16 value within +-2^16 is its own canonical value, and bf16_bits inverts
     rng = np.random.default_rng(2)
-    b = synth.f32_to_bf16_bits(rng.standard_normal(5000).astype(np.float32) * 100)
+    b = synth.f32_to_bf16_bits((rng.standard_normal(5000) * np.exp(rng.uniform(-80, 10, 5000))).astype(np.float32))
     v = R.canonicalize(b)[0]
-    assert np.array_equal(v, R.bf16_to_f64(b))
+    assert np.array_equal(v, R.bf16_to_f64(b)) and np.array_equal(R.bf16_bits(v), b)
 
 
 def test_synth_bf16_rounding_half_even():
@@ -102,12 +105,12 @@ def test_sign_vector_splitmix64_reference_values():
 
 
 def test_canonicalize_non_finite_inputs():
-    """Infinities saturate like any value beyond fp16; a NaN (which the pages' finite
+    """Infinities saturate like any value beyond +-2^16; a NaN (which the pages' finite
     tensors never hold) is stored as 0 and reported, so one NaN cannot poison a tile's
     scales: a prefill with a NaN raises FLAG_NAN and quantizes that element as a zero."""
     bits = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x3F80], dtype=np.uint16)  # +inf -inf nan -nan 1
     v, sat, nan = R.canonicalize(bits)
-    assert v.tolist() == [65504.0, -65504.0, 0.0, 0.0, 1.0] and sat and nan
+    assert v.tolist() == [65536.0, -65536.0, 0.0, 0.0, 1.0] and sat and nan
     v, sat, nan = R.canonicalize(np.array([0x3F80, 0xC000], dtype=np.uint16))
     assert not sat and not nan
     k, v2 = synth.kv_host(3, 1, 40, 1)
