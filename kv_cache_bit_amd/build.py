@@ -15,6 +15,9 @@ LIB = os.path.join(HERE, "libkvarn.so")
 # a measurement kernel of the benchmark (streaming reads and writes), kept out of libkvarn
 BENCH_SOURCES = ["stream_mix.hip"]
 BENCH_LIB = os.path.join(HERE, "libkvarn_bench.so")
+# the same library with the rotation as a VALU butterfly instead of the matrix cores, built
+# only to measure the one against the other (KVARN_LIB=<this file> selects it in the binding)
+FWHT_LIB = os.path.join(HERE, "libkvarn_fwht.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -31,9 +34,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(sources, lib, verbose):
+def _compile(sources, lib, verbose, defines=()):
     tmp = lib + ".tmp"
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
+    cmd = [hipcc(), *FLAGS, *defines, *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -78,9 +81,11 @@ def build_sanitized(out: str, verbose: bool = False) -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into kv_cache_bit_amd/libkvarn.so (and the benchmark's
-    measurement kernel into libkvarn_bench.so); returns the library's path."""
+    measurement kernel into libkvarn_bench.so, the butterfly-rotation build into
+    libkvarn_fwht.so); returns the library's path."""
     _compile(SOURCES, LIB, verbose)
     _compile(BENCH_SOURCES, BENCH_LIB, verbose)
+    _compile(SOURCES, FWHT_LIB, verbose, defines=("-DKVARN_ROTATION_BUTTERFLY=1",))
     return LIB
 
 

@@ -80,7 +80,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, uint8_t* cac
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) av[mb][ks] = sign8(raw[mb][ks], m[ks]);
-      d[mb] = rotate_squares_mb_v<ABL>(idr, av[mb], hf, w4[mb], p[mb], c);
+      d[mb] = rotate_squares_mb_v<ABL>(idr, av[mb], hf, w4[mb], p[mb], c, sh.xt[sub]);
       __builtin_amdgcn_sched_barrier(0);
     }
     st = gram_own_v<ABL>(idr, d[0], d[1], c);
@@ -96,7 +96,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, uint8_t* cac
           asm volatile("" : "+v"(r));
           return *reinterpret_cast<const uint4*>(r + mb * row16 + 32 * ks);
         },
-        hdr, hf, av, w4, p, g, c, flags, sx_own);
+        hdr, hf, av, w4, p, g, c, flags, sx_own, sh.xt[sub]);
 
   float* dw = nullptr;
   float* dy = nullptr;
@@ -208,9 +208,10 @@ __global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
   }
   float p[2][8][4];
   f4v w4[2][8];
-  float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+  float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c, sh.xt[sub]);
   int sx_own = 0;
-  if (__any(!rotation_stands(idr, st))) st = rotate_checked<ABL>(idr, load, hdr, hf, av, w4, p, g, c, flags, sx_own);
+  if (__any(!rotation_stands(idr, st)))
+    st = rotate_checked<ABL>(idr, load, hdr, hf, av, w4, p, g, c, flags, sx_own, sh.xt[sub]);
   tile_finish<NW, false, ABL>(av, hf, w4, p, st, sx_own, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr,
                               nullptr, 0);
   if (valid) {

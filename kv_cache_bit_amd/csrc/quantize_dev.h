@@ -312,6 +312,109 @@ __device__ __forceinline__ void rotate_block(const b8v (&a)[2][4], const Frags& 
   }
 }
 
+// ----------------------------------------------------------------------------- butterfly form
+// The library built with KVARN_ROTATION_BUTTERFLY=1 (libkvarn_fwht.so, for measurement only)
+// rotates on the VALU instead of the matrix cores: a 128-point fast Walsh-Hadamard
+// transform. Lane (g, c) holds token 16 mb + c, channels k = 32 ks + 8 g + e: bits 0..2
+// and 5..6 of k are in the lane's registers, bits 3..4 are lane bits 4..5. The five stages
+// on the register bits are adds; a stage on a lane bit pairs two registers whose channels
+// differ in bit 5 or 6 and swaps half of the lanes of each with v_permlane16_swap or
+// v_permlane32_swap, which leaves that lane bit and that register bit exchanged. After
+// both, register (ks, e) of lane (g, c) holds output channel 32 g + 8 ks + e, and the
+// block goes through LDS (xt[token][channel], rows of 132 floats: 16-B aligned writes, and
+// the four rows g of one read on different banks) into the layout the MFMA path leaves
+// and VarN works on. The token's sum of squares (the first token-axis pass) is summed in
+// the input layout, where gram_own finds it.
+#ifndef KVARN_ROTATION_BUTTERFLY
+#define KVARN_ROTATION_BUTTERFLY 0
+#endif
+constexpr int kXtRow = 132;
+__device__ __forceinline__ float fwht_squares_mb(const b8v (&a)[4], f4v (&w4)[8], float (&p)[8][4], int c,
+                                                 float* xt) {
+  const int g = (int)(threadIdx.x & 63) >> 4;
+  float x[4][8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 u = __builtin_bit_cast(uint4, a[ks]);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      x[ks][2 * d] = bf16lo(w[d]);
+      x[ks][2 * d + 1] = bf16hi(w[d]);
+    }
+  }
+  float d = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d = fmaf(x[ks][e], x[ks][e], d);
+  {  // over the four lanes g that hold the token's channels
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_int(d), __float_as_int(d), false, false);
+    d = __int_as_float(s1[0]) + __int_as_float(s1[1]);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_int(d), __float_as_int(d), false, false);
+    d = __int_as_float(s2[0]) + __int_as_float(s2[1]);
+  }
+#pragma unroll
+  for (int b = 1; b < 8; b <<= 1)  // channel bits 0..2
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!(e & b)) {
+          const float u = x[ks][e], v = x[ks][e | b];
+          x[ks][e] = u + v;
+          x[ks][e | b] = u - v;
+        }
+#pragma unroll
+  for (int b = 1; b < 4; b <<= 1)  // channel bits 5..6
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      if (!(ks & b))
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float u = x[ks][e], v = x[ks | b][e];
+          x[ks][e] = u + v;
+          x[ks | b][e] = u - v;
+        }
+  // channel bit 4 (lane bit 5) against register bit ks/2, then bit 3 (lane bit 4) against ks%2
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const auto t = __builtin_amdgcn_permlane32_swap(__float_as_int(x[ks][e]), __float_as_int(x[ks + 2][e]),
+                                                      false, false);
+      x[ks][e] = __int_as_float(t[0]) + __int_as_float(t[1]);
+      x[ks + 2][e] = __int_as_float(t[0]) - __int_as_float(t[1]);
+    }
+#pragma unroll
+  for (int ks = 0; ks < 4; ks += 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const auto t = __builtin_amdgcn_permlane16_swap(__float_as_int(x[ks][e]), __float_as_int(x[ks + 1][e]),
+                                                      false, false);
+      x[ks][e] = __int_as_float(t[0]) + __int_as_float(t[1]);
+      x[ks + 1][e] = __int_as_float(t[0]) - __int_as_float(t[1]);
+    }
+  // to the MFMA output layout: lane (g, c) takes tokens 4 g + i of channel 16 nb + c
+  wave_sync();  // the previous block's reads are issued before these writes
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    float* row = xt + c * kXtRow + 32 * g + 8 * ks;
+    *reinterpret_cast<float4*>(row) = make_float4(x[ks][0], x[ks][1], x[ks][2], x[ks][3]);
+    *reinterpret_cast<float4*>(row + 4) = make_float4(x[ks][4], x[ks][5], x[ks][6], x[ks][7]);
+  }
+  wave_sync();
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = xt[(4 * g + i) * kXtRow + 16 * nb + c];
+      w4[nb][i] = v;
+      p[nb][i] = v * v;
+    }
+  return d;
+}
+
 // Rotation fused with the squares: each chain's W' block is squared as soon as it is
 // complete, so the fp32 block is never held whole. Returns the first token-axis sum
 // (u = 1) of the lane's own token, 16 (c/8) + 4 g + (c/2) % 4 (identical in lanes c and
@@ -323,7 +426,8 @@ __device__ __forceinline__ void rotate_block(const b8v (&a)[2][4], const Frags& 
 // the diagonal sits in lanes c = 4 g + j at element j, and the owner lane fetches it.
 template <bool ID>
 __device__ __forceinline__ float rotate_squares_mb(const b8v (&a)[4], const Frags& hf, f4v (&w4)[8], float (&p)[8][4],
-                                                   int c) {
+                                                   int c, float* xt) {
+  if constexpr (!ID && KVARN_ROTATION_BUTTERFLY) return fwht_squares_mb(a, w4, p, c, xt);
   // the Gram block first: the token block's inputs are dead once its rotation is done
   f4v gm = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -369,9 +473,9 @@ __device__ __forceinline__ float gram_own(float d0, float d1, int c) {
 }
 template <bool ID>
 __device__ __forceinline__ float rotate_squares(const b8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
-                                                float (&p)[2][8][4], int c) {
-  const float d0 = rotate_squares_mb<ID>(a[0], hf, w4[0], p[0], c);
-  const float d1 = rotate_squares_mb<ID>(a[1], hf, w4[1], p[1], c);
+                                                float (&p)[2][8][4], int c, float* xt) {
+  const float d0 = rotate_squares_mb<ID>(a[0], hf, w4[0], p[0], c, xt);
+  const float d1 = rotate_squares_mb<ID>(a[1], hf, w4[1], p[1], c, xt);
   return gram_own<ID>(d0, d1, c);
 }
 
@@ -379,19 +483,19 @@ __device__ __forceinline__ float rotate_squares(const b8v (&a)[2][4], const Frag
 // the standard build compiles the Hadamard path only.
 template <bool ABL>
 __device__ __forceinline__ float rotate_squares_v(bool idr, const b8v (&a)[2][4], const Frags& hf, f4v (&w4)[2][8],
-                                                  float (&p)[2][8][4], int c) {
+                                                  float (&p)[2][8][4], int c, float* xt) {
   if constexpr (ABL) {
-    if (idr) return rotate_squares<true>(a, hf, w4, p, c);
+    if (idr) return rotate_squares<true>(a, hf, w4, p, c, xt);
   }
-  return rotate_squares<false>(a, hf, w4, p, c);
+  return rotate_squares<false>(a, hf, w4, p, c, xt);
 }
 template <bool ABL>
 __device__ __forceinline__ float rotate_squares_mb_v(bool idr, const b8v (&a)[4], const Frags& hf, f4v (&w4)[8],
-                                                     float (&p)[8][4], int c) {
+                                                     float (&p)[8][4], int c, float* xt) {
   if constexpr (ABL) {
-    if (idr) return rotate_squares_mb<true>(a, hf, w4, p, c);
+    if (idr) return rotate_squares_mb<true>(a, hf, w4, p, c, xt);
   }
-  return rotate_squares_mb<false>(a, hf, w4, p, c);
+  return rotate_squares_mb<false>(a, hf, w4, p, c, xt);
 }
 template <bool ABL>
 __device__ __forceinline__ float gram_own_v(bool idr, float d0, float d1, int c) {
@@ -451,7 +555,8 @@ __device__ __forceinline__ float rows_max4(float x) {
 // that maps W' to Y, which the owner lane corrects with its token's sx (sx_own).
 template <bool ABL, typename Load>
 __device__ float rotate_checked(bool idr, Load&& load, const uint8_t* hdr, const Frags& hf, b8v (&av)[2][4],
-                                f4v (&w4)[2][8], float (&p)[2][8][4], int g, int c, uint32_t& flags, int& sx_own) {
+                                f4v (&w4)[2][8], float (&p)[2][8][4], int g, int c, uint32_t& flags, int& sx_own,
+                                float* xt) {
   // two passes over the rows (the second reads them again rather than holding them):
   // each token's largest magnitude, then the scaled, signed operands
   float mx[2] = {0.0f, 0.0f};
@@ -477,7 +582,7 @@ __device__ float rotate_checked(bool idr, Load&& load, const uint8_t* hdr, const
       av[mb][ks] = sign8(sx[mb] ? scale8(x, sx[mb]) : x, m);
     }
   }
-  const float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+  const float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c, xt);
   // the owner lane of token 16 (c/8) + 4 g + (c/2) % 4 reads sx where that token is an A row
   const int src = 4 * (20 * g + ((c >> 1) & 3));
   const int s0 = __builtin_amdgcn_ds_bpermute(src, sx[0]), s1 = __builtin_amdgcn_ds_bpermute(src, sx[1]);
@@ -506,6 +611,7 @@ struct TileLds {
   float red_b[NW][kD];
   float gcol[NW][kD] __attribute__((aligned(16)));  // per-wave gather buffers
   float grow[NW][32] __attribute__((aligned(16)));
+  float xt[NW][KVARN_ROTATION_BUTTERFLY ? 16 * kXtRow : 1] __attribute__((aligned(16)));  // butterfly form only
 };
 
 // Per-channel reduction of a tile: 4-row reduce-scatter inside the wave, then (G=64)
@@ -1042,9 +1148,10 @@ __device__ void append_job(const AppendArgs& a, int job, int sub, int lane, Tile
     }
     float p[2][8][4];
     f4v w4[2][8];
-    float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c);
+    float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c, sh.xt[sub]);
     int sx_own = 0;
-    if (__any(!rotation_stands(idr, st))) st = rotate_checked<ABL>(idr, load, hdr, hf, av, w4, p, g, c, flags, sx_own);
+    if (__any(!rotation_stands(idr, st)))
+      st = rotate_checked<ABL>(idr, load, hdr, hf, av, w4, p, g, c, flags, sx_own, sh.xt[sub]);
     tile_finish<NW, false, ABL>(av, hf, w4, p, st, sx_own, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags,
                                 nullptr, nullptr, 0);
     const long long ro = record_at(a.cache, L, b, h, (pos + 1) / G - 1, s);

@@ -51,19 +51,21 @@ def check_asm(text: str) -> list[str]:
 
 
 def main() -> int:
-    with tempfile.TemporaryDirectory() as tmp:
-        bad = []
-        for src in B.SOURCES:
-            cmd = [B.hipcc(), *[f for f in B.FLAGS if f != "-shared"], "-c", os.path.join(B.CSRC, src),
-                   "-o", os.path.join(tmp, src + ".o"), "--save-temps"]
-            subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
-            for f in os.listdir(tmp):
-                if f.endswith(".s") and "gfx950" in f and f.startswith(src.split(".")[0]):
-                    bad += check_asm(open(os.path.join(tmp, f)).read())
-        for b in bad:
-            print("MFMA destination overlaps a source:", b)
-        print("isa_check:", "FAIL" if bad else "ok")
-        return 1 if bad else 0
+    bad = []
+    # the library and its butterfly-rotation build (libkvarn_fwht.so)
+    for defines in ((), ("-DKVARN_ROTATION_BUTTERFLY=1",)):
+        with tempfile.TemporaryDirectory() as tmp:
+            for src in B.SOURCES:
+                cmd = [B.hipcc(), *[f for f in B.FLAGS if f != "-shared"], *defines, "-c",
+                       os.path.join(B.CSRC, src), "-o", os.path.join(tmp, src + ".o"), "--save-temps"]
+                subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
+                for f in os.listdir(tmp):
+                    if f.endswith(".s") and "gfx950" in f and f.startswith(src.split(".")[0]):
+                        bad += check_asm(open(os.path.join(tmp, f)).read())
+    for b in bad:
+        print("MFMA destination overlaps a source:", b)
+    print("isa_check:", "FAIL" if bad else "ok")
+    return 1 if bad else 0
 
 
 if __name__ == "__main__":
