@@ -59,22 +59,33 @@ struct OpMax { __device__ float operator()(float a, float b) const { return vmax
 // lane c with c^15, c^7, c^2, c^1 (row_mirror, row_half_mirror, quad perms); at each
 // stage a lane keeps half of its tokens (chosen by bits 3, 2, 1 of c) and adds the
 // partner's partial of the same tokens. Lane c ends with the row total of token
-// c/2 (identical in lanes c and c^1).
+// c/2 (identical in lanes c and c^1). The first two stages choose by lane bits 3 and 2,
+// which are bits of the DPP bank (4 lanes): each kept value is two DPP adds that write
+// complementary banks, instead of two selects and an add.
 __device__ __forceinline__ float row_rs8(const float (&v)[8], int c) {
-  const bool b3 = c & 8, b2 = c & 4, b1 = c & 2;
-  float a[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float send = b3 ? v[k] : v[k + 4], keep = b3 ? v[k + 4] : v[k];
-    a[k] = keep + dppf<kMirror>(send);
-  }
-  float bb[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float send = b2 ? a[k] : a[k + 2], keep = b2 ? a[k + 2] : a[k];
-    bb[k] = keep + dppf<kHalfMirror>(send);
-  }
-  const float send = b1 ? bb[0] : bb[1], keep = b1 ? bb[1] : bb[0];
+  const bool b1 = c & 2;
+  float a0, a1, a2, a3, bb0, bb1;
+  // lanes 0..7 of a row (banks 0, 1) keep tokens 0..3, lanes 8..15 (banks 2, 3) tokens 4..7
+  asm("s_nop 1\n"
+      "v_add_f32_dpp %0, %4, %4 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %0, %8, %8 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %1, %5, %5 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %1, %9, %9 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %2, %6, %6 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %2, %10, %10 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %3, %7, %7 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %3, %11, %11 row_mirror row_mask:0xf bank_mask:0xc"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+  // lanes with bit 2 clear (banks 0, 2) keep the first two, the others the last two
+  asm("s_nop 1\n"
+      "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %1, %3, %3 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0xa"
+      : "=&v"(bb0), "=&v"(bb1)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+  const float send = b1 ? bb0 : bb1, keep = b1 ? bb1 : bb0;
   const float d = keep + dppf<kQx2>(send);
   return d + dppf<kQx1>(d);
 }
