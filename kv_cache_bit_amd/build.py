@@ -83,9 +83,12 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source into kv_cache_bit_amd/libkvarn.so (and the benchmark's
     measurement kernel into libkvarn_bench.so, the butterfly-rotation build into
     libkvarn_fwht.so); returns the library's path."""
-    _compile(SOURCES, LIB, verbose)
-    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
-    _compile(SOURCES, FWHT_LIB, verbose, defines=("-DKVARN_ROTATION_BUTTERFLY=1",))
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(SOURCES, LIB, ()), (BENCH_SOURCES, BENCH_LIB, ()),
+            (SOURCES, FWHT_LIB, ("-DKVARN_ROTATION_BUTTERFLY=1",))]
+    with ThreadPoolExecutor(len(jobs)) as ex:  # independent hipcc processes
+        for f in [ex.submit(_compile, s, lib, verbose, d) for s, lib, d in jobs]:
+            f.result()
     return LIB
 
 

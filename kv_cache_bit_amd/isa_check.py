@@ -5,7 +5,7 @@ wrong results on gfx950 (rows read after the first pass see the partial output).
 The compiler may allocate such a destination when a source dies at that MFMA; the
 kernels keep their sources alive, and this check verifies it on the generated code.
 
-Usage: python -m kv_cache_bit_amd.isa_check   (compiles with --save-temps into a temp dir)
+Usage: python -m kv_cache_bit_amd.isa_check   (compiles the device code to assembly in a temp dir)
 """
 from __future__ import annotations
 
@@ -50,18 +50,31 @@ def check_asm(text: str) -> list[str]:
     return bad
 
 
+def device_asm(src: str, defines: tuple, tmp: str) -> str:
+    """The gfx950 assembly of one source, as the library build compiles it."""
+    out = os.path.join(tmp, src + ".s")
+    cmd = [B.hipcc(), *[f for f in B.FLAGS if f != "-shared"], *defines, "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    with open(out) as f:
+        return f.read()
+
+
 def main() -> int:
-    bad = []
-    # the library and its butterfly-rotation build (libkvarn_fwht.so)
-    for defines in ((), ("-DKVARN_ROTATION_BUTTERFLY=1",)):
-        with tempfile.TemporaryDirectory() as tmp:
-            for src in B.SOURCES:
-                cmd = [B.hipcc(), *[f for f in B.FLAGS if f != "-shared"], *defines, "-c",
-                       os.path.join(B.CSRC, src), "-o", os.path.join(tmp, src + ".o"), "--save-temps"]
-                subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
-                for f in os.listdir(tmp):
-                    if f.endswith(".s") and "gfx950" in f and f.startswith(src.split(".")[0]):
-                        bad += check_asm(open(os.path.join(tmp, f)).read())
+    from concurrent.futures import ThreadPoolExecutor
+    # the library and its butterfly-rotation build (libkvarn_fwht.so), one hipcc per source
+    variants = ((), ("-DKVARN_ROTATION_BUTTERFLY=1",))
+    with tempfile.TemporaryDirectory() as tmp, ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        jobs = []
+        for i, defines in enumerate(variants):
+            d = os.path.join(tmp, str(i))
+            os.makedirs(d)
+            jobs += [ex.submit(device_asm, src, defines, d) for src in B.SOURCES]
+        texts = [j.result() for j in jobs]
+    if sum(t.count("v_mfma") for t in texts) == 0:
+        print("isa_check: no MFMA found in the generated code")
+        return 1
+    bad = [b for t in texts for b in check_asm(t)]
     for b in bad:
         print("MFMA destination overlaps a source:", b)
     print("isa_check:", "FAIL" if bad else "ok")
