@@ -486,19 +486,27 @@ def _oracle_decode_row(job):
 
 
 def _pool_map(fn, jobs, workers):
-    """Run jobs in `workers` fresh processes (spawned: they never touch the GPU); every
-    worker has exited when this returns. Returns (results, wall seconds)."""
-    import multiprocessing as mp
-    ctx = mp.get_context("spawn")
-    pool = ctx.Pool(workers)
-    try:
-        t0 = time.perf_counter()
-        out = pool.map(fn, jobs, chunksize=1)
-        wall = time.perf_counter() - t0
-    finally:
-        pool.close()
-        pool.join()
-    return out, wall
+    """Run fn(job) for every job in a child interpreter of its own, at most `workers` at a
+    time. The children are plain subprocesses: they never touch the GPU, every one of them
+    has exited when this returns, and no helper process (such as the multiprocessing
+    module's resource tracker) is left running. Returns (results, wall seconds from the
+    first job's start to the last job's end)."""
+    import subprocess
+    from concurrent.futures import ThreadPoolExecutor
+    root = os.path.dirname(os.path.abspath(__file__))
+    prog = ("import json, sys, time; import bench; t0 = time.time(); "
+            "r = getattr(bench, sys.argv[1])(json.loads(sys.argv[2])); print(json.dumps([r, t0, time.time()]))")
+
+    def run(job):
+        p = subprocess.run([sys.executable, "-c", prog, fn.__name__, json.dumps(list(job))], cwd=root,
+                           capture_output=True, text=True, timeout=900)
+        if p.returncode != 0:
+            raise RuntimeError(f"oracle worker failed ({p.returncode}): {p.stderr[-2000:]}")
+        return json.loads(p.stdout.strip().splitlines()[-1])
+
+    with ThreadPoolExecutor(workers) as ex:  # threads only wait on the children
+        res = list(ex.map(run, jobs))
+    return [r[0] for r in res], max(r[2] for r in res) - min(r[1] for r in res)
 
 
 def host_cores():
