@@ -294,8 +294,9 @@ def test_attention_more_spans_than_merge_groups(G, T, min_spans):
 
 # ----------------------------------------------------------------------------- full-size spot checks
 def test_full_size_llama_layer_prefill_sampled():
-    """Llama-3.1-8B-shaped layer (8 KV heads, 32768 tokens, G=32, 3 iterations), the
-    benchmark's launch configuration; 64 sampled tiles through the full chain."""
+    """Llama-3.1-8B-shaped layer (8 KV heads, 32768 tokens, G=32, 3 iterations) through the
+    per-layer call, as the benchmark's per-layer line launches it; 64 sampled tiles through
+    the full chain."""
     say("full-size prefill layer")
     torch.manual_seed(0)
     kd, vd = synth.kv_device(synth.sub_seed(2, 0, 0), 1, 32768, 8)
@@ -312,6 +313,42 @@ def test_full_size_llama_layer_prefill_sampled():
         v[0, t * 32:(t + 1) * 32, h] = to_u16(vd[0, t * 32:(t + 1) * 32, h])
     st = check_prefill(gc, k, v, 32768, tiles=picks)
     say("stats", st)
+
+
+def test_full_size_llama_32_layer_prefill_sampled():
+    """The benchmark's headline launch: the 32 Llama-3.1-8B-shaped layers (8 KV heads, 32768
+    tokens each, G=32, 3 iterations, the benchmark's inputs and sign vector) quantized by one
+    kvarn_quantize_prefill_layers call. Sampled tiles of the first, a middle and the last
+    layer (their corner tiles included) go through the full chain against the oracle, and
+    the last layer's cache equals, byte for byte, a per-layer call on the same input."""
+    say("full-size 32-layer prefill launch")
+    layers, T, H = 32, 32768, 8
+    ks, vs = [], []
+    for l in range(layers):
+        k, v = synth.kv_device(synth.sub_seed(2, l, 0), 1, T, H)
+        ks.append(k)
+        vs.append(v)
+    caches = [GpuCache(1, H, T) for _ in range(layers)]
+    K.kvarn_quantize_prefill_layers(caches[0].g, [c.buf for c in caches], ks, vs, T)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for l in (0, 13, layers - 1):
+        picks = sorted({(0, int(rng.integers(H)), int(rng.integers(T // 32))) for _ in range(16)}
+                       | {(0, 0, 0), (0, H - 1, T // 32 - 1)})
+        k = np.zeros((1, T, H, 128), dtype=np.uint16)
+        v = np.zeros_like(k)
+        for _, h, t in picks:
+            k[0, t * 32:(t + 1) * 32, h] = to_u16(ks[l][0, t * 32:(t + 1) * 32, h])
+            v[0, t * 32:(t + 1) * 32, h] = to_u16(vs[l][0, t * 32:(t + 1) * 32, h])
+        st = check_prefill(caches[l], k, v, T, tiles=picks)
+        say("layer", l, "stats", st)
+    one = GpuCache(1, H, T)
+    K.kvarn_quantize_prefill(one.g, one.buf, ks[-1], vs[-1], T)
+    torch.cuda.synchronize()
+    ha, hb = caches[-1].host_cache(), one.host_cache()
+    m = ha.defined_mask()
+    assert np.array_equal(ha.buf[m], hb.buf[m])
+    assert K.kvarn_cache_flags(caches[-1].buf) == K.kvarn_cache_flags(one.buf)
 
 
 def test_full_size_phi4_decode_sampled():
