@@ -265,7 +265,7 @@ def dequantize_tile(q, r16, c16, s16, z16) -> np.ndarray:
             * (np.asarray(z16)[..., None, :] + np.asarray(s16)[..., None, :] * q))
 
 
-# ----------------------------------------------------------------------------- tile record (format v2)
+# ----------------------------------------------------------------------------- tile record (unchanged since format v2)
 def record_bytes(g: int, d: int, bits: int = 2) -> int:
     """codes G*D*bits/8 | r fp16[G] | c fp16[D] | s fp16[D] | z fp16[D]."""
     return g * d * bits // 8 + 2 * g + 6 * d
@@ -397,7 +397,7 @@ def unpack_record(rec, g: int, d: int, stream: int, bits: int = 2) -> dict:
                 s16=f(n + 2 * g + 2 * d, d), z16=f(n + 2 * g + 4 * d, d))
 
 
-# ----------------------------------------------------------------------------- cache buffer (format v2)
+# ----------------------------------------------------------------------------- cache buffer (format v3)
 class Geom:
     """batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant (VARIANT_* bits),
     num_pages (0: tiles stored per sequence; > 0: a pool of pages found through a page map)."""
