@@ -24,6 +24,9 @@ HIP graph). Beside it:
   * roundtrip: Qwen3-4B-shaped prefill (36 layers x 8 KV heads, batch 8 x 16384
     tokens, group 64, 2 VarN iterations) followed by a bf16 dequantization of every
     layer, with both kernels' launch times and algorithmic GB/s;
+  * paged_chunked: decode attention of one Phi-4-shaped layer over a paged cache (a
+    shuffled page map) against the per-sequence layout, and a Llama-3.1-8B-shaped layer
+    written as 4 chunks by kvarn_append_tokens against one prefill call;
   * cpu_baseline: the CPU oracle on a bounded sample of the same workloads, one
     single-threaded process per host core used (at most --cpu-workers).
 
@@ -356,6 +359,103 @@ def bench_roundtrip(K, synth, torch, steps, warmup=2, layers=36, B=8, T=16384, H
     }
 
 
+def bench_paged_chunked(K, synth, torch, reps=5, calls=20, bits=2):
+    """The paged and ragged row, each measured beside the per-sequence layout it replaces:
+    decode attention of one Phi-4-shaped layer (B = 32, 10 KV heads, 40 query heads, 16,900
+    stored tokens) over a paged cache whose page map is a seeded permutation of the pool,
+    against the same tokens in a per-sequence cache (calls alternate between the two); and
+    a Llama-3.1-8B-shaped layer (32,768 tokens, 8 KV heads) written as 4 chunks of 8,192
+    tokens by kvarn_append_tokens into an emptied cache, against one kvarn_quantize_prefill
+    of all of it. Event-timed, `calls` calls per sample, best of `reps` samples."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+    sig = synth.sign_vector(0)
+    B, H, Hq, cap, ctx, G, n_it = 32, 10, 40, 17408, 16900, 32, 3
+    tiles = cap // G
+    log(f"paged attention workload: B={B} x Hkv={H} x Hq={Hq}, {ctx} tokens, pool of {B * tiles} pages")
+    gs = K.geom(B, H, cap, G, n_it, bits=bits)
+    gp = K.geom(B, H, cap, G, n_it, bits=bits, num_pages=B * tiles)
+    k, v = synth.kv_device(synth.sub_seed(4, 0, 0), B, ctx, H)
+    cs, cp = K.alloc_cache(gs, sig), K.alloc_cache(gp, sig)
+    perm = np.random.default_rng(11).permutation(B * tiles).reshape(B, tiles).astype(np.int32)
+    K.kvarn_cache_set_pages(gp, cp, torch.from_numpy(perm).cuda(), 0, tiles)
+    K.kvarn_quantize_prefill(gs, cs, k, v, ctx)
+    K.kvarn_quantize_prefill(gp, cp, k, v, ctx)
+    del k, v
+    q = synth.q_device(synth.sub_seed(4, 0, 2, 0), B, Hq)
+    runs = {}
+    for name, g, c in (("per_sequence", gs, cs), ("paged", gp, cp)):
+        ws, nws = K.alloc_workspace(g, Hq)
+        runs[name] = (g, c, ws, nws, torch.empty(B, Hq, 128, device="cuda"))
+
+    def attn(name):
+        g, c, ws, nws, out = runs[name]
+        K.kvarn_attn_decode(g, c, q, Hq, 0.0, 0, ws, nws, out, stream)
+
+    def timed(fns, n):
+        best = {}
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            for f in fns:
+                e0.record(stream)
+                for _ in range(n):
+                    f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / n
+                best[f] = min(best.get(f, us), us)
+        return [best[f] for f in fns]
+
+    us_seq, us_pg = timed([lambda: attn("per_sequence"), lambda: attn("paged")], calls)
+    nfull = ctx // G
+    bytes_seq = B * H * (2 * nfull * record_bytes(G, bits) + 2 * (ctx % G) * 256) + B * Hq * (256 + 512)
+    bytes_pg = bytes_seq + B * nfull * 4  # plus the page map entries
+    same = torch.equal(runs["per_sequence"][4], runs["paged"][4])
+    paged = {"workload": f"phi-4-14b-shaped decode attention, one layer, {ctx} stored tokens per sequence",
+             "page_map": "a seeded permutation of a pool of B x capacity/G pages",
+             "us_per_call_paged": round(us_pg, 2), "us_per_call_per_sequence": round(us_seq, 2),
+             "paged_over_per_sequence": round(us_pg / us_seq, 4), "bytes_per_call": bytes_pg,
+             "achieved_paged": round(bytes_pg / (us_pg * 1e-6) / 1e9, 1),
+             "frac_paged": round(bytes_pg / (us_pg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+             "outputs_bit_equal": bool(same)}
+    log(f"paged attention: {paged}")
+    del runs, cs, cp
+    torch.cuda.empty_cache()
+
+    Bc, Tc, Hc, nch = 1, 32768, 8, 4
+    gc = K.geom(Bc, Hc, Tc, G, n_it, bits=bits)
+    kc, vc = synth.kv_device(synth.sub_seed(2, 0, 0), Bc, Tc, Hc)
+    step = Tc // nch
+    chunks = [(kc[:, i * step:(i + 1) * step].contiguous(), vc[:, i * step:(i + 1) * step].contiguous())
+              for i in range(nch)]
+    ca, cb = K.alloc_cache(gc, sig), K.alloc_cache(gc, sig)
+
+    def one():
+        K.kvarn_quantize_prefill(gc, ca, kc, vc, Tc, stream)
+
+    def chunked():
+        K.kvarn_quantize_prefill(gc, cb, kc, vc, 0, stream)  # empties the cache (len = 0)
+        for kk, vv in chunks:
+            K.kvarn_append_tokens(gc, cb, kk, vv, step, None, stream)
+
+    us_one, us_ch = timed([one, chunked], 10)
+    bytes_in = 2 * 2 * Bc * Tc * Hc * 128
+    bytes_all = bytes_in + 2 * Bc * Hc * (Tc // G) * record_bytes(G, bits)
+    chunk = {"workload": f"llama3.1-8b-shaped layer, {Tc} tokens x {Hc} KV heads, {nch} chunks of {step} tokens "
+                         "appended to an emptied cache",
+             "us_one_prefill_call": round(us_one, 2), "us_chunked": round(us_ch, 2),
+             "chunked_over_one_call": round(us_ch / us_one, 4),
+             "value_chunked": round(bytes_in / (us_ch * 1e-6) / 1e9, 1), "unit": "GB/s bf16-in",
+             "frac_chunked": round(bytes_all / (us_ch * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"chunked prefill: {chunk}")
+    del ca, cb, kc, vc, chunks
+    torch.cuda.empty_cache()
+    return {"paged_attention": paged, "chunked_prefill": chunk}
+
+
 def bench_bf16_decode(torch, steps=8, warmup=2, layers=40, B=32, H=10, Hq=40, T=16384):
     """Plain bf16 decode attention over a bf16 KV cache of the same shapes (no quantization):
     per layer scores = q K^T (K stored transposed, [B][H][D][T]), fp32 softmax, out = p V,
@@ -596,6 +696,8 @@ def main():
                     help="skip the long-reasoning prefill and decode (64 x 32768-token contexts, Llama-3.1-8B KV geometry)")
     ap.add_argument("--no-roundtrip", action="store_true",
                     help="skip the Qwen3-4B-shaped prefill + dequantize round trip")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-attention and chunked-prefill measurements")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--cpu-workers", type=int, default=8,
@@ -745,6 +847,8 @@ def main():
         log(f"round trip: {rt['ms_per_step']} ms/step; prefill {rt['prefill']['avg_launch_us']} us "
             f"({rt['prefill']['achieved']} GB/s), dequantize {rt['dequantize']['avg_launch_us']} us "
             f"({rt['dequantize']['achieved']} GB/s) per layer")
+    if not args.no_paged:
+        res["paged_chunked"] = bench_paged_chunked(K, synth, torch, bits=args.bits)
     if not args.no_cpu:
         workers = max(1, min(args.cpu_workers, host_cores()))
         log(f"cpu baseline (oracle) on {workers} processes ...")

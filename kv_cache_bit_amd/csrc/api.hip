@@ -235,6 +235,8 @@ kvarn_status kvarn_append_tokens(const kvarn_geom* gin, void* cache, const void*
   const long long jobs = (long long)g->batch * a.max_tiles * 2 * g->num_kv_heads;
   if (jobs >= (1LL << 31)) return KVARN_ERR_RANGE;
   a.jobs = (int)jobs;
+  a.dhkv = make_fastdiv((uint32_t)g->num_kv_heads);
+  a.dmt = make_fastdiv((uint32_t)a.max_tiles);
   return dev(launch_tokens(a, static_cast<hipStream_t>(stream)));
 }
 

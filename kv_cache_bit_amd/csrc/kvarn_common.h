@@ -32,7 +32,7 @@ struct Geo {
   int32_t batch, num_kv_heads, head_dim, capacity, group, varn_iters, bits, variant, num_pages;
 };
 
-// Byte layout of one layer cache (format v2), computed on the host and passed by value.
+// Byte layout of one layer cache (format v3), computed on the host and passed by value.
 // Records are stored per sequence ([B][Hkv][tiles][2][TR]) or, for a paged cache
 // (num_pages > 0), in a pool of pages [num_pages][Hkv][2][TR] named by the page map
 // int32 [B][tiles] at map_off; record_at resolves either.

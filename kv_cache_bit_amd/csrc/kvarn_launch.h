@@ -36,6 +36,7 @@ struct TokensArgs {
   int T;
   int max_tiles;           // groups one sequence can complete: (G - 1 + T) / G
   int jobs;                // B * max_tiles * 2 * Hkv tile jobs
+  FastDiv dhkv, dmt;       // division by Hkv and by max_tiles
 };
 
 struct PrefillArgs {

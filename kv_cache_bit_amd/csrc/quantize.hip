@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(AppendArgs a) {
 // counts[b] tokens (T when counts is null) go after each sequence's stored ones, as that
 // many single-token appends would place them. Tile pass: each group the new tokens
 // complete is quantized from its stored tail tokens and the new input rows; job
-// (b, j, s, h) takes the j-th such group, 4/NW jobs per work-group, and jobs past the
+// (b, j, s, h) takes the j-th such group, one job per work-group, and jobs past the
 // sequence's last completed group run on clamped inputs and store nothing (the
 // work-group's barriers stay uniform). Tail pass, a second launch so that the tail is read
 // before it is overwritten: the new tokens after the last complete group go to the tail
@@ -164,21 +164,20 @@ __device__ __forceinline__ void tokens_range(const TokensArgs& a, int b, int h, 
 }
 
 template <int NW, bool ABL>
-__global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
-  constexpr int TPW = 4 / NW;
+__global__ __launch_bounds__(64 * NW) void tokens_tile_kernel(TokensArgs a) {
   constexpr int G = 32 * NW;
-  __shared__ TileLds<NW> sh_all[TPW];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ TileLds<NW> sh;
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const int tw = wave / NW, sub = wave % NW;
-  TileLds<NW>& sh = sh_all[tw];
   const Layout& L = a.L;
   uint8_t* hdr = a.cache;
-  int job = blockIdx.x * TPW + tw;
-  const bool in_grid = job < a.jobs;
-  if (!in_grid) job = 0;
-  const int h = job % L.Hkv, s = (job / L.Hkv) % 2, j = (job / L.Hkv / 2) % a.max_tiles;
-  const int b = job / L.Hkv / 2 / a.max_tiles;
+  uint32_t job = blockIdx.x;
+  const bool in_grid = job < (uint32_t)a.jobs;
+  if (!in_grid) job = 0;  // keep the barrier sequence uniform; results are discarded
+  // job = ((b * max_tiles + j) * 2 + s) * Hkv + h: neighbouring work-groups read neighbouring heads
+  const uint32_t q1 = fdiv(job, a.dhkv), q2 = q1 >> 1, q3 = fdiv(q2, a.dmt);
+  const int h = (int)(job - q1 * (uint32_t)L.Hkv), s = (int)(q1 & 1u);
+  const int j = (int)(q2 - q3 * (uint32_t)a.max_tiles), b = (int)q3;
   int l0, l1;
   bool dropped;
   tokens_range(a, b, h, s, l0, l1, dropped);
@@ -188,30 +187,49 @@ __global__ __launch_bounds__(256) void tokens_tile_kernel(TokensArgs a) {
   const Frags hf = frags_v<ABL>(idr, lane);
   const uint16_t* src = (s ? a.v : a.k) + ((long long)b * a.T * L.Hkv + h) * kD;  // + row * Hkv * D
   uint32_t flags = 0;
-  // token 16 mb + c of this wave's block, channels 8 (4 ks + g) .. +7: stored in the tail,
-  // or a new token (canonical; its flags count where the job is valid)
-  auto load = [&](int mb, int ks) -> uint4 {
+  // token 16 mb + c of this wave's block, channels 8 (4 ks + g) .. +7, as given: stored in
+  // the tail (canonical already), or a new input row (clamped in range for the rows of a
+  // job that stores nothing). As in the prefill, the values go into the rotation as they
+  // are, and a token whose sum of squares leaves the range takes the checked rotation,
+  // which canonicalizes and raises the flags.
+  auto row = [&](int mb, int ks, const uint16_t* sp, const uint8_t* cp) -> uint4 {
     const int tt = tile * G + sub * 32 + 16 * mb + c;  // token of this A row in the sequence
-    if (tt < l0) return *reinterpret_cast<const uint4*>(a.cache + L.tail_row(b, h, s, tt % G) + 16 * (4 * ks + g));
-    const int row = min(tt - l0, a.T - 1);
-    uint32_t f = 0;
-    const uint4 w = canon8(*reinterpret_cast<const uint4*>(src + (long long)row * L.Hkv * kD + 8 * (4 * ks + g)), f);
-    if (valid) flags |= f;
-    return w;
+    if (tt < l0) return *reinterpret_cast<const uint4*>(cp + L.tail_row(b, h, s, tt % G) + 16 * (4 * ks + g));
+    const int r = min(tt - l0, a.T - 1);
+    return *reinterpret_cast<const uint4*>(sp + (long long)r * L.Hkv * kD + 8 * (4 * ks + g));
   };
   b8v av[2][4];
+  {
+    SigMask m[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const SigMask m = masks_v<ABL>(idr, hdr, 4 * ks + g);
+    for (int ks = 0; ks < 4; ++ks) m[ks] = masks_v<ABL>(idr, hdr, 4 * ks + g);
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 raw[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) av[mb][ks] = sign8(load(mb, ks), m);
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) raw[mb][ks] = row(mb, ks, src, a.cache);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) av[mb][ks] = sign8(raw[mb][ks], m[ks]);
   }
   float p[2][8][4];
   f4v w4[2][8];
   float st = rotate_squares_v<ABL>(idr, av, hf, w4, p, c, sh.xt[sub]);
   int sx_own = 0;
   if (__any(!rotation_stands(idr, st)))
-    st = rotate_checked<ABL>(idr, load, hdr, hf, av, w4, p, g, c, flags, sx_own, sh.xt[sub]);
+    st = rotate_checked<ABL>(
+        idr,
+        [&](int mb, int ks) {
+          // a fresh read each time: the compiler must not keep the first pass's registers for it
+          const uint16_t* sp = src;
+          const uint8_t* cp = a.cache;
+          asm volatile("" : "+v"(sp), "+v"(cp));
+          return row(mb, ks, sp, cp);
+        },
+        hdr, hf, av, w4, p, g, c, flags, sx_own, sh.xt[sub]);
   tile_finish<NW, false, ABL>(av, hf, w4, p, st, sx_own, lane, sub, s, L.n_it, L.variant, L.bits, sh, flags, nullptr,
                               nullptr, 0);
   if (valid) {
@@ -306,20 +324,20 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tokens(const TokensArgs& a, hipStream_t st) {
-  const int tpw = 4 / (a.L.G / 32);
   if (a.jobs > 0) {
-    const dim3 grid((unsigned)((a.jobs + tpw - 1) / tpw));
+    // one tile job per work-group of G/32 waves, as in the prefill
+    const dim3 grid((unsigned)a.jobs);
     const bool abl = a.L.variant != 0 || a.L.bits != 2;  // the extended build
     if (a.L.G == 32) {
       if (abl)
-        hipLaunchKernelGGL((tokens_tile_kernel<1, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((tokens_tile_kernel<1, true>), grid, dim3(64), 0, st, a);
       else
-        hipLaunchKernelGGL((tokens_tile_kernel<1, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((tokens_tile_kernel<1, false>), grid, dim3(64), 0, st, a);
     } else {
       if (abl)
-        hipLaunchKernelGGL((tokens_tile_kernel<2, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((tokens_tile_kernel<2, true>), grid, dim3(128), 0, st, a);
       else
-        hipLaunchKernelGGL((tokens_tile_kernel<2, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((tokens_tile_kernel<2, false>), grid, dim3(128), 0, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
