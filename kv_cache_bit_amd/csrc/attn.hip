@@ -255,8 +255,22 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) o[0][k] = o[1][k] = 0.0f;
 
-  for (int tile = t0 + wave; tile < t1; tile += 4) {
-    const long long roff = record_at(a.cache, L, b, h, tile, 0);
+  // paged cache: the page map entries of this wave's tiles t0 + wave + 4 i, lane i holding
+  // entry i (64 at a time), so that no tile waits on a map read before its record loads
+  const int32_t* pmap = reinterpret_cast<const int32_t*>(a.cache + L.map_off) + (long long)b * L.tiles;
+  int page_i = -1;
+  for (int tile = t0 + wave, it = 0; tile < t1; tile += 4, ++it) {
+    long long roff;
+    if (L.num_pages == 0) {
+      roff = L.record_seq(b, h, tile, 0);
+    } else {
+      if ((it & 63) == 0) {
+        const int tl = tile + 4 * lane;
+        page_i = tl < t1 ? pmap[tl] : -1;
+      }
+      const int page = __builtin_amdgcn_readlane(page_i, it & 63);
+      roff = (page < 0 || page >= L.num_pages) ? -1 : L.page_record(page, h, 0);
+    }
     if (roff < 0) continue;  // paged cache, no page for this tile: its tokens are left out
     const uint8_t* rk = a.cache + roff;
     const uint8_t* rv = rk + L.tr;
