@@ -924,7 +924,7 @@ __device__ __forceinline__ void emit_codes(const f4v (&acc)[2][8], const float (
 // its scale at 1 (the other pass then repeats the same sums every iteration). The
 // centered reading of "variance" runs its own loop (centered_varn).
 template <int NW, bool DBG, bool ABL>
-__device__ void tile_finish(const b8v (&av)[2][4], const Frags& hf, f4v (&acc)[2][8], float (&p)[2][8][4],
+__device__ __forceinline__ void tile_finish(const b8v (&av)[2][4], const Frags& hf, f4v (&acc)[2][8], float (&p)[2][8][4],
                             float st_own, int sx_own, int lane,
                             int sub, int stream, int n_it, int var, int bits_in, TileLds<NW>& sh, uint32_t& flags,
                             float* dbg_w, float* dbg_y, long long dstride) {
