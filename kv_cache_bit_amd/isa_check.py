@@ -1,9 +1,11 @@
-"""Check the gfx950 assembly of libkvarn for MFMA operand aliasing.
+"""Check the gfx950 assembly of libkvarn for MFMA operand aliasing, scratch and calls.
 
 An MFMA whose destination registers overlap its A or B source registers computes
 wrong results on gfx950 (rows read after the first pass see the partial output).
 The compiler may allocate such a destination when a source dies at that MFMA; the
 kernels keep their sources alive, and this check verifies it on the generated code.
+It also refuses any function that uses scratch memory or calls another: the kernels
+keep their state in registers and LDS.
 
 Usage: python -m kv_cache_bit_amd.isa_check   (compiles the device code to assembly in a temp dir)
 """
@@ -50,6 +52,23 @@ def check_asm(text: str) -> list[str]:
     return bad
 
 
+def check_resources(text: str) -> list[str]:
+    """Functions of the generated code that use scratch memory or call other functions:
+    every kernel of the library keeps its state in registers and LDS (a device function
+    called for real passes its arrays through scratch, at a heavy cost per tile)."""
+    bad = []
+    fn = "?"
+    for line in text.splitlines():
+        s = line.strip()
+        if s.endswith(":") and not s.startswith(".") and not s.startswith(";"):
+            fn = s[:-1]
+        if s.startswith("s_swappc") or s.startswith("s_setpc"):
+            bad.append(f"{fn}: call ({s.split()[0]})")
+        if s.startswith("; ScratchSize:") and s.split(":")[1].strip() not in ("0", "0 bytes/lane"):
+            bad.append(f"{fn}: {s[2:]}")
+    return bad
+
+
 def device_asm(src: str, defines: tuple, tmp: str) -> str:
     """The gfx950 assembly of one source, as the library build compiles it."""
     out = os.path.join(tmp, src + ".s")
@@ -77,6 +96,10 @@ def main() -> int:
     bad = [b for t in texts for b in check_asm(t)]
     for b in bad:
         print("MFMA destination overlaps a source:", b)
+    res = [b for t in texts for b in check_resources(t)]
+    for b in res:
+        print("scratch memory or a call:", b)
+    bad += res
     print("isa_check:", "FAIL" if bad else "ok")
     return 1 if bad else 0
 
