@@ -1,7 +1,8 @@
 """GPU parity on token rows at the edges of the input range, inside tiles of ordinary
 outlier-bearing rows: all-zero rows, small rows (1e-6, 2^-22), and rows whose squares
 would underflow fp32 (1e-30, and bf16 subnormals around 2^-128), which the kernels route
-through the checked rotation with a per-token power-of-two scale. The first token-axis
+through the checked rotation with a per-token power-of-two scale; prefill, single-token
+appends and multi-token appends in uneven chunks write the same bytes. The first token-axis
 pass of VarN takes its sums from the Gram diagonal (exact products of the inputs on the
 matrix cores); with one iteration those sums fix the token scale r directly. Run on an
 MI355X: pytest -m gpu.
@@ -15,6 +16,18 @@ from kv_cache_bit_amd import synth
 from parity import GpuCache, check_prefill, from_u16, gpu_prefill
 
 pytestmark = pytest.mark.gpu
+
+
+def chunked_appends(gc, kd, vd, T, G):
+    """The T tokens through kvarn_append_tokens in uneven chunks from an emptied cache, so
+    that completed groups mix tokens stored in the tail with new input rows."""
+    t = 0
+    for n in (5, G - 2, T):
+        n = min(n, T - t)
+        if n == 0:
+            break
+        K.kvarn_append_tokens(gc.g, gc.buf, kd[:, t:t + n].contiguous(), vd[:, t:t + n].contiguous(), n)
+        t += n
 
 
 def edge_rows_kv(seed, B, T, H, span):
@@ -51,6 +64,12 @@ def test_prefill_zero_and_tiny_token_rows(G, n_it):
     ha, hb = gc.host_cache(), ap.host_cache()
     m = ha.defined_mask()
     assert np.array_equal(ha.buf[m], hb.buf[m])
+    # and through multi-token appends in uneven chunks
+    ch = GpuCache(B, H, cap, G, n_it)
+    gpu_prefill(ch, k, v, 0)
+    chunked_appends(ch, kd, vd, T, G)
+    assert np.array_equal(ha.buf[m], ch.host_cache().buf[m])
+    assert K.kvarn_cache_flags(ch.buf) == K.kvarn_cache_flags(gc.buf)
 
 
 @pytest.mark.parametrize("G", [32, 64])
@@ -81,3 +100,9 @@ def test_non_finite_inputs(G):
     ha, hb = gc.host_cache(), ap.host_cache()
     m = ha.defined_mask()
     assert np.array_equal(ha.buf[m], hb.buf[m])
+    # and through multi-token appends in uneven chunks
+    ch = GpuCache(B, H, cap, G, 3)
+    gpu_prefill(ch, k, v, 0)
+    chunked_appends(ch, kd, vd, T, G)
+    assert K.kvarn_cache_flags(ch.buf) == want
+    assert np.array_equal(ha.buf[m], ch.host_cache().buf[m])
