@@ -43,6 +43,13 @@ __device__ __forceinline__ void cvt2f(uint32_t plane, float& lo, float& hi) {
   lo = v[0];
   hi = v[1];
 }
+// The same for plane B of 4-bit codes, worth 4x: scale 8 turns the e2m1 value q_B/2 into 4 q_B.
+template <int BY>
+__device__ __forceinline__ void cvt2f8(uint32_t plane, float& lo, float& hi) {
+  const f2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(plane, 8.0f, BY);
+  lo = v[0];
+  hi = v[1];
+}
 
 // Butterfly stage across lanes in one v_fmac_f32_dpp per element: a <- a + m * a(partner),
 // m = +1 where the lane's stage bit is clear and -1 where it is set. A set lane then holds
@@ -107,8 +114,9 @@ __device__ __forceinline__ void fwht16(float (&a)[16]) {
 
 // ----------------------------------------------------------------------------- dequantize
 // One wave per 32-token block of one (b, h, s): undo grid and scales, rotate back.
-// TWO: the 2-bit path, with a lane layout that follows each stream's code layout (below);
-// otherwise the general path for 2-, 3- and 4-bit codes.
+// FAST (2 or 4): the path with a lane layout that follows each stream's code layout
+// (below), for 2-bit codes and for 4-bit ones, whose plane B repeats the 2-bit layout;
+// FAST = 0: the general path for 2-, 3- and 4-bit codes (taken by 3-bit ones).
 // bf16 K rows of a 2-bit block staged in LDS: 32 tokens x 64 dwords, dword column c of
 // token row t at t * 64 + (c ^ 8 ((t / 4) % 8)): the lanes of one write (8 token quads x 8
 // words) hit 64 distinct banks, and the XOR keeps each aligned 4-dword group together for
@@ -116,8 +124,10 @@ __device__ __forceinline__ void fwht16(float (&a)[16]) {
 constexpr int kKRow = 64;
 __device__ __forceinline__ int kst_col(int t, int c) { return c ^ (8 * ((t >> 2) & 7)); }
 
-template <bool TWO>
+template <int FAST>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  constexpr bool TWO = FAST != 0;  // the code-layout path
+  constexpr bool PB = FAST == 4;   // with plane B (4-bit codes: q = q_A + 4 q_B)
   __shared__ uint32_t kst[TWO ? 4 : 1][TWO ? 32 * kKRow : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: job math on the SALU
   const int lane = threadIdx.x & 63;
@@ -169,7 +179,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   } else if (TWO && tile < nfull) {
     const uint8_t* rec = a.cache + roff;
     const int G = L.G;
-    const int ro = G * kD / 4, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
+    const int ro = G * kD * FAST / 8, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
+    const uint8_t* recb = rec + G * kD / 4;  // plane B (PB)
     const bool idr = (L.variant & KVARN_VARIANT_NO_ROTATION) != 0;  // uniform
     const float kf = idr ? 1.0f : kInvSqrtD;
     const int tb0 = (blk * 32) % G;  // first token of the block inside the tile
@@ -183,9 +194,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       // 1..3 = w on the lane (3 stages across lanes).
       const int w = relabel_t(cg & 7), tq = 2 * rg + (cg >> 3);
       const int tb = tb0 + 4 * tq;
-      uint32_t x[4];
+      uint32_t x[4], xb[PB ? 4 : 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const uint32_t*>(rec + (tb + i) * 32 + 4 * w);
+      if constexpr (PB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[i] = *reinterpret_cast<const uint32_t*>(recb + (tb + i) * 32 + 4 * w);
+      }
       const uint2 rw = *reinterpret_cast<const uint2*>(rec + ro + 2 * tb);
       float cs[16], cz[16];  // c s and c z of channel 16 nb + 2 w + d at [2 nb + d]
 #pragma unroll
@@ -212,6 +227,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         cvt2f<2>(o, v[i][10], v[i][11]);
         cvt2f<3>(e, v[i][12], v[i][13]);
         cvt2f<3>(o, v[i][14], v[i][15]);
+        if constexpr (PB) {  // the code q_A + 4 q_B (exact): plane B converted with scale 8
+          const uint32_t eb = xb[i] & kNib2, ob = (xb[i] >> 2) & kNib2;
+          float u[16];
+          cvt2f8<0>(eb, u[0], u[1]);
+          cvt2f8<0>(ob, u[2], u[3]);
+          cvt2f8<1>(eb, u[4], u[5]);
+          cvt2f8<1>(ob, u[6], u[7]);
+          cvt2f8<2>(eb, u[8], u[9]);
+          cvt2f8<2>(ob, u[10], u[11]);
+          cvt2f8<3>(eb, u[12], u[13]);
+          cvt2f8<3>(ob, u[14], u[15]);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) v[i][k] += u[k];
+        }
 #pragma unroll
         for (int k = 0; k < 16; ++k) v[i][k] = fmaf(v[i][k], cs[k], cz[k]);
         if (!idr) fwht16(v[i]);
@@ -300,6 +329,26 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         cvt2f<2>(o, w8[1][2 * k + 1], w8[3][2 * k + 1]);
         cvt2f<3>(e, w8[4][2 * k + 1], w8[6][2 * k + 1]);
         cvt2f<3>(o, w8[5][2 * k + 1], w8[7][2 * k + 1]);
+        if constexpr (PB) {  // + 4 q_B: the same nibble-plane bytes of plane B, scale 8
+          const uint32_t lb = *reinterpret_cast<const uint16_t*>(recb + (8 * cb + 2 * k) * (G / 4) + tw0 / 4);
+          const uint32_t hb = *reinterpret_cast<const uint16_t*>(recb + (8 * cb + 2 * k + 1) * (G / 4) + tw0 / 4);
+          const uint32_t xb2 = lb | (hb << 16);
+          const uint32_t eb = xb2 & kNib2, ob = (xb2 >> 2) & kNib2;
+          float u[16];  // token i of channel 2k at u[i], of channel 2k + 1 at u[8 + i]
+          cvt2f8<0>(eb, u[0], u[2]);
+          cvt2f8<0>(ob, u[1], u[3]);
+          cvt2f8<1>(eb, u[4], u[6]);
+          cvt2f8<1>(ob, u[5], u[7]);
+          cvt2f8<2>(eb, u[8], u[10]);
+          cvt2f8<2>(ob, u[9], u[11]);
+          cvt2f8<3>(eb, u[12], u[14]);
+          cvt2f8<3>(ob, u[13], u[15]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            w8[i][2 * k] += u[i];
+            w8[i][2 * k + 1] += u[8 + i];
+          }
+        }
       }
       float csj[8], czj[8];
 #pragma unroll
@@ -530,9 +579,11 @@ hipError_t launch_set_pages(const SetPagesArgs& a, hipStream_t st) {
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.jobs + 3) / 4));
   if (a.L.bits == 2)
-    hipLaunchKernelGGL(dequant_kernel<true>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(dequant_kernel<2>, grid, dim3(256), 0, st, a);
+  else if (a.L.bits == 4)
+    hipLaunchKernelGGL(dequant_kernel<4>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(dequant_kernel<false>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(dequant_kernel<0>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -629,8 +629,8 @@ struct TileLds {
 // the partials of the NW waves through LDS in wave order. own[q] is channel
 // 16 (4q + g) + c. The trailing barrier lets the next call reuse the LDS slots.
 template <int NW, typename Op>
-__device__ __forceinline__ void chan_reduce(const float (&v)[8], float (&own)[2], TileLds<NW>& sh, int g,
-                                            int c, int sub, float (*red)[kD], Op op) {
+__device__ __forceinline__ void chan_reduce(const float (&v)[8], float (&own)[2], int g, int c, int sub,
+                                            float (*red)[kD], Op op) {
   col_rs8(v, own, op);
   if constexpr (NW > 1) {
 #pragma unroll
@@ -706,8 +706,8 @@ __device__ void centered_varn(const b8v (&av)[2][4], const Frags& hf, bool idr, 
         s2[nb] = b;
       }
       float m1[2], m2[2];
-      chan_reduce<NW>(s1, m1, sh, g, c, sub, sh.red_a, OpAdd());
-      chan_reduce<NW>(s2, m2, sh, g, c, sub, sh.red_b, OpAdd());
+      chan_reduce<NW>(s1, m1, g, c, sub, sh.red_a, OpAdd());
+      chan_reduce<NW>(s2, m2, g, c, sub, sh.red_b, OpAdd());
       float icn[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -974,7 +974,7 @@ __device__ __forceinline__ void tile_finish(const b8v (&av)[2][4], const Frags& 
           for (int i = 0; i < 4; ++i) t = fmaf(p[mb][nb][i], v[4 * mb + i], t);
         cp[nb] = t;
       }
-      chan_reduce<NW>(cp, s_ch, sh, g, c, sub, sh.red_a, OpAdd());
+      chan_reduce<NW>(cp, s_ch, g, c, sub, sh.red_a, OpAdd());
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (s_ch[q] > 0.0f) u_own[q] = (float)G * __builtin_amdgcn_rcpf(s_ch[q]);
@@ -1045,8 +1045,8 @@ __device__ __forceinline__ void tile_finish(const b8v (&av)[2][4], const Frags& 
     mxl[nb] = hi;
   }
   float mn_own[2], mx_own[2];
-  chan_reduce<NW>(mnl, mn_own, sh, g, c, sub, sh.red_a, OpMin());
-  chan_reduce<NW>(mxl, mx_own, sh, g, c, sub, sh.red_b, OpMax());
+  chan_reduce<NW>(mnl, mn_own, g, c, sub, sh.red_a, OpMin());
+  chan_reduce<NW>(mxl, mx_own, g, c, sub, sh.red_b, OpMax());
   float s16_own[2], z16_own[2], al_own[2], ga_own[2];
   bool need_clamp_own = false;
 #pragma unroll
