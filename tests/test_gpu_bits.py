@@ -59,15 +59,20 @@ def test_dequantize_bits_parity(bits, G):
     gc = GpuCache(B, H, 256, G, 3, bits=bits)
     gpu_prefill(gc, k, v, T)
     kr, vr = R.dequantize(gc.host_cache(), maxT)
-    ko = torch.full((B, maxT, H, 128), 7.0, device="cuda")
-    vo = torch.full((B, maxT, H, 128), 7.0, device="cuda")
-    K.kvarn_dequantize(gc.g, gc.buf, ko, vo, maxT, K.KVARN_OUT_F32)
-    torch.cuda.synchronize()
-    for got, ref in ((ko, kr), (vo, vr)):
-        g = got.cpu().numpy().astype(np.float64)
-        rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
-        assert np.all(np.abs(g - ref) <= 1e-5 * np.maximum(rms, 1e-30) + 1e-30)
-        assert np.all(g[:, T:] == 0)
+    for dt in (K.KVARN_OUT_F32, K.KVARN_OUT_BF16):
+        tdt = torch.float32 if dt == K.KVARN_OUT_F32 else torch.bfloat16
+        ko = torch.full((B, maxT, H, 128), 7.0, dtype=tdt, device="cuda")
+        vo = torch.full((B, maxT, H, 128), 7.0, dtype=tdt, device="cuda")
+        K.kvarn_dequantize(gc.g, gc.buf, ko, vo, maxT, dt)
+        torch.cuda.synchronize()
+        for got, ref in ((ko, kr), (vo, vr)):
+            g = got.float().cpu().numpy().astype(np.float64)
+            rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+            if dt == K.KVARN_OUT_F32:
+                assert np.all(np.abs(g - ref) <= 1e-5 * np.maximum(rms, 1e-30) + 1e-30)
+            else:  # one bf16 rounding of a value that already carries the fp32 error
+                assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) * 1.01 + 1e-5 * rms + 1e-30)
+            assert np.all(g[:, T:] == 0)
 
 
 @pytest.mark.parametrize("bits", [3, 4])
