@@ -1,5 +1,6 @@
 """3- and 4-bit codes on the GPU against the oracle, through the C ABI: the prefill parity
-chain with the fp32 intermediates, append equal to prefill, dequantization, decode
+chain with the fp32 intermediates, append equal to prefill, the multi-layer call equal to
+per-layer calls, dequantization, decode
 attention (plain and fused), a paged cache, and the reconstruction error falling with the
 width.
 """
@@ -48,6 +49,30 @@ def test_append_equals_prefill_bits(bits, G):
     ha, hb = a.host_cache(), b.host_cache()
     m = ha.defined_mask()
     assert np.array_equal(m, hb.defined_mask()) and np.array_equal(ha.buf[m], hb.buf[m])
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("G", [32, 64])
+def test_prefill_layers_bits(bits, G):
+    """kvarn_quantize_prefill_layers over 3 caches of 3- or 4-bit codes writes the bytes and
+    flags of 3 kvarn_quantize_prefill calls; the first layer also goes through the chain."""
+    T, n = 2 * G + 9, 3
+    say("prefill layers bits", bits, G, T)
+    B, H = 2, 2
+    ins = [synth.kv_host(60 + i, B, T, H) for i in range(n)]
+    a = [GpuCache(B, H, 4 * G, G, 3, seed_sigma=i, bits=bits) for i in range(n)]
+    b = [GpuCache(B, H, 4 * G, G, 3, seed_sigma=i, bits=bits) for i in range(n)]
+    for i in range(n):
+        gpu_prefill(a[i], ins[i][0], ins[i][1], T)
+    K.kvarn_quantize_prefill_layers(b[0].g, [c.buf for c in b], [from_u16(k) for k, _ in ins],
+                                    [from_u16(v) for _, v in ins], T)
+    torch.cuda.synchronize()
+    for i in range(n):
+        ha, hb = a[i].host_cache(), b[i].host_cache()
+        m = ha.defined_mask()
+        assert np.array_equal(ha.buf[m], hb.buf[m]), i
+        assert K.kvarn_cache_flags(a[i].buf) == K.kvarn_cache_flags(b[i].buf), i
+    check_prefill(b[0], ins[0][0], ins[0][1], T)
 
 
 @pytest.mark.parametrize("bits", [3, 4])
