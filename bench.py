@@ -351,7 +351,7 @@ def bench_roundtrip(K, synth, torch, steps, warmup=2, layers=36, B=8, T=16384, H
         "prefill": {"kernel": f"prefill_kernel<2,false,{'false' if bits == 2 else 'true'},1>",
                     "avg_launch_us": round(pf_avg * 1e3, 2), "bytes_per_launch": bytes_in + bytes_rec,
                     "achieved": round(pf_gbs, 1), "frac": round(pf_gbs / HBM_PEAK_GBS, 4), "unit": "GB/s"},
-        "dequantize": {"kernel": f"dequant_kernel<{bits if bits != 3 else 0}> (bf16 out)",
+        "dequantize": {"kernel": f"dequant_kernel<{bits}> (bf16 out)",
                        "avg_launch_us": round(dq_avg * 1e3, 2),
                        "bytes_per_launch": bytes_rec + bytes_in, "bytes_read": bytes_rec, "bytes_written": bytes_in,
                        "achieved": round(dq_gbs, 1), "frac": round(dq_gbs / HBM_PEAK_GBS, 4), "unit": "GB/s"},

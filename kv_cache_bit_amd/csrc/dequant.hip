@@ -4,12 +4,12 @@
 // Dequantization undoes the grid and both VarN scales (ai-paper-analysis page,
 // section 3.2: the grouped scales are restored at dequantization) and rotates back
 // by H_D^T = H_syl diag(sigma) / sqrt(D) (section 3.1). One wave per 32-token block of one
-// stream. The 2-bit path lays the lanes out after each stream's code layout: K lanes hold
-// one code word (16 channels) of 4 tokens, V lanes 8 channels of 8 tokens; codes become
-// fp32 through the packed fp4 conversion, the inverse Walsh-Hadamard transform runs as
+// stream. The lanes are laid out after each stream's code layout: K lanes hold one code
+// word (16 channels) of 4 tokens, V lanes 8 channels of 8 tokens; codes become fp32
+// through the packed fp4 conversion (3- and 4-bit codes add plane B, brought into the
+// same nibble planes by shifts and masks), the inverse Walsh-Hadamard transform runs as
 // butterfly stages in registers plus fused DPP stages across lanes, and K's bf16 rows pass
-// through LDS so that both streams store whole 256-byte token rows. The general path (3-
-// and 4-bit codes) keeps lane = 16 rg + cg on tokens 8 rg + i and channels 8 cg + e.
+// through LDS so that both streams store whole 256-byte token rows.
 #include "kvarn_common.h"
 #include "kvarn_launch.h"
 
@@ -34,6 +34,7 @@ __device__ __forceinline__ void widen8_bf16(const uint4 w, float (&x)[8]) {
 
 // ----------------------------------------------------------------------------- 2-bit helpers
 constexpr uint32_t kNib2 = 0x33333333u;  // bits 0..1 of every nibble
+constexpr uint32_t kBit1 = 0x11111111u;  // bit 0 of every nibble
 
 // Two codes from byte BY of a nibble plane as fp32: a 2-bit code zero-extended to a nibble
 // is the e2m1 value q/2, which the packed fp4 conversion with scale 2 turns into q.
@@ -114,9 +115,8 @@ __device__ __forceinline__ void fwht16(float (&a)[16]) {
 
 // ----------------------------------------------------------------------------- dequantize
 // One wave per 32-token block of one (b, h, s): undo grid and scales, rotate back.
-// FAST (2 or 4): the path with a lane layout that follows each stream's code layout
-// (below), for 2-bit codes and for 4-bit ones, whose plane B repeats the 2-bit layout;
-// FAST = 0: the general path for 2-, 3- and 4-bit codes (taken by 3-bit ones).
+// BITS 2, 3 or 4. Plane A (bits 0..1 of every code) has the 2-bit layout; plane B of
+// 4-bit codes repeats it, plane B of 3-bit codes is the 1-bit layout (include/kvarn.h).
 // bf16 K rows of a 2-bit block staged in LDS: 32 tokens x 64 dwords, dword column c of
 // token row t at t * 64 + (c ^ 8 ((t / 4) % 8)): the lanes of one write (8 token quads x 8
 // words) hit 64 distinct banks, and the XOR keeps each aligned 4-dword group together for
@@ -124,11 +124,10 @@ __device__ __forceinline__ void fwht16(float (&a)[16]) {
 constexpr int kKRow = 64;
 __device__ __forceinline__ int kst_col(int t, int c) { return c ^ (8 * ((t >> 2) & 7)); }
 
-template <int FAST>
+template <int BITS>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
-  constexpr bool TWO = FAST != 0;  // the code-layout path
-  constexpr bool PB = FAST == 4;   // with plane B (4-bit codes: q = q_A + 4 q_B)
-  __shared__ uint32_t kst[TWO ? 4 : 1][TWO ? 32 * kKRow : 1];
+  constexpr bool PB = BITS > 2;  // with plane B: q = q_A + 4 q_B
+  __shared__ uint32_t kst[4][32 * kKRow];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: job math on the SALU
   const int lane = threadIdx.x & 63;
   const int rg = lane >> 4, cg = lane & 15;
@@ -176,11 +175,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     const float zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 8; ++i) store_row(blk * 32 + rg * 8 + i, zero, nosign);
-  } else if (TWO && tile < nfull) {
+  } else if (tile < nfull) {
     const uint8_t* rec = a.cache + roff;
     const int G = L.G;
-    const int ro = G * kD * FAST / 8, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
-    const uint8_t* recb = rec + G * kD / 4;  // plane B (PB)
+    const int ro = G * kD * BITS / 8, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
+    const uint8_t* recb = rec + G * kD / 4;  // plane B
     const bool idr = (L.variant & KVARN_VARIANT_NO_ROTATION) != 0;  // uniform
     const float kf = idr ? 1.0f : kInvSqrtD;
     const int tb0 = (blk * 32) % G;  // first token of the block inside the tile
@@ -197,9 +196,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       uint32_t x[4], xb[PB ? 4 : 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const uint32_t*>(rec + (tb + i) * 32 + 4 * w);
-      if constexpr (PB) {
+      if constexpr (BITS == 4) {  // word w of the token's plane B
 #pragma unroll
         for (int i = 0; i < 4; ++i) xb[i] = *reinterpret_cast<const uint32_t*>(recb + (tb + i) * 32 + 4 * w);
+      } else if constexpr (BITS == 3) {
+        // one 1-bit word per pair of 2-bit words (w = 2 p + r): the bits of slots 2 n and
+        // 2 n + 1 of word w sit at 4 n + 2 r and 4 n + 2 r + 1
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xb[i] = *reinterpret_cast<const uint32_t*>(recb + (tb + i) * 16 + 4 * (w >> 1)) >> (2 * (w & 1));
       }
       const uint2 rw = *reinterpret_cast<const uint2*>(rec + ro + 2 * tb);
       float cs[16], cz[16];  // c s and c z of channel 16 nb + 2 w + d at [2 nb + d]
@@ -228,7 +233,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         cvt2f<3>(e, v[i][12], v[i][13]);
         cvt2f<3>(o, v[i][14], v[i][15]);
         if constexpr (PB) {  // the code q_A + 4 q_B (exact): plane B converted with scale 8
-          const uint32_t eb = xb[i] & kNib2, ob = (xb[i] >> 2) & kNib2;
+          const uint32_t eb = BITS == 4 ? xb[i] & kNib2 : xb[i] & kBit1;
+          const uint32_t ob = BITS == 4 ? (xb[i] >> 2) & kNib2 : (xb[i] >> 1) & kBit1;
           float u[16];
           cvt2f8<0>(eb, u[0], u[1]);
           cvt2f8<0>(ob, u[2], u[3]);
@@ -329,11 +335,27 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         cvt2f<2>(o, w8[1][2 * k + 1], w8[3][2 * k + 1]);
         cvt2f<3>(e, w8[4][2 * k + 1], w8[6][2 * k + 1]);
         cvt2f<3>(o, w8[5][2 * k + 1], w8[7][2 * k + 1]);
-        if constexpr (PB) {  // + 4 q_B: the same nibble-plane bytes of plane B, scale 8
-          const uint32_t lb = *reinterpret_cast<const uint16_t*>(recb + (8 * cb + 2 * k) * (G / 4) + tw0 / 4);
-          const uint32_t hb = *reinterpret_cast<const uint16_t*>(recb + (8 * cb + 2 * k + 1) * (G / 4) + tw0 / 4);
-          const uint32_t xb2 = lb | (hb << 16);
-          const uint32_t eb = xb2 & kNib2, ob = (xb2 >> 2) & kNib2;
+        if constexpr (PB) {  // + 4 q_B, in the same nibble planes as e and o, scale 8
+          uint32_t eb, ob;
+          if constexpr (BITS == 4) {
+            const uint32_t lb = *reinterpret_cast<const uint16_t*>(recb + (8 * cb + 2 * k) * (G / 4) + tw0 / 4);
+            const uint32_t hb =
+                *reinterpret_cast<const uint16_t*>(recb + (8 * cb + 2 * k + 1) * (G / 4) + tw0 / 4);
+            const uint32_t xb2 = lb | (hb << 16);
+            eb = xb2 & kNib2;
+            ob = (xb2 >> 2) & kNib2;
+          } else {
+            // channel 16 cbk + cc (cbk = 4 hh + 2 ip + ii): the bits of its tokens 8 o + 2 n
+            // and 8 o + 2 n + 1 are bits 4 (n + 4 hh) + 2 ii (+1) of 1-bit word
+            // (16 ip + cc) G/8 + o; channels 2k and 2k + 1 of this lane share cbk
+            const int c0 = 8 * cb + 2 * k, cbk = c0 >> 4, cc = c0 & 15;
+            const int sh = 16 * (cbk >> 2) + 2 * (cbk & 1);
+            const uint8_t* wp = recb + 4 * ((16 * ((cbk >> 1) & 1) + cc) * (G / 8) + tw0 / 8);
+            const uint32_t y0 = *reinterpret_cast<const uint32_t*>(wp) >> sh;
+            const uint32_t y1 = *reinterpret_cast<const uint32_t*>(wp + 4 * (G / 8)) >> sh;
+            eb = (y0 & 0x1111u) | ((y1 & 0x1111u) << 16);
+            ob = ((y0 >> 1) & 0x1111u) | (((y1 >> 1) & 0x1111u) << 16);
+          }
           float u[16];  // token i of channel 2k at u[i], of channel 2k + 1 at u[8 + i]
           cvt2f8<0>(eb, u[0], u[2]);
           cvt2f8<0>(ob, u[1], u[3]);
@@ -400,112 +422,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
           store8f(reinterpret_cast<float*>(outp) + off, z);
         }
       }
-    }
-  } else if (!TWO && tile < nfull) {
-    const uint8_t* rec = a.cache + roff;
-    const int G = L.G;
-    const int ro = G * kD * L.bits / 8, co = ro + 2 * G, so = co + 2 * kD, zo = so + 2 * kD;
-    const int tw0 = (blk * 32) % G + rg * 8;
-    float cj[8], sj[8], zj[8], ri[8];
-    widen8_f16(*reinterpret_cast<const uint4*>(rec + co + 16 * cg), cj);
-    widen8_f16(*reinterpret_cast<const uint4*>(rec + so + 16 * cg), sj);
-    widen8_f16(*reinterpret_cast<const uint4*>(rec + zo + 16 * cg), zj);
-    widen8_f16(*reinterpret_cast<const uint4*>(rec + ro + 2 * tw0), ri);
-    float w[8][8];
-    if (s == 0) {
-      // channel j = 8cg + e = 16m + 2w + d (m = cg/2, w = 4(cg%2) + e/2, d = e%2) sits in
-      // word w at slot 4(m/2) + m%2 + 2d
-      const int sbase = 2 * (4 * (cg >> 2) + ((cg >> 1) & 1));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 q4 = *reinterpret_cast<const uint4*>(rec + (tw0 + i) * 32 + 16 * (cg & 1));
-        const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[i][e] = (float)((qw[e >> 1] >> (sbase + 4 * (e & 1))) & 3u);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t hq = *reinterpret_cast<const uint16_t*>(rec + (8 * cg + e) * (G / 4) + tw0 / 4);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i][e] = (float)((hq >> (2 * i)) & 3u);
-      }
-    }
-    // plane B of 3- and 4-bit codes (the code is plane A + 4 * plane B)
-    const uint8_t* pb = rec + G * kD / 4;
-    if (L.bits == 4) {  // the 2-bit layout again
-      if (s == 0) {
-        const int sbase = 2 * (4 * (cg >> 2) + ((cg >> 1) & 1));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 q4 = *reinterpret_cast<const uint4*>(pb + (tw0 + i) * 32 + 16 * (cg & 1));
-          const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) w[i][e] += 4.0f * (float)((qw[e >> 1] >> (sbase + 4 * (e & 1))) & 3u);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t hq = *reinterpret_cast<const uint16_t*>(pb + (8 * cg + e) * (G / 4) + tw0 / 4);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) w[i][e] += 4.0f * (float)((hq >> (2 * i)) & 3u);
-        }
-      }
-    } else if (L.bits == 3) {  // the 1-bit layout
-      if (s == 0) {
-        // channel 8cg + e: 2-bit word wd = 4(cg%2) + e/2, slot k = 4(m/2) + m%2 + 2(e%2) with
-        // m = cg/2; its bit: word wd/2 of the token's four, bit 4(k/2) + k%2 + 2(wd%2)
-        const int m = cg >> 1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 q4 = *reinterpret_cast<const uint4*>(pb + (tw0 + i) * 16);
-          const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int wd = 4 * (cg & 1) + (e >> 1), k = 4 * (m >> 1) + (m & 1) + 2 * (e & 1);
-            const int bit = 4 * (k >> 1) + (k & 1) + 2 * (wd & 1);
-            w[i][e] += 4.0f * (float)((qw[wd >> 1] >> bit) & 1u);
-          }
-        }
-      } else {
-        // token t = 8o + 2n + par of channel 16 blk + c (blk = i4 + 4hh, i4 = 2ip + ii): word
-        // (16 ip + c) G/8 + o, bit 4(n + 4hh) + par + 2ii; this lane's 8 tokens are one octet
-        const int blk = cg >> 1, i4 = blk & 3, hh = blk >> 2, ip = i4 >> 1, ii = i4 & 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int cc = 8 * (cg & 1) + e;
-          const uint32_t word = *reinterpret_cast<const uint32_t*>(pb + 4 * ((16 * ip + cc) * (G / 8) + tw0 / 8));
-#pragma unroll
-          for (int i = 0; i < 8; ++i) w[i][e] += 4.0f * (float)((word >> (4 * ((i >> 1) + 4 * hh) + (i & 1) + 2 * ii)) & 1u);
-        }
-      }
-    }
-    // x = r (c s q + c z) H_syl^T diag(sigma) / sqrt(D): the per-channel factors take
-    // 1/sqrt(D) (the transform is linear), sigma is a sign flip at the store
-    const bool idr = (L.variant & KVARN_VARIANT_NO_ROTATION) != 0;  // uniform
-    const float kf = idr ? 1.0f : kInvSqrtD;
-    float csj[8], czj[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      csj[e] = cj[e] * sj[e] * kf;
-      czj[e] = cj[e] * zj[e] * kf;
-    }
-    uint32_t sgn[4] = {0u, 0u, 0u, 0u};
-    if (!idr) {
-      const uint2 sw = *reinterpret_cast<const uint2*>(a.cache + kSigmaOff + 8 * cg);  // int8 sigma
-      const uint32_t sb[2] = {sw.x, sw.y};
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t x = sb[d >> 1] >> (16 * (d & 1));  // bytes: sigma of channels 2d, 2d + 1
-        sgn[d] = ((x << 8) & 0x8000u) | ((x << 16) & 0x80000000u);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w[i][e] = ri[i] * fmaf(csj[e], w[i][e], czj[e]);
-      if (!idr) fwht128(w[i], cg);
-      store_row(blk * 32 + rg * 8 + i, w[i], sgn);
     }
   } else {
 #pragma unroll
@@ -580,10 +496,10 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.jobs + 3) / 4));
   if (a.L.bits == 2)
     hipLaunchKernelGGL(dequant_kernel<2>, grid, dim3(256), 0, st, a);
-  else if (a.L.bits == 4)
-    hipLaunchKernelGGL(dequant_kernel<4>, grid, dim3(256), 0, st, a);
+  else if (a.L.bits == 3)
+    hipLaunchKernelGGL(dequant_kernel<3>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(dequant_kernel<0>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(dequant_kernel<4>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
