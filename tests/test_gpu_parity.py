@@ -10,7 +10,7 @@ from kv_cache_bit_amd import kvarn as K
 from kv_cache_bit_amd import synth
 from oracle import kvarn_ref as R
 
-from parity import GpuCache, check_attention, check_prefill, close_rowwise, from_u16, gpu_prefill, to_u16
+from parity import GpuCache, check_attention, check_prefill, from_u16, gpu_prefill, to_u16
 
 pytestmark = pytest.mark.gpu
 

@@ -8,7 +8,6 @@ from fractions import Fraction
 import math
 
 import numpy as np
-import pytest
 
 from oracle import kvarn_ref as R
 from kv_cache_bit_amd import synth

@@ -8,7 +8,6 @@ single-token appends, and a chunk appended to a prefilled cache must equal one p
 the whole sequence (appends are bit-identical to prefill).
 """
 import numpy as np
-import pytest
 
 from oracle import kvarn_ref as R
 from kv_cache_bit_amd import synth

@@ -2,7 +2,6 @@
 channel-axis variance normalization, repeated 2-3 times, Sinkhorn-Knopp like).
 """
 import numpy as np
-import pytest
 
 from oracle import kvarn_ref as R
 from kv_cache_bit_amd import synth
