@@ -28,9 +28,9 @@ def say(*a):
 
 
 class PagedCache(GpuCache):
-    def __init__(self, B, H, cap, G, n_it, num_pages, seed_sigma=0):
-        self.g = K.geom(B, H, cap, G, n_it, num_pages=num_pages)
-        self.og = R.Geom(B, H, 128, cap, G, n_it, 2, 0, num_pages)
+    def __init__(self, B, H, cap, G, n_it, num_pages, seed_sigma=0, bits=2):
+        self.g = K.geom(B, H, cap, G, n_it, bits=bits, num_pages=num_pages)
+        self.og = R.Geom(B, H, 128, cap, G, n_it, bits, 0, num_pages)
         self.sigma = synth.sign_vector(seed_sigma, 128)
         self.buf = K.alloc_cache(self.g, self.sigma)
 
@@ -106,9 +106,9 @@ def test_ragged_counts_and_mask():
     assert K.kvarn_cache_flags(gc.buf) & K.KVARN_FLAG_CAPACITY
 
 
-@pytest.mark.parametrize("G", [32, 64])
-def test_paged_equals_per_sequence_layout(G):
-    say("paged == per-sequence", G)
+@pytest.mark.parametrize("G,bits", [(32, 2), (64, 2), (32, 3), (64, 4)])
+def test_paged_equals_per_sequence_layout(G, bits):
+    say("paged == per-sequence", G, bits)
     B, H, Hq, n_it = 3, 2, 8, 2
     cap = 4 * G
     tiles = cap // G
@@ -118,8 +118,8 @@ def test_paged_equals_per_sequence_layout(G):
     T0, T1 = 2 * G - 3, 5
     k, v = synth.kv_host(83, B, T0 + T1 + 8, H)
     kd, vd = from_u16(k), from_u16(v)
-    flat = GpuCache(B, H, cap, G, n_it)
-    paged = PagedCache(B, H, cap, G, n_it, npages)
+    flat = GpuCache(B, H, cap, G, n_it, bits=bits)
+    paged = PagedCache(B, H, cap, G, n_it, npages, bits=bits)
     paged.set_pages(pages[:, :2])
     paged.set_pages(pages[:, 2:], tile_first=2)
     ws, n = K.alloc_workspace(flat.g, Hq)
