@@ -277,6 +277,9 @@ __device__ __forceinline__ uint4 scale8(const uint4 w, int e) {
 // pins it after the MFMAs, so every source is still live when each of them issues and
 // the register allocator cannot hand a source's registers to the result.
 __device__ __forceinline__ void h32_steps(const b8v (&a)[4], const Frags& hf, int h, f4v (&y)[4]) {
+  // the wave's priority is raised while it issues these MFMAs, so that they start while
+  // the other waves of the SIMD keep the VALU busy
+  __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     f4v t = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -284,6 +287,7 @@ __device__ __forceinline__ void h32_steps(const b8v (&a)[4], const Frags& hf, in
     asm volatile("" : "+v"(t) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(hf.v[0]), "v"(hf.v[2]));
     y[ks] = t;
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 // out[nb'] = sum_ks H_4[ks][nb'] y[ks], element by element
 __device__ __forceinline__ void h4_combine(const f4v (&y)[4], f4v (&out)[4]) {
