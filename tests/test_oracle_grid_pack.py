@@ -3,7 +3,7 @@
 Brute force: each code must be the nearest of the 4 levels z + s k (ties to even k).
 Recovery: the stored scales restore the pre-rounding tensor (ai-paper-analysis page,
 section 3.2: the grouped scales are undone at dequantization, nothing is lost).
-Layout: hand-computed bytes in tests/golden/layout_v2.txt.
+Layout: hand-computed bytes in tests/golden/layout_v3.txt.
 """
 import os
 
@@ -13,7 +13,7 @@ import pytest
 from oracle import kvarn_ref as R
 from kv_cache_bit_amd import synth
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "layout_v2.txt")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "layout_v3.txt")
 
 
 def brute_codes(y, s, z):
