@@ -213,7 +213,8 @@ KVARN_API kvarn_status kvarn_cache_set_pages(const kvarn_geom* g, void* cache, c
 /* Dequantize into k_out, v_out: device [B][max_tokens][Hkv][D], f32 or bf16 per
  * out_dtype. Tile tokens undo grid and scales and rotate back by H_D^T
  * (ai-paper-analysis page, section 3.2: the scaling is restored at
- * dequantization); tail tokens are copied; rows at or past len are zero. */
+ * dequantization); tail tokens are copied; rows at or past len are zero.
+ * 0 <= max_tokens <= capacity, else KVARN_ERR_RANGE; 0 is a no-op. */
 KVARN_API kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, void* k_out, void* v_out,
                               int32_t max_tokens, int32_t out_dtype, void* stream);
 

@@ -1,0 +1,102 @@
+"""GPU parity over seeded random geometries (run on an MI355X: pytest -m gpu).
+
+Each case draws batch, KV heads, query heads per KV head, group size, VarN iterations,
+code width, token law, prefill length and a number of decode appends from its own seed,
+then runs the whole path on the GPU against the oracle:
+
+  prefill(T)                    full parity chain (W/Y chain through the stored fields,
+                                codes, record bytes, bf16 tail)
+  T + n single-token appends    byte-identical to prefill(T + n) of the same tokens
+  decode attention              within 2e-3 of max |ref| (oracle over the same bytes)
+  dequantization (f32 out)      within 1e-5 of the row RMS, zeros past each length
+
+The geometries mix ragged tails, empty prefills, appends that complete one or more
+groups, GQA ratios 1..8 and every code width, so combinations the fixed-shape tests do
+not name are still checked against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_bit_amd import kvarn as K
+from kv_cache_bit_amd import synth
+from oracle import kvarn_ref as R
+
+from parity import GpuCache, check_attention, check_prefill, from_u16, gpu_prefill
+
+pytestmark = pytest.mark.gpu
+
+LAWS = ("lognormal", "spike", "student_t", "none")
+
+
+def draw(seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    G = int(rng.choice((32, 64)))
+    cfg = dict(
+        B=int(rng.integers(1, 4)),
+        H=int(rng.integers(1, 5)),
+        grp=int(rng.choice((1, 2, 3, 4, 5, 8))),
+        G=G,
+        n_it=int(rng.integers(0, 5)),
+        bits=int(rng.choice((2, 3, 4))),
+        law=str(rng.choice(LAWS)),
+        T=int(rng.integers(0, 5 * G + 18)),
+        n_app=int(rng.integers(1, G + 4)),
+    )
+    if rng.random() < 0.2:
+        cfg["T"] = 0  # an empty prefill, every token appended
+    law_kw = {"lognormal": {}, "spike": {"p": 0.05, "factor": 40.0}, "student_t": {"nu": 3.0}, "none": {}}
+    cfg["law_kw"] = law_kw[cfg["law"]]
+    return cfg
+
+
+SEEDS = list(range(40))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_geometry_path(seed):
+    c = draw(1000 + seed)
+    print("[case] random geometry", seed, {k: v for k, v in c.items() if k != "law_kw"}, flush=True)
+    B, H, G, T, n_app = c["B"], c["H"], c["G"], c["T"], c["n_app"]
+    total = T + n_app
+    cap = (total // G + 1) * G
+    k, v = synth.kv_host(synth.sub_seed(77, seed), B, total, H, law=c["law"], **c["law_kw"])
+
+    # prefill of the first T tokens
+    gc = GpuCache(B, H, cap, G, c["n_it"], seed_sigma=seed, bits=c["bits"])
+    gpu_prefill(gc, k, v, T)
+    check_prefill(gc, k, v, T)
+
+    # n single-token appends == one prefill of T + n tokens
+    kd, vd = from_u16(k), from_u16(v)
+    for t in range(T, total):
+        K.kvarn_append_decode(gc.g, gc.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+    ref = GpuCache(B, H, cap, G, c["n_it"], seed_sigma=seed, bits=c["bits"])
+    gpu_prefill(ref, k, v, total)
+    ha, hb = gc.host_cache(), ref.host_cache()
+    m = hb.defined_mask()
+    assert np.array_equal(ha.defined_mask(), m)
+    assert np.array_equal(ha.buf[m], hb.buf[m]), "appends differ from prefill"
+    assert np.all(ha.lens == total)
+
+    # decode attention over the appended cache
+    Hq = H * c["grp"]
+    q = synth.q_host(synth.sub_seed(78, seed), B, Hq)
+    ws, n = K.alloc_workspace(gc.g, Hq)
+    out = torch.full((B, Hq, 128), float("nan"), device="cuda")
+    K.kvarn_attn_decode(gc.g, gc.buf, from_u16(q), Hq, 0.0, 0, ws, n, out)
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy().astype(np.float64), ha, q, Hq)
+
+    # dequantization, f32 out, rows past the length where the capacity leaves room
+    maxT = min(total + 5, cap)
+    kr, vr = R.dequantize(ha, maxT)
+    ko = torch.full((B, maxT, H, 128), 7.0, dtype=torch.float32, device="cuda")
+    vo = torch.full((B, maxT, H, 128), 7.0, dtype=torch.float32, device="cuda")
+    K.kvarn_dequantize(gc.g, gc.buf, ko, vo, maxT, K.KVARN_OUT_F32)
+    torch.cuda.synchronize()
+    for got, want in ((ko, kr), (vo, vr)):
+        g = got.cpu().numpy().astype(np.float64)
+        rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
+        assert np.all(np.abs(g - want) <= 1e-5 * np.maximum(rms, 1e-30) + 1e-30)
+        assert np.all(g[:, total:] == 0)
