@@ -13,6 +13,14 @@ then runs the whole path on the GPU against the oracle:
 The geometries mix ragged tails, empty prefills, appends that complete one or more
 groups, GQA ratios 1..8 and every code width, so combinations the fixed-shape tests do
 not name are still checked against the oracle.
+
+A second sweep drives kvarn_append_tokens with ragged per-sequence counts over several
+calls, into a per-sequence cache and into a paged cache under a shuffled page map:
+
+  each sequence                 records and tail equal to a prefill of that sequence's
+                                own token stream, which passes the oracle parity chain
+  paged against per-sequence    stored bytes, attention and dequantization bit-equal
+  attention, dequantization     against the oracle over the stored bytes
 """
 import numpy as np
 import pytest
@@ -23,6 +31,7 @@ from kv_cache_bit_amd import synth
 from oracle import kvarn_ref as R
 
 from parity import GpuCache, check_attention, check_prefill, from_u16, gpu_prefill
+from test_gpu_paged import PagedCache, same_stored
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +109,91 @@ def test_random_geometry_path(seed):
         rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
         assert np.all(np.abs(g - want) <= 1e-5 * np.maximum(rms, 1e-30) + 1e-30)
         assert np.all(g[:, total:] == 0)
+
+
+def check_dequant(gc, hc, maxT, lens):
+    """f32 dequantization of gc against the oracle over hc: 1e-5 of the row RMS, zeros past
+    each sequence's length. Returns the device outputs."""
+    B, H = gc.og.batch, gc.og.num_kv_heads
+    kr, vr = R.dequantize(hc, maxT)
+    ko = torch.full((B, maxT, H, 128), 7.0, dtype=torch.float32, device="cuda")
+    vo = torch.full((B, maxT, H, 128), 7.0, dtype=torch.float32, device="cuda")
+    K.kvarn_dequantize(gc.g, gc.buf, ko, vo, maxT, K.KVARN_OUT_F32)
+    torch.cuda.synchronize()
+    for got, want in ((ko, kr), (vo, vr)):
+        g = got.cpu().numpy().astype(np.float64)
+        rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
+        assert np.all(np.abs(g - want) <= 1e-5 * np.maximum(rms, 1e-30) + 1e-30)
+        for b in range(B):
+            assert np.all(g[b, lens[b]:] == 0)
+    return ko, vo
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_chunked_paged(seed):
+    c = draw(5000 + seed)
+    rng = np.random.Generator(np.random.PCG64(6000 + seed))
+    B, H, G, bits, n_it = c["B"], c["H"], c["G"], c["bits"], c["n_it"]
+    calls = int(rng.integers(2, 6))
+    counts = rng.integers(0, 2 * G + 8, size=(calls, B)).astype(np.int32)
+    counts[rng.random((calls, B)) < 0.2] = 0  # sequences left out of a call
+    lens = counts.sum(axis=0)
+    cap = (int(lens.max()) // G + 2) * G
+    print("[case] random chunked/paged", seed, {k: v for k, v in c.items() if k not in ("law_kw", "T", "n_app")},
+          "counts", counts.tolist(), "cap", cap, flush=True)
+    tiles = cap // G
+    npages = B * tiles + int(rng.integers(0, 5))
+    pages = rng.permutation(npages)[:B * tiles].reshape(B, tiles).astype(np.int32)
+
+    flat = GpuCache(B, H, cap, G, n_it, seed_sigma=seed, bits=bits)
+    paged = PagedCache(B, H, cap, G, n_it, npages, seed_sigma=seed, bits=bits)
+    paged.set_pages(pages)
+    streams = [[[], []] for _ in range(B)]  # per sequence: K rows, V rows (uint16 [H][D] each)
+    for i in range(calls):
+        n = int(counts[i].max())
+        k, v = synth.kv_host(synth.sub_seed(79, seed, i), B, max(n, 1), H, law=c["law"], **c["law_kw"])
+        for b in range(B):
+            streams[b][0].extend(k[b, :counts[i, b]])
+            streams[b][1].extend(v[b, :counts[i, b]])
+        cnt = torch.from_numpy(counts[i].copy()).cuda()
+        kd, vd = from_u16(k[:, :n]), from_u16(v[:, :n])
+        for gc in (flat, paged):
+            K.kvarn_append_tokens(gc.g, gc.buf, kd, vd, n, cnt)
+    torch.cuda.synchronize()
+    hf, hp = flat.host_cache(), paged.host_cache()
+    assert np.array_equal(hf.lens[:, 0, 0], lens)
+    same_stored(hf, hp)
+    assert np.array_equal(hp.page_map, pages)
+    assert K.kvarn_cache_flags(flat.buf) & (K.KVARN_FLAG_CAPACITY | K.KVARN_FLAG_UNMAPPED) == 0
+    assert K.kvarn_cache_flags(paged.buf) & (K.KVARN_FLAG_CAPACITY | K.KVARN_FLAG_UNMAPPED) == 0
+
+    # every sequence: the bytes of a prefill of its own stream, which passes the oracle chain
+    for b in range(B):
+        T = int(lens[b])
+        one = GpuCache(B, H, cap, G, n_it, seed_sigma=seed, bits=bits)
+        ks = np.zeros((B, max(T, 1), H, 128), np.uint16)
+        vs = np.zeros((B, max(T, 1), H, 128), np.uint16)
+        if T:
+            ks[:] = np.stack(streams[b][0])[None]
+            vs[:] = np.stack(streams[b][1])[None]
+        gpu_prefill(one, ks, vs, T)
+        same_stored(one.host_cache(), hf, seqs=[b])
+        if b == 0:
+            check_prefill(one, ks, vs, T)
+
+    # attention and dequantization: paged bit-equal to per-sequence, both against the oracle
+    Hq = H * c["grp"]
+    q = synth.q_host(synth.sub_seed(80, seed), B, Hq)
+    ws, n = K.alloc_workspace(flat.g, Hq)
+    outs = []
+    for gc in (flat, paged):
+        out = torch.full((B, Hq, 128), float("nan"), device="cuda")
+        K.kvarn_attn_decode(gc.g, gc.buf, from_u16(q), Hq, 0.0, 0, ws, n, out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+    check_attention(outs[0].numpy().astype(np.float64), hf, q, Hq)
+    maxT = min(int(lens.max()) + 3, cap)
+    kf, vf = check_dequant(flat, hf, maxT, lens)
+    kp, vp = check_dequant(paged, hp, maxT, lens)
+    assert torch.equal(kf, kp) and torch.equal(vf, vp)
