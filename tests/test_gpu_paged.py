@@ -18,40 +18,13 @@ from kv_cache_bit_amd import kvarn as K
 from kv_cache_bit_amd import synth
 from oracle import kvarn_ref as R
 
-from parity import GpuCache, check_prefill, from_u16, gpu_prefill
+from parity import GpuCache, PagedCache, check_prefill, from_u16, gpu_prefill, same_stored
 
 pytestmark = pytest.mark.gpu
 
 
 def say(*a):
     print("[case]", *a, flush=True)
-
-
-class PagedCache(GpuCache):
-    def __init__(self, B, H, cap, G, n_it, num_pages, seed_sigma=0, bits=2):
-        self.g = K.geom(B, H, cap, G, n_it, bits=bits, num_pages=num_pages)
-        self.og = R.Geom(B, H, 128, cap, G, n_it, bits, 0, num_pages)
-        self.sigma = synth.sign_vector(seed_sigma, 128)
-        self.buf = K.alloc_cache(self.g, self.sigma)
-
-    def set_pages(self, pages, tile_first=0):
-        p = torch.from_numpy(np.ascontiguousarray(pages, dtype=np.int32)).cuda()
-        K.kvarn_cache_set_pages(self.g, self.buf, p, tile_first, p.shape[1])
-
-
-def same_stored(a: R.Cache, b: R.Cache, seqs=None):
-    """Equal lengths, and equal tail bytes and records of every stored tile."""
-    g = a.g
-    seqs = range(g.batch) if seqs is None else seqs
-    for bb in seqs:
-        assert np.array_equal(a.lens[bb], b.lens[bb]), bb
-        for h in range(g.num_kv_heads):
-            for s in range(2):
-                n = int(a.lens[bb, h, s])
-                for tile in range(n // g.group):
-                    ra, rb = a.record(bb, h, tile, s), b.record(bb, h, tile, s)
-                    assert ra is not None and rb is not None and np.array_equal(ra, rb), (bb, h, tile, s)
-                assert np.array_equal(a.tail(bb, h, s)[:n % g.group], b.tail(bb, h, s)[:n % g.group])
 
 
 @pytest.mark.parametrize("G,n_it,T1,T2", [(32, 3, 45, 50), (64, 2, 64, 130), (32, 3, 0, 77)])

@@ -30,8 +30,7 @@ from kv_cache_bit_amd import kvarn as K
 from kv_cache_bit_amd import synth
 from oracle import kvarn_ref as R
 
-from parity import GpuCache, check_attention, check_prefill, from_u16, gpu_prefill
-from test_gpu_paged import PagedCache, same_stored
+from parity import GpuCache, PagedCache, check_attention, check_prefill, from_u16, gpu_prefill, same_stored
 
 pytestmark = pytest.mark.gpu
 
