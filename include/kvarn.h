@@ -3,9 +3,9 @@
  *
  * C ABI. Plain pointers and sizes only. Device pointers are HIP device memory
  * owned by the caller; `stream` is a hipStream_t passed as void*. The library
- * never allocates or frees, keeps no global mutable state, enqueues all work on the
- * caller's stream, and synchronizes that stream only in kvarn_cache_init and
- * kvarn_cache_flags.
+ * never allocates or frees, enqueues all work on the caller's stream, and synchronizes
+ * that stream only in kvarn_cache_init and kvarn_cache_flags. Its only global mutable
+ * state is the device array behind kvarn_attn_decode_noalloc (below).
  *
  * Method (KVarN pages): each K/V token is rotated along head_dim by a randomized
  * Hadamard matrix H with H H^T = I (ai-paper-analysis page, section 3.1); VarN then
@@ -220,8 +220,10 @@ KVARN_API kvarn_status kvarn_dequantize(const kvarn_geom* g, const void* cache, 
 
 /* Workspace bytes kvarn_attn_decode and kvarn_append_attn_decode need for num_q_heads
  * query heads. Host only. The workspace holds one f32 partial (m, l, 2 pad, o[D]) per
- * (batch, query head, span), a span being 4 x tpw tiles with tpw in [2, 16] chosen from
- * the geometry alone, followed by one i32 per (batch, kv head) (padded to 16 bytes). */
+ * (batch, query head, span), followed by one i32 per (batch, kv head) (padded to 16
+ * bytes). The span count depends on the geometry alone (about 2048 work-groups of 4
+ * waves, each wave taking 2 to 16 tiles of a full sequence); a call cuts each
+ * sequence's full tiles into that many spans of equal size, or fewer for a short one. */
 KVARN_API kvarn_status kvarn_attn_workspace_bytes(const kvarn_geom* g, int32_t num_q_heads, size_t* bytes);
 
 /* Single-query decode attention over every cached token:
