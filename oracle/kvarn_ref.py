@@ -681,7 +681,7 @@ def stream_values(cache: Cache, b: int, h: int, s: int, rotated: bool = False, w
         u = unpack_record(rec, g.group, g.head_dim, s, g.bits)
         w = dequantize_tile(u["q"], u["r16"], u["c16"], u["s16"], u["z16"])
         out[tile * g.group:(tile + 1) * g.group] = w if rotated else undo_rotation(w, cache.sigma, g.variant)
-    tail = cache.tail_values(b, h, s)
+    tail = bf16_to_f64(cache.tail(b, h, s)[:n - nfull * g.group])  # the stored slots only
     for t in range(nfull * g.group, n):
         out[t] = apply_rotation(tail[t % g.group], cache.sigma, g.variant) if rotated else tail[t % g.group]
     return (out, present) if with_mask else out
