@@ -135,3 +135,32 @@ def test_scale_clamp_flag():
     t = R.quantize_tile(w, 3)
     assert t["flags"] & R.FLAG_SCALE_CLAMPED
     assert np.all(t["r16"] >= R.SCALE_MIN)
+
+
+def test_rank_one_tile_end_to_end_closed_form():
+    """The whole tile quantizer on a rank-one tile W = sgn * sqrt(alpha_t beta_j), with
+    both signs in every channel. From the closed form above: r16 = fp16(sqrt(alpha_t mean
+    beta)) and c16 = fp16(sqrt(beta_j / mean beta)); Y = W / (r16 c16) is +-1 up to the two
+    fp16 roundings, so each channel's grid spans [-1, 1]: z near -1, s near 2/(2^bits - 1),
+    and every code is 0 where sgn < 0 and the top level 2^bits - 1 where sgn > 0, far from
+    any rounding edge. Dequantization returns W to the grid's resolution."""
+    rng = np.random.default_rng(7)
+    alpha = rng.uniform(0.25, 40.0, 32)
+    beta = rng.uniform(0.05, 6.0, 128)
+    sgn = rng.choice([-1.0, 1.0], size=(32, 128))
+    sgn[0], sgn[1] = 1.0, -1.0  # both signs in every channel
+    w = sgn * np.sqrt(alpha[:, None] * beta[None, :])
+    r_cf = np.sqrt(alpha * beta.mean())
+    c_cf = np.sqrt(beta / beta.mean())
+    for bits in (2, 3, 4):
+        top = 2 ** bits - 1
+        t = R.quantize_tile(w, 3, 0, bits)
+        assert np.array_equal(t["r16"], R.fp16_round(r_cf))
+        assert np.array_equal(t["c16"], R.fp16_round(c_cf))
+        assert np.array_equal(t["q"], np.where(sgn > 0, top, 0))
+        # Y within 2^-9 of +-1 moves min and max by that much: a few fp16 ulps at most
+        assert np.all(np.abs(t["z16"] + 1.0) <= 2.0 ** -8)
+        assert np.all(np.abs(t["s16"] - 2.0 / top) <= 2.0 ** -8 * (2.0 / top) + 2.0 ** -11)
+        assert t["flags"] == 0
+        w_hat = R.dequantize_tile(t["q"], t["r16"], t["c16"], t["s16"], t["z16"])
+        assert np.all(np.abs(w_hat - w) <= 2.0 ** -7 * np.abs(w))
