@@ -21,6 +21,11 @@ calls, into a per-sequence cache and into a paged cache under a shuffled page ma
                                 own token stream, which passes the oracle parity chain
   paged against per-sequence    stored bytes, attention and dequantization bit-equal
   attention, dequantization     against the oracle over the stored bytes
+
+A third sweep runs fused decode steps (kvarn_append_attn_decode) across group
+boundaries: every step's output against the oracle's append_attn_decode on the same
+bytes, the cache byte-equal to plain appends, and kvarn_attn_decode_noalloc equal to
+kvarn_attn_decode on the final cache.
 """
 import numpy as np
 import pytest
@@ -196,3 +201,49 @@ def test_random_chunked_paged(seed):
     kf, vf = check_dequant(flat, hf, maxT, lens)
     kp, vp = check_dequant(paged, hp, maxT, lens)
     assert torch.equal(kf, kp) and torch.equal(vf, vp)
+
+
+def attn_close(got, ref, tol=2e-3):
+    for b in range(ref.shape[0]):
+        for g in range(ref.shape[1]):
+            m = np.abs(ref[b, g]).max()
+            d = np.abs(got[b, g] - ref[b, g]).max()
+            assert d <= tol * m or (m == 0 and d == 0), (b, g, d, m)
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_random_fused_steps(seed):
+    rng = np.random.Generator(np.random.PCG64(70000 + seed))
+    G = int(rng.choice((32, 64)))
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    grp, n_it, bits = int(rng.choice((1, 2, 3, 4, 8))), int(rng.integers(0, 5)), int(rng.choice((2, 3, 4)))
+    T0, steps = int(rng.integers(0, 4 * G)), int(rng.integers(G // 2, G + 6))
+    cap, Hq = ((T0 + steps) // G + 1) * G, H * grp
+    print("[case] random fused steps", seed, dict(B=B, H=H, grp=grp, G=G, n_it=n_it, bits=bits, T0=T0, steps=steps),
+          flush=True)
+    k, v = synth.kv_host(synth.sub_seed(71, seed), B, T0 + steps, H)
+    kd, vd = from_u16(k), from_u16(v)
+    fused = GpuCache(B, H, cap, G, n_it, seed_sigma=seed, bits=bits)
+    plain = GpuCache(B, H, cap, G, n_it, seed_sigma=seed, bits=bits)
+    for gc in (fused, plain):
+        gpu_prefill(gc, k, v, T0)
+    ws, n = K.alloc_workspace(fused.g, Hq)
+    out = torch.full((B, Hq, 128), float("nan"), device="cuda")
+    for t in range(T0, T0 + steps):
+        qb = synth.q_host(synth.sub_seed(72, seed, t), B, Hq)
+        ref = R.append_attn_decode(fused.host_cache(), k[:, t], v[:, t], qb, Hq, 0.0, 0)
+        K.kvarn_append_attn_decode(fused.g, fused.buf, kd[:, t].contiguous(), vd[:, t].contiguous(), from_u16(qb), Hq,
+                                   0.0, 0, ws, n, out)
+        K.kvarn_append_decode(plain.g, plain.buf, kd[:, t].contiguous(), vd[:, t].contiguous())
+        torch.cuda.synchronize()
+        attn_close(out.cpu().numpy().astype(np.float64), ref)
+    hf, hp = fused.host_cache(), plain.host_cache()
+    m = hf.defined_mask()
+    assert np.array_equal(m, hp.defined_mask()) and np.array_equal(hf.buf[m], hp.buf[m])
+    assert np.all(hf.lens == T0 + steps)
+    q = from_u16(synth.q_host(synth.sub_seed(73, seed), B, Hq))
+    o1, o2 = torch.empty(B, Hq, 128, device="cuda"), torch.empty(B, Hq, 128, device="cuda")
+    K.kvarn_attn_decode(fused.g, fused.buf, q, Hq, 0.0, 0, ws, n, o1)
+    K.kvarn_attn_decode_noalloc(fused.g, fused.buf, q, Hq, 0.0, 0, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
