@@ -514,18 +514,21 @@ def mix_ceiling(torch, bytes_in, bytes_out, layers=32, steps=10, grids=(1024, 20
     """The practical ceiling of a kernel with a given mix of reads and writes (the prefill's
     or the dequantizer's): a plain streaming kernel (libkvarn_bench.so) that reads `bytes_in`
     and writes `bytes_out` per launch, over `layers` distinct buffer pairs per step like the
-    benchmarked step; the best grid of a small sweep, timed with events over `steps` steps."""
+    benchmarked step; the best of a small sweep over grids and over plain or non-temporal
+    stores, timed with events over `steps` steps."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "kv_cache_bit_amd",
                                    "libkvarn_bench.so"))
-    f = lib.kvarn_bench_stream_mix
-    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
-    f.restype = ctypes.c_int
+    kernels = {"plain": lib.kvarn_bench_stream_mix, "nt_stores": lib.kvarn_bench_stream_mix_nt}
+    for f in kernels.values():
+        f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                      ctypes.c_void_p]
+        f.restype = ctypes.c_int
     ins = [torch.ones(bytes_in, dtype=torch.uint8, device="cuda") for _ in range(layers)]
     outs = [torch.empty(bytes_out, dtype=torch.uint8, device="cuda") for _ in range(layers)]
     st = torch.cuda.current_stream()
     best = None
-    for grid in grids:
+    for (kind, f), grid in [(kf, g) for kf in kernels.items() for g in grids]:
         def step():
             for l in range(layers):
                 assert f(ins[l].data_ptr(), bytes_in, outs[l].data_ptr(), bytes_out, grid, st.cuda_stream) == 0
@@ -540,7 +543,7 @@ def mix_ceiling(torch, bytes_in, bytes_out, layers=32, steps=10, grids=(1024, 20
         us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
         gbs = (bytes_in + bytes_out) / (us * 1e-6) / 1e9
         if best is None or gbs > best["GBps"]:
-            best = dict(GBps=round(gbs, 1), launch_us=round(us, 2), grid=grid)
+            best = dict(GBps=round(gbs, 1), launch_us=round(us, 2), grid=grid, stores=kind)
     del ins, outs
     torch.cuda.empty_cache()
     return dict(best, bytes_read=bytes_in, bytes_written=bytes_out,

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     // ---- loads
     uint2 kc[NMB];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) kc[mb] = *reinterpret_cast<const uint2*>(rk + krow[mb] * 32 + 8 * g);
+    for (int mb = 0; mb < NMB; ++mb) kc[mb] = ld_nt8(rk + krow[mb] * 32 + 8 * g);
     uint2 kcb[BITS > 2 ? NMB : 1];  // plane B: two 2-bit words (BITS 4) or one 1-bit word in .x
     if constexpr (BITS == 4) {
 #pragma unroll
@@ -296,16 +296,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     uint4 kr[NKB], vr[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      kr[kb] = *reinterpret_cast<const uint4*>(rk + RO + 2 * (32 * kb + 8 * g));
-      vr[kb] = *reinterpret_cast<const uint4*>(rv + RO + 2 * (32 * kb + 8 * g));
+      kr[kb] = ld_nt16(rk + RO + 2 * (32 * kb + 8 * g));
+      vr[kb] = ld_nt16(rv + RO + 2 * (32 * kb + 8 * g));
     }
     uint32_t vq[4][NKB];  // channel 16 i + c (low half) and 16 (i + 4) + c (high half)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(rv + (16 * i + c) * (G / 4) + 2 * (4 * kb + g));
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(rv + (16 * (i + 4) + c) * (G / 4) + 2 * (4 * kb + g));
+        const uint32_t lo =
+            __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rv + (16 * i + c) * (G / 4) + 2 * (4 * kb + g)));
+        const uint32_t hi = __builtin_nontemporal_load(
+            reinterpret_cast<const uint16_t*>(rv + (16 * (i + 4) + c) * (G / 4) + 2 * (4 * kb + g)));
         vq[i][kb] = lo | (hi << 16);
       }
     // plane B of V: BITS 4 as vq; BITS 3 one 1-bit word per channel pair {i, i + 1} (i even)

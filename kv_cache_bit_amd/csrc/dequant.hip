@@ -122,6 +122,7 @@ __device__ __forceinline__ void fwht16(float (&a)[16]) {
 // words) hit 64 distinct banks, and the XOR keeps each aligned 4-dword group together for
 // the 16-byte row reads. 32 KB per work-group of 4 waves.
 constexpr int kKRow = 64;
+
 __device__ __forceinline__ int kst_col(int t, int c) { return c ^ (8 * ((t >> 2) & 7)); }
 
 template <int BITS>
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         o[d] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){y[2 * d], y[2 * d + 1]}, bf2v)) ^ sgn[d];
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(outp) + off) = make_uint4(o[0], o[1], o[2], o[3]);
+      st_nt16(reinterpret_cast<uint16_t*>(outp) + off, make_uint4(o[0], o[1], o[2], o[3]));
     } else {
       float z[8];
 #pragma unroll
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         for (int i = 0; i < 8; ++i) {
           if (blk * 32 + rg * 8 + i >= a.maxT) continue;
           const uint4 row = *reinterpret_cast<const uint4*>(&tile_l[(8 * rg + i) * kKRow + kst_col(8 * rg + i, 4 * cg)]);
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(outp) + offr + i * rowstep) = row;
+          st_nt16(reinterpret_cast<uint16_t*>(outp) + offr + i * rowstep, row);
         }
       } else {
 #pragma unroll
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
           for (int d = 0; d < 4; ++d)
             o[d] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){w8[i][2 * d] * rk, w8[i][2 * d + 1] * rk},
                                                                        bf2v)) ^ sgn[d];
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(outp) + off) = make_uint4(o[0], o[1], o[2], o[3]);
+          st_nt16(reinterpret_cast<uint16_t*>(outp) + off, make_uint4(o[0], o[1], o[2], o[3]));
         } else {
           float z[8];
 #pragma unroll

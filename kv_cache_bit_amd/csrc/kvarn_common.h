@@ -267,6 +267,24 @@ __device__ __forceinline__ void load_sigma(const uint8_t* hdr, int cg, float (&s
   }
 }
 
+// Non-temporal 16-byte global accesses, for data a kernel streams exactly once (inputs
+// read once, outputs it never reads again): the hint keeps them from displacing cached
+// lines that are reused.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+  const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(x.x, x.y);
+}
+__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ void store8f(float* p, const float (&a)[8]) {
   reinterpret_cast<float4*>(p)[0] = make_float4(a[0], a[1], a[2], a[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(a[4], a[5], a[6], a[7]);

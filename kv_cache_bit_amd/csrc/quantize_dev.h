@@ -1110,7 +1110,7 @@ __device__ __forceinline__ void copy_record(const TileLds<NW>& sh, uint8_t* dst,
   const int n16 = tr / 16;
   const uint4* s = reinterpret_cast<const uint4*>(sh.rec);
   uint4* d = reinterpret_cast<uint4*>(dst);
-  for (int k = sub * 64 + lane; k < n16; k += 64 * NW) d[k] = s[k];
+  for (int k = sub * 64 + lane; k < n16; k += 64 * NW) st_nt16(d + k, s[k]);
 }
 
 __device__ __forceinline__ void raise_flags(uint8_t* hdr, uint32_t f) {
